@@ -1,0 +1,353 @@
+"""fp64 CPU oracle of the spectral hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and
+this package imports nothing from it: the two share only the seeded input
+generators.
+
+What it computes, each function citing the passage it follows:
+
+* :func:`covariance`      C = alpha * X^T X with no centring ("Random matrix
+  theory spectral methods" page, section 2.1: S = (1/n) X^T X; section 3.2 code:
+  C = H^T H / N), accumulated chunk by chunk by plain matrix addition (Swift-SVD
+  page, sections 2 and 7).
+* :func:`window_gram`     G_w = (1/N) H_w H_w^T for each full sliding window of
+  N steps (RMT page, section 3.1: the window H = [h_{t-N+1}..h_t]^T and its
+  covariance (1/N) H^T H, whose nonzero spectrum equals that of G_w).
+* :func:`band_gram`       <h_t, h_{t-j}> for 0 <= j < N, the only inner products
+  the windows use.
+* :func:`eigvalsh_small`  cyclic Jacobi (C, fp64), descending.
+* :func:`eigvalsh_large`  Householder tridiagonalisation + Sturm bisection.
+* :func:`mp_quantiles`    quantiles of the Marchenko-Pastur law (RMT page,
+  section 2.1) by Gauss-Legendre quadrature of the density.
+* :func:`descriptors`     spectral entropy, effective rank, leading mass,
+  eigengap, MP edge and outlier count, W1 distance to MP (RMT page, section
+  2.3), top-20 % energy share, tail level and small-sigma count (S3 page,
+  sections 1 and 2).
+
+All arithmetic is fp64.  bf16 inputs arrive as uint16 bit patterns and are
+widened exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so (no fast-math, portable ISA)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, dp, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_jacobi_eigvalsh.argtypes = [i64, dp, dp, ctypes.c_double, ctypes.c_int]
+        lib.oracle_jacobi_eigvalsh.restype = ctypes.c_int
+        lib.oracle_jacobi_batched.argtypes = [i64, i64, dp, dp, ip, ctypes.c_double, ctypes.c_int]
+        lib.oracle_jacobi_batched.restype = None
+        lib.oracle_householder_tridiag.argtypes = [i64, dp, dp, dp]
+        lib.oracle_householder_tridiag.restype = None
+        lib.oracle_tridiag_count_below.argtypes = [i64, dp, dp, ctypes.c_double, ctypes.c_double]
+        lib.oracle_tridiag_count_below.restype = i64
+        lib.oracle_tridiag_eigvals.argtypes = [i64, dp, dp, dp]
+        lib.oracle_tridiag_eigvals.restype = None
+        lib.oracle_ldlt_count_below.argtypes = [i64, dp, ctypes.c_double]
+        lib.oracle_ldlt_count_below.restype = i64
+        lib.oracle_eigvalsh_dense.argtypes = [i64, dp, dp]
+        lib.oracle_eigvalsh_dense.restype = None
+        _lib = lib
+    return _lib
+
+
+def _dp(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+# ---------------------------------------------------------------- inputs
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of an input given as f32 values or bf16 bit patterns."""
+    if dtype == "bf16":
+        b = np.ascontiguousarray(x, dtype=np.uint16)
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- aggregation
+
+def covariance(X: np.ndarray, dtype: str, alpha: float = 1.0, C0: np.ndarray | None = None,
+               beta: float = 0.0, row_block: int = 4096) -> np.ndarray:
+    """C = beta * C0 + alpha * X^T X in fp64, rows of X are samples, no centring.
+
+    The sum over rows is taken block by block, each block's X_b^T X_b added to
+    the running matrix: the incremental aggregation of the Swift-SVD page
+    (sections 2 and 7).  A matrix product serves as the step inside a block."""
+    n, d = X.shape
+    acc = np.zeros((d, d), dtype=np.float64)
+    for r0 in range(0, n, row_block):
+        xb = widen(X[r0:r0 + row_block], dtype)
+        acc += xb.T @ xb
+    C = alpha * acc
+    if beta != 0.0 and C0 is not None:
+        C = C + beta * np.asarray(C0, dtype=np.float64)
+    return C
+
+
+def band_gram(H: np.ndarray, dtype: str, N: int) -> np.ndarray:
+    """B[s, t, j] = <h_t, h_{t-j}> for 0 <= j < N (0 where t - j < 0), fp64.
+
+    H is [streams, T, d] (or [T, d])."""
+    h = widen(H, dtype)
+    if h.ndim == 2:
+        h = h[None]
+    S, T, d = h.shape
+    B = np.zeros((S, T, N), dtype=np.float64)
+    for j in range(min(N, T)):
+        B[:, j:, j] = np.einsum("std,std->st", h[:, j:, :], h[:, :T - j, :])
+    return B
+
+
+def window_gram(H: np.ndarray, dtype: str, N: int, windows=None, stride: int = 1) -> np.ndarray:
+    """Dense G_w = (1/N) H_w H_w^T for the full windows w (rows [w*stride, w*stride + N)).
+
+    H is [T, d] for one stream; ``windows`` selects window indices (default all
+    W = (T - N) // stride + 1 of them)."""
+    h = widen(H, dtype)
+    T = h.shape[0]
+    W = (T - N) // stride + 1
+    idx = range(W) if windows is None else windows
+    out = []
+    for w in idx:
+        hw = h[w * stride: w * stride + N]
+        out.append(hw @ hw.T / N)
+    return np.array(out, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- spectra
+
+def eigvalsh_small(A: np.ndarray, tol: float = 1e-15, max_sweeps: int = 100):
+    """Eigenvalues (descending) of one n x n or a batch [b, n, n] of symmetric
+    matrices by cyclic Jacobi; returns (w, sweeps)."""
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    single = A.ndim == 2
+    if single:
+        A = A[None]
+    b, n, _ = A.shape
+    w = np.empty((b, n), dtype=np.float64)
+    sw = np.empty(b, dtype=np.int32)
+    _load().oracle_jacobi_batched(b, n, _dp(A), _dp(w),
+                                  sw.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), tol, max_sweeps)
+    return (w[0], sw[0]) if single else (w, sw)
+
+
+def tridiagonalize(A: np.ndarray):
+    """(d, e) of the Householder tridiagonal form of the symmetric matrix A."""
+    M = np.array(A, dtype=np.float64, order="C", copy=True)
+    n = M.shape[0]
+    d = np.empty(n, dtype=np.float64)
+    e = np.empty(max(n - 1, 1), dtype=np.float64)
+    _load().oracle_householder_tridiag(n, _dp(M), _dp(d), _dp(e))
+    return d, e[: n - 1]
+
+
+def tridiag_eigvals(d: np.ndarray, e: np.ndarray) -> np.ndarray:
+    d = np.ascontiguousarray(d, dtype=np.float64)
+    e = np.ascontiguousarray(e if len(e) else np.zeros(1), dtype=np.float64)
+    w = np.empty(len(d), dtype=np.float64)
+    _load().oracle_tridiag_eigvals(len(d), _dp(d), _dp(e), _dp(w))
+    return w
+
+
+def tridiag_count_below(d: np.ndarray, e: np.ndarray, x: float) -> int:
+    d = np.ascontiguousarray(d, dtype=np.float64)
+    e = np.ascontiguousarray(e if len(e) else np.zeros(1), dtype=np.float64)
+    pivmin = max(1.0, float(np.max(e * e)) if len(e) else 1.0) * 1e-300
+    return int(_load().oracle_tridiag_count_below(len(d), _dp(d), _dp(e), float(x), pivmin))
+
+
+def eigvalsh_large(A: np.ndarray) -> np.ndarray:
+    """Eigenvalues (descending) of a dense symmetric matrix: Householder
+    tridiagonalisation, then bisection on Sturm counts.  Only the lower
+    triangle of A is read (it is mirrored first)."""
+    L = np.tril(np.asarray(A, dtype=np.float64))
+    M = np.ascontiguousarray(L + np.tril(L, -1).T)
+    n = M.shape[0]
+    w = np.empty(n, dtype=np.float64)
+    _load().oracle_eigvalsh_dense(n, _dp(M), _dp(w))
+    return w
+
+
+def count_below_dense(A: np.ndarray, x: float) -> int:
+    """#{lambda < x} of a dense symmetric matrix from the inertia of LDL^T(A - xI)."""
+    L = np.tril(np.asarray(A, dtype=np.float64))
+    M = np.ascontiguousarray(L + np.tril(L, -1).T)
+    return int(_load().oracle_ldlt_count_below(M.shape[0], _dp(M), float(x)))
+
+
+# ---------------------------------------------------------------- Marchenko-Pastur
+
+def mp_edges(sigma2: float, c: float):
+    """(lambda_minus, lambda_plus) = sigma^2 (1 -/+ sqrt(c))^2 (RMT page, section 2.1)."""
+    return sigma2 * (1.0 - math.sqrt(c)) ** 2, sigma2 * (1.0 + math.sqrt(c)) ** 2
+
+
+def mp_density(x, sigma2: float, c: float):
+    """rho(x) = sqrt((l+ - x)(x - l-)) / (2 pi sigma^2 c x) on [l-, l+] (RMT page, section 2.1)."""
+    lm, lp = mp_edges(sigma2, c)
+    x = np.asarray(x, dtype=np.float64)
+    inside = (x > lm) & (x < lp)
+    r = np.zeros_like(x)
+    xi = x[inside]
+    r[inside] = np.sqrt((lp - xi) * (xi - lm)) / (2.0 * math.pi * sigma2 * c * xi)
+    return r
+
+
+_GL = {}
+
+
+def _gauss_legendre(m: int):
+    if m not in _GL:
+        _GL[m] = np.polynomial.legendre.leggauss(m)
+    return _GL[m]
+
+
+def _mp_cdf_phi(phi, sigma2: float, c: float, nodes: int = 96) -> np.ndarray:
+    """F at lambda(phi) = m - h cos(phi), m = (l+ + l-)/2, h = (l+ - l-)/2.
+
+    In phi the measure rho(lambda) dlambda = h^2 sin^2(phi) / (2 pi sigma^2 c
+    lambda(phi)) dphi is smooth on [0, pi]; Gauss-Legendre on [0, phi]."""
+    lm, lp = mp_edges(sigma2, c)
+    m, h = 0.5 * (lp + lm), 0.5 * (lp - lm)
+    phi = np.atleast_1d(np.asarray(phi, dtype=np.float64))
+    t, wt = _gauss_legendre(nodes)
+    ph = 0.5 * phi[:, None] * (t[None, :] + 1.0)
+    lam = m - h * np.cos(ph)
+    f = h * h * np.sin(ph) ** 2 / (2.0 * math.pi * sigma2 * c * lam)
+    return 0.5 * phi * np.sum(wt[None, :] * f, axis=1)
+
+
+def mp_cdf(x: float, sigma2: float, c: float, nodes: int = 96) -> float:
+    """F(x) = integral of rho from lambda_minus to x, for 0 < c <= 1."""
+    lm, lp = mp_edges(sigma2, c)
+    if x <= lm:
+        return 0.0
+    if x >= lp:
+        return 1.0
+    m, h = 0.5 * (lp + lm), 0.5 * (lp - lm)
+    phi_x = math.acos(max(-1.0, min(1.0, (m - x) / h)))
+    return float(_mp_cdf_phi(phi_x, sigma2, c, nodes)[0])
+
+
+def mp_quantiles(sigma2: float, c: float, r: int, u=None) -> np.ndarray:
+    """Midpoint quantiles Q((i - 1/2)/r), i = 1..r, ascending (or Q(u) for the
+    given levels), for 0 < c <= 1: each by bisection in phi on [0, pi] until
+    the bracket stops shrinking, all levels side by side."""
+    lm, lp = mp_edges(sigma2, c)
+    m, h = 0.5 * (lp + lm), 0.5 * (lp - lm)
+    if u is None:
+        u = (np.arange(1, r + 1, dtype=np.float64) - 0.5) / r
+    u = np.atleast_1d(np.asarray(u, dtype=np.float64))
+    a = np.zeros_like(u)
+    b = np.full_like(u, math.pi)
+    for _ in range(64):
+        mid = 0.5 * (a + b)
+        below = _mp_cdf_phi(mid, sigma2, c) < u
+        a = np.where(below, mid, a)
+        b = np.where(below, b, mid)
+    return m - h * np.cos(0.5 * (a + b))
+
+
+def mp_quantile(u: float, sigma2: float, c: float) -> float:
+    return float(mp_quantiles(sigma2, c, 1, u=[u])[0])
+
+
+# ---------------------------------------------------------------- descriptors
+
+EIG, SINGULAR = 0, 1
+SIGMA2_GIVEN, SIGMA2_MEDIAN, SIGMA2_MEAN = 0, 1, 2
+
+
+def descriptors(w, *, mode: int = EIG, n_samples: int = 1, p_dim: int = 1, k: int = 1,
+                sigma2: float = 1.0, sigma2_mode: int = SIGMA2_GIVEN, top_frac: float = 0.2,
+                small_rel: float = 1e-2, tail_frac: float = 0.7, with_mp: bool = True) -> dict:
+    """Spectral descriptors of one spectrum ``w`` (eigenvalues of a covariance,
+    any order).  Negative round-off is clamped to zero first.
+
+    * S = sum(lambda); p_i = lambda_i / S
+    * H = -sum p_i ln p_i with 0 ln 0 = 0 (spectral entropy); erank = exp(H)
+    * m1 = lambda_1 / S (leading eigenvalue mass); g_k = lambda_k / lambda_{k+1}
+      (eigengap as a ratio); g1 = lambda_1 / lambda_2
+      -- RMT page, section 2.3
+    * c = p / n; lambda_plus = sigma^2 (1 + sqrt c)^2; n_above = #{lambda > lambda_plus}
+      -- RMT page, section 2.1
+    * mp_w1: W1 distance between the spectrum and the MP law, as the mean of
+      |mu_(i) - Q((i - 1/2)/r)| over the ascending spectrum; for p > n the
+      companion spectrum mu = (n/p) lambda with ratio n/p is used
+    * sigma_i = sqrt(lambda_i): top_energy = sum_{i<=floor(f r)} sigma_i^2 / sum sigma^2,
+      top_sigma_share the same with sigma_i; tail_head = sigma at rank
+      floor(0.7 r) + 1, tail_min = sigma_r; n_small = #{sigma_i < small_rel sigma_1}
+      -- S3 page, section 1 (the long-tail test) and section 2 (the count of
+      near-zero singular values)
+    """
+    lam = np.sort(np.maximum(np.asarray(w, dtype=np.float64), 0.0))[::-1]
+    r = lam.size
+    S = float(np.sum(lam))
+    out = {"S": S}
+    p = lam / S if S > 0 else np.full(r, np.nan)
+    nz = p > 0
+    H = float(-np.sum(p[nz] * np.log(p[nz]))) if S > 0 else float("nan")
+    out["H"] = H
+    out["erank"] = math.exp(H) if S > 0 else float("nan")
+    out["m1"] = float(lam[0] / S) if S > 0 else float("nan")
+    out["gk"] = float(lam[k - 1] / lam[k]) if (k < r and lam[k] > 0) else float("nan")
+    out["g1"] = float(lam[0] / lam[1]) if (r > 1 and lam[1] > 0) else float("nan")
+    if sigma2_mode == SIGMA2_MEDIAN:
+        s2 = float(np.median(lam))
+    elif sigma2_mode == SIGMA2_MEAN:
+        s2 = S / p_dim
+    else:
+        s2 = float(sigma2)
+    out["sigma2"] = s2
+    c = p_dim / n_samples
+    out["lambda_plus"] = s2 * (1.0 + math.sqrt(c)) ** 2
+    out["n_above"] = int(np.sum(lam > out["lambda_plus"]))
+    out["r_pos"] = int(np.sum(lam > 0))
+    if with_mp and s2 > 0:
+        if p_dim <= n_samples:
+            mu, cc = lam[::-1], c
+        else:
+            mu, cc = (n_samples / p_dim) * lam[::-1], n_samples / p_dim
+        q = mp_quantiles(s2, cc, r)
+        out["mp_w1"] = float(np.mean(np.abs(mu - q)))
+    else:
+        out["mp_w1"] = float("nan")
+    sig = np.sqrt(lam)
+    kt = int(math.floor(top_frac * r))
+    e2 = float(np.sum(sig * sig))
+    out["top_energy"] = float(np.sum(sig[:kt] ** 2) / e2) if e2 > 0 else float("nan")
+    s1 = float(np.sum(sig))
+    out["top_sigma_share"] = float(np.sum(sig[:kt]) / s1) if s1 > 0 else float("nan")
+    out["tail_head"] = float(sig[min(r - 1, int(math.floor(tail_frac * r)))])
+    out["tail_min"] = float(sig[-1])
+    out["sigma1"] = float(sig[0])
+    out["n_small"] = int(np.sum(sig < small_rel * sig[0]))
+    return out

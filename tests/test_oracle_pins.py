@@ -1,0 +1,309 @@
+"""Pins of the fp64 oracle against what the mathematics and the pages fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+closed form, an invariant, a textbook special case, a library routine on the
+same input, or brute force on a tiny input, chosen so that a dropped term, a
+wrong sign, a wrong index or a transposed operand in the oracle fails one of
+them.  No test here needs a GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+
+import oracle
+from weights_bf16_fp32_amd import synth
+
+
+def _sym(rng, n, scale=1.0):
+    a = rng.standard_normal((n, n)) * scale
+    return a + a.T
+
+
+# ------------------------------------------------------------- P1/P2 invariants
+
+@pytest.mark.parametrize("n,d", [(64, 32), (50, 7), (7, 50)])
+def test_trace_and_frobenius(n, d):
+    rng = np.random.default_rng(n * 100 + d)
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    alpha = 1.0 / n
+    C = oracle.covariance(X, "f32", alpha)
+    w = oracle.eigvalsh_large(C)
+    wj, _ = oracle.eigvalsh_small(C)
+    tr = alpha * float(np.sum(X.astype(np.float64) ** 2))  # alpha ||X||_F^2
+    for ev in (w, wj):
+        assert abs(ev.sum() - tr) <= 1e-12 * tr
+        fro2 = float(np.sum(C * C))
+        assert abs(np.sum(ev ** 2) - fro2) <= 1e-11 * fro2
+
+
+def test_covariance_brute_force():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((9, 5)).astype(np.float32)
+    C = oracle.covariance(X, "f32", 0.5, C0=np.eye(5), beta=2.0, row_block=4)
+    for i in range(5):
+        for j in range(5):
+            s = sum(float(X[r, i]) * float(X[r, j]) for r in range(9))
+            assert abs(C[i, j] - (0.5 * s + 2.0 * (i == j))) <= 1e-13
+
+
+def test_bf16_widening_and_rounding():
+    import torch
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(10000) * 10.0 ** rng.uniform(-5, 5, 10000)).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]  # exact ties
+    bits = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    wide = oracle.widen(bits, "bf16")
+    assert np.array_equal(wide, torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+# ------------------------------------------------------------- P3 library eigvalsh
+
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 30, 32, 64, 200])
+def test_eigensolvers_vs_lapack(n):
+    rng = np.random.default_rng(n)
+    A = _sym(rng, n)
+    ref = np.linalg.eigvalsh(A)[::-1]
+    lmax = max(1.0, np.max(np.abs(ref)))
+    w_large = oracle.eigvalsh_large(A)
+    assert np.max(np.abs(w_large - ref)) <= 1e-12 * lmax
+    if n <= 64:
+        w_small, sweeps = oracle.eigvalsh_small(A)
+        assert sweeps >= 0
+        assert np.max(np.abs(w_small - ref)) <= 1e-12 * lmax
+        # P11: both oracle eigensolvers agree
+        assert np.max(np.abs(w_small - w_large)) <= 1e-12 * lmax
+
+
+def test_eigensolvers_degenerate():
+    # repeated eigenvalues, rank deficiency, zero matrix, huge dynamic range
+    rng = np.random.default_rng(11)
+    Q, _ = np.linalg.qr(rng.standard_normal((40, 40)))
+    lam = np.array([5.0] * 10 + [1e-9] * 5 + [0.0] * 10 + list(np.logspace(-6, 6, 15)))
+    A = (Q * lam) @ Q.T
+    A = 0.5 * (A + A.T)
+    ref = np.sort(lam)[::-1]
+    for w in (oracle.eigvalsh_large(A), oracle.eigvalsh_small(A)[0]):
+        assert np.max(np.abs(w - ref)) <= 1e-9 * ref[0]
+    Z = np.zeros((8, 8))
+    assert np.all(np.abs(oracle.eigvalsh_large(Z)) <= 1e-290) and np.all(oracle.eigvalsh_small(Z)[0] == 0)
+
+
+def test_tridiagonal_form_is_similar():
+    rng = np.random.default_rng(4)
+    A = _sym(rng, 25)
+    d, e = oracle.tridiagonalize(A)
+    T = np.diag(d) + np.diag(e, 1) + np.diag(e, -1)
+    assert np.allclose(np.linalg.eigvalsh(T), np.linalg.eigvalsh(A), atol=1e-12)
+    # Sturm count against the eigenvalues of T from LAPACK
+    ev = scipy.linalg.eigvalsh_tridiagonal(d, e)
+    for x in [-5.0, 0.0, 0.3, 2.0, 10.0]:
+        assert oracle.tridiag_count_below(d, e, x) == int(np.sum(ev < x))
+
+
+# ------------------------------------------------------------- P4 Gram duality
+
+def test_window_gram_duality_and_band():
+    H = synth.eigentrack(streams=2, T=40, d=96)
+    N = 30
+    G = oracle.window_gram(H[1], "bf16", N)
+    assert G.shape == (40 - N + 1, N, N)
+    h = oracle.widen(H[1], "bf16")
+    for w in [0, 5, 10]:
+        hw = h[w:w + N]
+        cov = hw.T @ hw / N  # d x d covariance of the window
+        ev_cov = np.linalg.eigvalsh(cov)[::-1]
+        ev_g, _ = oracle.eigvalsh_small(G[w])
+        assert np.max(np.abs(ev_cov[:N] - ev_g)) <= 1e-11 * ev_g[0]
+        assert np.max(np.abs(ev_cov[N:])) <= 1e-11 * ev_g[0]
+    # band entries by brute-force dot products, and the window Gram from the band
+    B = oracle.band_gram(H, "bf16", N)
+    for (s, t, j) in [(0, 0, 0), (0, 39, 29), (1, 17, 3), (1, 29, 29), (1, 5, 9)]:
+        hs = oracle.widen(H[s], "bf16")
+        ref = sum(hs[t, k] * hs[t - j, k] for k in range(96)) if t - j >= 0 else 0.0
+        assert abs(B[s, t, j] - ref) <= 1e-12 * max(1.0, abs(ref))
+    for w in [0, 7, 10]:
+        for i in range(N):
+            for j in range(N):
+                assert abs(G[w, i, j] - B[1, w + max(i, j), abs(i - j)] / N) <= 1e-12 * G[w, 0, 0]
+
+
+# ------------------------------------------------------------- P5 MP bulk
+
+def test_mp_bulk_pure_noise():
+    rng = np.random.default_rng(21)
+    n, p = 4096, 1024
+    X = rng.standard_normal((n, p)).astype(np.float32)
+    C = oracle.covariance(X, "f32", 1.0 / n)
+    w = oracle.eigvalsh_large(C)
+    c = p / n
+    lm, lp = oracle.mp_edges(1.0, c)
+    sj = (math.sqrt(n - 1) + math.sqrt(p)) * (1 / math.sqrt(n - 1) + 1 / math.sqrt(p)) ** (1 / 3)
+    delta = 5 * sj / n
+    assert w.min() >= lm - delta and w.max() <= lp + delta
+    # Kolmogorov distance to F_MP
+    ws = np.sort(w)
+    F = np.array([oracle.mp_cdf(x, 1.0, c) for x in ws])
+    emp = np.arange(1, p + 1) / p
+    assert np.max(np.abs(F - emp)) < 0.02
+    # the W1 descriptor is small on pure noise and grows with a spike
+    d0 = oracle.descriptors(w, n_samples=n, p_dim=p)["mp_w1"]
+    assert d0 < 0.01
+    X2 = X + 3.0 * rng.standard_normal((n, 1)).astype(np.float32) @ np.ones((1, p), np.float32) / math.sqrt(p)
+    d1 = oracle.descriptors(oracle.eigvalsh_large(oracle.covariance(X2, "f32", 1.0 / n)),
+                            n_samples=n, p_dim=p)["mp_w1"]
+    assert d1 > d0
+
+
+# ------------------------------------------------------------- P6 BBP outliers
+
+def test_bbp_outliers_tiny_config():
+    X = synth.tiny()
+    C = oracle.covariance(X, "f32", 1.0 / 64)
+    w = oracle.eigvalsh_large(C)
+    D = oracle.descriptors(w, n_samples=64, p_dim=32, k=1)
+    assert abs(D["lambda_plus"] - (1 + math.sqrt(0.5)) ** 2) < 1e-15
+    assert D["n_above"] == 2  # the two planted spikes, both far above the edge
+
+
+def test_bbp_outlier_location():
+    # additive spike theta u u^T on sigma^2 = 1 noise; above sigma^2 sqrt(c) the top
+    # sample eigenvalue sits near (1 + theta)(1 + c / theta) (Baik-Silverstein, Paul 2007)
+    rng = np.random.default_rng(8)
+    n, p = 8000, 400
+    c = p / n
+    thetas = np.array([3.0, 1.0])
+    u, _ = np.linalg.qr(rng.standard_normal((p, 2)))
+    X = rng.standard_normal((n, p)) + (rng.standard_normal((n, 2)) * np.sqrt(thetas)) @ u.T
+    w = oracle.eigvalsh_large(oracle.covariance(X.astype(np.float32), "f32", 1.0 / n))
+    for i, th in enumerate(thetas):
+        pred = (1 + th) * (1 + c / th)
+        sd = math.sqrt(2.0 / n) * (1 + th) * math.sqrt(1 - c / th ** 2)
+        assert abs(w[i] - pred) < 5 * sd
+    lp = oracle.mp_edges(1.0, c)[1]
+    assert np.sum(w > lp) == 2
+
+
+# ------------------------------------------------------------- P7 descriptors
+
+def test_descriptors_diagonal_identity_rank1():
+    lam = np.array([4.0, 3.0, 2.0, 1.0, 0.0])
+    D = oracle.descriptors(lam[::-1], n_samples=10, p_dim=5, k=2)  # any input order
+    p = lam / 10.0
+    H = -sum(x * math.log(x) for x in p if x > 0)
+    assert abs(D["S"] - 10.0) < 1e-15 and abs(D["H"] - H) < 1e-15
+    assert abs(D["erank"] - math.exp(H)) < 1e-14
+    assert D["m1"] == 0.4 and D["gk"] == 1.5 and abs(D["g1"] - 4 / 3) < 1e-15
+    assert D["r_pos"] == 4
+    n = 37
+    Di = oracle.descriptors(np.ones(n), n_samples=1000, p_dim=n, k=3)
+    assert abs(Di["H"] - math.log(n)) < 1e-13 and abs(Di["m1"] - 1 / n) < 1e-15 and Di["gk"] == 1.0
+    Dr = oracle.descriptors(np.array([7.0] + [0.0] * 9), n_samples=100, p_dim=10, k=1)
+    assert Dr["H"] == 0.0 and Dr["m1"] == 1.0 and math.isnan(Dr["gk"])
+    # negative round-off is clamped before anything else
+    Dn = oracle.descriptors(np.array([2.0, 1.0, -1e-17]), n_samples=100, p_dim=3)
+    assert Dn["r_pos"] == 2 and Dn["tail_min"] == 0.0
+
+
+def test_descriptors_singular_mode_counts():
+    d = 4096
+    sig = synth.s3_sigma(d)
+    assert sig[0] == 1.0 and abs(sig[-1] - 1e-3) < 1e-15
+    assert np.min(np.abs(sig - 1e-2)) > 1e-5  # no tie at the small-sigma threshold
+    D = oracle.descriptors(sig ** 2, mode=oracle.SINGULAR, n_samples=d, p_dim=d)
+    assert D["n_small"] == int(np.sum(sig < 1e-2)) == d - 203
+    k = int(0.2 * d)
+    assert abs(D["top_energy"] - np.sum(sig[:k] ** 2) / np.sum(sig ** 2)) < 1e-14
+    assert abs(D["top_sigma_share"] - np.sum(sig[:k]) / np.sum(sig)) < 1e-14
+    assert D["tail_head"] == sig[int(0.7 * d)] and D["tail_min"] == sig[-1]
+
+
+@pytest.mark.parametrize("c", [0.01, 0.25, 0.5, 0.9, 1.0])
+def test_mp_law_moments_and_cdf(c):
+    s2 = 1.7
+    lm, lp = oracle.mp_edges(s2, c)
+    # total mass 1 (c <= 1), mean sigma^2, second moment sigma^4 (1 + c)
+    mass = scipy.integrate.quad(lambda x: oracle.mp_density([x], s2, c)[0], lm, lp, limit=200)[0]
+    assert abs(mass - 1.0) < 1e-6
+    assert abs(oracle.mp_cdf(lp * (1 - 1e-15), s2, c) - 1.0) < 1e-9
+    r = 2000
+    q = oracle.mp_quantiles(s2, c, r)
+    assert np.all(np.diff(q) > 0) and q[0] > lm and q[-1] < lp
+    assert abs(q.mean() - s2) < 2e-3 * s2
+    assert abs(np.mean(q ** 2) - s2 ** 2 * (1 + c)) < 5e-3 * s2 ** 2
+    # the quadrature CDF against adaptive quadrature of the printed density
+    for u in [0.1, 0.5, 0.9]:
+        x = oracle.mp_quantile(u, s2, c)
+        F = scipy.integrate.quad(lambda t: oracle.mp_density([t], s2, c)[0], lm, x, limit=200)[0]
+        assert abs(F - u) < 1e-7
+
+
+def test_w1_zero_on_quantiles():
+    r, c = 50, 0.3
+    q = oracle.mp_quantiles(1.0, c, r)
+    D = oracle.descriptors(q, n_samples=1000, p_dim=int(round(c * 1000)), k=1)
+    assert D["mp_w1"] < 1e-12
+    # companion form when p > n: eigenvalues lambda = (p/n) mu with mu ~ MP(n/p)
+    n, p = 30, 4096
+    qc = oracle.mp_quantiles(1.0, n / p, n)
+    Dc = oracle.descriptors(qc * p / n, n_samples=n, p_dim=p)
+    assert Dc["mp_w1"] < 1e-12
+
+
+# ------------------------------------------------------------- P8 brute-force SVD
+
+def test_singular_values_closed_form_2x2_and_svd():
+    a, b, c_, d = 3.0, 1.0, -2.0, 0.5
+    W = np.array([[a, b], [c_, d]], dtype=np.float32)
+    C = oracle.covariance(W, "f32", 1.0)
+    s = np.sqrt(np.maximum(oracle.eigvalsh_large(C), 0))
+    # closed form: s1 s2 = |det W|, s1^2 + s2^2 = ||W||_F^2
+    assert abs(s[0] * s[1] - abs(a * d - b * c_)) < 1e-13
+    assert abs(s[0] ** 2 + s[1] ** 2 - (a * a + b * b + c_ * c_ + d * d)) < 1e-13
+    rng = np.random.default_rng(9)
+    for m in (5, 33, 64):
+        W = rng.standard_normal((m + 3, m)).astype(np.float32)
+        s = np.sqrt(np.maximum(oracle.eigvalsh_small(oracle.covariance(W, "f32", 1.0))[0], 0))
+        ref = np.linalg.svd(W.astype(np.float64), compute_uv=False)
+        assert np.max(np.abs(s - ref)) < 1e-12 * ref[0]
+
+
+# ------------------------------------------------------------- P9 Weyl on the S3 layer
+
+def test_s3_weyl_bound_reduced():
+    d = 256
+    W64 = synth.s3_layer_f64(0, d)
+    W32 = W64.astype(np.float32)
+    planted = synth.s3_sigma(d)
+    s = np.sqrt(np.maximum(oracle.eigvalsh_large(oracle.covariance(W32, "f32", 1.0)), 0))
+    bound = np.linalg.norm(W32.astype(np.float64) - W64, 2)
+    # Weyl: |sigma_i(W32) - sigma_i(W64)| <= ||W32 - W64||_2; the Gram route adds
+    # fp64 rounding of order eps * sigma_1^2 / sigma_i on the smallest values
+    err = np.abs(s - planted)
+    assert np.all(err <= bound + 1e-12 / planted)
+
+
+# ------------------------------------------------------------- P10 inertia counts
+
+def test_inertia_counts_match_spectrum():
+    X = synth.tiny()
+    C = oracle.covariance(X, "f32", 1.0 / 64)
+    w = oracle.eigvalsh_large(C)
+    lp = oracle.mp_edges(1.0, 0.5)[1]
+    assert C.shape[0] - oracle.count_below_dense(C, lp) == int(np.sum(w > lp)) == 2
+    rng = np.random.default_rng(2)
+    A = _sym(rng, 120)
+    ev = np.linalg.eigvalsh(A)
+    for x in [-10.0, -1.0, 0.0, 2.5, 30.0]:
+        assert oracle.count_below_dense(A, x) == int(np.sum(ev < x))
+
+
+def test_jacobi_reports_non_convergence():
+    rng = np.random.default_rng(1)
+    A = _sym(rng, 30)
+    w, sweeps = oracle.eigvalsh_small(A, max_sweeps=1)
+    assert sweeps < 0
