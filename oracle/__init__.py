@@ -230,22 +230,29 @@ def _gauss_legendre(m: int):
     return _GL[m]
 
 
-def _mp_cdf_phi(phi, sigma2: float, c: float, nodes: int = 96) -> np.ndarray:
+def _mp_cdf_phi(phi, sigma2: float, c: float, nodes: int = 24) -> np.ndarray:
     """F at lambda(phi) = m - h cos(phi), m = (l+ + l-)/2, h = (l+ - l-)/2.
 
     In phi the measure rho(lambda) dlambda = h^2 sin^2(phi) / (2 pi sigma^2 c
-    lambda(phi)) dphi is smooth on [0, pi]; Gauss-Legendre on [0, phi]."""
+    lambda(phi)) dphi is smooth on [0, pi] but, for c close to 1, sharply
+    peaked near phi = 0 (lambda_minus -> 0); composite Gauss-Legendre on the
+    panels [0, 2^-20 phi], [2^-20 phi, 2^-19 phi], ..., [phi / 2, phi]."""
     lm, lp = mp_edges(sigma2, c)
     m, h = 0.5 * (lp + lm), 0.5 * (lp - lm)
     phi = np.atleast_1d(np.asarray(phi, dtype=np.float64))
     t, wt = _gauss_legendre(nodes)
-    ph = 0.5 * phi[:, None] * (t[None, :] + 1.0)
-    lam = m - h * np.cos(ph)
-    f = h * h * np.sin(ph) ** 2 / (2.0 * math.pi * sigma2 * c * lam)
-    return 0.5 * phi * np.sum(wt[None, :] * f, axis=1)
+    edges = np.concatenate([[0.0], 2.0 ** np.arange(-20, 1)])  # fractions of phi
+    total = np.zeros_like(phi)
+    for a, b in zip(edges[:-1], edges[1:]):
+        lo, hi = a * phi, b * phi
+        ph = 0.5 * (hi - lo)[:, None] * (t[None, :] + 1.0) + lo[:, None]
+        lam = lm + 2.0 * h * np.sin(0.5 * ph) ** 2  # = m - h cos(phi), no cancellation
+        f = h * h * np.sin(ph) ** 2 / (2.0 * math.pi * sigma2 * c * lam)
+        total += 0.5 * (hi - lo) * np.sum(wt[None, :] * f, axis=1)
+    return total
 
 
-def mp_cdf(x: float, sigma2: float, c: float, nodes: int = 96) -> float:
+def mp_cdf(x: float, sigma2: float, c: float, nodes: int = 24) -> float:
     """F(x) = integral of rho from lambda_minus to x, for 0 < c <= 1."""
     lm, lp = mp_edges(sigma2, c)
     if x <= lm:
@@ -257,10 +264,16 @@ def mp_cdf(x: float, sigma2: float, c: float, nodes: int = 96) -> float:
     return float(_mp_cdf_phi(phi_x, sigma2, c, nodes)[0])
 
 
+_QCACHE = {}
+
+
 def mp_quantiles(sigma2: float, c: float, r: int, u=None) -> np.ndarray:
     """Midpoint quantiles Q((i - 1/2)/r), i = 1..r, ascending (or Q(u) for the
     given levels), for 0 < c <= 1: each by bisection in phi on [0, pi] until
     the bracket stops shrinking, all levels side by side."""
+    key = (float(sigma2), float(c), int(r)) if u is None else None
+    if key is not None and key in _QCACHE:
+        return _QCACHE[key].copy()
     lm, lp = mp_edges(sigma2, c)
     m, h = 0.5 * (lp + lm), 0.5 * (lp - lm)
     if u is None:
@@ -273,7 +286,10 @@ def mp_quantiles(sigma2: float, c: float, r: int, u=None) -> np.ndarray:
         below = _mp_cdf_phi(mid, sigma2, c) < u
         a = np.where(below, mid, a)
         b = np.where(below, b, mid)
-    return m - h * np.cos(0.5 * (a + b))
+    q = lm + 2.0 * h * np.sin(0.25 * (a + b)) ** 2
+    if key is not None:
+        _QCACHE[key] = q.copy()
+    return q
 
 
 def mp_quantile(u: float, sigma2: float, c: float) -> float:

@@ -222,7 +222,7 @@ def test_descriptors_singular_mode_counts():
     assert D["tail_head"] == sig[int(0.7 * d)] and D["tail_min"] == sig[-1]
 
 
-@pytest.mark.parametrize("c", [0.01, 0.25, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("c", [0.01, 0.25, 0.5, 0.9, 0.99, 1.0])
 def test_mp_law_moments_and_cdf(c):
     s2 = 1.7
     lm, lp = oracle.mp_edges(s2, c)
