@@ -1,0 +1,220 @@
+/*
+ * spec.h -- C ABI of the MI355X (gfx950) spectral hot path:
+ *   covariance / Gram aggregation  ->  symmetric eigenvalue spectrum  ->  spectral descriptors.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees device memory, never synchronises the device, and only
+ *     enqueues work on `stream` (a hipStream_t; NULL means the default stream).
+ *   - Matrices are row-major.  `ld*` arguments are leading dimensions in elements.
+ *   - Symmetric matrices: only the LOWER triangle (row >= column) is read or
+ *     written; the strict upper triangle is never touched.
+ *   - Eigenvalues are returned in DESCENDING order.
+ *   - Every argument is validated on the host before anything is enqueued.  On an
+ *     error the call returns a negative spec_status and enqueues nothing.  A
+ *     failed kernel launch returns SPEC_EHIP.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Device pointers must be 16-byte aligned (4-byte for int32 outputs).
+ *   - The library holds no state between calls and is thread-safe; calls that
+ *     share output or workspace buffers on different streams race, as any
+ *     stream-ordered work does.
+ *
+ * Page citations name the page title and its section:
+ *   [RMT]   "Random matrix theory spectral methods: EigenTrack and RMT-KD"
+ *           (large-model reliability monitoring and compression, lpnh.cn)
+ *   [SWIFT] Swift-SVD news article (TeleAI et al., arXiv:2604.01609)
+ *   [S3]    "S3 Spectral Null-Space Swap" blog post (xxqk.cn)
+ */
+#ifndef SPEC_H
+#define SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,       /* bad pointer, size, stride, or parameter value */
+    SPEC_EUNSUPPORTED = -2, /* valid request the library does not implement (dtype pair, size) */
+    SPEC_EWORKSPACE = -3,   /* workspace NULL or smaller than the *_workspace query returned */
+    SPEC_EHIP = -4          /* a HIP runtime call (launch) failed */
+} spec_status;
+
+typedef enum { SPEC_BF16 = 0, SPEC_F32 = 1, SPEC_F64 = 2 } spec_dtype;
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *spec_strerror(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char *spec_version(void);
+
+/* ------------------------------------------------------------------------
+ * A1  Covariance aggregation (symmetric rank-k update)
+ *
+ *   C <- beta * C + alpha * X^T X            (lower triangle of C only)
+ *
+ * X is n x d (rows are samples, no centring), C is d x d.  This is the
+ * second-moment matrix S = (1/n) X^T X of [RMT] section 2.1 (alpha = 1/n), the
+ * window covariance (1/N) H^T H of [RMT] section 3.1, and the incremental
+ * aggregation of [SWIFT] sections 2 and 7: each new block of samples is added
+ * to the running matrix (beta = 1) with no recomputation.
+ *
+ * Supported (xt, ct) pairs and their arithmetic:
+ *   (SPEC_BF16, SPEC_F32)  bf16 products on MFMA, fp32 accumulation
+ *   (SPEC_F32,  SPEC_F32)  fp32 products and accumulation
+ *   (SPEC_F32,  SPEC_F64)  exact fp64 products of fp32 inputs, fp64 accumulation (MFMA)
+ * beta == 0 ignores the previous contents of C (NaNs included).
+ * n == 0 scales C by beta.  Requires d >= 1, ldx >= d, ldc >= d.
+ * Errors: SPEC_EINVAL (NULL pointer, n < 0, d < 1, ld too small, misaligned),
+ *         SPEC_EUNSUPPORTED (other dtype pairs).
+ * ---------------------------------------------------------------------- */
+int spec_cov_accumulate(void *stream, const void *X, int xt, int64_t n, int64_t d, int64_t ldx,
+                        void *C, int ct, int64_t ldc, double alpha, double beta);
+
+/* ------------------------------------------------------------------------
+ * A2  Sliding-window Gram ([RMT] section 3.1: window H = [h_{t-N+1}..h_t]^T,
+ *     covariance (1/N) H^T H; its nonzero spectrum is that of the N x N Gram
+ *     (1/N) H H^T, so the N x N form is computed when N << d).
+ *
+ * H holds `streams` independent activation sequences of T steps of d values:
+ * element (s, t, k) is at H[s*ld_s + t*ld_t + k].  ht must be SPEC_BF16 or
+ * SPEC_F32; products are fp32-accumulated.
+ *
+ * layout SPEC_GRAM_BAND: out is f32 [streams][T][N] with
+ *     out[s][t][j] = <h_t, h_{t-j}>      (0 <= j < N; 0 when t - j < 0; unscaled)
+ *   All windows' Grams follow from it: G_w[i][j] = scale * out[s][w*stride + max(i,j)][|i-j|].
+ *   `scale` and `stride` are ignored.
+ * layout SPEC_GRAM_DENSE: out is f32 [streams * W][N][N], W = (T - N) / stride + 1,
+ *     out[s*W + w] = scale * H_w H_w^T, H_w = rows [w*stride, w*stride + N) of stream s
+ *   (both triangles written).
+ * Requires 1 <= N <= 64, N <= T, stride >= 1, ld_t >= d, ld_s >= T*ld_t.
+ * ---------------------------------------------------------------------- */
+enum { SPEC_GRAM_BAND = 0, SPEC_GRAM_DENSE = 1 };
+
+int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64_t T, int64_t d,
+                     int64_t ld_t, int64_t ld_s, int N, int stride, double scale, int layout,
+                     float *out);
+
+/* ------------------------------------------------------------------------
+ * A3  Batched small symmetric eigenvalues (n <= 64), cyclic Jacobi with a
+ *     parallel (round-robin) ordering, one workgroup per matrix, matrix
+ *     resident in LDS.  The pages call a library eigvalsh per window and flip
+ *     it to descending order ([RMT] section 3.2 code).
+ *
+ * Source of the matrices (fp32):
+ *   SPEC_SRC_DENSE: matrix b is a[b*stride_a + i*lda + j]; the lower triangle is read.
+ *   SPEC_SRC_BAND:  the band Gram of spec_gram_window; matrix b is window
+ *                   w = b % W of stream s = b / W (W = (T - n) / stride + 1):
+ *                   A[i][j] = scale * a[s*T*n + (w*stride + max(i,j))*n + |i-j|];
+ *                   batch must equal streams * W.
+ * w:    f32 [batch][n], eigenvalues descending.
+ * info: int32 [batch] (may be NULL): sweeps used, or -1 if max_sweeps was reached
+ *       before every off-diagonal element satisfied |a_pq| <= eps32 * sqrt(|a_pp a_qq|).
+ * max_sweeps in [1, 100].
+ * ---------------------------------------------------------------------- */
+enum { SPEC_SRC_DENSE = 0, SPEC_SRC_BAND = 1 };
+
+typedef struct {
+    int kind;            /* SPEC_SRC_DENSE or SPEC_SRC_BAND */
+    const float *a;      /* device pointer */
+    int64_t lda;         /* DENSE: row stride (>= n) */
+    int64_t stride_a;    /* DENSE: elements between matrices (>= n*lda) */
+    int64_t streams;     /* BAND: number of streams */
+    int64_t T;           /* BAND: steps per stream */
+    int stride;          /* BAND: window stride (>= 1) */
+    float scale;         /* BAND: 1/N for the window covariance */
+} spec_batch_src;
+
+int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w,
+                          int max_sweeps, int32_t *info);
+
+/* ------------------------------------------------------------------------
+ * A4  Large symmetric eigenvalues (the single eigendecomposition of the
+ *     aggregated covariance in [SWIFT] sections 2 and 7; the O(d^3) step [RMT]
+ *     section 6.1 names as the cost for large d).
+ *
+ * Two-stage reduction: blocked Householder reduction of the dense matrix to
+ * band form (bandwidth 32; trailing updates on MFMA), bulge chasing from band
+ * to tridiagonal, then all eigenvalues of the tridiagonal by Sturm-count
+ * bisection.  t is SPEC_F32 or SPEC_F64; arithmetic is in t.
+ *
+ * A: n x n, lower triangle read, DESTROYED (used as the working matrix).
+ * w: n values of type t, descending.
+ * ws: device workspace of at least spec_eigvalsh_large_workspace(n, t) bytes.
+ * info: int32 [1] device (may be NULL): 0 on success, 1 if the bulge-chasing
+ *       pipeline hit its spin limit (results invalid).
+ * Requires 1 <= n <= 32768 (SPEC_F32) or n <= 16384 (SPEC_F64), lda >= n.
+ * ---------------------------------------------------------------------- */
+int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes);
+
+int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, void *w, void *ws,
+                        size_t ws_bytes, int32_t *info);
+
+/* ------------------------------------------------------------------------
+ * A5  Spectral descriptors of `batch` spectra of r values each
+ *     (w[b*ldw + i], i < r, sorted DESCENDING; type wt = SPEC_F32 or SPEC_F64).
+ *
+ * Negative values (round-off) are clamped to 0 first.  With S = sum(lambda),
+ * p_i = lambda_i / S, all in fp64:
+ *   H      = -sum p_i ln p_i  (0 ln 0 = 0)      spectral entropy     [RMT] 2.3
+ *   erank  = exp(H)                             effective rank       [SWIFT] 3
+ *   m1     = lambda_1 / S                        leading mass         [RMT] 2.3
+ *   gk     = lambda_k / lambda_{k+1}, g1 = lambda_1 / lambda_2   (eigengap ratio) [RMT] 2.3
+ *   c = p_dim / n_samples; lambda_plus = sigma2 (1 + sqrt c)^2   (MP edge) [RMT] 2.1
+ *   n_above = #{lambda_i > lambda_plus}                          (BBP outliers) [RMT] 2.2
+ *   mp_w1  = (1/r) sum_i |mu_(i) - Q_MP((i - 1/2)/r)|, mu ascending: the
+ *            Wasserstein-1 distance to the MP law ([RMT] 2.3); if p_dim <= n_samples,
+ *            mu = lambda and the MP ratio is c; else mu = (n/p) lambda, ratio n/p.
+ *   sigma_i = sqrt(lambda_i) (singular values when the matrix was W^T W):
+ *   top_energy = sum_{i <= floor(top_frac r)} sigma_i^2 / sum sigma_i^2,
+ *   top_sigma_share = the same ratio of sigma_i               [S3] 1
+ *   tail_head = sigma at rank floor(tail_frac r) + 1, tail_min = sigma_r   [S3] 1
+ *   n_small = #{sigma_i < small_rel * sigma_1}                [S3] 2
+ * sigma2 by sigma2_mode: SPEC_SIGMA2_GIVEN (the value given), SPEC_SIGMA2_MEDIAN
+ * (median of the r clamped values, [RMT] 4.2), SPEC_SIGMA2_MEAN (S / p_dim).
+ * Undefined ratios (zero denominators) are NaN and set a flag bit.
+ *
+ * out: device array of `batch` spec_desc records.
+ * ws:  device workspace of spec_descriptors_workspace(r) bytes (the MP quantile table).
+ * Requires r >= 1, ldw >= r, 1 <= k < r (k is clamped to r-1 when r == 1 is not allowed),
+ * n_samples >= 1, p_dim >= 1, top_frac and tail_frac in [0, 1], small_rel >= 0.
+ * ---------------------------------------------------------------------- */
+enum { SPEC_MODE_EIG = 0, SPEC_MODE_SINGULAR = 1 };
+enum { SPEC_SIGMA2_GIVEN = 0, SPEC_SIGMA2_MEDIAN = 1, SPEC_SIGMA2_MEAN = 2 };
+enum {
+    SPEC_FLAG_NONFINITE = 1, /* a NaN or Inf eigenvalue was seen */
+    SPEC_FLAG_GK_UNDEF = 2,  /* lambda_{k+1} <= 0 */
+    SPEC_FLAG_S_ZERO = 4     /* all eigenvalues are <= 0 */
+};
+
+typedef struct {
+    int mode;            /* SPEC_MODE_EIG or SPEC_MODE_SINGULAR (informational) */
+    int sigma2_mode;     /* SPEC_SIGMA2_* */
+    double sigma2;       /* used when sigma2_mode == SPEC_SIGMA2_GIVEN */
+    int64_t n_samples;   /* n */
+    int64_t p_dim;       /* p */
+    int64_t k;           /* eigengap index (1-based) */
+    double top_frac;     /* 0.2 */
+    double small_rel;    /* 1e-2 */
+    double tail_frac;    /* 0.7 */
+} spec_desc_params;
+
+typedef struct {
+    double S, H, erank, m1, gk, g1, sigma2, lambda_plus, mp_w1;
+    double top_energy, top_sigma_share, tail_head, tail_min, sigma1;
+    int64_t n_above, n_small, r_pos, flags;
+} spec_desc; /* 144 bytes */
+
+int spec_descriptors_workspace(int64_t r, size_t *bytes);
+
+int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                     const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_H */

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every entry point include/spec.h declares,
+and rejects bad arguments on the host before anything is enqueued (no GPU
+needed: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weights_bf16_fp32_amd as spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec.h")
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(spec.LIB_PATH):
+        from weights_bf16_fp32_amd import build
+        build.build()
+    return spec.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(spec_\w+)\s*\(", text, re.M))
+    assert {"spec_cov_accumulate", "spec_gram_window", "spec_eigvalsh_batched", "spec_eigvalsh_large",
+            "spec_descriptors"} <= declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(spec.EXPORTS) == declared
+
+
+def test_strerror_and_version(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert len(L.spec_strerror(s)) > 0
+    assert L.spec_version() == b"0.1.0"
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(spec.BatchSrc) == 56
+    assert ctypes.sizeof(spec.DescParams) == 64
+    assert spec.DESC_DTYPE.itemsize == 144
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced because validation fails first
+
+
+def test_cov_accumulate_validation(L):
+    f = L.spec_cov_accumulate
+    assert f(None, FAKE, spec.BF16, 10, 8, 8, None, spec.F32, 8, 1.0, 0.0) == EINVAL  # C NULL
+    assert f(None, None, spec.BF16, 10, 8, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL  # X NULL, n > 0
+    assert f(None, FAKE, spec.BF16, 10, 8, 4, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL  # ldx < d
+    assert f(None, FAKE, spec.BF16, 10, 8, 8, FAKE, spec.F32, 7, 1.0, 0.0) == EINVAL  # ldc < d
+    assert f(None, FAKE, spec.BF16, -1, 8, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL
+    assert f(None, FAKE, spec.BF16, 10, 0, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL
+    assert f(None, FAKE, spec.BF16, 10, 8, 8, FAKE, spec.F64, 8, 1.0, 0.0) == EUNSUPPORTED
+    assert f(None, FAKE, spec.F64, 10, 8, 8, FAKE, spec.F64, 8, 1.0, 0.0) == EUNSUPPORTED
+    assert f(None, FAKE + 1, spec.F32, 10, 8, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL  # misaligned
+    assert f(None, FAKE, spec.F32, 10, 8, 8, FAKE, spec.F32, 8, float("nan"), 0.0) == EINVAL
+
+
+def test_gram_validation(L):
+    f = L.spec_gram_window
+    ok = (None, FAKE, spec.BF16, 2, 100, 64, 64, 6400, 30, 1, 1 / 30, spec.GRAM_BAND, FAKE)
+    bad = [
+        (5, 65), (5, 0), (8, 0), (1, 101),  # N > 64, N = 0, stride 0, T < N
+    ]
+    for idx, val in [(8, 65), (8, 0), (9, 0)]:
+        a = list(ok); a[idx] = val
+        assert f(*a) == EINVAL
+    a = list(ok); a[4] = 20  # T < N
+    assert f(*a) == EINVAL
+    a = list(ok); a[6] = 32  # ld_t < d
+    assert f(*a) == EINVAL
+    a = list(ok); a[2] = spec.F64
+    assert f(*a) == EUNSUPPORTED
+    a = list(ok); a[11] = 7
+    assert f(*a) == EINVAL
+    a = list(ok); a[12] = None
+    assert f(*a) == EINVAL
+
+
+def test_batched_validation(L):
+    f = L.spec_eigvalsh_batched
+    src = spec.BatchSrc(spec.SRC_DENSE, FAKE, 30, 900, 0, 0, 1, 1.0)
+    assert f(None, ctypes.byref(src), 4, 65, FAKE, 15, None) == EUNSUPPORTED
+    assert f(None, ctypes.byref(src), 4, 0, FAKE, 15, None) == EINVAL
+    assert f(None, ctypes.byref(src), 4, 30, FAKE, 0, None) == EINVAL
+    assert f(None, ctypes.byref(src), 4, 31, FAKE, 15, None) == EINVAL  # lda < n
+    band = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 100, 1, 1 / 30)
+    assert f(None, ctypes.byref(band), 2 * 70, 30, FAKE, 15, None) == EINVAL  # batch != S * W
+    assert f(None, None, 4, 30, FAKE, 15, None) == EINVAL
+
+
+def test_large_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.spec_eigvalsh_large_workspace(4096, spec.F32, ctypes.byref(b)) == 0 and b.value > 0
+    assert L.spec_eigvalsh_large_workspace(4096, spec.BF16, ctypes.byref(b)) == EUNSUPPORTED
+    assert L.spec_eigvalsh_large_workspace(0, spec.F32, ctypes.byref(b)) == EINVAL
+    assert L.spec_eigvalsh_large_workspace(40000, spec.F32, ctypes.byref(b)) == EUNSUPPORTED
+    L.spec_eigvalsh_large_workspace(512, spec.F64, ctypes.byref(b))
+    f = L.spec_eigvalsh_large
+    assert f(None, FAKE, spec.F64, 512, 512, FAKE, FAKE, b.value - 1, None) == EWORKSPACE
+    assert f(None, FAKE, spec.F64, 512, 512, FAKE, None, b.value, None) == EWORKSPACE
+    assert f(None, FAKE, spec.F64, 512, 500, FAKE, FAKE, b.value, None) == EINVAL
+
+
+def test_descriptors_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.spec_descriptors_workspace(30, ctypes.byref(b)) == 0 and b.value >= 30 * 8
+    p = spec.DescParams(0, 0, 1.0, 64, 32, 1, 0.2, 1e-2, 0.7)
+    f = L.spec_descriptors
+    assert f(None, FAKE, spec.F32, 1, 32, 32, ctypes.byref(p), FAKE, FAKE, 8, ) == EWORKSPACE
+    for field, val in [("k", 0), ("k", 32), ("n_samples", 0), ("top_frac", 1.5), ("sigma2", -1.0),
+                       ("sigma2_mode", 5), ("small_rel", -1.0)]:
+        q = spec.DescParams(0, 0, 1.0, 64, 32, 1, 0.2, 1e-2, 0.7)
+        setattr(q, field, val)
+        assert f(None, FAKE, spec.F32, 1, 32, 32, ctypes.byref(q), FAKE, FAKE, 4096) == EINVAL, field
+    assert f(None, FAKE, spec.BF16, 1, 32, 32, ctypes.byref(p), FAKE, FAKE, 4096) == EUNSUPPORTED
+    assert f(None, FAKE, spec.F32, 1, 1, 1, ctypes.byref(p), FAKE, FAKE, 4096) == EINVAL

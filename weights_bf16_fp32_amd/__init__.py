@@ -1,0 +1,238 @@
+"""Python binding of the gfx950 spectral library (libspec.so, C ABI in include/spec.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The library
+is loaded on first use and a missing library raises immediately; there is no
+fallback of any kind.
+
+    import weights_bf16_fp32_amd as spec
+    spec.cov_accumulate(X, C, alpha=1/n, beta=0.0)          # C <- beta C + alpha X^T X (lower)
+    band = spec.gram_window(H, N=30)                          # [S, T, N] <h_t, h_{t-j}>
+    w, info = spec.eigvalsh_batched_band(band, n=30, scale=1/30)
+    w = spec.eigvalsh_large(C)                                # destroys C
+    rec = spec.descriptors(w, n_samples=n, p_dim=d, k=1)      # structured numpy array
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "SpecError", "lib", "cov_accumulate", "gram_window", "eigvalsh_batched_dense",
+    "eigvalsh_batched_band", "eigvalsh_large", "eigvalsh_large_workspace", "descriptors",
+    "descriptors_workspace", "DESC_DTYPE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspec.so")
+
+BF16, F32, F64 = 0, 1, 2
+GRAM_BAND, GRAM_DENSE = 0, 1
+SRC_DENSE, SRC_BAND = 0, 1
+MODE_EIG, MODE_SINGULAR = 0, 1
+SIGMA2_GIVEN, SIGMA2_MEDIAN, SIGMA2_MEAN = 0, 1, 2
+FLAG_NONFINITE, FLAG_GK_UNDEF, FLAG_S_ZERO = 1, 2, 4
+
+_DESC_FIELDS_F = ["S", "H", "erank", "m1", "gk", "g1", "sigma2", "lambda_plus", "mp_w1",
+                  "top_energy", "top_sigma_share", "tail_head", "tail_min", "sigma1"]
+_DESC_FIELDS_I = ["n_above", "n_small", "r_pos", "flags"]
+DESC_DTYPE = np.dtype([(f, "<f8") for f in _DESC_FIELDS_F] + [(f, "<i8") for f in _DESC_FIELDS_I])
+assert DESC_DTYPE.itemsize == 144
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"spec status {status}: {msg}")
+        self.status = status
+
+
+class BatchSrc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("a", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("stride_a", ctypes.c_int64), ("streams", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("stride", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+class DescParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("sigma2_mode", ctypes.c_int), ("sigma2", ctypes.c_double),
+                ("n_samples", ctypes.c_int64), ("p_dim", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("top_frac", ctypes.c_double), ("small_rel", ctypes.c_double),
+                ("tail_frac", ctypes.c_double)]
+
+
+EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_window",
+           "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
+           "spec_descriptors_workspace", "spec_descriptors"]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspec.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(weights_bf16_fp32_amd/build.py); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.spec_strerror.argtypes = [i32]
+        L.spec_strerror.restype = ctypes.c_char_p
+        L.spec_version.argtypes = []
+        L.spec_version.restype = ctypes.c_char_p
+        L.spec_cov_accumulate.argtypes = [vp, vp, i32, i64, i64, i64, vp, i32, i64, dbl, dbl]
+        L.spec_gram_window.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, dbl, i32, vp]
+        L.spec_eigvalsh_batched.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, i32, vp]
+        L.spec_eigvalsh_large_workspace.argtypes = [i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.spec_eigvalsh_large.argtypes = [vp, vp, i32, i64, i64, vp, vp, ctypes.c_size_t, vp]
+        L.spec_descriptors_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.spec_descriptors.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp, vp,
+                                       ctypes.c_size_t]
+        for f in EXPORTS[2:]:
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SpecError(status, lib().spec_strerror(status).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float64:
+        return F64
+    raise SpecError(-2, f"unsupported dtype {t.dtype}")
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise SpecError(-1, "tensor must be on the GPU")
+    return t.data_ptr()
+
+
+def cov_accumulate(X, C, alpha: float = 1.0, beta: float = 0.0):
+    """C <- beta C + alpha X^T X on the lower triangle of C (X: [n, d], C: [d, d])."""
+    n, d = X.shape
+    if X.stride(1) != 1 or C.stride(1) != 1:
+        raise SpecError(-1, "inner dimension must be contiguous")
+    _check(lib().spec_cov_accumulate(_stream(), _dev(X), _dt(X), n, d, X.stride(0), _dev(C), _dt(C),
+                                     C.stride(0), float(alpha), float(beta)))
+    return C
+
+
+def gram_window(H, N: int, stride: int = 1, scale: float = 1.0, layout: int = GRAM_BAND, out=None):
+    """Band <h_t, h_{t-j}> [S, T, N] (layout BAND) or dense scale*H_w H_w^T [S*W, N, N]."""
+    torch = _torch()
+    if H.dim() == 2:
+        H = H.unsqueeze(0)
+    S, T, d = H.shape
+    if H.stride(2) != 1:
+        raise SpecError(-1, "feature dimension must be contiguous")
+    if out is None:
+        if layout == GRAM_BAND:
+            out = torch.empty((S, T, N), dtype=torch.float32, device=H.device)
+        else:
+            W = (T - N) // stride + 1
+            out = torch.empty((S * W, N, N), dtype=torch.float32, device=H.device)
+    _check(lib().spec_gram_window(_stream(), _dev(H), _dt(H), S, T, d, H.stride(1), H.stride(0), N, stride,
+                                  float(scale), layout, _dev(out)))
+    return out
+
+
+def _batched(src: BatchSrc, batch: int, n: int, w, info, max_sweeps: int, device):
+    torch = _torch()
+    if w is None:
+        w = torch.empty((batch, n), dtype=torch.float32, device=device)
+    if info is None:
+        info = torch.empty((batch,), dtype=torch.int32, device=device)
+    _check(lib().spec_eigvalsh_batched(_stream(), ctypes.byref(src), batch, n, _dev(w), max_sweeps,
+                                       _dev(info)))
+    return w, info
+
+
+def eigvalsh_batched_dense(A, w=None, info=None, max_sweeps: int = 15):
+    """Eigenvalues (descending) of A [batch, n, n] f32 (lower triangle read)."""
+    if A.dim() == 2:
+        A = A.unsqueeze(0)
+    batch, n, _ = A.shape
+    src = BatchSrc(SRC_DENSE, _dev(A), A.stride(1), A.stride(0), 0, 0, 1, 1.0)
+    return _batched(src, batch, n, w, info, max_sweeps, A.device)
+
+
+def eigvalsh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, info=None,
+                          max_sweeps: int = 15):
+    """Eigenvalues of every window's Gram scale * G_w from the band [S, T, n] of gram_window."""
+    S, T, N = band.shape
+    if N != n or not band.is_contiguous():
+        raise SpecError(-1, "band must be a contiguous [streams, T, n] tensor")
+    batch = S * ((T - n) // stride + 1)
+    src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
+    return _batched(src, batch, n, w, info, max_sweeps, band.device)
+
+
+def eigvalsh_large_workspace(n: int, dtype) -> int:
+    torch = _torch()
+    t = F32 if dtype == torch.float32 else F64
+    b = ctypes.c_size_t(0)
+    _check(lib().spec_eigvalsh_large_workspace(n, t, ctypes.byref(b)))
+    return b.value
+
+
+def eigvalsh_large(A, w=None, ws=None, info=None):
+    """Eigenvalues (descending) of the symmetric A [n, n] (lower triangle read, A destroyed)."""
+    torch = _torch()
+    n = A.shape[0]
+    if A.stride(1) != 1:
+        raise SpecError(-1, "A must be row-major")
+    if w is None:
+        w = torch.empty((n,), dtype=A.dtype, device=A.device)
+    if ws is None:
+        ws = torch.empty((eigvalsh_large_workspace(n, A.dtype),), dtype=torch.uint8, device=A.device)
+    ip = _dev(info) if info is not None else None
+    _check(lib().spec_eigvalsh_large(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(w), _dev(ws),
+                                     ws.numel(), ip))
+    return w
+
+
+def descriptors_workspace(r: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().spec_descriptors_workspace(r, ctypes.byref(b)))
+    return b.value
+
+
+def descriptors(w, *, n_samples: int, p_dim: int, k: int = 1, mode: int = MODE_EIG,
+                sigma2: float = 1.0, sigma2_mode: int = SIGMA2_GIVEN, top_frac: float = 0.2,
+                small_rel: float = 1e-2, tail_frac: float = 0.7, out=None, ws=None, to_host: bool = True):
+    """Descriptors of each row of w [batch, r] (sorted descending).  Returns a numpy
+    structured array of DESC_DTYPE (or the raw device buffer if to_host is False)."""
+    torch = _torch()
+    if w.dim() == 1:
+        w = w.unsqueeze(0)
+    batch, r = w.shape
+    if out is None:
+        out = torch.empty((batch, DESC_DTYPE.itemsize), dtype=torch.uint8, device=w.device)
+    if ws is None:
+        ws = torch.empty((descriptors_workspace(r),), dtype=torch.uint8, device=w.device)
+    p = DescParams(mode, sigma2_mode, float(sigma2), int(n_samples), int(p_dim), int(k), float(top_frac),
+                   float(small_rel), float(tail_frac))
+    _check(lib().spec_descriptors(_stream(), _dev(w), _dt(w), batch, r, w.stride(0), ctypes.byref(p),
+                                  _dev(out), _dev(ws), ws.numel()))
+    if not to_host:
+        return out
+    return out.cpu().numpy().view(DESC_DTYPE).reshape(batch)

@@ -1,0 +1,136 @@
+// C ABI of the spectral library: argument validation and dispatch to the
+// gfx950 kernels.  Every check runs on the host before anything is enqueued;
+// nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_EHIP; }
+
+inline size_t elt_size(int t) { return t == SPEC_BF16 ? 2 : (t == SPEC_F32 ? 4 : 8); }
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_strerror(int status)
+{
+    switch (status) {
+    case SPEC_OK: return "success";
+    case SPEC_EINVAL: return "invalid argument (pointer, size, stride or parameter)";
+    case SPEC_EUNSUPPORTED: return "unsupported dtype combination or size";
+    case SPEC_EWORKSPACE: return "workspace missing or too small";
+    case SPEC_EHIP: return "HIP runtime error while enqueueing a kernel";
+    default: return "unknown status";
+    }
+}
+
+const char *spec_version(void) { return "0.1.0"; }
+
+int spec_cov_accumulate(void *stream, const void *X, int xt, int64_t n, int64_t d, int64_t ldx, void *C, int ct,
+                        int64_t ldc, double alpha, double beta)
+{
+    if (C == nullptr || (X == nullptr && n > 0)) return SPEC_EINVAL;
+    if (n < 0 || d < 1 || ldc < d || (n > 0 && ldx < d)) return SPEC_EINVAL;
+    if (!isfinite(alpha) || !isfinite(beta)) return SPEC_EINVAL;
+    const bool pair_ok = (xt == SPEC_BF16 && ct == SPEC_F32) || (xt == SPEC_F32 && ct == SPEC_F32) ||
+                         (xt == SPEC_F32 && ct == SPEC_F64);
+    if (!pair_ok) return SPEC_EUNSUPPORTED;
+    if (!aligned(C, elt_size(ct)) || (X != nullptr && !aligned(X, elt_size(xt)))) return SPEC_EINVAL;
+    if (d > (int64_t)1 << 20 || n > ((int64_t)1 << 40)) return SPEC_EUNSUPPORTED;
+    return from_hip(launch_syrk((hipStream_t)stream, X, xt, n, d, ldx, C, ct, ldc, alpha, beta));
+}
+
+int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64_t T, int64_t d, int64_t ld_t,
+                     int64_t ld_s, int N, int stride, double scale, int layout, float *out)
+{
+    if (H == nullptr || out == nullptr) return SPEC_EINVAL;
+    if (ht != SPEC_BF16 && ht != SPEC_F32) return SPEC_EUNSUPPORTED;
+    if (streams < 1 || T < 1 || d < 1 || N < 1 || N > 64 || N > T || stride < 1) return SPEC_EINVAL;
+    if (ld_t < d || ld_s < T * ld_t) return SPEC_EINVAL;
+    if (!aligned(H, elt_size(ht)) || !aligned(out, 4)) return SPEC_EINVAL;
+    if (!isfinite(scale)) return SPEC_EINVAL;
+    if (layout == SPEC_GRAM_BAND)
+        return from_hip(launch_gram_band((hipStream_t)stream, H, ht, streams, T, d, ld_t, ld_s, N, out));
+    if (layout == SPEC_GRAM_DENSE) {
+        if (streams * ((T - N) / stride + 1) > ((int64_t)1 << 31) - 1) return SPEC_EUNSUPPORTED;
+        return from_hip(
+            launch_gram_dense((hipStream_t)stream, H, ht, streams, T, d, ld_t, ld_s, N, stride, (float)scale, out));
+    }
+    return SPEC_EINVAL;
+}
+
+int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int max_sweeps,
+                          int32_t *info)
+{
+    if (src == nullptr || w == nullptr || src->a == nullptr) return SPEC_EINVAL;
+    if (n < 1 || n > 64) return n > 64 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+    if (batch < 0 || batch > ((int64_t)1 << 31) - 1) return SPEC_EINVAL;
+    if (max_sweeps < 1 || max_sweeps > 100) return SPEC_EINVAL;
+    if (!aligned(w, 4) || !aligned(src->a, 4) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
+    if (src->kind == SPEC_SRC_DENSE) {
+        if (src->lda < n || src->stride_a < (int64_t)n * src->lda) return SPEC_EINVAL;
+    } else if (src->kind == SPEC_SRC_BAND) {
+        if (src->streams < 1 || src->T < n || src->stride < 1 || !isfinite(src->scale)) return SPEC_EINVAL;
+        const int64_t W = (src->T - n) / src->stride + 1;
+        if (batch != src->streams * W) return SPEC_EINVAL;
+    } else {
+        return SPEC_EINVAL;
+    }
+    return from_hip(launch_jacobi_batched((hipStream_t)stream, src, batch, n, w, max_sweeps, info));
+}
+
+int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes)
+{
+    if (bytes == nullptr || n < 1) return SPEC_EINVAL;
+    if (t != SPEC_F32 && t != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if ((t == SPEC_F32 && n > 32768) || (t == SPEC_F64 && n > 16384)) return SPEC_EUNSUPPORTED;
+    *bytes = eig_large_workspace_bytes(n, t);
+    return SPEC_OK;
+}
+
+int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, void *w, void *ws, size_t ws_bytes,
+                        int32_t *info)
+{
+    size_t need = 0;
+    int st = spec_eigvalsh_large_workspace(n, t, &need);
+    if (st != SPEC_OK) return st;
+    if (A == nullptr || w == nullptr || lda < n) return SPEC_EINVAL;
+    if (!aligned(A, 16) || !aligned(w, elt_size(t)) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    return from_hip(launch_eig_large((hipStream_t)stream, A, t, n, lda, w, ws, info));
+}
+
+int spec_descriptors_workspace(int64_t r, size_t *bytes)
+{
+    if (bytes == nullptr || r < 1) return SPEC_EINVAL;
+    *bytes = descriptors_workspace_bytes(r);
+    return SPEC_OK;
+}
+
+int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                     const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes)
+{
+    if (w == nullptr || p == nullptr || out == nullptr) return SPEC_EINVAL;
+    if (wt != SPEC_F32 && wt != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if (batch < 0 || batch > ((int64_t)1 << 31) - 1 || r < 2 || ldw < r) return SPEC_EINVAL;
+    if (p->k < 1 || p->k >= r || p->n_samples < 1 || p->p_dim < 1) return SPEC_EINVAL;
+    if (!(p->top_frac >= 0.0 && p->top_frac <= 1.0) || !(p->tail_frac >= 0.0 && p->tail_frac <= 1.0) ||
+        !(p->small_rel >= 0.0))
+        return SPEC_EINVAL;
+    if (p->sigma2_mode < SPEC_SIGMA2_GIVEN || p->sigma2_mode > SPEC_SIGMA2_MEAN) return SPEC_EINVAL;
+    if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
+    if (!aligned(w, elt_size(wt)) || !aligned(out, 8)) return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < descriptors_workspace_bytes(r)) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 8)) return SPEC_EINVAL;
+    return from_hip(launch_descriptors((hipStream_t)stream, w, wt, batch, r, ldw, p, out, ws));
+}
+
+}  // extern "C"

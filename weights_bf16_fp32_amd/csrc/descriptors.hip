@@ -1,0 +1,206 @@
+// Spectral descriptors of sorted spectra, fp64 arithmetic.
+//
+// Descriptors of the "Random matrix theory spectral methods" page: spectral
+// entropy H, leading-eigenvalue mass m1, eigengap g_k = lambda_k / lambda_{k+1}
+// and the deviation from the Marchenko-Pastur law (section 2.3), the MP edge
+// lambda_plus = sigma^2 (1 + sqrt c)^2 (section 2.1) and the count of
+// eigenvalues beyond it (spiked model, section 2.2); the effective rank of the
+// Swift-SVD page (section 3) as exp(H); the S3 page's long-tail test (top 20 %
+// share, tail level; section 1) and its count of near-zero singular values
+// (section 2).
+//
+// mp_table: Q_i = F^{-1}((i + 1/2) / r) of the MP law with sigma^2 = 1 and
+//   ratio c <= 1, one thread per level.  With lambda = m - h cos(phi)
+//   (m = 1 + c, h = 2 sqrt c) the distribution function has the closed form
+//     F(phi) = [ sin(phi) / sqrt(c) + (1 + c) phi / (2c)
+//                - ((1 - c) / c) atan(kappa tan(phi / 2)) ] / pi,
+//   kappa = (1 + sqrt c) / (1 - sqrt c)   (the antiderivative of
+//   h^2 sin^2(phi) / (2 pi c lambda(phi))), inverted by bisection on phi.
+//   MP(sigma^2, c) is MP(1, c) scaled by sigma^2.
+// descriptors: one 64-lane wave per spectrum; every sum is an fp64 wave
+//   reduction.
+#include <float.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+__device__ double mp_cdf_phi(double phi, double c)
+{
+    const double sc = sqrt(c);
+    double third = 0.0;
+    if (c < 1.0) {
+        const double kappa = (1.0 + sc) / (1.0 - sc);
+        third = ((1.0 - c) / c) * atan2(kappa * sin(0.5 * phi), cos(0.5 * phi));
+    }
+    return (sin(phi) / sc + (1.0 + c) * phi / (2.0 * c) - third) / M_PI;
+}
+
+__global__ void mp_table(double c, int64_t r, double *__restrict__ q)
+{
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= r) return;
+    const double u = ((double)i + 0.5) / (double)r;
+    double a = 0.0, b = M_PI;
+    for (int it = 0; it < 64; ++it) {
+        const double mid = 0.5 * (a + b);
+        if (mp_cdf_phi(mid, c) < u)
+            a = mid;
+        else
+            b = mid;
+    }
+    const double phi = 0.5 * (a + b);
+    const double sc = sqrt(c);
+    const double lminus = (1.0 - sc) * (1.0 - sc);
+    const double s = sin(0.5 * phi);
+    q[i] = lminus + 4.0 * sc * s * s;  // = m - h cos(phi)
+}
+
+__device__ __forceinline__ double wsum(double x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ int64_t wsum_i(int64_t x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void descriptors_kernel(const T *__restrict__ w, int64_t batch, int64_t r,
+                                                         int64_t ldw, spec_desc_params p,
+                                                         const double *__restrict__ qtab, spec_desc *__restrict__ out)
+{
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const T *wb = w + b * ldw;
+    auto lam = [&](int64_t i) -> double {
+        double v = (double)wb[i];
+        return v > 0.0 ? v : (v == v ? 0.0 : v);  // clamp round-off, keep NaN
+    };
+
+    // pass 1: S, positives, non-finite, top-k sums
+    const int64_t kt = (int64_t)floor(p.top_frac * (double)r);
+    double S = 0.0, Ssig = 0.0, Stop = 0.0, Stop_sig = 0.0;
+    int64_t rpos = 0, bad = 0;
+    for (int64_t i = lane; i < r; i += 64) {
+        const double v = lam(i);
+        if (!isfinite(v)) {
+            ++bad;
+            continue;
+        }
+        const double sg = sqrt(v);
+        S += v;
+        Ssig += sg;
+        if (v > 0.0) ++rpos;
+        if (i < kt) {
+            Stop += v;
+            Stop_sig += sg;
+        }
+    }
+    S = wsum(S);
+    Ssig = wsum(Ssig);
+    Stop = wsum(Stop);
+    Stop_sig = wsum(Stop_sig);
+    rpos = wsum_i(rpos);
+    bad = wsum_i(bad);
+
+    const double l0 = lam(0);
+    const double l1 = r > 1 ? lam(1) : 0.0;
+    double sigma2;
+    if (p.sigma2_mode == SPEC_SIGMA2_MEDIAN)
+        sigma2 = 0.5 * (lam((r - 1) / 2) + lam(r / 2));
+    else if (p.sigma2_mode == SPEC_SIGMA2_MEAN)
+        sigma2 = S / (double)p.p_dim;
+    else
+        sigma2 = p.sigma2;
+    const double c = (double)p.p_dim / (double)p.n_samples;
+    const double lplus = sigma2 * (1.0 + sqrt(c)) * (1.0 + sqrt(c));
+    const double sig1 = sqrt(l0);
+    const double small_thr = p.small_rel * sig1;
+
+    // pass 2: entropy, counts, W1
+    const bool companion = p.p_dim > p.n_samples;
+    const double mu_scale = companion ? (double)p.n_samples / (double)p.p_dim : 1.0;
+    double Hs = 0.0, w1 = 0.0;
+    int64_t above = 0, small = 0;
+    for (int64_t i = lane; i < r; i += 64) {
+        const double v = lam(i);
+        if (!isfinite(v)) continue;
+        if (S > 0.0) {
+            const double pi = v / S;
+            if (pi > 0.0) Hs -= pi * log(pi);
+        }
+        if (v > lplus) ++above;
+        if (sqrt(v) < small_thr) ++small;
+        // ascending rank of lambda_i is r - 1 - i
+        w1 += fabs(mu_scale * v - sigma2 * qtab[r - 1 - i]);
+    }
+    Hs = wsum(Hs);
+    w1 = wsum(w1);
+    above = wsum_i(above);
+    small = wsum_i(small);
+
+    if (lane == 0) {
+        spec_desc d;
+        const double nan = __builtin_nan("");
+        int64_t flags = 0;
+        if (bad) flags |= SPEC_FLAG_NONFINITE;
+        if (!(S > 0.0)) flags |= SPEC_FLAG_S_ZERO;
+        d.S = S;
+        d.H = S > 0.0 ? Hs : nan;
+        d.erank = S > 0.0 ? exp(Hs) : nan;
+        d.m1 = S > 0.0 ? l0 / S : nan;
+        const int64_t k = p.k;
+        if (k < r && lam(k) > 0.0) {
+            d.gk = lam(k - 1) / lam(k);
+        } else {
+            d.gk = nan;
+            flags |= SPEC_FLAG_GK_UNDEF;
+        }
+        d.g1 = (r > 1 && l1 > 0.0) ? l0 / l1 : nan;
+        d.sigma2 = sigma2;
+        d.lambda_plus = lplus;
+        d.mp_w1 = sigma2 > 0.0 ? w1 / (double)r : nan;
+        d.top_energy = S > 0.0 ? Stop / S : nan;
+        d.top_sigma_share = Ssig > 0.0 ? Stop_sig / Ssig : nan;
+        int64_t th = (int64_t)floor(p.tail_frac * (double)r);
+        if (th > r - 1) th = r - 1;
+        d.tail_head = sqrt(lam(th));
+        d.tail_min = sqrt(lam(r - 1));
+        d.sigma1 = sig1;
+        d.n_above = above;
+        d.n_small = small;
+        d.r_pos = rpos;
+        d.flags = flags;
+        out[b] = d;
+    }
+}
+
+}  // namespace
+
+size_t descriptors_workspace_bytes(int64_t r) { return (size_t)((r + 31) / 32 * 32) * sizeof(double); }
+
+hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                              const spec_desc_params *p, spec_desc *out, void *ws)
+{
+    double *q = (double *)ws;
+    const double c = p->p_dim <= p->n_samples ? (double)p->p_dim / (double)p->n_samples
+                                               : (double)p->n_samples / (double)p->p_dim;
+    hipLaunchKernelGGL(mp_table, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, stream, c, r, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (batch == 0) return hipSuccess;
+    if (wt == SPEC_F32)
+        hipLaunchKernelGGL(descriptors_kernel<float>, dim3((unsigned)batch), dim3(64), 0, stream, (const float *)w,
+                           batch, r, ldw, *p, q, out);
+    else
+        hipLaunchKernelGGL(descriptors_kernel<double>, dim3((unsigned)batch), dim3(64), 0, stream, (const double *)w,
+                           batch, r, ldw, *p, q, out);
+    return hipGetLastError();
+}

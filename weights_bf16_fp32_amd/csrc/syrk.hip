@@ -1,0 +1,361 @@
+// Covariance aggregation C <- beta C + alpha X^T X (lower triangle), gfx950.
+//
+// The second-moment matrix S = (1/n) X^T X of the Marchenko-Pastur setting and
+// the window covariance of EigenTrack ("Random matrix theory spectral methods"
+// page, sections 2.1 and 3.1), summed block by block as Swift-SVD's incremental
+// covariance aggregation (Swift-SVD page, sections 2 and 7).
+//
+// Kernels
+//   syrk_bf16_mfma  bf16 X, fp32 C.  128x128 lower-triangle tiles of C, one
+//                   workgroup (4 waves, 64x64 each) per tile, K-loop over the
+//                   samples in steps of 64.  X is row-major with the reduction
+//                   index (samples) as the slow dimension, while the MFMA wants
+//                   8 consecutive samples per lane, so each thread loads an 8x8
+//                   (samples x features) block with 16-byte loads, transposes it
+//                   in registers and stores feature-major rows into LDS.  LDS is
+//                   double-buffered; the next block's global loads are in flight
+//                   during the current block's MFMAs.  v_mfma_f32_32x32x16_bf16.
+//   syrk_f64_mfma   f32 X, fp64 C.  Products of two f32 values are exact in
+//                   fp64; v_mfma_f64_16x16x4_f64 accumulates them.  The MFMA
+//                   takes one sample per lane, so X's natural layout is used
+//                   as is (converted to fp64 on the way into LDS).
+//   syrk_generic    any of the above pairs plus f32 -> f32, plain VALU FMAs on
+//                   64x64 tiles; used for f32 -> f32 and for shapes the MFMA
+//                   kernels do not take (d or ldx not a multiple of 8).
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int SB_TILE = 128;  // C tile edge
+constexpr int SB_BK = 64;     // samples per K-step
+constexpr int SB_LDS_ROW = 72;  // uint16 per LDS row: 64 samples + 8 pad (144 B)
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict__ X, int64_t n, int64_t d,
+                                                      int64_t ldx, float *__restrict__ C, int64_t ldc, float alpha,
+                                                      float beta)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][SB_TILE * SB_LDS_ROW];
+
+    int ti, tj;
+    tri_tile(xcd_remap(blockIdx.x, gridDim.x), ti, tj);
+    const int64_t i0 = (int64_t)ti * SB_TILE, j0 = (int64_t)tj * SB_TILE;
+    const bool diag = ti == tj;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // loader role: operand (0 = rows of C, 1 = columns of C), 8-feature block, 8-sample block
+    const int op = tid >> 7;
+    const int fb = (tid & 127) >> 3;
+    const int kb = tid & 7;
+    const bool loader = !(diag && op == 1);
+    const int64_t fbase = (op == 0 ? i0 : j0) + fb * 8;
+    const bool f_ok = fbase < d;  // d % 8 == 0: a block is wholly inside or outside
+
+    // v[e] holds samples (k0 + 8 kb + e), features fbase .. fbase + 7 (two per word)
+    u32x4_t v[8];
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int64_t k = k0 + kb * 8 + e;
+            if (loader && f_ok && k < n) {
+                v[e] = *reinterpret_cast<const u32x4_t *>(X + k * ldx + fbase);
+            } else {
+                v[e] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // transpose: LDS row (feature f) gets samples 8 kb .. 8 kb + 7 (two per word)
+    auto lstore = [&](int stage) {
+        if (!loader) return;
+        uint16_t *base = &lds[stage][op][0];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            u32x4_t o;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint32_t a = v[2 * p][f >> 1], b = v[2 * p + 1][f >> 1];
+                o[p] = (f & 1) ? pack_hi(a, b) : pack_lo(a, b);
+            }
+            *reinterpret_cast<u32x4_t *>(base + (fb * 8 + f) * SB_LDS_ROW + kb * 8) = o;
+        }
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool active = !(diag && wm == 0 && wn == 1);  // strictly upper quadrant of a diagonal tile
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int cur = 0;
+    for (int64_t k0 = 0; k0 < n; k0 += SB_BK) {
+        const bool more = k0 + SB_BK < n;
+        if (more) gload(k0 + SB_BK);
+        if (active) {
+            const uint16_t *la = &lds[cur][0][0];
+            const uint16_t *lb = &lds[cur][diag ? 0 : 1][0];
+#pragma unroll
+            for (int kk = 0; kk < SB_BK / 16; ++kk) {
+                bf16x8_t fa[2], fbv[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    int row = wm * 64 + m * 32 + (lane & 31);
+                    fa[m] = *reinterpret_cast<const bf16x8_t *>(la + row * SB_LDS_ROW + kk * 16 + (lane >> 5) * 8);
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    int row = wn * 64 + m * 32 + (lane & 31);
+                    fbv[m] = *reinterpret_cast<const bf16x8_t *>(lb + row * SB_LDS_ROW + kk * 16 + (lane >> 5) * 8);
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fbv[b], acc[a][b], 0, 0, 0);
+            }
+        }
+        if (more) lstore(cur ^ 1);
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    if (!active) return;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t col = j0 + wn * 64 + b * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = i0 + wm * 64 + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+                if (row < d && col < d && row >= col) {
+                    float *p = C + row * ldc + col;
+                    float val = alpha * acc[a][b][e];
+                    if (beta != 0.f) val += beta * *p;
+                    *p = val;
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------- fp64 MFMA
+
+constexpr int SD_TILE = 128;
+constexpr int SD_BK = 16;
+constexpr int SD_LDS_ROW = SD_TILE + 2;  // doubles per LDS row (pad 16 B)
+
+__global__ __launch_bounds__(256) void syrk_f64_mfma(const float *__restrict__ X, int64_t n, int64_t d, int64_t ldx,
+                                                     double *__restrict__ C, int64_t ldc, double alpha, double beta)
+{
+    __shared__ __attribute__((aligned(16))) double lds[2][2][SD_BK * SD_LDS_ROW];
+
+    int ti, tj;
+    tri_tile(xcd_remap(blockIdx.x, gridDim.x), ti, tj);
+    const int64_t i0 = (int64_t)ti * SD_TILE, j0 = (int64_t)tj * SD_TILE;
+    const bool diag = ti == tj;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // loader: operand op = tid >> 7; each thread loads 2 x float4 (rows kr, kr + 8; 4 features)
+    const int op = tid >> 7;
+    const int u = tid & 127;
+    const int fq = u & 31;       // 4-feature group within the 128 features
+    const int kr = u >> 5;       // 0..3 -> rows kr, kr+4, kr+8, kr+12
+    const bool loader = !(diag && op == 1);
+    const int64_t fbase = (op == 0 ? i0 : j0) + fq * 4;
+    const bool f_ok = fbase < d;  // d % 4 == 0
+
+    float4 v[4];
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int64_t k = k0 + kr + 4 * e;
+            if (loader && f_ok && k < n)
+                v[e] = *reinterpret_cast<const float4 *>(X + k * ldx + fbase);
+            else
+                v[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto lstore = [&](int stage) {
+        if (!loader) return;
+        double *base = &lds[stage][op][0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            double *p = base + (kr + 4 * e) * SD_LDS_ROW + fq * 4;
+            p[0] = (double)v[e].x;
+            p[1] = (double)v[e].y;
+            p[2] = (double)v[e].z;
+            p[3] = (double)v[e].w;
+        }
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool active = !(diag && wm == 0 && wn == 1);
+    f64x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int cur = 0;
+    for (int64_t k0 = 0; k0 < n; k0 += SD_BK) {
+        const bool more = k0 + SD_BK < n;
+        if (more) gload(k0 + SD_BK);
+        if (active) {
+            const double *la = &lds[cur][0][0];
+            const double *lb = &lds[cur][diag ? 0 : 1][0];
+#pragma unroll
+            for (int kk = 0; kk < SD_BK / 4; ++kk) {
+                const int krow = kk * 4 + (lane >> 4);
+                double fa[4], fbv[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) fa[m] = la[krow * SD_LDS_ROW + wm * 64 + m * 16 + (lane & 15)];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) fbv[m] = lb[krow * SD_LDS_ROW + wn * 64 + m * 16 + (lane & 15)];
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[a], fbv[b], acc[a][b], 0, 0, 0);
+            }
+        }
+        if (more) lstore(cur ^ 1);
+        __syncthreads();
+        cur ^= 1;
+    }
+    if (!active) return;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t col = j0 + wn * 64 + b * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // v_mfma_f64_16x16x4f64 result: lane l holds column l % 16, rows l / 16 + 4 e
+                const int64_t row = i0 + wm * 64 + a * 16 + (lane >> 4) + 4 * e;
+                if (row < d && col < d && row >= col) {
+                    double *p = C + row * ldc + col;
+                    double val = alpha * acc[a][b][e];
+                    if (beta != 0.0) val += beta * *p;
+                    *p = val;
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------- generic VALU
+
+template <typename TIn>
+__device__ __forceinline__ float load_in(const TIn *p);
+template <>
+__device__ __forceinline__ float load_in<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+constexpr int SG_TILE = 64;
+constexpr int SG_BK = 16;
+
+template <typename TIn, typename TAcc>
+__global__ __launch_bounds__(256) void syrk_generic(const TIn *__restrict__ X, int64_t n, int64_t d, int64_t ldx,
+                                                    TAcc *__restrict__ C, int64_t ldc, TAcc alpha, TAcc beta)
+{
+    __shared__ TAcc As[SG_BK][SG_TILE + 1], Bs[SG_BK][SG_TILE + 1];
+    int ti, tj;
+    tri_tile(blockIdx.x, ti, tj);
+    const int64_t i0 = (int64_t)ti * SG_TILE, j0 = (int64_t)tj * SG_TILE;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    TAcc acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0;
+    for (int64_t k0 = 0; k0 < n; k0 += SG_BK) {
+        for (int idx = threadIdx.x; idx < SG_BK * SG_TILE; idx += 256) {
+            int kk = idx / SG_TILE, f = idx % SG_TILE;
+            int64_t k = k0 + kk;
+            TAcc va = 0, vb = 0;
+            if (k < n && i0 + f < d) va = (TAcc)load_in<TIn>(X + k * ldx + i0 + f);
+            if (k < n && j0 + f < d) vb = (TAcc)load_in<TIn>(X + k * ldx + j0 + f);
+            As[kk][f] = va;
+            Bs[kk][f] = vb;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < SG_BK; ++kk) {
+            TAcc a[4], b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = As[kk][ty * 4 + e];
+                b[e] = Bs[kk][tx * 4 + e];
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[p][q] += a[p] * b[q];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int64_t row = i0 + ty * 4 + p, col = j0 + tx * 4 + q;
+            if (row < d && col < d && row >= col) {
+                TAcc *ptr = C + row * ldc + col;
+                TAcc val = alpha * acc[p][q];
+                if (beta != (TAcc)0) val += beta * *ptr;
+                *ptr = val;
+            }
+        }
+}
+
+inline int64_t tri_count(int64_t t) { return t * (t + 1) / 2; }
+
+}  // namespace
+
+hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int64_t d, int64_t ldx, void *C, int ct,
+                       int64_t ldc, double alpha, double beta)
+{
+    if (xt == SPEC_BF16 && ct == SPEC_F32) {
+        if (d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0) {
+            int64_t tiles = tri_count((d + SB_TILE - 1) / SB_TILE);
+            hipLaunchKernelGGL(syrk_bf16_mfma, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint16_t *)X, n, d,
+                               ldx, (float *)C, ldc, (float)alpha, (float)beta);
+        } else {
+            int64_t tiles = tri_count((d + SG_TILE - 1) / SG_TILE);
+            hipLaunchKernelGGL((syrk_generic<uint16_t, float>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                               (const uint16_t *)X, n, d, ldx, (float *)C, ldc, (float)alpha, (float)beta);
+        }
+    } else if (xt == SPEC_F32 && ct == SPEC_F32) {
+        int64_t tiles = tri_count((d + SG_TILE - 1) / SG_TILE);
+        hipLaunchKernelGGL((syrk_generic<float, float>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                           (const float *)X, n, d, ldx, (float *)C, ldc, (float)alpha, (float)beta);
+    } else if (xt == SPEC_F32 && ct == SPEC_F64) {
+        if (d % 4 == 0 && ldx % 4 == 0 && ((uintptr_t)X % 16) == 0) {
+            int64_t tiles = tri_count((d + SD_TILE - 1) / SD_TILE);
+            hipLaunchKernelGGL(syrk_f64_mfma, dim3((unsigned)tiles), dim3(256), 0, stream, (const float *)X, n, d, ldx,
+                               (double *)C, ldc, alpha, beta);
+        } else {
+            int64_t tiles = tri_count((d + SG_TILE - 1) / SG_TILE);
+            hipLaunchKernelGGL((syrk_generic<float, double>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                               (const float *)X, n, d, ldx, (double *)C, ldc, alpha, beta);
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
