@@ -137,16 +137,19 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
  *     section 6.1 names as the cost for large d).
  *
  * Two-stage reduction: blocked Householder reduction of the dense matrix to
- * band form (bandwidth 32; trailing updates on MFMA), bulge chasing from band
- * to tridiagonal, then all eigenvalues of the tridiagonal by Sturm-count
- * bisection.  t is SPEC_F32 or SPEC_F64; arithmetic is in t.
+ * band form (bandwidth 32; tall panels by TSQR with Householder reconstruction;
+ * trailing updates on MFMA), bulge chasing from band to tridiagonal in one
+ * persistent kernel, then all eigenvalues of the tridiagonal by multisection
+ * on Sturm counts (fp64).  t is SPEC_F32 or SPEC_F64; the reductions run in t.
  *
  * A: n x n, lower triangle read, DESTROYED (used as the working matrix).
  * w: n values of type t, descending.
- * ws: device workspace of at least spec_eigvalsh_large_workspace(n, t) bytes.
+ * ws: device workspace of at least spec_eigvalsh_large_workspace(n, t) bytes
+ *     (256-byte aligned); its contents on entry are ignored.
  * info: int32 [1] device (may be NULL): 0 on success, 1 if the bulge-chasing
- *       pipeline hit its spin limit (results invalid).
- * Requires 1 <= n <= 32768 (SPEC_F32) or n <= 16384 (SPEC_F64), lda >= n.
+ *       pipeline hit its bounded wait (results invalid).
+ * Calls sharing one workspace must be ordered on one stream.
+ * Requires 1 <= n <= 32768 (SPEC_F32) or n <= 8192 (SPEC_F64), lda >= n.
  * ---------------------------------------------------------------------- */
 int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes);
 
@@ -179,8 +182,8 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
  *
  * out: device array of `batch` spec_desc records.
  * ws:  device workspace of spec_descriptors_workspace(r) bytes (the MP quantile table).
- * Requires r >= 1, ldw >= r, 1 <= k < r (k is clamped to r-1 when r == 1 is not allowed),
- * n_samples >= 1, p_dim >= 1, top_frac and tail_frac in [0, 1], small_rel >= 0.
+ * Requires r >= 2, ldw >= r, 1 <= k < r, n_samples >= 1, p_dim >= 1, top_frac and
+ * tail_frac in [0, 1], small_rel >= 0, sigma2 > 0 when sigma2_mode is GIVEN.
  * ---------------------------------------------------------------------- */
 enum { SPEC_MODE_EIG = 0, SPEC_MODE_SINGULAR = 1 };
 enum { SPEC_SIGMA2_GIVEN = 0, SPEC_SIGMA2_MEDIAN = 1, SPEC_SIGMA2_MEAN = 2 };

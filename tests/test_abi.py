@@ -101,6 +101,7 @@ def test_large_validation(L):
     assert L.spec_eigvalsh_large_workspace(4096, spec.BF16, ctypes.byref(b)) == EUNSUPPORTED
     assert L.spec_eigvalsh_large_workspace(0, spec.F32, ctypes.byref(b)) == EINVAL
     assert L.spec_eigvalsh_large_workspace(40000, spec.F32, ctypes.byref(b)) == EUNSUPPORTED
+    assert L.spec_eigvalsh_large_workspace(8193, spec.F64, ctypes.byref(b)) == EUNSUPPORTED
     L.spec_eigvalsh_large_workspace(512, spec.F64, ctypes.byref(b))
     f = L.spec_eigvalsh_large
     assert f(None, FAKE, spec.F64, 512, 512, FAKE, FAKE, b.value - 1, None) == EWORKSPACE

@@ -90,7 +90,7 @@ int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes)
 {
     if (bytes == nullptr || n < 1) return SPEC_EINVAL;
     if (t != SPEC_F32 && t != SPEC_F64) return SPEC_EUNSUPPORTED;
-    if ((t == SPEC_F32 && n > 32768) || (t == SPEC_F64 && n > 16384)) return SPEC_EUNSUPPORTED;
+    if ((t == SPEC_F32 && n > 32768) || (t == SPEC_F64 && n > 8192)) return SPEC_EUNSUPPORTED;
     *bytes = eig_large_workspace_bytes(n, t);
     return SPEC_OK;
 }
