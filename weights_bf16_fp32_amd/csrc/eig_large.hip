@@ -65,21 +65,36 @@ __device__ T block_sum256(T x, T *red)
 
 // Householder QR of the rows x NB matrix P (LDS, stride LDP) by 256 threads:
 // kr reflectors H_k = I - tau_k v_k v_k^T (v_k[k] = 1 implicit, v_k below the
-// diagonal of column k), R in the upper triangle.  Then T (NB x NB, upper) of
-// the forward product H_0 ... H_{kr-1} = I - V T V^T into Tl.
+// diagonal of column k), R in the upper triangle, and T (NB x NB, upper) of the
+// forward product H_0 ... H_{kr-1} = I - V T V^T in Tl.
+// Per column k, thread (c, g) = (tid % 32, tid / 32) covers rows k+1+g, +8, ...:
+//   pass 1 forms the dot products d_c = v_k^T P[k:, c] for every column c, which
+//     gives w_c (c > k) for the update and G[c][k] = v_c^T v_k (c < k) for T;
+//   pass 2 updates the columns c > k, writes v_k, accumulates the squared norm
+//     of column k+1 below its diagonal (the next reflector's sigma) and forms
+//     T[0:k, k] = -tau_k T[0:k, 0:k] G[0:k, k].
+// v_k is produced on the fly as scale * x in pass 1 and stored in pass 2.
 template <typename T>
 __device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
 {
     const int tid = threadIdx.x;
-    T *red2 = red + 8;  // 8 x 32 partials
+    const int c = tid & 31, g = tid >> 5;
+    T *dots = red;         // 8 x 32 partial dot products
+    T *sig = red + 256;    // 8 partial sums of squares (next column)
+    T *bc = red + 264;     // broadcast: [0] scale, [1] tau
+    for (int p = tid; p < NB * NB; p += 256) Tl[p] = 0;
+    // sigma of column 0
+    if (c == 0) {
+        T s = 0;
+        for (int i = 1 + g; i < rows; i += 8) s += P[i * LDP] * P[i * LDP];
+        sig[g] = s;
+    }
+    __syncthreads();
     for (int k = 0; k < kr; ++k) {
-        T part = 0;
-        for (int i = k + 1 + tid; i < rows; i += 256) {
-            T x = P[i * LDP + k];
-            part += x * x;
-        }
-        const T sigma = block_sum256(part, red);
         if (tid == 0) {
+            T sigma = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sigma += sig[q];
             const T x0 = P[k * LDP + k];
             T t = 0, scale = 0;
             if (sigma > 0) {
@@ -87,58 +102,62 @@ __device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
                 const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
                 t = 2 * v0 * v0 / (sigma + v0 * v0);
                 scale = 1 / v0;
-                P[k * LDP + k] = mu;
+                P[k * LDP + k] = mu;  // R_kk; column k, row k is not read by pass 1 below
             }
             tau[k] = t;
-            red[4] = scale;
+            bc[0] = scale;
+            bc[1] = t;
         }
         __syncthreads();
-        const T t = tau[k], scale = red[4];
-        if (t != 0) {
-            for (int i = k + 1 + tid; i < rows; i += 256) P[i * LDP + k] *= scale;
-            __syncthreads();
-            const int c = tid & 31, g = tid >> 5;
-            T wp = 0;
-            if (c > k) {
-                if (g == 0) wp = P[k * LDP + c];
-                for (int i = k + 1 + g; i < rows; i += 8) wp += P[i * LDP + k] * P[i * LDP + c];
-            }
-            red2[g * 32 + c] = wp;
-            __syncthreads();
-            if (c > k) {
-                T wc = 0;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) wc += red2[q * 32 + c];
-                if (g == 0) P[k * LDP + c] -= t * wc;
-                for (int i = k + 1 + g; i < rows; i += 8) P[i * LDP + c] -= t * P[i * LDP + k] * wc;
-            }
-            __syncthreads();
+        const T scale = bc[0], t = bc[1];
+        // pass 1: d_c = P[k][c] (v_k[k] = 1; for c == k the row-k value is R_kk, unused)
+        //             + sum_{i > k} scale * P[i][k] * P[i][c]
+        T d0 = 0, d1 = 0;
+        int i = k + 1 + g;
+        for (; i + 8 < rows; i += 16) {
+            d0 += P[i * LDP + k] * P[i * LDP + c];
+            d1 += P[(i + 8) * LDP + k] * P[(i + 8) * LDP + c];
         }
+        if (i < rows) d0 += P[i * LDP + k] * P[i * LDP + c];
+        dots[g * 32 + c] = (d0 + d1) * scale;
+        __syncthreads();
+        T dc = P[k * LDP + c];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dc += dots[q * 32 + c];
+        // pass 2
+        if (t != 0 && c > k) {
+            const T wc = t * dc;
+            if (g == 0) P[k * LDP + c] -= wc;
+            T s2 = 0;
+            for (int r = k + 1 + g; r < rows; r += 8) {
+                const T nv = P[r * LDP + c] - wc * scale * P[r * LDP + k];
+                P[r * LDP + c] = nv;
+                if (c == k + 1 && r > k + 1) s2 += nv * nv;
+            }
+            if (c == k + 1) sig[g] = s2;
+        } else if (t == 0 && c == k + 1) {
+            T s2 = 0;
+            for (int r = k + 2 + g; r < rows; r += 8) s2 += P[r * LDP + c] * P[r * LDP + c];
+            sig[g] = s2;
+        }
+        if (c == k && t != 0)
+            for (int r = k + 1 + g; r < rows; r += 8) P[r * LDP + k] *= scale;
+        if (tid < k) {
+            // G[j][k] = d_j for j < k (read from the dot buffer of this step)
+            T s = 0;
+            for (int j = tid; j < k; ++j) {
+                T gj = P[k * LDP + j];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) gj += dots[q * 32 + j];
+                s += Tl[tid * NB + j] * gj;
+            }
+            Tl[tid * NB + k] = -t * s;
+        }
+        if (tid == 0) Tl[k * NB + k] = t;
+        __syncthreads();
     }
     for (int k = kr + tid; k < NB; k += 256) tau[k] = 0;
-    // G = V^T V (strict upper part), V[i][j] = [i == j] + [i > j] P[i][j]
-    T *G = red2 + 256;  // NB x NB
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int j = p / NB, k = p % NB;
-        T g = 0;
-        if (j < k && k < kr) {
-            g = P[k * LDP + j];
-            for (int i = k + 1; i < rows; ++i) g += P[i * LDP + j] * P[i * LDP + k];
-        }
-        G[p] = g;
-    }
-    for (int p = tid; p < NB * NB; p += 256) Tl[p] = 0;
     __syncthreads();
-    for (int k = 0; k < kr; ++k) {
-        // T[0:k, k] = -tau_k T[0:k, 0:k] G[0:k, k]
-        if (tid < k) {
-            T s = 0;
-            for (int j = tid; j < k; ++j) s += Tl[tid * NB + j] * G[j * NB + k];
-            Tl[tid * NB + k] = -tau[k] * s;
-        }
-        if (tid == 0) Tl[k * NB + k] = tau[k];
-        __syncthreads();
-    }
 }
 
 // LDS budget of the QR kernels: panel rows x LDP + tau + T + reduction scratch
@@ -147,7 +166,7 @@ struct QrLds {
     T P[Cfg<T>::RB * LDP];
     T tau[NB];
     T Tl[NB * NB];
-    T red[8 + 256 + NB * NB];
+    T red[272];
 };
 
 // ---- direct panel: m <= RB rows, one workgroup
@@ -643,6 +662,24 @@ __device__ __forceinline__ T wave_sum(T x)
     return x;
 }
 
+// Band elements are exchanged between workgroups on different XCDs.  Every
+// band access is a relaxed agent-scope atomic (a load or store that is coherent
+// across the device by itself), so no cache-wide writeback or invalidation is
+// needed; a task's stores are complete (s_waitcnt) before its progress counter
+// is published, and a waiting task issues its loads only after it has seen the
+// counter.  The wait is bounded: on time-out the error flag is set and every
+// workgroup leaves.
+template <typename T>
+__device__ __forceinline__ T cload(const T *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void cstore(T *p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One 64-lane workgroup per in-flight sweep; sweeps s = blockIdx.x + j gridDim.x.
 template <typename T>
 __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ prog,
@@ -656,7 +693,8 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
     const int ci = lane & 31, h = lane >> 5;
     int32_t *err = prog + n;
     const int64_t nsw = n - 2;
-    auto B = [&](int64_t r, int64_t c) -> T & { return band[c * BW + (r - c)]; };
+    auto ldB = [&](int64_t r, int64_t c) -> T { return cload(band + c * BW + (r - c)); };
+    auto stB = [&](int64_t r, int64_t c, T x) { cstore(band + c * BW + (r - c), x); };
 
     for (int64_t s = blockIdx.x; s < nsw; s += gridDim.x) {
         const int nt = ntasks_of(s, n);
@@ -669,26 +707,26 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
             if (s > 0) {
                 if (lane == 0) {
                     const int need = min(k + 2, ntasks_of(s - 1, n));
-                    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                     int ok = 1;
-                    while (__hip_atomic_load(prog + s - 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                        if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
-                            __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
-                            ok = 0;
-                            break;
+                    if (cload(prog + s - 1) < need) {
+                        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                        while (cload(prog + s - 1) < need) {
+                            if (cload(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
+                                ok = 0;
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(1);
                         }
-                        __builtin_amdgcn_s_sleep(1);
                     }
-                    if (!ok) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (!ok) cstore(err, 1);
                     go = ok;
                 }
                 __syncthreads();
                 if (!go) return;
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             T tau = 0, mu = 0;
             if (k == 0) {
-                const T x = lane < L ? B(r0 + lane, s) : (T)0;
+                const T x = lane < L ? ldB(r0 + lane, s) : (T)0;
                 const T sigma = wave_sum(lane >= 1 && lane < L ? x * x : (T)0);
                 const T x0 = __shfl(x, 0, 64);
                 T vi = 0;
@@ -697,12 +735,12 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
                     tau = 2 * v0 * v0 / (sigma + v0 * v0);
                     vi = lane == 0 ? (T)1 : x / v0;
-                    if (lane < L) B(r0 + lane, s) = lane == 0 ? mu : (T)0;
+                    if (lane < L) stB(r0 + lane, s, lane == 0 ? mu : (T)0);
                 }
                 if (lane < NB) v[lane] = vi;
             } else {
                 const int64_t c0 = r0 - NB;
-                for (int i = h; i < L; i += 2) O[i * LDP + ci] = B(r0 + i, c0 + ci);
+                for (int i = h; i < L; i += 2) O[i * LDP + ci] = ldB(r0 + i, c0 + ci);
                 __syncthreads();
                 // right: O <- O (I - taup vp vp^T)
                 if (taup != 0) {
@@ -728,7 +766,7 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
                 if (lane < NB) v[lane] = lane < L ? vi : (T)0;
                 __syncthreads();
                 if (tau != 0) {
-                    // left: O <- (I - tau v v^T) O, columns 1.. ; column 0 becomes mu e_0
+                    // left: O <- (I - tau v v^T) O; column 0 becomes mu e_0
                     T w = 0;
                     for (int i = h; i < L; i += 2) w += v[i] * O[i * LDP + ci];
                     w += __shfl_xor(w, 32, 64);
@@ -737,13 +775,13 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
                     if (lane < L) O[lane * LDP] = lane == 0 ? mu : (T)0;
                     __syncthreads();
                 }
-                for (int i = h; i < L; i += 2) B(r0 + i, c0 + ci) = O[i * LDP + ci];
+                for (int i = h; i < L; i += 2) stB(r0 + i, c0 + ci, O[i * LDP + ci]);
             }
             __syncthreads();
             if (tau != 0) {
                 // two-sided on the diagonal block D = A[r0..r1, r0..r1]
                 for (int i = h; i < L; i += 2)
-                    if (ci < L) D[i * LDP + ci] = ci <= i ? B(r0 + i, r0 + ci) : B(r0 + ci, r0 + i);
+                    if (ci < L) D[i * LDP + ci] = ci <= i ? ldB(r0 + i, r0 + ci) : ldB(r0 + ci, r0 + i);
                 __syncthreads();
                 T p = 0;
                 if (ci < L)
@@ -755,12 +793,14 @@ __global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, i
                 if (h == 0) red[ci] = ci < L ? wv : (T)0;
                 __syncthreads();
                 for (int i = h; i < L; i += 2)
-                    if (ci <= i) B(r0 + i, r0 + ci) = D[i * LDP + ci] - v[i] * red[ci] - red[i] * v[ci];
+                    if (ci <= i) stB(r0 + i, r0 + ci, D[i * LDP + ci] - v[i] * red[ci] - red[i] * v[ci]);
             }
             if (lane < NB) vp[lane] = v[lane];
             taup = tau;
+            // every band store of this task is complete before the counter moves
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (lane == 0) __hip_atomic_store(prog + s, k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) cstore(prog + s, k + 1);
         }
     }
 }
@@ -928,6 +968,9 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     Bufs<T> b;
     layout<T>(n, (char *)ws, b);
     constexpr int RB = Cfg<T>::RB;
+    constexpr int TOP_BLOCKS = RB / NB;  // stacked R rows fit the LDS panel
+    constexpr int DIRECT_ROWS = 256;
+    static_assert(DIRECT_ROWS <= RB, "direct panel must fit");
     // ---- stage 1: dense -> band
     for (int64_t c0 = 0;; c0 += NB) {
         const int64_t r0 = c0 + NB;
@@ -935,11 +978,13 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         if (m < 2) break;
         T *P = A + r0 * lda + c0;
         T *A22 = A + r0 * lda + r0;
-        if (m <= RB) {
+        if (m <= DIRECT_ROWS) {
             hipLaunchKernelGGL(k_panel_direct<T>, dim3(1), dim3(256), 0, st, P, lda, (int)m, b.V, b.Tm);
             LAUNCH_OK();
         } else {
-            const int nblk = (int)cdiv_h(m, RB);
+            // row blocks of about 256 rows, at most TOP_BLOCKS of them (the stacked R
+            // factors of all blocks are factored by one workgroup)
+            const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
             const int per = (int)cdiv_h(m, nblk);
             hipLaunchKernelGGL(k_tsqr_local<T>, dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per, b.Vloc, b.Tloc,
                                b.Rstack);
@@ -982,7 +1027,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     if (n >= 3) {
         const int64_t nsw = n - 2;
         const int grid = (int)std::min<int64_t>(nsw, 240);
-        const uint64_t spin_ticks = 100000000ull * 20;  // 20 s at the 100 MHz real-time counter
+        const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
         hipLaunchKernelGGL(k_bulge<T>, dim3(grid), dim3(64), 0, st, b.band, n, b.prog, spin_ticks);
         LAUNCH_OK();
     }
