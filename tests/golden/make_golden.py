@@ -6,7 +6,6 @@ of the generated input (so a test can confirm it regenerated the same bits),
 the oracle's eigenvalues (descending) and the oracle's descriptors.
 
     python tests/golden/make_golden.py swiftsvd      # 32 x 2048 x 4096 bf16 chunks
-    python tests/golden/make_golden.py s3 0 13 31    # selected 4096 x 4096 layers
     python tests/golden/make_golden.py ffn           # 65536 x 14336 bf16
 
 Outputs: tests/golden/<workload>[_<layer>].npz with arrays ``eig`` (fp64),

@@ -21,7 +21,7 @@ PCG64, in a fixed draw order):
                  incremental covariance of the Swift-SVD page, sections 2 and 7.
 * ``ffn``        X bf16 [65536, 14336]: N(0,1) plus a rank-64 additive spike
                  with theta log-uniform in [0.5, 50] (FFN width 14336 from the
-                 S3 page, section 5.1).
+                 S3 page, section 5.1); generated bit-identically on any host.
 * ``s3``         32 layers W f32 [4096, 4096] = U diag(sigma) V^T with Haar
                  U, V and sigma_i = (2i-1)^(-a), a = 3 / log10(2d-1), so that
                  sigma_1 = 1, sigma_d = 1e-3 (S3 page, section 2).
@@ -73,6 +73,22 @@ def orthonormal(rng: np.random.Generator, d: int, k: int) -> np.ndarray:
     g = rng.standard_normal((d, k))
     q, r = np.linalg.qr(g)
     return q * np.sign(np.diag(r))
+
+
+def orthonormal_exact(rng: np.random.Generator, d: int, k: int) -> np.ndarray:
+    """d x k orthonormal columns by twice-applied modified Gram-Schmidt on a
+    Gaussian, every inner product an exactly rounded sum (math.fsum), so the
+    result has the same bits on any host (BLAS and LAPACK round differently on
+    different CPUs)."""
+    g = rng.standard_normal((d, k))
+    q = np.empty((d, k))
+    for j in range(k):
+        v = g[:, j].copy()
+        for _ in range(2):
+            for i in range(j):
+                v = v - math.fsum(v * q[:, i]) * q[:, i]
+        q[:, j] = v / math.sqrt(math.fsum(v * v))
+    return q
 
 
 def haar_orthogonal(rng: np.random.Generator, d: int) -> np.ndarray:
@@ -136,26 +152,32 @@ def swiftsvd(chunks: int = 32, n: int = 2048, d: int = 4096, outliers: int = 16,
 
 
 def ffn_spikes(d: int = 14336, rank: int = 64, theta_lo: float = 0.5, theta_hi: float = 50.0):
-    """(theta [rank], U [d, rank]) of the FFN-width spiked covariance."""
+    """(theta [rank], U [d, rank]) of the FFN-width spiked covariance, and the
+    spike loadings L = sqrt(theta_k) u_k rounded to the grid 2^-20 ([rank, d])."""
     rng = rng_for("ffn")
     u01 = rng.uniform(0.0, 1.0, size=rank)
     theta = theta_lo * (theta_hi / theta_lo) ** u01
-    U = orthonormal(rng, d, rank)
-    return theta, U
+    U = orthonormal_exact(rng, d, rank)
+    L = np.round(np.sqrt(theta)[:, None] * U.T * 2.0 ** 20) / 2.0 ** 20
+    return theta, U, L
 
 
 def ffn(n: int = 65536, d: int = 14336, rank: int = 64, theta_lo: float = 0.5,
         theta_hi: float = 50.0, row_block: int = 4096) -> np.ndarray:
-    """bf16 bits [n, d]: X = Z + S diag(sqrt(theta)) U^T."""
-    theta, U = ffn_spikes(d, rank, theta_lo, theta_hi)
-    L = (np.sqrt(theta)[:, None] * U.T).astype(np.float32)  # [rank, d]
+    """bf16 bits [n, d]: X = Z + S L with Z ~ N(0, 1), S ~ +-1 (Rademacher; mean 0,
+    variance 1, so E[x x^T] = I + sum_k theta_k u_k u_k^T).  L sits on the grid
+    2^-20 and S is +-1, so every entry of S L is an integer multiple of 2^-20 below
+    2^26 ulps and the fp64 product is exact in any summation order: the same bits
+    on every host."""
+    _, _, L = ffn_spikes(d, rank, theta_lo, theta_hi)
     out = np.empty((n, d), dtype=np.uint16)
     for i, r0 in enumerate(range(0, n, row_block)):
         r1 = min(n, r0 + row_block)
         rng = rng_for("ffn", 1 + i)
         z = rng.standard_normal((r1 - r0, d), dtype=np.float32)
-        s = rng.standard_normal((r1 - r0, rank), dtype=np.float32)
-        out[r0:r1] = f32_to_bf16_bits(z + s @ L)
+        s = rng.integers(0, 2, size=(r1 - r0, rank)).astype(np.float64) * 2.0 - 1.0
+        x = z.astype(np.float64) + s @ L
+        out[r0:r1] = f32_to_bf16_bits(x.astype(np.float32))
     return out
 
 
