@@ -21,9 +21,11 @@
 //   applies the previous reflector from the right to the off-diagonal block,
 //   builds a reflector from its first column, applies it from the left and to
 //   the diagonal block from both sides.  Task (s, k) may run once task
-//   (s-1, k+1) is done, so one persistent kernel runs many sweeps at once,
-//   one 64-lane wave per sweep, ordered by per-sweep progress counters with
-//   agent-scope release/acquire and a bounded wait.
+//   (s-1, k+1) is done, so the tasks (s, t - 2s) of one time step t are
+//   independent.  A workgroup runs G consecutive sweeps, one wave each, a time
+//   step at a time, with their rows in an LDS ring; consecutive groups are
+//   ordered by a row watermark (rows below it are final and stored back),
+//   with a bounded wait.
 // Stage 3, eigenvalues of the tridiagonal: 16-section on the Sturm count
 //   (number of negative pivots of LDL^T(T - xI)) in fp64, 16 lanes per
 //   eigenvalue, from the Gershgorin interval; results in descending order.
@@ -82,6 +84,7 @@ __device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
     T *dots = red;         // 8 x 32 partial dot products
     T *sig = red + 256;    // 8 partial sums of squares (next column)
     T *bc = red + 264;     // broadcast: [0] scale, [1] tau
+    T *gk = red + 272;     // G[0:k, k] of the previous step
     for (int p = tid; p < NB * NB; p += 256) Tl[p] = 0;
     // sigma of column 0
     if (c == 0) {
@@ -90,7 +93,17 @@ __device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
         sig[g] = s;
     }
     __syncthreads();
+    // T[0:k, k] = -tau_k T[0:k, 0:k] G[0:k, k], from the G column published by step k
+    auto t_column = [&](int k) {
+        if (tid < k) {
+            T acc = 0;
+            for (int j = tid; j < k; ++j) acc += Tl[tid * NB + j] * gk[j];
+            Tl[tid * NB + k] = -tau[k] * acc;
+        }
+        if (tid == 0) Tl[k * NB + k] = tau[k];
+    };
     for (int k = 0; k < kr; ++k) {
+        if (k > 0) t_column(k - 1);
         if (tid == 0) {
             T sigma = 0;
 #pragma unroll
@@ -142,20 +155,10 @@ __device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
         }
         if (c == k && t != 0)
             for (int r = k + 1 + g; r < rows; r += 8) P[r * LDP + k] *= scale;
-        if (tid < k) {
-            // G[j][k] = d_j for j < k (read from the dot buffer of this step)
-            T s = 0;
-            for (int j = tid; j < k; ++j) {
-                T gj = P[k * LDP + j];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) gj += dots[q * 32 + j];
-                s += Tl[tid * NB + j] * gj;
-            }
-            Tl[tid * NB + k] = -t * s;
-        }
-        if (tid == 0) Tl[k * NB + k] = t;
+        if (g == 0 && c < k) gk[c] = dc;  // G[c][k] = v_c^T v_k
         __syncthreads();
     }
+    if (kr > 0) t_column(kr - 1);
     for (int k = kr + tid; k < NB; k += 256) tau[k] = 0;
     __syncthreads();
 }
@@ -166,7 +169,7 @@ struct QrLds {
     T P[Cfg<T>::RB * LDP];
     T tau[NB];
     T Tl[NB * NB];
-    T red[272];
+    T red[272 + NB];
 };
 
 // ---- direct panel: m <= RB rows, one workgroup
@@ -642,14 +645,16 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_band_copy(const T *__restrict__ A, int64_t lda, int64_t n,
                                                    T *__restrict__ band, int32_t *__restrict__ prog)
 {
+    // row-major band: band[r * BW + j] = A[r][r - j], 0 <= j < BW (zero beyond the
+    // stage-1 bandwidth; the extra columns hold the bulges of stage 2)
     const int64_t idx = blockIdx.x * 256 + threadIdx.x;
     if (idx < n * BW) {
-        const int64_t c = idx / BW, d = idx % BW;
+        const int64_t r = idx / BW, j = idx % BW;
         T v = 0;
-        if (d <= NB && c + d < n) v = A[(c + d) * lda + c];
+        if (j <= NB && r - j >= 0) v = A[r * lda + (r - j)];
         band[idx] = v;
     }
-    if (idx <= n) prog[idx] = 0;  // prog[n] is the error flag
+    if (idx <= n) prog[idx] = 0;  // per-group row watermarks; prog[n] is the error flag
 }
 
 __device__ __forceinline__ int ntasks_of(int64_t s, int64_t n) { return (int)((n - 2 - s) / NB) + 1; }
@@ -662,13 +667,12 @@ __device__ __forceinline__ T wave_sum(T x)
     return x;
 }
 
-// Band elements are exchanged between workgroups on different XCDs.  Every
-// band access is a relaxed agent-scope atomic (a load or store that is coherent
+// Band rows are exchanged between workgroups on different XCDs.  Every such
+// access is a relaxed agent-scope atomic (a load or store that is coherent
 // across the device by itself), so no cache-wide writeback or invalidation is
-// needed; a task's stores are complete (s_waitcnt) before its progress counter
-// is published, and a waiting task issues its loads only after it has seen the
-// counter.  The wait is bounded: on time-out the error flag is set and every
-// workgroup leaves.
+// needed; a group's row stores are complete (s_waitcnt) before its watermark is
+// published, and the next group loads rows only after it has seen it.  Waits
+// are bounded: on time-out the error flag is set and every workgroup leaves.
 template <typename T>
 __device__ __forceinline__ T cload(const T *p)
 {
@@ -680,128 +684,197 @@ __device__ __forceinline__ void cstore(T *p, T v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One 64-lane workgroup per in-flight sweep; sweeps s = blockIdx.x + j gridDim.x.
-template <typename T>
-__global__ __launch_bounds__(64) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ prog,
-                                              uint64_t spin_ticks)
+// Orders LDS traffic between the lanes of one wave (a wave's LDS operations
+// complete in program order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_sync()
 {
-    __shared__ T O[NB * LDP];
-    __shared__ T D[NB * LDP];
-    __shared__ T v[NB], vp[NB], red[64];
-    __shared__ int go;
-    const int lane = threadIdx.x;
-    const int ci = lane & 31, h = lane >> 5;
-    int32_t *err = prog + n;
-    const int64_t nsw = n - 2;
-    auto ldB = [&](int64_t r, int64_t c) -> T { return cload(band + c * BW + (r - c)); };
-    auto stB = [&](int64_t r, int64_t c, T x) { cstore(band + c * BW + (r - c), x); };
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    for (int64_t s = blockIdx.x; s < nsw; s += gridDim.x) {
-        const int nt = ntasks_of(s, n);
-        T taup = 0;
-        for (int k = 0; k < nt; ++k) {
-            const int64_t r0 = s + 1 + (int64_t)k * NB;
-            const int64_t r1 = min(s + (int64_t)(k + 1) * NB, n - 1);
-            const int L = (int)(r1 - r0 + 1);
-            // wait for task (s - 1, k + 1)
-            if (s > 0) {
-                if (lane == 0) {
-                    const int need = min(k + 2, ntasks_of(s - 1, n));
-                    int ok = 1;
-                    if (cload(prog + s - 1) < need) {
-                        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                        while (cload(prog + s - 1) < need) {
-                            if (cload(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
-                                ok = 0;
-                                break;
+// One workgroup of G waves per group of G consecutive sweeps s0 .. s0+G-1.
+// At time step t wave i runs task (s0 + i, t - 2 (s0 + i)): the tasks of one
+// time step touch disjoint rows and depend only on tasks of earlier steps
+// ("(s, k) after (s - 1, k + 1)"), so the G waves run them side by side.  The
+// rows of the group stay in an LDS ring (row r at slot r & (CAPR - 1), its band
+// entries A[r][r - j] contiguous).  The lead sweep s0 loads each row once, after
+// the previous group's watermark has passed it; after every time step the rows
+// no future task of the group touches are stored back and the group's
+// watermark moves.
+template <typename T, int G, int CAPR>
+__global__ __launch_bounds__(64 * G) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
+                                                  uint64_t spin_ticks)
+{
+    static_assert((CAPR & (CAPR - 1)) == 0 && 2 * G * NB + NB <= CAPR, "ring too small");
+    constexpr int LDW = BW + 1;
+    __shared__ T WR[CAPR * LDW];
+    __shared__ T vsw[G][NB];
+    __shared__ T red[G][NB];
+    __shared__ int go;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ci = lane & 31, h = lane >> 5;
+    const int nn = (int)n;
+    const int nsw = nn - 2;
+    int32_t *err = wm + n;
+    const int g = blockIdx.x;
+    const int s0 = g * G;
+    const int Ge = min(G, nsw - s0);
+    auto E = [&](int r, int c) -> T & { return WR[(r & (CAPR - 1)) * LDW + (r - c)]; };
+    auto ntasks = [&](int s) { return (nn - 2 - s) / NB + 1; };
+    // a task (s, k) reads and writes only rows s + 1 + k NB .. s + (k + 1) NB
+    auto minrow = [&](int s, int k) { return k <= 0 ? s + 1 : s + 1 + k * NB; };
+
+    int lw = s0 + 1;   // rows [s0 + 1, lw) are in the ring
+    int wmk = s0 + 1;  // rows [s0 + 1, wmk) have been stored back
+    T taup = 0;        // this wave's previous reflector (v in vsw[wv])
+    for (int t = 2 * s0;; ++t) {
+        // ---- the lead sweep's rows, once the previous group has released them
+        const int k0 = t - 2 * s0;
+        if (k0 < ntasks(s0)) {
+            const int r1 = min(s0 + (k0 + 1) * NB, nn - 1);
+            if (r1 >= lw) {
+                if (g > 0) {
+                    if (tid == 0) {
+                        int ok = 1;
+                        if (cload(wm + g - 1) <= r1) {
+                            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                            while (cload(wm + g - 1) <= r1) {
+                                if (cload(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
+                                    ok = 0;
+                                    break;
+                                }
+                                __builtin_amdgcn_s_sleep(1);
                             }
-                            __builtin_amdgcn_s_sleep(1);
                         }
+                        if (!ok) cstore(err, 1);
+                        go = ok;
                     }
-                    if (!ok) cstore(err, 1);
-                    go = ok;
+                    __syncthreads();
+                    if (!go) return;
                 }
+                if (r1 + 1 - wmk > CAPR) {  // cannot happen: the ring holds (2G + 1) NB rows
+                    if (tid == 0) cstore(err, 2);
+                    return;
+                }
+                const int cnt = r1 + 1 - lw;  // <= NB
+                if (wv == 0) {
+                    T tmp[NB];
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) tmp[q] = q < cnt ? cload(band + (int64_t)(lw + q) * BW + lane) : (T)0;
+#pragma unroll
+                    for (int q = 0; q < NB; ++q)
+                        if (q < cnt) E(lw + q, lw + q - lane) = tmp[q];
+                }
+                lw = r1 + 1;
                 __syncthreads();
-                if (!go) return;
             }
-            T tau = 0, mu = 0;
+        }
+        // ---- this wave's task
+        const int s = s0 + wv;
+        const int k = t - 2 * s;
+        if (wv < Ge && k >= 0 && k < ntasks(s)) {
+            const int r0 = s + 1 + k * NB;
+            const int r1 = min(s + (k + 1) * NB, nn - 1);
+            const int L = r1 - r0 + 1;
+            T *v = vsw[wv];
+            T tau_k = 0, mu = 0;
             if (k == 0) {
-                const T x = lane < L ? ldB(r0 + lane, s) : (T)0;
+                const T x = lane < L ? E(r0 + lane, s) : (T)0;
                 const T sigma = wave_sum(lane >= 1 && lane < L ? x * x : (T)0);
                 const T x0 = __shfl(x, 0, 64);
                 T vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
-                    tau = 2 * v0 * v0 / (sigma + v0 * v0);
+                    tau_k = 2 * v0 * v0 / (sigma + v0 * v0);
                     vi = lane == 0 ? (T)1 : x / v0;
-                    if (lane < L) stB(r0 + lane, s, lane == 0 ? mu : (T)0);
+                    if (lane < L) E(r0 + lane, s) = lane == 0 ? mu : (T)0;
                 }
                 if (lane < NB) v[lane] = vi;
             } else {
-                const int64_t c0 = r0 - NB;
-                for (int i = h; i < L; i += 2) O[i * LDP + ci] = ldB(r0 + i, c0 + ci);
-                __syncthreads();
-                // right: O <- O (I - taup vp vp^T)
+                const int c0 = r0 - NB;
+                // right: O <- O (I - taup vp vp^T), O = A[r0.., c0..c0+NB)
                 if (taup != 0) {
                     T u = 0;
                     if (ci < L)
-                        for (int c = h * 16; c < h * 16 + 16; ++c) u += O[ci * LDP + c] * vp[c];
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) u += E(r0 + ci, c0 + h * 16 + c) * v[h * 16 + c];
                     u += __shfl_xor(u, 32, 64);
                     if (ci < L)
-                        for (int c = h * 16; c < h * 16 + 16; ++c) O[ci * LDP + c] -= taup * u * vp[c];
-                    __syncthreads();
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) E(r0 + ci, c0 + h * 16 + c) -= taup * u * v[h * 16 + c];
+                    wave_sync();
                 }
-                // reflector from column 0
-                const T x = lane < L ? O[lane * LDP] : (T)0;
+                // reflector from column c0
+                const T x = lane < L ? E(r0 + lane, c0) : (T)0;
                 const T sigma = wave_sum(lane >= 1 && lane < L ? x * x : (T)0);
                 const T x0 = __shfl(x, 0, 64);
                 T vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
-                    tau = 2 * v0 * v0 / (sigma + v0 * v0);
+                    tau_k = 2 * v0 * v0 / (sigma + v0 * v0);
                     vi = lane == 0 ? (T)1 : x / v0;
                 }
+                wave_sync();
                 if (lane < NB) v[lane] = lane < L ? vi : (T)0;
-                __syncthreads();
-                if (tau != 0) {
-                    // left: O <- (I - tau v v^T) O; column 0 becomes mu e_0
+                wave_sync();
+                if (tau_k != 0) {
+                    // left: O <- (I - tau v v^T) O; column c0 becomes mu e_0
                     T w = 0;
-                    for (int i = h; i < L; i += 2) w += v[i] * O[i * LDP + ci];
+                    for (int r = h; r < L; r += 2) w += v[r] * E(r0 + r, c0 + ci);
                     w += __shfl_xor(w, 32, 64);
-                    for (int i = h; i < L; i += 2) O[i * LDP + ci] -= tau * v[i] * w;
-                    __syncthreads();
-                    if (lane < L) O[lane * LDP] = lane == 0 ? mu : (T)0;
-                    __syncthreads();
+                    for (int r = h; r < L; r += 2) E(r0 + r, c0 + ci) -= tau_k * v[r] * w;
+                    wave_sync();
+                    if (lane < L) E(r0 + lane, c0) = lane == 0 ? mu : (T)0;
                 }
-                for (int i = h; i < L; i += 2) stB(r0 + i, c0 + ci, O[i * LDP + ci]);
             }
-            __syncthreads();
-            if (tau != 0) {
-                // two-sided on the diagonal block D = A[r0..r1, r0..r1]
-                for (int i = h; i < L; i += 2)
-                    if (ci < L) D[i * LDP + ci] = ci <= i ? ldB(r0 + i, r0 + ci) : ldB(r0 + ci, r0 + i);
-                __syncthreads();
+            wave_sync();
+            if (tau_k != 0) {
+                // two-sided on the diagonal block A[r0..r1, r0..r1] (lower part stored)
                 T p = 0;
                 if (ci < L)
-                    for (int j = h * 16; j < min(L, h * 16 + 16); ++j) p += D[ci * LDP + j] * v[j];
+                    for (int j = h * 16; j < min(L, h * 16 + 16); ++j)
+                        p += (j <= ci ? E(r0 + ci, r0 + j) : E(r0 + j, r0 + ci)) * v[j];
                 p += __shfl_xor(p, 32, 64);
-                p *= tau;
-                const T pv = wave_sum(h == 0 && ci < L ? p * v[ci] : (T)0);
-                const T wv = p - (T)0.5 * tau * pv * (ci < L ? v[ci] : (T)0);
-                if (h == 0) red[ci] = ci < L ? wv : (T)0;
-                __syncthreads();
-                for (int i = h; i < L; i += 2)
-                    if (ci <= i) stB(r0 + i, r0 + ci, D[i * LDP + ci] - v[i] * red[ci] - red[i] * v[ci]);
+                p *= tau_k;
+                const T vci = ci < L ? v[ci] : (T)0;
+                const T pv = wave_sum(h == 0 ? p * vci : (T)0);
+                if (h == 0) red[wv][ci] = ci < L ? p - (T)0.5 * tau_k * pv * vci : (T)0;
+                wave_sync();
+                for (int r = h; r < L; r += 2)
+                    if (ci <= r) E(r0 + r, r0 + ci) -= v[r] * red[wv][ci] + red[wv][r] * v[ci];
             }
-            if (lane < NB) vp[lane] = v[lane];
-            taup = tau;
-            // every band store of this task is complete before the counter moves
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (lane == 0) cstore(prog + s, k + 1);
+            taup = tau_k;
         }
+        __syncthreads();
+        // ---- rows below the first row of every remaining task are final
+        int nwm = lw;
+        bool more = false;
+        for (int i = 0; i < Ge; ++i) {
+            const int kk = t + 1 - 2 * (s0 + i);
+            if (kk < ntasks(s0 + i)) {
+                nwm = min(nwm, minrow(s0 + i, kk));
+                more = true;
+            }
+        }
+        if (!more) break;
+        if (nwm > wmk) {
+            if (wv == 0) {
+                for (int r = wmk; r < nwm; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+                __builtin_amdgcn_s_waitcnt(0);
+                wave_sync();
+                if (lane == 0) cstore(wm + g, (int32_t)nwm);
+            }
+            wmk = nwm;
+        }
+    }
+    if (wv == 0) {
+        for (int r = wmk; r < lw; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+        __builtin_amdgcn_s_waitcnt(0);
+        wave_sync();
+        if (lane == 0) cstore(wm + g, (int32_t)nn);
     }
 }
 
@@ -815,9 +888,9 @@ __global__ __launch_bounds__(256) void k_tridiag_prep(const T *__restrict__ band
     const int tid = threadIdx.x;
     double lo = INFINITY, hi = -INFINITY, em = 0.0;
     for (int64_t i = tid; i < n; i += 256) {
-        const double d = (double)band[i * BW];
-        const double e = i + 1 < n ? (double)band[i * BW + 1] : 0.0;
-        const double ep = i > 0 ? (double)band[(i - 1) * BW + 1] : 0.0;
+        const double d = (double)band[i * BW];                         // A[i][i]
+        const double e = i + 1 < n ? (double)band[(i + 1) * BW + 1] : 0.0;  // A[i+1][i]
+        const double ep = i > 0 ? (double)band[i * BW + 1] : 0.0;           // A[i][i-1]
         dd[i] = d;
         ee2[i] = e * e;
         const double r = fabs(e) + fabs(ep);
@@ -1025,10 +1098,14 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                        b.prog);
     LAUNCH_OK();
     if (n >= 3) {
+        // G sweeps per workgroup (one wave each); the LDS ring holds >= (2G + 1) NB rows
+        constexpr int G = sizeof(T) == 4 ? 4 : 3;
+        constexpr int CAPR = sizeof(T) == 4 ? 512 : 256;
         const int64_t nsw = n - 2;
-        const int grid = (int)std::min<int64_t>(nsw, 240);
+        const int64_t ngroups = cdiv_h(nsw, G);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
-        hipLaunchKernelGGL(k_bulge<T>, dim3(grid), dim3(64), 0, st, b.band, n, b.prog, spin_ticks);
+        hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * G), 0, st, b.band, n, b.prog,
+                           spin_ticks);
         LAUNCH_OK();
     }
     // ---- stage 3: eigenvalues of the tridiagonal
