@@ -8,11 +8,15 @@
 //   - round-robin ("circle") ordering: n' = n rounded up to even, n'/2 disjoint
 //     pivot pairs per step, n' - 1 steps per sweep, so every pair (p, q) is
 //     visited once per sweep and all rotations of a step commute;
+//   - the matrix is stored as packed 2 x 2 blocks of position pairs (only
+//     blocks K <= L), and the indices are renumbered every step so that the
+//     step's pivot pairs are always positions (2k, 2k+1): a rotation then acts
+//     inside blocks, and each rotated block is written straight to the
+//     positions its entries take in the next step (a second LDS buffer);
 //   - lanes 0 .. n'/2 - 1 compute the step's rotations from a_pp, a_qq, a_pq
 //     (t = sign(tau) / (|tau| + sqrt(1 + tau^2)), tau = (a_qq - a_pp) / (2 a_pq));
-//   - the update A <- J^T A J is applied by 2 x 2 blocks {p_K, q_K} x {p_L, q_L}
-//     (K <= L), each block read and written by one lane, its mirror image
-//     written by the same lane, so a step has no cross-lane hazard;
+//     every other lane reads one block (16 bytes), applies J_K^T (.) J_L and
+//     writes four entries, so a step has no cross-lane hazard;
 //   - a pair is rotated only if |a_pq| > eps_f32 sqrt(|a_pp a_qq|); the solve
 //     stops after a sweep that rotates nothing (or max_sweeps);
 //   - the diagonal is sorted descending with a 64-lane bitonic network.
@@ -24,14 +28,6 @@
 namespace {
 
 constexpr int JB_MAXN = 64;
-constexpr int JB_LD = JB_MAXN + 1;
-
-// position of index slot i in round r of the circle method for n' players:
-// slot 0 is fixed, the others rotate by r
-__device__ __forceinline__ int circle_member(int slot, int r, int np)
-{
-    return slot == 0 ? 0 : 1 + (slot - 1 + r) % (np - 1);
-}
 
 __device__ __forceinline__ float wave_bcast_sort_desc(float x, int lane)
 {
@@ -51,121 +47,146 @@ __device__ __forceinline__ float wave_bcast_sort_desc(float x, int lane)
     return x;
 }
 
+// Pair-block index of the packed symmetric storage: block (K, L), K <= L, holds
+// rows 2K, 2K+1 x columns 2L, 2L+1 as (a00, a01, a10, a11); a diagonal block
+// keeps its off-diagonal entry in a01 only.
+__device__ __forceinline__ int bidx(int K, int L) { return L * (L + 1) / 2 + K; }
+
+// Circle-method positions: position 2k holds slot k, position 2k+1 holds slot
+// np-1-k, so the step's pairs are (slot k, slot np-1-k).  From one step to the
+// next every index moves from slot s to slot s-1 (slot 1 to slot np-1, slot 0
+// stays), i.e. position x moves to npos(x).
+__device__ __forceinline__ int slot_of(int pos, int np) { return (pos & 1) ? np - 1 - (pos >> 1) : (pos >> 1); }
+__device__ __forceinline__ int pos_of(int s, int np) { return s < np / 2 ? 2 * s : 2 * (np - 1 - s) + 1; }
+__device__ __forceinline__ int npos(int x, int np)
+{
+    const int s = slot_of(x, np);
+    const int ps = s == 0 ? 0 : (s == 1 ? np - 1 : s - 1);
+    return pos_of(ps, np);
+}
+
+// destination (block * 4 + component) of element (x, y) in the next step
+__device__ __forceinline__ int dest(int x, int y)
+{
+    if ((x >> 1) > (y >> 1)) {
+        const int t = x;
+        x = y;
+        y = t;
+    }
+    int comp = ((x & 1) << 1) | (y & 1);
+    if ((x >> 1) == (y >> 1) && comp == 2) comp = 1;
+    return bidx(x >> 1, y >> 1) * 4 + comp;
+}
+
+template <int NBL>
 __global__ __launch_bounds__(64) void jacobi_batched(spec_batch_src src, int64_t batch, int n, float *__restrict__ w,
                                                      int max_sweeps, int32_t *__restrict__ info)
 {
-    __shared__ float A[JB_MAXN * JB_LD];
-    __shared__ float cs_c[JB_MAXN / 2], cs_s[JB_MAXN / 2], cs_t[JB_MAXN / 2];
-    __shared__ int pp[JB_MAXN / 2], qq[JB_MAXN / 2];
+    constexpr int MAXB = (JB_MAXN / 2) * (JB_MAXN / 2 + 1) / 2;
+    __shared__ float4 Bk[2][MAXB > 64 * NBL ? 64 * NBL : MAXB];
+    __shared__ float4 rot[JB_MAXN / 2];
 
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x;
     const int np = (n + 1) & ~1;
     const int m = np / 2;
+    const int nblk = m * (m + 1) / 2;
 
-    // ---- load the lower triangle and mirror it
-    if (src.kind == SPEC_SRC_DENSE) {
-        const float *a = src.a + b * src.stride_a;
-        for (int idx = lane; idx < n * n; idx += 64) {
-            int i = idx / n, j = idx % n;
-            if (i >= j) {
-                float v = a[i * src.lda + j];
-                A[i * JB_LD + j] = v;
-                A[j * JB_LD + i] = v;
-            }
+    // ---- the lane's blocks, their (K, L) and the destinations of their entries
+    int KK[NBL], LL[NBL], dst[NBL][4];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+        const int blk = lane + 64 * j;
+        int L = 0;
+        while ((L + 1) * (L + 2) / 2 <= blk) ++L;
+        KK[j] = blk - L * (L + 1) / 2;
+        LL[j] = L;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dst[j][a * 2 + c] = dest(npos(2 * KK[j] + a, np), npos(2 * LL[j] + c, np));
+    }
+
+    // ---- load: position p holds original index slot_of(p)
+    auto value = [&](int i, int j) -> float {
+        if (i >= n || j >= n) return 0.f;  // the dummy index of odd n
+        if (src.kind == SPEC_SRC_DENSE) {
+            const int r = max(i, j), c = min(i, j);
+            return src.a[b * src.stride_a + (int64_t)r * src.lda + c];
         }
-    } else {
         const int64_t W = (src.T - n) / src.stride + 1;
         const int64_t s = b / W, win = b % W;
-        const float *band = src.a + s * src.T * n;
-        const int64_t t0 = win * src.stride;
-        for (int idx = lane; idx < n * n; idx += 64) {
-            int i = idx / n, j = idx % n;
-            if (i >= j) {
-                float v = src.scale * band[(t0 + i) * n + (i - j)];
-                A[i * JB_LD + j] = v;
-                A[j * JB_LD + i] = v;
-            }
-        }
-    }
-    if (np != n) {  // dummy index n: an isolated zero row and column
-        for (int j = lane; j <= n; j += 64) {
-            A[n * JB_LD + j] = 0.f;
-            A[j * JB_LD + n] = 0.f;
+        return src.scale * src.a[s * src.T * n + (win * src.stride + max(i, j)) * n + abs(i - j)];
+    };
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+        const int blk = lane + 64 * j;
+        if (blk < nblk) {
+            const int r0 = slot_of(2 * KK[j], np), r1 = slot_of(2 * KK[j] + 1, np);
+            const int c0 = slot_of(2 * LL[j], np), c1 = slot_of(2 * LL[j] + 1, np);
+            const float a01 = value(r0, c1);
+            Bk[0][blk] = make_float4(value(r0, c0), a01, KK[j] == LL[j] ? a01 : value(r1, c0), value(r1, c1));
         }
     }
     __syncthreads();
 
-    const int nblk = m * (m + 1) / 2;
+    int cur = 0;
     int sweeps = 0;
     bool converged = false;
     for (; sweeps < max_sweeps; ++sweeps) {
         int rotated = 0;
-        for (int r = 0; r < np - 1; ++r) {
+        for (int step = 0; step < np - 1; ++step) {
             if (lane < m) {
-                int p = circle_member(lane, r, np);
-                int q = circle_member(np - 1 - lane, r, np);
-                if (p > q) { int tmp = p; p = q; q = tmp; }
+                const float4 d = Bk[cur][bidx(lane, lane)];
+                const float app = d.x, apq = d.y, aqq = d.w;
                 float c = 1.f, s = 0.f, t = 0.f;
-                if (q < n) {
-                    const float apq = A[p * JB_LD + q];
-                    const float app = A[p * JB_LD + p], aqq = A[q * JB_LD + q];
-                    const float thr = FLT_EPSILON * sqrtf(fabsf(app)) * sqrtf(fabsf(aqq));
-                    if (fabsf(apq) > thr && fabsf(apq) > FLT_MIN) {
-                        const float tau = (aqq - app) / (2.f * apq);
-                        if (fabsf(tau) < 1e18f)
-                            t = copysignf(1.f, tau) / (fabsf(tau) + sqrtf(1.f + tau * tau));
-                        else
-                            t = 0.5f / tau;
-                        c = 1.f / sqrtf(1.f + t * t);
-                        s = t * c;
-                        rotated = 1;
-                    }
+                const float thr = FLT_EPSILON * sqrtf(fabsf(app)) * sqrtf(fabsf(aqq));
+                if (fabsf(apq) > thr && fabsf(apq) > FLT_MIN) {
+                    const float tau = (aqq - app) / (2.f * apq);
+                    if (fabsf(tau) < 1e18f)
+                        t = copysignf(1.f, tau) / (fabsf(tau) + sqrtf(1.f + tau * tau));
+                    else
+                        t = 0.5f / tau;
+                    c = 1.f / sqrtf(1.f + t * t);
+                    s = t * c;
+                    rotated = 1;
                 }
-                pp[lane] = p;
-                qq[lane] = q;
-                cs_c[lane] = c;
-                cs_s[lane] = s;
-                cs_t[lane] = t;
+                rot[lane] = make_float4(c, s, t, 0.f);
             }
             __syncthreads();
-            for (int blk = lane; blk < nblk; blk += 64) {
-                // blk -> (K, L) with K <= L
-                int L = (int)((sqrtf(8.f * blk + 1.f) - 1.f) * 0.5f);
-                while ((L + 1) * (L + 2) / 2 <= blk) ++L;
-                while (L * (L + 1) / 2 > blk) --L;
-                const int K = blk - L * (L + 1) / 2;
-                const int pK = pp[K], qK = qq[K], pL = pp[L], qL = qq[L];
-                const float cK = cs_c[K], sK = cs_s[K], cL = cs_c[L], sL = cs_s[L];
-                if (K == L) {
-                    if (sK != 0.f) {
-                        const float apq = A[pK * JB_LD + qK];
-                        const float tK = cs_t[K];
-                        A[pK * JB_LD + pK] -= tK * apq;
-                        A[qK * JB_LD + qK] += tK * apq;
-                        A[pK * JB_LD + qK] = 0.f;
-                        A[qK * JB_LD + pK] = 0.f;
+            float *nx = reinterpret_cast<float *>(Bk[cur ^ 1]);
+#pragma unroll
+            for (int j = 0; j < NBL; ++j) {
+                const int blk = lane + 64 * j;
+                if (blk < nblk) {
+                    const float4 a = Bk[cur][blk];
+                    const float4 rK = rot[KK[j]];
+                    if (KK[j] == LL[j]) {
+                        if (rK.y != 0.f) {
+                            nx[dst[j][0]] = a.x - rK.z * a.y;
+                            nx[dst[j][3]] = a.w + rK.z * a.y;
+                            nx[dst[j][1]] = 0.f;
+                        } else {
+                            nx[dst[j][0]] = a.x;
+                            nx[dst[j][3]] = a.w;
+                            nx[dst[j][1]] = a.y;
+                        }
+                    } else {
+                        const float4 rL = rot[LL[j]];
+                        const float cK = rK.x, sK = rK.y, cL = rL.x, sL = rL.y;
+                        // right: columns by J_L = [[c, s], [-s, c]]; left: rows by J_K^T
+                        const float r00 = cL * a.x - sL * a.y, r01 = sL * a.x + cL * a.y;
+                        const float r10 = cL * a.z - sL * a.w, r11 = sL * a.z + cL * a.w;
+                        nx[dst[j][0]] = cK * r00 - sK * r10;
+                        nx[dst[j][1]] = cK * r01 - sK * r11;
+                        nx[dst[j][2]] = sK * r00 + cK * r10;
+                        nx[dst[j][3]] = sK * r01 + cK * r11;
                     }
-                } else if (sK != 0.f || sL != 0.f) {
-                    const float a00 = A[pK * JB_LD + pL], a01 = A[pK * JB_LD + qL];
-                    const float a10 = A[qK * JB_LD + pL], a11 = A[qK * JB_LD + qL];
-                    // right: columns (pL, qL) by J_L = [[c, s], [-s, c]]
-                    const float r00 = cL * a00 - sL * a01, r01 = sL * a00 + cL * a01;
-                    const float r10 = cL * a10 - sL * a11, r11 = sL * a10 + cL * a11;
-                    // left: rows (pK, qK) by J_K^T
-                    const float b00 = cK * r00 - sK * r10, b01 = cK * r01 - sK * r11;
-                    const float b10 = sK * r00 + cK * r10, b11 = sK * r01 + cK * r11;
-                    A[pK * JB_LD + pL] = b00;
-                    A[pK * JB_LD + qL] = b01;
-                    A[qK * JB_LD + pL] = b10;
-                    A[qK * JB_LD + qL] = b11;
-                    A[pL * JB_LD + pK] = b00;
-                    A[qL * JB_LD + pK] = b01;
-                    A[pL * JB_LD + qK] = b10;
-                    A[qL * JB_LD + qK] = b11;
                 }
             }
             __syncthreads();
+            cur ^= 1;
         }
         rotated = __any(rotated);
         if (!rotated) {
@@ -173,8 +194,13 @@ __global__ __launch_bounds__(64) void jacobi_batched(spec_batch_src src, int64_t
             break;
         }
     }
-    float x = (lane < n) ? A[lane * JB_LD + lane] : -INFINITY;
-    if (x != x) x = INFINITY;  // a NaN sorts first as +inf so the descriptors flag it
+    // after whole sweeps every index is back at its starting position
+    float x = -INFINITY;
+    if (lane < np && slot_of(lane, np) < n) {
+        const float4 d = Bk[cur][bidx(lane >> 1, lane >> 1)];
+        x = (lane & 1) ? d.w : d.x;
+        if (x != x) x = INFINITY;  // a NaN sorts first as +inf so the descriptors flag it
+    }
     x = wave_bcast_sort_desc(x, lane);
     if (lane < n) w[b * n + lane] = x;
     if (info != nullptr && lane == 0) info[b] = converged ? sweeps : -1;
@@ -186,7 +212,11 @@ hipError_t launch_jacobi_batched(hipStream_t stream, const spec_batch_src *src, 
                                  int max_sweeps, int32_t *info)
 {
     if (batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(jacobi_batched, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, max_sweeps,
-                       info);
+    if (n <= 32)
+        hipLaunchKernelGGL(jacobi_batched<3>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w,
+                           max_sweeps, info);
+    else
+        hipLaunchKernelGGL(jacobi_batched<9>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w,
+                           max_sweeps, info);
     return hipGetLastError();
 }
