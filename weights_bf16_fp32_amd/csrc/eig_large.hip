@@ -32,6 +32,7 @@
 #include <float.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -65,201 +66,247 @@ __device__ T block_sum256(T x, T *red)
     return s;
 }
 
-// Householder QR of the rows x NB matrix P (LDS, stride LDP) by 256 threads:
-// kr reflectors H_k = I - tau_k v_k v_k^T (v_k[k] = 1 implicit, v_k below the
-// diagonal of column k), R in the upper triangle, and T (NB x NB, upper) of the
-// forward product H_0 ... H_{kr-1} = I - V T V^T in Tl.
-// Per column k, thread (c, g) = (tid % 32, tid / 32) covers rows k+1+g, +8, ...:
-//   pass 1 forms the dot products d_c = v_k^T P[k:, c] for every column c, which
-//     gives w_c (c > k) for the update and G[c][k] = v_c^T v_k (c < k) for T;
-//   pass 2 updates the columns c > k, writes v_k, accumulates the squared norm
-//     of column k+1 below its diagonal (the next reflector's sigma) and forms
-//     T[0:k, k] = -tau_k T[0:k, 0:k] G[0:k, k].
-// v_k is produced on the fly as scale * x in pass 1 and stored in pass 2.
-template <typename T>
-__device__ void lds_qr_larft(T *P, int rows, int kr, T *tau, T *Tl, T *red)
+// Register-resident Householder QR of a rows x NB block (rows <= NT) by NT
+// threads, one row per thread, all NB columns in registers; the column loop is
+// expanded at compile time (static_for) so every register index is static.
+// Per column k:
+//   * every thread forms tau_k and v_k[k] = 1, v_k[r] = x_r / v0 from sigma =
+//     sum_{r > k} x_r^2 and x_k (published in LDS by the previous column's update);
+//   * the dot products d_c = v_k^T P[:, c] of all NB columns come from one
+//     butterfly reduce-scatter across the wave (31 lane exchanges leave the sum
+//     of column c in lane c) and a sum across the waves in LDS; d_c for c > k
+//     gives the update P[:, c] -= tau v d_c, and d_c = v_c^T v_k for c < k gives
+//     column k of T: T[0:k, k] = -tau_k T[0:k, 0:k] d[0:k];
+//   * the update leaves sigma and x of column k + 1 for the next column.
+// On exit R is in the upper triangle of the block, v_k below the diagonal of
+// column k, tau in tau[], T (NB x NB, upper, H_0 ... H_{kr-1} = I - V T V^T) in Tl.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
 {
-    const int tid = threadIdx.x;
-    const int c = tid & 31, g = tid >> 5;
-    T *dots = red;         // 8 x 32 partial dot products
-    T *sig = red + 256;    // 8 partial sums of squares (next column)
-    T *bc = red + 264;     // broadcast: [0] scale, [1] tau
-    T *gk = red + 272;     // G[0:k, k] of the previous step
-    for (int p = tid; p < NB * NB; p += 256) Tl[p] = 0;
-    // sigma of column 0
-    if (c == 0) {
-        T s = 0;
-        for (int i = 1 + g; i < rows; i += 8) s += P[i * LDP] * P[i * LDP];
-        sig[g] = s;
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <typename T, int NT>
+struct RegQr {
+    static constexpr int NW = NT / 64;
+    T red[NW][NB];  // per-wave column sums
+    T dvec[NB];     // d_c of the current column
+    T sig[NW];      // per-wave partial sigma of the next column
+    T x0;           // P[k][k] of the next column
+    T tau[NB];
+    T Tl[NB * NB];
+};
+
+template <typename T>
+__device__ __forceinline__ T wave_sum64(T x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// butterfly reduce-scatter: returns, in every lane, the sum over the wave of
+// x[lane % 32]
+template <typename T>
+__device__ __forceinline__ T reduce_scatter32(const T (&x)[NB], int lane)
+{
+    T y16[16], y8[8], y4[4], y2[2];
+    const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const T keep = b4 ? x[m + 16] : x[m], send = b4 ? x[m] : x[m + 16];
+        y16[m] = keep + __shfl_xor(send, 16, 64);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const T keep = b3 ? y16[m + 8] : y16[m], send = b3 ? y16[m] : y16[m + 8];
+        y8[m] = keep + __shfl_xor(send, 8, 64);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const T keep = b2 ? y8[m + 4] : y8[m], send = b2 ? y8[m] : y8[m + 4];
+        y4[m] = keep + __shfl_xor(send, 4, 64);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const T keep = b1 ? y4[m + 2] : y4[m], send = b1 ? y4[m] : y4[m + 2];
+        y2[m] = keep + __shfl_xor(send, 2, 64);
+    }
+    const T keep = b0 ? y2[1] : y2[0], send = b0 ? y2[0] : y2[1];
+    const T y1 = keep + __shfl_xor(send, 1, 64);
+    return y1 + __shfl_xor(y1, 32, 64);
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ void reg_qr(T (&p)[NB], int rows, int kr, RegQr<T, NT> &S)
+{
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool live = tid < rows;
+    for (int q = tid; q < NB * NB; q += NT) S.Tl[q] = 0;
+    {
+        T part = (tid > 0 && live) ? p[0] * p[0] : (T)0;
+        part = wave_sum64(part);
+        if (lane == 0) S.sig[wv] = part;
+        if (tid == 0) S.x0 = p[0];
     }
     __syncthreads();
-    // T[0:k, k] = -tau_k T[0:k, 0:k] G[0:k, k], from the G column published by step k
-    auto t_column = [&](int k) {
-        if (tid < k) {
-            T acc = 0;
-            for (int j = tid; j < k; ++j) acc += Tl[tid * NB + j] * gk[j];
-            Tl[tid * NB + k] = -tau[k] * acc;
-        }
-        if (tid == 0) Tl[k * NB + k] = tau[k];
-    };
-    for (int k = 0; k < kr; ++k) {
-        if (k > 0) t_column(k - 1);
-        if (tid == 0) {
+    static_for<0, NB>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        if (k < kr) {
             T sigma = 0;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sigma += sig[q];
-            const T x0 = P[k * LDP + k];
-            T t = 0, scale = 0;
+            for (int w = 0; w < NW; ++w) sigma += S.sig[w];
+            const T x0 = S.x0;
+            T t = 0, scale = 0, mu = 0;
             if (sigma > 0) {
-                const T mu = sqrt(x0 * x0 + sigma);
+                mu = sqrt(x0 * x0 + sigma);
                 const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
                 t = 2 * v0 * v0 / (sigma + v0 * v0);
                 scale = 1 / v0;
-                P[k * LDP + k] = mu;  // R_kk; column k, row k is not read by pass 1 below
             }
-            tau[k] = t;
-            bc[0] = scale;
-            bc[1] = t;
-        }
-        __syncthreads();
-        const T scale = bc[0], t = bc[1];
-        // pass 1: d_c = P[k][c] (v_k[k] = 1; for c == k the row-k value is R_kk, unused)
-        //             + sum_{i > k} scale * P[i][k] * P[i][c]
-        T d0 = 0, d1 = 0;
-        int i = k + 1 + g;
-        for (; i + 8 < rows; i += 16) {
-            d0 += P[i * LDP + k] * P[i * LDP + c];
-            d1 += P[(i + 8) * LDP + k] * P[(i + 8) * LDP + c];
-        }
-        if (i < rows) d0 += P[i * LDP + k] * P[i * LDP + c];
-        dots[g * 32 + c] = (d0 + d1) * scale;
-        __syncthreads();
-        T dc = P[k * LDP + c];
+            if (t != 0) {
+                const T v = live ? (tid > k ? scale * p[k] : (tid == k ? (T)1 : (T)0)) : (T)0;
+                T x[NB];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dc += dots[q * 32 + c];
-        // pass 2
-        if (t != 0 && c > k) {
-            const T wc = t * dc;
-            if (g == 0) P[k * LDP + c] -= wc;
-            T s2 = 0;
-            for (int r = k + 1 + g; r < rows; r += 8) {
-                const T nv = P[r * LDP + c] - wc * scale * P[r * LDP + k];
-                P[r * LDP + c] = nv;
-                if (c == k + 1 && r > k + 1) s2 += nv * nv;
+                for (int c = 0; c < NB; ++c) x[c] = v * p[c];
+                const T dsum = reduce_scatter32<T>(x, lane);
+                __syncthreads();  // readers of the previous column's red/dvec are done
+                if (lane < NB) S.red[wv][lane] = dsum;
+                __syncthreads();
+                if (tid < NB) {
+                    T acc = 0;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) acc += S.red[w][tid];
+                    S.dvec[tid] = acc;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int c = k + 1; c < NB; ++c) p[c] -= t * v * S.dvec[c];
+                if (tid == k) p[k] = mu;
+                if (tid > k) p[k] = v;
+                // T[i][k] = -t sum_{i <= j < k} T[i][j] d_j: thread (i, j mod 8), 8-lane sum
+                if (k > 0 && tid < 8 * NB) {
+                    const int i = tid >> 3, jg = tid & 7;
+                    T acc = 0;
+#pragma unroll
+                    for (int j = jg; j < k; j += 8)
+                        if (j >= i) acc += S.Tl[i * NB + j] * S.dvec[j];
+                    acc += __shfl_xor(acc, 1, 64);
+                    acc += __shfl_xor(acc, 2, 64);
+                    acc += __shfl_xor(acc, 4, 64);
+                    if (jg == 0 && i < k) S.Tl[i * NB + k] = -t * acc;
+                }
             }
-            if (c == k + 1) sig[g] = s2;
-        } else if (t == 0 && c == k + 1) {
-            T s2 = 0;
-            for (int r = k + 2 + g; r < rows; r += 8) s2 += P[r * LDP + c] * P[r * LDP + c];
-            sig[g] = s2;
+            if (tid == k) S.Tl[k * NB + k] = t;
+            if (tid == 0) S.tau[k] = t;
+            if constexpr (k + 1 < NB) {
+                T part = (tid > k + 1 && live) ? p[k + 1] * p[k + 1] : (T)0;
+                part = wave_sum64(part);
+                __syncthreads();  // every thread has read sig/x0 of column k
+                if (lane == 0) S.sig[wv] = part;
+                if (tid == k + 1) S.x0 = p[k + 1];
+                __syncthreads();
+            }
         }
-        if (c == k && t != 0)
-            for (int r = k + 1 + g; r < rows; r += 8) P[r * LDP + k] *= scale;
-        if (g == 0 && c < k) gk[c] = dc;  // G[c][k] = v_c^T v_k
-        __syncthreads();
-    }
-    if (kr > 0) t_column(kr - 1);
-    for (int k = kr + tid; k < NB; k += 256) tau[k] = 0;
+    });
+    for (int k = kr + tid; k < NB; k += NT) S.tau[k] = 0;
     __syncthreads();
 }
 
-// LDS budget of the QR kernels: panel rows x LDP + tau + T + reduction scratch
-template <typename T>
-struct QrLds {
-    T P[Cfg<T>::RB * LDP];
-    T tau[NB];
-    T Tl[NB * NB];
-    T red[272 + NB];
-};
-
-// ---- direct panel: m <= RB rows, one workgroup
+// ---- direct panel: m <= 256 rows, one workgroup
 template <typename T>
 __global__ __launch_bounds__(256) void k_panel_direct(T *__restrict__ Pg, int64_t lda, int m, T *__restrict__ V,
                                                       T *__restrict__ Tm)
 {
-    __shared__ QrLds<T> L;
+    __shared__ RegQr<T, 256> S;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < m * NB; idx += 256) {
-        const int i = idx / NB, c = idx % NB;
-        L.P[i * LDP + c] = Pg[i * lda + c];
-    }
-    __syncthreads();
+    T p[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) p[c] = tid < m ? Pg[(int64_t)tid * lda + c] : (T)0;
     const int kr = min(m - 1, NB);
-    lds_qr_larft<T>(L.P, m, kr, L.tau, L.Tl, L.red);
-    for (int idx = tid; idx < m * NB; idx += 256) {
-        const int i = idx / NB, c = idx % NB;
-        if (i <= c) Pg[i * lda + c] = L.P[i * LDP + c];
-        T v = 0;
-        if (c < kr) v = i == c ? (T)1 : (i > c ? L.P[i * LDP + c] : (T)0);
-        V[(int64_t)i * NB + c] = v;
+    reg_qr<T, 256>(p, m, kr, S);
+    if (tid < m) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            if (tid <= c) Pg[(int64_t)tid * lda + c] = p[c];
+            T v = 0;
+            if (c < kr) v = tid == c ? (T)1 : (tid > c ? p[c] : (T)0);
+            V[(int64_t)tid * NB + c] = v;
+        }
     }
-    for (int p = tid; p < NB * NB; p += 256) Tm[p] = L.Tl[p];
+    for (int q = tid; q < NB * NB; q += 256) Tm[q] = S.Tl[q];
 }
 
-// ---- TSQR, step 1: local QR of row block b (rows [b*per, min(m, (b+1)*per)))
-template <typename T>
-__global__ __launch_bounds__(256) void k_tsqr_local(const T *__restrict__ Pg, int64_t lda, int m, int per,
-                                                    T *__restrict__ Vloc, T *__restrict__ Tloc,
-                                                    T *__restrict__ Rstack)
+// ---- TSQR, step 1: local QR of row block b (rows [b*per, min(m, (b+1)*per)), per <= NT)
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_tsqr_local(const T *__restrict__ Pg, int64_t lda, int m, int per,
+                                                   T *__restrict__ Vloc, T *__restrict__ Tloc, T *__restrict__ Rstack)
 {
-    __shared__ QrLds<T> L;
+    __shared__ RegQr<T, NT> S;
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const int r0 = b * per;
     const int rows = min(per, m - r0);
-    for (int idx = tid; idx < rows * NB; idx += 256) {
-        const int i = idx / NB, c = idx % NB;
-        L.P[i * LDP + c] = Pg[(int64_t)(r0 + i) * lda + c];
+    T p[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) p[c] = tid < rows ? Pg[(int64_t)(r0 + tid) * lda + c] : (T)0;
+    reg_qr<T, NT>(p, rows, NB, S);
+    if (tid < rows) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            Vloc[(int64_t)(r0 + tid) * NB + c] = tid == c ? (T)1 : (tid > c ? p[c] : (T)0);
+            if (tid < NB) Rstack[(int64_t)b * NB * NB + tid * NB + c] = tid <= c ? p[c] : (T)0;
+        }
     }
-    __syncthreads();
-    lds_qr_larft<T>(L.P, rows, NB, L.tau, L.Tl, L.red);
-    for (int idx = tid; idx < rows * NB; idx += 256) {
-        const int i = idx / NB, c = idx % NB;
-        Vloc[(int64_t)(r0 + i) * NB + c] = i == c ? (T)1 : (i > c ? L.P[i * LDP + c] : (T)0);
-    }
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int i = p / NB, c = p % NB;
-        Rstack[(int64_t)b * NB * NB + p] = i <= c ? L.P[i * LDP + c] : (T)0;
-        Tloc[(int64_t)b * NB * NB + p] = L.Tl[p];
-    }
+    for (int q = tid; q < NB * NB; q += NT) Tloc[(int64_t)b * NB * NB + q] = S.Tl[q];
 }
 
 // ---- TSQR, step 2: QR of the stacked R factors; Rf and Qt = Q_top [I; 0]
-template <typename T>
-__global__ __launch_bounds__(256) void k_tsqr_top(const T *__restrict__ Rstack, int nblk, T *__restrict__ Rf,
-                                                  T *__restrict__ Qt)
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_tsqr_top(const T *__restrict__ Rstack, int nblk, T *__restrict__ Rf,
+                                                 T *__restrict__ Qt)
 {
-    __shared__ QrLds<T> L;
-    __shared__ T K[NB * NB];
+    __shared__ RegQr<T, NT> S;
+    __shared__ T Vt[NB * LDP], K[NB * NB];
     const int tid = threadIdx.x;
     const int rows = nblk * NB;
-    for (int idx = tid; idx < rows * NB; idx += 256) L.P[(idx / NB) * LDP + idx % NB] = Rstack[idx];
-    __syncthreads();
-    lds_qr_larft<T>(L.P, rows, NB, L.tau, L.Tl, L.red);
-    // K = T V_top[0:NB]^T  (NB x NB); V_top[0:NB] is unit lower triangular
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int j = p / NB, c = p % NB;  // K[j][c] = sum_l T[j][l] V[c][l]
-        T s = 0;
-        for (int l = j; l < NB; ++l) {
-            const T vcl = c == l ? (T)1 : (c > l ? L.P[c * LDP + l] : (T)0);
-            s += L.Tl[j * NB + l] * vcl;
+    T p[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) p[c] = tid < rows ? Rstack[(int64_t)tid * NB + c] : (T)0;
+    reg_qr<T, NT>(p, rows, NB, S);
+    if (tid < NB) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            Vt[tid * LDP + c] = tid == c ? (T)1 : (tid > c ? p[c] : (T)0);
+            Rf[tid * NB + c] = tid <= c ? p[c] : (T)0;
         }
-        K[p] = s;
     }
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int i = p / NB, c = p % NB;
-        Rf[p] = i <= c ? L.P[i * LDP + c] : (T)0;
+    __syncthreads();
+    // K = T V_top[0:NB]^T
+    for (int q = tid; q < NB * NB; q += NT) {
+        const int j = q / NB, c = q % NB;
+        T acc = 0;
+        for (int l = j; l <= c; ++l) acc += S.Tl[j * NB + l] * Vt[c * LDP + l];
+        K[q] = acc;
     }
     __syncthreads();
     // Qt[r][c] = [r == c] - sum_j V[r][j] K[j][c]
-    for (int idx = tid; idx < rows * NB; idx += 256) {
-        const int r = idx / NB, c = idx % NB;
-        T s = r == c ? (T)1 : (T)0;
+    if (tid < rows) {
+        T q[NB];
+#pragma unroll
+        for (int c = 0; c < NB; ++c) q[c] = tid == c ? (T)1 : (T)0;
+#pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const T vrj = r == j ? (T)1 : (r > j ? L.P[r * LDP + j] : (T)0);
-            s -= vrj * K[j * NB + c];
+            const T vrj = tid == j ? (T)1 : (tid > j ? p[j] : (T)0);
+#pragma unroll
+            for (int c = 0; c < NB; ++c) q[c] -= vrj * K[j * NB + c];
         }
-        Qt[idx] = s;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) Qt[(int64_t)tid * NB + c] = q[c];
     }
 }
 
@@ -299,7 +346,11 @@ __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, con
     if (i < rows) {
         T s = i < NB ? Qb[i * NB + c] : (T)0;
         const T *vr = Vloc + (int64_t)(r0 + i) * NB;
-        for (int j = 0; j < NB; ++j) s -= vr[j] * K[j * NB + c];
+        T vrow[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) vrow[j] = vr[j];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) s -= vrow[j] * K[j * NB + c];
         Q1[(int64_t)(r0 + i) * NB + c] = s;
     }
 }
@@ -389,8 +440,12 @@ __global__ __launch_bounds__(256) void k_make_w(const T *__restrict__ V, const T
     const int64_t r = blockIdx.x * 8 + (tid >> 5);
     const int c = tid & 31;
     if (r >= m) return;
+    T vrow[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) vrow[j] = V[r * NB + j];
     T s = 0;
-    for (int j = 0; j <= c; ++j) s += V[r * NB + j] * Ts[j * NB + c];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s += vrow[j] * Ts[j * NB + c];  // T is upper: terms j > c vanish
     W[r * NB + c] = s;
 }
 
@@ -407,39 +462,75 @@ __global__ __launch_bounds__(256) void k_symm(const T *__restrict__ A, int64_t l
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i0 = blockIdx.x * SY_RB;
     const int jlo = blockIdx.y * chunk, jhi = min(m, jlo + chunk);
-    constexpr int NACC = sizeof(T) == 4 ? 1 : 4;
-    f32x16_t acc32 = {};
-    f64x4_t acc64[4] = {};
-    for (int j0 = jlo; j0 < jhi; j0 += SY_JB) {
+    constexpr int NA = SY_RB * SY_JB / 256, NWL = SY_JB * NB / 256;
+    T ra[NA], rw[NWL];
+    // the A tile (rows i0.., columns j0..) of the lower-stored symmetric matrix,
+    // loaded into registers (all loads in flight together)
+    auto gload = [&](int j0) {
         const bool lowerTile = j0 + SY_JB - 1 <= i0;
         const bool upperTile = i0 + SY_RB - 1 < j0;
         if (lowerTile) {
-            for (int idx = tid; idx < SY_RB * SY_JB; idx += 256) {
-                const int r = idx / SY_JB, c = idx % SY_JB;
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + 256 * q, r = idx / SY_JB, c = idx % SY_JB;
                 const int i = i0 + r, j = j0 + c;
-                As[r * (SY_JB + 1) + c] = (i < m && j < jhi) ? A[(int64_t)i * lda + j] : (T)0;
+                ra[q] = (i < m && j < jhi) ? A[(int64_t)i * lda + j] : (T)0;
             }
         } else if (upperTile) {
-            for (int idx = tid; idx < SY_RB * SY_JB; idx += 256) {
-                const int c = idx / SY_RB, r = idx % SY_RB;
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + 256 * q, c = idx / SY_RB, r = idx % SY_RB;
                 const int i = i0 + r, j = j0 + c;
-                As[r * (SY_JB + 1) + c] = (i < m && j < jhi) ? A[(int64_t)j * lda + i] : (T)0;
+                ra[q] = (i < m && j < jhi) ? A[(int64_t)j * lda + i] : (T)0;
             }
         } else {
-            for (int idx = tid; idx < SY_RB * SY_JB; idx += 256) {
-                const int r = idx / SY_JB, c = idx % SY_JB;
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + 256 * q, r = idx / SY_JB, c = idx % SY_JB;
                 const int i = i0 + r, j = j0 + c;
                 T v = 0;
                 if (i < m && j < jhi) v = i >= j ? A[(int64_t)i * lda + j] : A[(int64_t)j * lda + i];
-                As[r * (SY_JB + 1) + c] = v;
+                ra[q] = v;
             }
         }
-        for (int idx = tid; idx < SY_JB * NB; idx += 256) {
-            const int r = idx / NB, c = idx % NB;
+#pragma unroll
+        for (int q = 0; q < NWL; ++q) {
+            const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
             const int j = j0 + r;
-            Ws[r * (NB + 1) + c] = j < jhi ? W[(int64_t)j * NB + c] : (T)0;
+            rw[q] = j < jhi ? W[(int64_t)j * NB + c] : (T)0;
         }
-        __syncthreads();
+    };
+    auto lstore = [&](int j0) {
+        const bool upperTile = i0 + SY_RB - 1 < j0;
+        if (upperTile) {
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + 256 * q, c = idx / SY_RB, r = idx % SY_RB;
+                As[r * (SY_JB + 1) + c] = ra[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + 256 * q, r = idx / SY_JB, c = idx % SY_JB;
+                As[r * (SY_JB + 1) + c] = ra[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NWL; ++q) {
+            const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
+            Ws[r * (NB + 1) + c] = rw[q];
+        }
+    };
+    f32x16_t acc32 = {};
+    f64x4_t acc64[4] = {};
+    if (jlo < jhi) {
+        gload(jlo);
+        lstore(jlo);
+    }
+    __syncthreads();
+    for (int j0 = jlo; j0 < jhi; j0 += SY_JB) {
+        const bool more = j0 + SY_JB < jhi;
+        if (more) gload(j0 + SY_JB);
         if constexpr (sizeof(T) == 4) {
 #pragma unroll 4
             for (int kk = 0; kk < SY_JB; kk += 2) {
@@ -465,9 +556,10 @@ __global__ __launch_bounds__(256) void k_symm(const T *__restrict__ A, int64_t l
             }
         }
         __syncthreads();
+        if (more) lstore(j0 + SY_JB);
+        __syncthreads();
     }
     T *Xp = Xpart + (int64_t)blockIdx.y * m * NB;
-    (void)NACC;
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -487,30 +579,64 @@ __global__ __launch_bounds__(256) void k_symm(const T *__restrict__ A, int64_t l
     }
 }
 
-// ---- X = sum of partials; Ppart[blk] = V_blk^T X_blk
+// ---- X = sum of partials; Ppart[blk] = V_blk^T X_blk (XR-row blocks)
+constexpr int XR = 128;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_xreduce(const T *__restrict__ Xpart, int ks, int m, const T *__restrict__ V,
                                                  T *__restrict__ X, T *__restrict__ Ppart)
 {
-    __shared__ T Xs[256 * NB];
-    __shared__ T Vs[256 * NB];
+    __shared__ T Xs[XR * (NB + 1)];
+    __shared__ T Vs[XR * NB];
+    __shared__ T red[8][NB * NB];
     const int tid = threadIdx.x;
-    const int r0 = blockIdx.x * 256;
-    const int rows = min(256, m - r0);
-    for (int idx = tid; idx < rows * NB; idx += 256) {
-        const int64_t g = (int64_t)r0 * NB + idx;
-        T s = 0;
-        for (int q = 0; q < ks; ++q) s += Xpart[(int64_t)q * m * NB + g];
-        X[g] = s;
-        Xs[idx] = s;
-        Vs[idx] = V[g];
+    const int r0 = blockIdx.x * XR;
+    const int rows = min(XR, m - r0);
+    constexpr int PER = XR * NB / 256;
+    T acc[PER], vv[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        acc[q] = 0;
+        const int idx = tid + 256 * q;
+        vv[q] = idx / NB < rows ? V[(int64_t)r0 * NB + idx] : (T)0;
+    }
+    for (int p = 0; p < ks; ++p) {
+        const T *src = Xpart + (int64_t)p * m * NB + (int64_t)r0 * NB;
+        T part[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int idx = tid + 256 * q;
+            part[q] = idx / NB < rows ? src[idx] : (T)0;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) acc[q] += part[q];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
+        if (r < rows) X[(int64_t)r0 * NB + idx] = acc[q];
+        Xs[r * (NB + 1) + c] = acc[q];
+        Vs[idx] = vv[q];
     }
     __syncthreads();
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int j = p / NB, c = p % NB;
-        T s = 0;
-        for (int r = 0; r < rows; ++r) s += Vs[r * NB + j] * Xs[r * NB + c];
-        Ppart[(int64_t)blockIdx.x * NB * NB + p] = s;
+    // thread (c, g): P[j][c] over rows r = g, g + 8, ... for every j
+    const int c = tid & 31, g = tid >> 5;
+    T pj[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) pj[j] = 0;
+    for (int r = g; r < XR; r += 8) {
+        const T xc = Xs[r * (NB + 1) + c];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) pj[j] += Vs[r * NB + j] * xc;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) red[g][j * NB + c] = pj[j];
+    __syncthreads();
+    for (int q = tid; q < NB * NB; q += 256) {
+        T sum = 0;
+#pragma unroll
+        for (int gg = 0; gg < 8; ++gg) sum += red[gg][q];
+        Ppart[(int64_t)blockIdx.x * NB * NB + q] = sum;
     }
 }
 
@@ -547,8 +673,12 @@ __global__ __launch_bounds__(256) void k_zform(T *__restrict__ X, const T *__res
     const int64_t r = blockIdx.x * 8 + (tid >> 5);
     const int c = tid & 31;
     if (r >= m) return;
+    T vrow[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) vrow[j] = V[r * NB + j];
     T s = 0;
-    for (int j = 0; j < NB; ++j) s += V[r * NB + j] * Ms[j * NB + c];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s += vrow[j] * Ms[j * NB + c];
     X[r * NB + c] -= (T)0.5 * s;
 }
 
@@ -568,8 +698,9 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
     const bool diag = ti == tj;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // L = [V | Z] rows i0.., R = [Z | V] rows j0..
-    for (int idx = tid; idx < S2_T * NB; idx += 256) {
-        const int r = idx / NB, c = idx % NB;
+#pragma unroll
+    for (int q = 0; q < S2_T * NB / 256; ++q) {
+        const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
         const int i = i0 + r, j = j0 + r;
         const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
         const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
@@ -1022,7 +1153,7 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.U = ws.take<T>((size_t)NB * NB);
     b.Tm = ws.take<T>((size_t)NB * NB);
     b.Mm = ws.take<T>((size_t)NB * NB);
-    b.Ppart = ws.take<T>((size_t)cdiv_h(n, 256) * NB * NB);
+    b.Ppart = ws.take<T>((size_t)cdiv_h(n, XR) * NB * NB);
     b.dd = ws.take<double>((size_t)n);
     b.ee2 = ws.take<double>((size_t)n);
     b.bounds = ws.take<double>(4);
@@ -1041,7 +1172,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     Bufs<T> b;
     layout<T>(n, (char *)ws, b);
     constexpr int RB = Cfg<T>::RB;
-    constexpr int TOP_BLOCKS = RB / NB;  // stacked R rows fit the LDS panel
+    constexpr int TOP_BLOCKS = RB / NB;  // stacked R rows (<= 1024 f32, 512 f64) fit one workgroup's registers
     constexpr int DIRECT_ROWS = 256;
     static_assert(DIRECT_ROWS <= RB, "direct panel must fit");
     // ---- stage 1: dense -> band
@@ -1059,10 +1190,23 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             // factors of all blocks are factored by one workgroup)
             const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
             const int per = (int)cdiv_h(m, nblk);
-            hipLaunchKernelGGL(k_tsqr_local<T>, dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per, b.Vloc, b.Tloc,
-                               b.Rstack);
+            const int rows_top = nblk * NB;
+            if (per <= 256)
+                hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per, b.Vloc,
+                                   b.Tloc, b.Rstack);
+            else if (per <= 512)
+                hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, st, P, lda, (int)m, per, b.Vloc,
+                                   b.Tloc, b.Rstack);
+            else
+                hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, st, P, lda, (int)m, per,
+                                   b.Vloc, b.Tloc, b.Rstack);
             LAUNCH_OK();
-            hipLaunchKernelGGL(k_tsqr_top<T>, dim3(1), dim3(256), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
+            if (rows_top <= 256)
+                hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
+            else if (rows_top <= 512)
+                hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
+            else
+                hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
             LAUNCH_OK();
             hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
                                b.Qt, (int)m, per, b.Q1);
@@ -1081,7 +1225,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         ks = (int)cdiv_h(m, chunk);
         hipLaunchKernelGGL(k_symm<T>, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart, chunk);
         LAUNCH_OK();
-        const int nxb = (int)cdiv_h(m, 256);
+        const int nxb = (int)cdiv_h(m, XR);
         hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, b.V, b.X, b.Ppart);
         LAUNCH_OK();
         hipLaunchKernelGGL(k_mfin<T>, dim3(1), dim3(256), 0, st, b.Ppart, nxb, b.Tm, b.Mm);
