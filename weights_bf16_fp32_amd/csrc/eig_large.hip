@@ -798,6 +798,32 @@ __device__ __forceinline__ T wave_sum(T x)
     return x;
 }
 
+// sum over the 32 lanes of each half-wave
+template <typename T>
+__device__ __forceinline__ T half_sum(T x)
+{
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// butterfly reduce-scatter within each half-wave: lane ci (0..31) returns the
+// sum over the half of q[ci >> 1]
+template <typename T>
+__device__ __forceinline__ T reduce_scatter16(const T (&q)[16], int ci)
+{
+    T y8[8], y4[4], y2[2];
+    const bool b4 = ci & 16, b3 = ci & 8, b2 = ci & 4, b1 = ci & 2;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) y8[m] = (b4 ? q[m + 8] : q[m]) + __shfl_xor(b4 ? q[m] : q[m + 8], 16, 64);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) y4[m] = (b3 ? y8[m + 4] : y8[m]) + __shfl_xor(b3 ? y8[m] : y8[m + 4], 8, 64);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) y2[m] = (b2 ? y4[m + 2] : y4[m]) + __shfl_xor(b2 ? y4[m] : y4[m + 2], 4, 64);
+    const T y1 = (b1 ? y2[1] : y2[0]) + __shfl_xor(b1 ? y2[0] : y2[1], 2, 64);
+    return y1 + __shfl_xor(y1, 1, 64);
+}
+
 // Band rows are exchanged between workgroups on different XCDs.  Every such
 // access is a relaxed agent-scope atomic (a load or store that is coherent
 // across the device by itself), so no cache-wide writeback or invalidation is
@@ -824,25 +850,32 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One workgroup of G waves per group of G consecutive sweeps s0 .. s0+G-1.
-// At time step t wave i runs task (s0 + i, t - 2 (s0 + i)): the tasks of one
-// time step touch disjoint rows and depend only on tasks of earlier steps
-// ("(s, k) after (s - 1, k + 1)"), so the G waves run them side by side.  The
-// rows of the group stay in an LDS ring (row r at slot r & (CAPR - 1), its band
-// entries A[r][r - j] contiguous).  The lead sweep s0 loads each row once, after
-// the previous group's watermark has passed it; after every time step the rows
-// no future task of the group touches are stored back and the group's
-// watermark moves.
+// One workgroup per group of G consecutive sweeps s0 .. s0+G-1: G compute
+// waves, a loader wave and a storer wave.  At time step t compute wave i runs
+// task (s0 + i, t - 2 (s0 + i)); the tasks of one time step touch disjoint rows
+// and depend only on tasks of earlier steps ("(s, k) after (s - 1, k + 1)"), so
+// the G waves run them side by side.  The rows of the group stay in an LDS ring
+// (row r at slot r & (CAPR - 1), its band entries A[r][r - j] contiguous).
+//  * loader: the lead sweep s0 needs NB new rows per step.  The rows for step
+//    t + LA are requested at step t (after the previous group's watermark has
+//    passed them) and written into the ring at step t + 1, so no compute wave
+//    waits on a load.
+//  * storer: the rows no future task of the group touches (below the
+//    watermark) are stored at the step after their release; at the next step,
+//    once the stores are complete, the watermark is published for the next
+//    group.
 template <typename T, int G, int CAPR>
-__global__ __launch_bounds__(64 * G) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
-                                                  uint64_t spin_ticks)
+__global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
+                                                        uint64_t spin_ticks)
 {
-    static_assert((CAPR & (CAPR - 1)) == 0 && 2 * G * NB + NB <= CAPR, "ring too small");
+    constexpr int LA = 2;  // loader lookahead in time steps
+    static_assert((CAPR & (CAPR - 1)) == 0 && (LA + 2 * G) * NB <= CAPR, "ring too small");
     constexpr int LDW = BW + 1;
     __shared__ T WR[CAPR * LDW];
     __shared__ T vsw[G][NB];
     __shared__ T red[G][NB];
-    __shared__ int go;
+    __shared__ T w2s[G][NB];
+    __shared__ int abort_flag;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ci = lane & 31, h = lane >> 5;
     const int nn = (int)n;
@@ -855,133 +888,198 @@ __global__ __launch_bounds__(64 * G) void k_bulge(T *__restrict__ band, int64_t 
     auto ntasks = [&](int s) { return (nn - 2 - s) / NB + 1; };
     // a task (s, k) reads and writes only rows s + 1 + k NB .. s + (k + 1) NB
     auto minrow = [&](int s, int k) { return k <= 0 ? s + 1 : s + 1 + k * NB; };
+    auto lastrow = [&](int s, int k) { return min(s + (k + 1) * NB, nn - 1); };
+    const int ntl = ntasks(s0);  // tasks of the lead sweep
+    // rows loaded into the ring once the lead's task k has been fetched
+    auto loaded_to = [&](int k) { return k < 0 ? s0 + 1 : lastrow(s0, min(k, ntl - 1)) + 1; };
 
-    int lw = s0 + 1;   // rows [s0 + 1, lw) are in the ring
-    int wmk = s0 + 1;  // rows [s0 + 1, wmk) have been stored back
-    T taup = 0;        // this wave's previous reflector (v in vsw[wv])
-    for (int t = 2 * s0;; ++t) {
-        // ---- the lead sweep's rows, once the previous group has released them
-        const int k0 = t - 2 * s0;
-        if (k0 < ntasks(s0)) {
-            const int r1 = min(s0 + (k0 + 1) * NB, nn - 1);
-            if (r1 >= lw) {
-                if (g > 0) {
-                    if (tid == 0) {
-                        int ok = 1;
-                        if (cload(wm + g - 1) <= r1) {
-                            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                            while (cload(wm + g - 1) <= r1) {
-                                if (cload(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
-                                    ok = 0;
-                                    break;
-                                }
-                                __builtin_amdgcn_s_sleep(1);
-                            }
-                        }
-                        if (!ok) cstore(err, 1);
-                        go = ok;
+    // the loader's wait for the previous group; sets abort_flag on time-out
+    auto wait_rows = [&](int r1) {
+        int ok = 1;
+        if (g > 0 && lane == 0) {
+            if (cload(wm + g - 1) <= r1) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                while (cload(wm + g - 1) <= r1) {
+                    if (cload(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
+                        ok = 0;
+                        break;
                     }
-                    __syncthreads();
-                    if (!go) return;
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                if (r1 + 1 - wmk > CAPR) {  // cannot happen: the ring holds (2G + 1) NB rows
-                    if (tid == 0) cstore(err, 2);
-                    return;
-                }
-                const int cnt = r1 + 1 - lw;  // <= NB
-                if (wv == 0) {
-                    T tmp[NB];
+            }
+            if (!ok) {
+                cstore(err, 1);
+                abort_flag = 1;
+            }
+        }
+        return __shfl(ok, 0, 64);
+    };
+
+    if (tid == 0) abort_flag = 0;
+    __syncthreads();
+    // ---- prologue: the lead's first LA chunks, synchronously
+    if (wv == G) {
+        for (int k = 0; k < LA && k < ntl; ++k) {
+            const int lo = loaded_to(k - 1), hi = loaded_to(k);
+            if (!wait_rows(hi - 1)) break;
+            T tmp[NB];
 #pragma unroll
-                    for (int q = 0; q < NB; ++q) tmp[q] = q < cnt ? cload(band + (int64_t)(lw + q) * BW + lane) : (T)0;
+            for (int q = 0; q < NB; ++q) tmp[q] = lo + q < hi ? cload(band + (int64_t)(lo + q) * BW + lane) : (T)0;
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+                if (lo + q < hi) E(lo + q, lo + q - lane) = tmp[q];
+        }
+    }
+    __syncthreads();
+    if (abort_flag) return;
+
+    T ld[NB];            // loader: the chunk in flight
+    int ld_lo = 0, ld_hi = 0;  // loader: its rows
+    int st_pub = -1;     // storer: watermark to publish once its stores are complete
+    int wst = s0 + 1;    // rows below wst have been handed to the storer
+    int wmk = s0 + 1;    // rows below wmk are released
+    T taup = 0;          // compute wave: the previous reflector of its sweep
+    for (int t = 2 * s0;; ++t) {
+        const int k0 = t - 2 * s0;
+        if (wv == G) {
+            // write the chunk requested at the previous step, request the next one
+            if (ld_hi > ld_lo) {
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+                    if (ld_lo + q < ld_hi) E(ld_lo + q, ld_lo + q - lane) = ld[q];
+            }
+            ld_lo = ld_hi = 0;
+            const int kn = k0 + LA;
+            if (kn < ntl) {
+                const int lo = loaded_to(kn - 1), hi = loaded_to(kn);
+                if (wait_rows(hi - 1)) {
 #pragma unroll
                     for (int q = 0; q < NB; ++q)
-                        if (q < cnt) E(lw + q, lw + q - lane) = tmp[q];
+                        ld[q] = lo + q < hi ? cload(band + (int64_t)(lo + q) * BW + lane) : (T)0;
+                    ld_lo = lo;
+                    ld_hi = hi;
                 }
-                lw = r1 + 1;
-                __syncthreads();
             }
-        }
-        // ---- this wave's task
-        const int s = s0 + wv;
-        const int k = t - 2 * s;
-        if (wv < Ge && k >= 0 && k < ntasks(s)) {
-            const int r0 = s + 1 + k * NB;
-            const int r1 = min(s + (k + 1) * NB, nn - 1);
-            const int L = r1 - r0 + 1;
-            T *v = vsw[wv];
-            T tau_k = 0, mu = 0;
-            if (k == 0) {
-                const T x = lane < L ? E(r0 + lane, s) : (T)0;
-                const T sigma = wave_sum(lane >= 1 && lane < L ? x * x : (T)0);
+        } else if (wv == G + 1) {
+            // publish the watermark of the stores issued at the previous step
+            if (st_pub >= 0) {
+                __builtin_amdgcn_s_waitcnt(0);
+                if (lane == 0) cstore(wm + g, (int32_t)st_pub);
+                st_pub = -1;
+            }
+            if (wmk > wst) {
+                for (int r = wst; r < wmk; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+                st_pub = wmk;
+            }
+        } else {
+            const int s = s0 + wv;
+            const int k = t - 2 * s;
+            if (wv < Ge && k >= 0 && k < ntasks(s)) {
+                // Lane (ci, h) holds row r0 + ci of the task's block in registers: the
+                // columns h*16 .. h*16+15 of O = A[r0.., c0 .. c0+NB) (k > 0) and of the
+                // symmetric diagonal block D = A[r0.., r0..] (both triangles).
+                const int r0 = s + 1 + k * NB;
+                const int L = lastrow(s, k) - r0 + 1;
+                const bool rowok = ci < L;
+                const int rb = ((r0 + ci) & (CAPR - 1)) * LDW;  // ring slot of row r0 + ci
+                T *v = vsw[wv];
+                T o[16], dd[16];
+                T x;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const int j = h * 16 + c;
+                    dd[c] = rowok && j < L
+                                ? (j <= ci ? WR[rb + ci - j] : WR[((r0 + j) & (CAPR - 1)) * LDW + j - ci])
+                                : (T)0;
+                }
+                if (k == 0) {
+                    x = rowok ? WR[rb + ci + 1] : (T)0;  // column s
+                } else {
+                    T vp[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) {
+                        o[c] = rowok ? WR[rb + NB + ci - (h * 16 + c)] : (T)0;
+                        vp[c] = v[h * 16 + c];
+                    }
+                    // right: O <- O (I - taup vp vp^T)
+                    if (taup != 0) {
+                        T u = 0;
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) u += o[c] * vp[c];
+                        u += __shfl_xor(u, 32, 64);
+                        u *= taup;
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) o[c] -= u * vp[c];
+                    }
+                    x = __shfl(o[0], ci, 64);  // column c0
+                }
+                // reflector (I - tau v v^T) x = mu e_0, v_0 = 1
+                const T sigma = half_sum(ci >= 1 ? x * x : (T)0);
                 const T x0 = __shfl(x, 0, 64);
-                T vi = 0;
+                T tau_k = 0, mu = 0, vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
                     tau_k = 2 * v0 * v0 / (sigma + v0 * v0);
-                    vi = lane == 0 ? (T)1 : x / v0;
-                    if (lane < L) E(r0 + lane, s) = lane == 0 ? mu : (T)0;
-                }
-                if (lane < NB) v[lane] = vi;
-            } else {
-                const int c0 = r0 - NB;
-                // right: O <- O (I - taup vp vp^T), O = A[r0.., c0..c0+NB)
-                if (taup != 0) {
-                    T u = 0;
-                    if (ci < L)
-#pragma unroll
-                        for (int c = 0; c < 16; ++c) u += E(r0 + ci, c0 + h * 16 + c) * v[h * 16 + c];
-                    u += __shfl_xor(u, 32, 64);
-                    if (ci < L)
-#pragma unroll
-                        for (int c = 0; c < 16; ++c) E(r0 + ci, c0 + h * 16 + c) -= taup * u * v[h * 16 + c];
-                    wave_sync();
-                }
-                // reflector from column c0
-                const T x = lane < L ? E(r0 + lane, c0) : (T)0;
-                const T sigma = wave_sum(lane >= 1 && lane < L ? x * x : (T)0);
-                const T x0 = __shfl(x, 0, 64);
-                T vi = 0;
-                if (sigma > 0) {
-                    mu = sqrt(x0 * x0 + sigma);
-                    const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
-                    tau_k = 2 * v0 * v0 / (sigma + v0 * v0);
-                    vi = lane == 0 ? (T)1 : x / v0;
+                    vi = ci == 0 ? (T)1 : x / v0;
                 }
                 wave_sync();
-                if (lane < NB) v[lane] = lane < L ? vi : (T)0;
+                if (h == 0) v[ci] = vi;
+                if (k > 0 && tau_k != 0) {
+                    // left: w = O^T v, reduced over the 32 rows of each half; lane ci
+                    // ends with column h*16 + ci/2
+                    T q[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) q[c] = vi * o[c];
+                    const T wj = reduce_scatter16(q, ci);
+                    if ((ci & 1) == 0) red[wv][h * 16 + (ci >> 1)] = wj;
+                }
                 wave_sync();
                 if (tau_k != 0) {
-                    // left: O <- (I - tau v v^T) O; column c0 becomes mu e_0
-                    T w = 0;
-                    for (int r = h; r < L; r += 2) w += v[r] * E(r0 + r, c0 + ci);
-                    w += __shfl_xor(w, 32, 64);
-                    for (int r = h; r < L; r += 2) E(r0 + r, c0 + ci) -= tau_k * v[r] * w;
+                    T vr[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) vr[c] = v[h * 16 + c];
+                    if (k > 0) {
+                        const T tv = tau_k * vi;
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) o[c] -= tv * red[wv][h * 16 + c];
+                        if (h == 0) o[0] = ci == 0 ? mu : (T)0;
+                    }
+                    // two-sided on D: p = tau D v, w = p - (tau/2)(p^T v) v, D -= v w^T + w v^T
+                    T pp = 0;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) pp += dd[c] * vr[c];
+                    pp += __shfl_xor(pp, 32, 64);
+                    pp *= tau_k;
+                    const T pv = half_sum(pp * vi);
+                    const T w2 = pp - (T)0.5 * tau_k * pv * vi;
+                    if (h == 0) w2s[wv][ci] = w2;
                     wave_sync();
-                    if (lane < L) E(r0 + lane, c0) = lane == 0 ? mu : (T)0;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) dd[c] -= vi * w2s[wv][h * 16 + c] + w2 * vr[c];
                 }
+                if (rowok) {
+                    if (k == 0) {
+                        if (tau_k != 0) WR[rb + ci + 1] = ci == 0 ? mu : (T)0;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) WR[rb + NB + ci - (h * 16 + c)] = o[c];
+                    }
+                    if (tau_k != 0) {
+#pragma unroll
+                        for (int c = 0; c < 16; ++c)
+                            if (h * 16 + c <= ci) WR[rb + ci - (h * 16 + c)] = dd[c];
+                    }
+                }
+                taup = tau_k;
             }
-            wave_sync();
-            if (tau_k != 0) {
-                // two-sided on the diagonal block A[r0..r1, r0..r1] (lower part stored)
-                T p = 0;
-                if (ci < L)
-                    for (int j = h * 16; j < min(L, h * 16 + 16); ++j)
-                        p += (j <= ci ? E(r0 + ci, r0 + j) : E(r0 + j, r0 + ci)) * v[j];
-                p += __shfl_xor(p, 32, 64);
-                p *= tau_k;
-                const T vci = ci < L ? v[ci] : (T)0;
-                const T pv = wave_sum(h == 0 ? p * vci : (T)0);
-                if (h == 0) red[wv][ci] = ci < L ? p - (T)0.5 * tau_k * pv * vci : (T)0;
-                wave_sync();
-                for (int r = h; r < L; r += 2)
-                    if (ci <= r) E(r0 + r, r0 + ci) -= v[r] * red[wv][ci] + red[wv][r] * v[ci];
-            }
-            taup = tau_k;
         }
         __syncthreads();
-        // ---- rows below the first row of every remaining task are final
-        int nwm = lw;
+        if (abort_flag) return;
+        // ---- uniform bookkeeping: the storer has taken [wst, wmk); rows below the
+        // first row of every remaining task, and already in the ring, are released
+        wst = max(wst, wmk);
+        int nwm = loaded_to(k0 + LA - 1);
         bool more = false;
         for (int i = 0; i < Ge; ++i) {
             const int kk = t + 1 - 2 * (s0 + i);
@@ -990,21 +1088,14 @@ __global__ __launch_bounds__(64 * G) void k_bulge(T *__restrict__ band, int64_t 
                 more = true;
             }
         }
+        if (nwm > wmk) wmk = nwm;
         if (!more) break;
-        if (nwm > wmk) {
-            if (wv == 0) {
-                for (int r = wmk; r < nwm; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
-                __builtin_amdgcn_s_waitcnt(0);
-                wave_sync();
-                if (lane == 0) cstore(wm + g, (int32_t)nwm);
-            }
-            wmk = nwm;
-        }
     }
-    if (wv == 0) {
-        for (int r = wmk; r < lw; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+    // ---- epilogue: store what is left and publish the end
+    if (wv == G + 1) {
         __builtin_amdgcn_s_waitcnt(0);
-        wave_sync();
+        for (int r = wst; r < nn; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+        __builtin_amdgcn_s_waitcnt(0);
         if (lane == 0) cstore(wm + g, (int32_t)nn);
     }
 }
@@ -1243,13 +1334,13 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     LAUNCH_OK();
     if (n >= 3) {
         // G sweeps per workgroup (one wave each); the LDS ring holds >= (2G + 1) NB rows
-        constexpr int G = sizeof(T) == 4 ? 4 : 3;
+        constexpr int G = sizeof(T) == 4 ? 6 : 3;
         constexpr int CAPR = sizeof(T) == 4 ? 512 : 256;
         const int64_t nsw = n - 2;
         const int64_t ngroups = cdiv_h(nsw, G);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
-        hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * G), 0, st, b.band, n, b.prog,
-                           spin_ticks);
+        hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * (G + 2)), 0, st, b.band, n,
+                           b.prog, spin_ticks);
         LAUNCH_OK();
     }
     // ---- stage 3: eigenvalues of the tridiagonal
