@@ -798,30 +798,108 @@ __device__ __forceinline__ T wave_sum(T x)
     return x;
 }
 
+// Cross-lane moves without the LDS pipeline: DPP within rows of 16 lanes
+// (quad permutes 0xB1 = lane^1 and 0x4E = lane^2, half-row mirror 0x141,
+// row mirror 0x140) and the gfx950 row swaps (permlane16/32_swap), which
+// exchange the odd rows (16 lanes) or the upper half (32 lanes) of the first
+// operand with the even rows or the lower half of the second.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x)
+{
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
+                            __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
+}
+// (a, b) -> (a', b'): a' = a in even rows, b from the row below in odd rows;
+// b' = a from the row above in even rows, b in odd rows
+__device__ __forceinline__ void rowswap16(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void rowswap16(double &a, double &b)
+{
+    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
+    a = __hiloint2double((int)h[0], (int)l[0]);
+    b = __hiloint2double((int)h[1], (int)l[1]);
+}
+__device__ __forceinline__ void halfswap32(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void halfswap32(double &a, double &b)
+{
+    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
+    a = __hiloint2double((int)h[0], (int)l[0]);
+    b = __hiloint2double((int)h[1], (int)l[1]);
+}
+// x + x[lane ^ 32]
+template <typename T>
+__device__ __forceinline__ T pair32_sum(T x)
+{
+    T a = x, b = x;
+    halfswap32(a, b);
+    return a + b;
+}
+// in lanes 32..63 the value of lane - 32; lanes 0..31 keep their own
+template <typename T>
+__device__ __forceinline__ T from_lower_half(T x)
+{
+    T a = x, b = x;
+    halfswap32(a, b);
+    return a;
+}
 // sum over the 32 lanes of each half-wave
 template <typename T>
 __device__ __forceinline__ T half_sum(T x)
 {
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    T a = x, b = x;
+    rowswap16(a, b);
+    return a + b;
 }
 
 // butterfly reduce-scatter within each half-wave: lane ci (0..31) returns the
-// sum over the half of q[ci >> 1]
+// sum over the half of q[ci >> 1].  Level by level the partner differs in bit
+// 4 (row swap), 3 (row mirror), 2 (half-row mirror), 1 and 0 (quad permutes)
+// of the lane index and shares the higher bits, and each lane keeps the half
+// of its values selected by that bit.
 template <typename T>
 __device__ __forceinline__ T reduce_scatter16(const T (&q)[16], int ci)
 {
     T y8[8], y4[4], y2[2];
-    const bool b4 = ci & 16, b3 = ci & 8, b2 = ci & 4, b1 = ci & 2;
+    const bool b3 = ci & 8, b2 = ci & 4, b1 = ci & 2;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) y8[m] = (b4 ? q[m + 8] : q[m]) + __shfl_xor(b4 ? q[m] : q[m + 8], 16, 64);
+    for (int m = 0; m < 8; ++m) {
+        T a = q[m], b = q[m + 8];
+        rowswap16(a, b);
+        y8[m] = a + b;
+    }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) y4[m] = (b3 ? y8[m + 4] : y8[m]) + __shfl_xor(b3 ? y8[m] : y8[m + 4], 8, 64);
+    for (int m = 0; m < 4; ++m) y4[m] = (b3 ? y8[m + 4] : y8[m]) + dpp<0x140>(b3 ? y8[m] : y8[m + 4]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) y2[m] = (b2 ? y4[m + 2] : y4[m]) + __shfl_xor(b2 ? y4[m] : y4[m + 2], 4, 64);
-    const T y1 = (b1 ? y2[1] : y2[0]) + __shfl_xor(b1 ? y2[0] : y2[1], 2, 64);
-    return y1 + __shfl_xor(y1, 1, 64);
+    for (int m = 0; m < 2; ++m) y2[m] = (b2 ? y4[m + 2] : y4[m]) + dpp<0x141>(b2 ? y4[m] : y4[m + 2]);
+    const T y1 = (b1 ? y2[1] : y2[0]) + dpp<0x4E>(b1 ? y2[0] : y2[1]);
+    return y1 + dpp<0xB1>(y1);
+}
+
+__device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
+__device__ __forceinline__ double readlane0(double x)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 0), __builtin_amdgcn_readlane(__double2loint(x), 0));
 }
 
 // Band rows are exchanged between workgroups on different XCDs.  Every such
@@ -864,14 +942,40 @@ __device__ __forceinline__ void wave_sync()
 //    watermark) are stored at the step after their release; at the next step,
 //    once the stores are complete, the watermark is published for the next
 //    group.
+// Band rows move between the ring and global memory as buffer loads and
+// stores (one instruction per row, row offsets in the instruction; rows past
+// the end of the band read as zero) with the same cache policy as cload/cstore.
+template <typename T>
+__device__ __forceinline__ T band_load(__amdgpu_buffer_rsrc_t rs, int voff, int soff)
+{
+    if constexpr (sizeof(T) == 4)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 16));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 16));
+}
+template <typename T>
+__device__ __forceinline__ void band_store(__amdgpu_buffer_rsrc_t rs, T x, int voff, int soff)
+{
+    if constexpr (sizeof(T) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, voff, soff, 16);
+    else
+    {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), rs, voff, soff, 16);
+    }
+}
+
 template <typename T, int G, int CAPR>
 __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
                                                         uint64_t spin_ticks)
 {
     constexpr int LA = 2;  // loader lookahead in time steps
-    static_assert((CAPR & (CAPR - 1)) == 0 && (LA + 2 * G) * NB <= CAPR, "ring too small");
+    static_assert(CAPR % NB == 0 && (LA + 2 * G - 1) * NB <= CAPR, "ring too small");
     constexpr int LDW = BW + 1;
-    __shared__ T WR[CAPR * LDW];
+    constexpr int RB = BW * sizeof(T);  // bytes per band row
+    constexpr int QI = 4096 / RB;       // rows reachable from one base through the instruction offset
+    __shared__ T WRbuf[NB + CAPR * LDW];
+    T *const WR = WRbuf + NB;  // NB guard entries before the first ring row
     __shared__ T vsw[G][NB];
     __shared__ T red[G][NB];
     __shared__ T w2s[G][NB];
@@ -884,7 +988,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     const int g = blockIdx.x;
     const int s0 = g * G;
     const int Ge = min(G, nsw - s0);
-    auto E = [&](int r, int c) -> T & { return WR[(r & (CAPR - 1)) * LDW + (r - c)]; };
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(band, 0, nn * RB, 0x00020000);
+    // ring slot of row r, counted from the group's first row so that the lead's
+    // NB-row chunks never wrap
+    auto slot = [&](int r) { return (r - s0 - 1) % CAPR; };
     auto ntasks = [&](int s) { return (nn - 2 - s) / NB + 1; };
     // a task (s, k) reads and writes only rows s + 1 + k NB .. s + (k + 1) NB
     auto minrow = [&](int s, int k) { return k <= 0 ? s + 1 : s + 1 + k * NB; };
@@ -912,7 +1019,37 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 abort_flag = 1;
             }
         }
-        return __shfl(ok, 0, 64);
+        return __builtin_amdgcn_readfirstlane(ok);
+    };
+    // the NB rows lo .. lo+NB-1 of a lead chunk (rows past the end read as zero)
+    auto load_chunk = [&](int lo, T (&buf)[NB]) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+            buf[q] = band_load<T>(rs, lane * (int)sizeof(T) + (q % QI) * RB, (lo + q / QI * QI) * RB);
+    };
+    auto write_chunk = [&](int lo, const T (&buf)[NB]) {
+        T *p = WR + slot(lo) * LDW + lane;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) p[q * LDW] = buf[q];
+    };
+
+    // stores rows r0 .. r1-1 from the ring to the band
+    auto store_rows = [&](int r0, int r1) {
+        for (int r = r0; r < r1; r += NB) {
+            const int m = min(NB, r1 - r);
+            T tmp[NB];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) tmp[q] = WR[slot(min(r + q, r1 - 1)) * LDW + lane];
+            if (m == NB) {
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+                    band_store<T>(rs, tmp[q], lane * (int)sizeof(T) + (q % QI) * RB, (r + q / QI * QI) * RB);
+            } else {
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+                    if (q < m) band_store<T>(rs, tmp[q], lane * (int)sizeof(T), (r + q) * RB);
+            }
+        }
     };
 
     if (tid == 0) abort_flag = 0;
@@ -923,41 +1060,31 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
             const int lo = loaded_to(k - 1), hi = loaded_to(k);
             if (!wait_rows(hi - 1)) break;
             T tmp[NB];
-#pragma unroll
-            for (int q = 0; q < NB; ++q) tmp[q] = lo + q < hi ? cload(band + (int64_t)(lo + q) * BW + lane) : (T)0;
-#pragma unroll
-            for (int q = 0; q < NB; ++q)
-                if (lo + q < hi) E(lo + q, lo + q - lane) = tmp[q];
+            load_chunk(lo, tmp);
+            write_chunk(lo, tmp);
         }
     }
     __syncthreads();
     if (abort_flag) return;
 
-    T ld[NB];            // loader: the chunk in flight
-    int ld_lo = 0, ld_hi = 0;  // loader: its rows
-    int st_pub = -1;     // storer: watermark to publish once its stores are complete
-    int wst = s0 + 1;    // rows below wst have been handed to the storer
-    int wmk = s0 + 1;    // rows below wmk are released
+    T ld[NB];          // loader: the chunk in flight
+    int ld_lo = -1;    // loader: its first row (-1: none)
+    int st_pub = -1;   // storer: watermark to publish once its stores are complete
+    int wst = s0 + 1;  // rows below wst have been handed to the storer
+    int wmk = s0 + 1;  // rows below wmk are released
     T taup = 0;          // compute wave: the previous reflector of its sweep
     for (int t = 2 * s0;; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
             // write the chunk requested at the previous step, request the next one
-            if (ld_hi > ld_lo) {
-#pragma unroll
-                for (int q = 0; q < NB; ++q)
-                    if (ld_lo + q < ld_hi) E(ld_lo + q, ld_lo + q - lane) = ld[q];
-            }
-            ld_lo = ld_hi = 0;
+            if (ld_lo >= 0) write_chunk(ld_lo, ld);
+            ld_lo = -1;
             const int kn = k0 + LA;
             if (kn < ntl) {
                 const int lo = loaded_to(kn - 1), hi = loaded_to(kn);
                 if (wait_rows(hi - 1)) {
-#pragma unroll
-                    for (int q = 0; q < NB; ++q)
-                        ld[q] = lo + q < hi ? cload(band + (int64_t)(lo + q) * BW + lane) : (T)0;
+                    load_chunk(lo, ld);
                     ld_lo = lo;
-                    ld_hi = hi;
                 }
             }
         } else if (wv == G + 1) {
@@ -968,7 +1095,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 st_pub = -1;
             }
             if (wmk > wst) {
-                for (int r = wst; r < wmk; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+                store_rows(wst, wmk);
                 st_pub = wmk;
             }
         } else {
@@ -977,45 +1104,49 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
             if (wv < Ge && k >= 0 && k < ntasks(s)) {
                 // Lane (ci, h) holds row r0 + ci of the task's block in registers: the
                 // columns h*16 .. h*16+15 of O = A[r0.., c0 .. c0+NB) (k > 0) and of the
-                // symmetric diagonal block D = A[r0.., r0..] (both triangles).
+                // lower triangle of the diagonal block D = A[r0.., r0..].  All of it lies
+                // in the lane's own ring row at fixed offsets, so the loads issue back to
+                // back; entries outside the task are masked after loading (the guard
+                // before the ring keeps every offset inside the array).
                 const int r0 = s + 1 + k * NB;
                 const int L = lastrow(s, k) - r0 + 1;
                 const bool rowok = ci < L;
-                const int rb = ((r0 + ci) & (CAPR - 1)) * LDW;  // ring slot of row r0 + ci
+                const int rb = slot(r0 + ci) * LDW;  // ring slot of row r0 + ci
+                const int e = rowok ? ci - h * 16 : -1;          // D column c of this lane is in the lower triangle iff c <= e
                 T *v = vsw[wv];
-                T o[16], dd[16];
-                T x;
+                T o[16], dd[16], vp[16];
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
-                    const int j = h * 16 + c;
-                    dd[c] = rowok && j < L
-                                ? (j <= ci ? WR[rb + ci - j] : WR[((r0 + j) & (CAPR - 1)) * LDW + j - ci])
-                                : (T)0;
+                    dd[c] = WR[rb + ci - h * 16 - c];
+                    o[c] = WR[rb + NB + ci - h * 16 - c];
+                    vp[c] = v[h * 16 + c];
                 }
-                if (k == 0) {
-                    x = rowok ? WR[rb + ci + 1] : (T)0;  // column s
-                } else {
-                    T vp[16];
+                const T xs = WR[rb + ci + 1];  // column s
+                const T dg = rowok ? WR[rb] : (T)0;
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) {
-                        o[c] = rowok ? WR[rb + NB + ci - (h * 16 + c)] : (T)0;
-                        vp[c] = v[h * 16 + c];
-                    }
+                for (int c = 0; c < 16; ++c) dd[c] = c <= e ? dd[c] : (T)0;
+                if (L < NB) {
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) o[c] = rowok ? o[c] : (T)0;
+                }
+                T x;
+                if (k == 0) {
+                    x = rowok ? xs : (T)0;
+                } else {
                     // right: O <- O (I - taup vp vp^T)
                     if (taup != 0) {
                         T u = 0;
 #pragma unroll
                         for (int c = 0; c < 16; ++c) u += o[c] * vp[c];
-                        u += __shfl_xor(u, 32, 64);
-                        u *= taup;
+                        u = taup * pair32_sum(u);
 #pragma unroll
                         for (int c = 0; c < 16; ++c) o[c] -= u * vp[c];
                     }
-                    x = __shfl(o[0], ci, 64);  // column c0
+                    x = from_lower_half(o[0]);  // column c0, held by the lanes of half 0
                 }
                 // reflector (I - tau v v^T) x = mu e_0, v_0 = 1
                 const T sigma = half_sum(ci >= 1 ? x * x : (T)0);
-                const T x0 = __shfl(x, 0, 64);
+                const T x0 = readlane0(x);
                 T tau_k = 0, mu = 0, vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
@@ -1025,20 +1156,28 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 }
                 wave_sync();
                 if (h == 0) v[ci] = vi;
-                if (k > 0 && tau_k != 0) {
-                    // left: w = O^T v, reduced over the 32 rows of each half; lane ci
-                    // ends with column h*16 + ci/2
+                if (tau_k != 0) {
+                    // column sums, reduced over the 32 rows of each half (lane ci ends
+                    // with column h*16 + ci/2): w = O^T v and the part of D v that
+                    // comes from the upper triangle, sum_{j >= i} D[j][i] v_j
                     T q[16];
+                    if (k > 0) {
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) q[c] = vi * o[c];
-                    const T wj = reduce_scatter16(q, ci);
-                    if ((ci & 1) == 0) red[wv][h * 16 + (ci >> 1)] = wj;
+                        for (int c = 0; c < 16; ++c) q[c] = vi * o[c];
+                        const T wj = reduce_scatter16(q, ci);
+                        if ((ci & 1) == 0) red[wv][h * 16 + (ci >> 1)] = wj;
+                    }
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) q[c] = vi * dd[c];
+                    const T pj = reduce_scatter16(q, ci);
+                    if ((ci & 1) == 0) w2s[wv][h * 16 + (ci >> 1)] = pj;
                 }
                 wave_sync();
                 if (tau_k != 0) {
                     T vr[16];
 #pragma unroll
                     for (int c = 0; c < 16; ++c) vr[c] = v[h * 16 + c];
+                    const T pcol = w2s[wv][ci];
                     if (k > 0) {
                         const T tv = tau_k * vi;
 #pragma unroll
@@ -1049,10 +1188,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     T pp = 0;
 #pragma unroll
                     for (int c = 0; c < 16; ++c) pp += dd[c] * vr[c];
-                    pp += __shfl_xor(pp, 32, 64);
-                    pp *= tau_k;
+                    pp = tau_k * (pair32_sum(pp) + pcol - dg * vi);
                     const T pv = half_sum(pp * vi);
                     const T w2 = pp - (T)0.5 * tau_k * pv * vi;
+                    wave_sync();
                     if (h == 0) w2s[wv][ci] = w2;
                     wave_sync();
 #pragma unroll
@@ -1063,13 +1202,13 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                         if (tau_k != 0) WR[rb + ci + 1] = ci == 0 ? mu : (T)0;
                     } else {
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) WR[rb + NB + ci - (h * 16 + c)] = o[c];
+                        for (int c = 0; c < 16; ++c) WR[rb + NB + ci - h * 16 - c] = o[c];
                     }
-                    if (tau_k != 0) {
+                }
+                if (tau_k != 0) {
 #pragma unroll
-                        for (int c = 0; c < 16; ++c)
-                            if (h * 16 + c <= ci) WR[rb + ci - (h * 16 + c)] = dd[c];
-                    }
+                    for (int c = 0; c < 16; ++c)
+                        if (c <= e) WR[rb + ci - h * 16 - c] = dd[c];
                 }
                 taup = tau_k;
             }
@@ -1094,7 +1233,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     // ---- epilogue: store what is left and publish the end
     if (wv == G + 1) {
         __builtin_amdgcn_s_waitcnt(0);
-        for (int r = wst; r < nn; ++r) cstore(band + (int64_t)r * BW + lane, E(r, r - lane));
+        store_rows(wst, nn);
         __builtin_amdgcn_s_waitcnt(0);
         if (lane == 0) cstore(wm + g, (int32_t)nn);
     }
@@ -1334,8 +1473,8 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     LAUNCH_OK();
     if (n >= 3) {
         // G sweeps per workgroup (one wave each); the LDS ring holds >= (2G + 1) NB rows
-        constexpr int G = sizeof(T) == 4 ? 6 : 3;
-        constexpr int CAPR = sizeof(T) == 4 ? 512 : 256;
+        constexpr int G = sizeof(T) == 4 ? 8 : 3;
+        constexpr int CAPR = sizeof(T) == 4 ? 576 : 256;
         const int64_t nsw = n - 2;
         const int64_t ngroups = cdiv_h(nsw, G);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
