@@ -896,6 +896,15 @@ __device__ __forceinline__ T reduce_scatter16(const T (&q)[16], int ci)
     return y1 + dpp<0xB1>(y1);
 }
 
+// 1/x: hardware reciprocal with one Newton step in fp32 (within an ulp or so),
+// a correctly rounded division in fp64
+__device__ __forceinline__ float recip(float x)
+{
+    const float r = __builtin_amdgcn_rcpf(x);
+    return r * (2.f - x * r);
+}
+__device__ __forceinline__ double recip(double x) { return 1.0 / x; }
+
 __device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
 __device__ __forceinline__ double readlane0(double x)
 {
@@ -1037,9 +1046,16 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     auto store_rows = [&](int r0, int r1) {
         for (int r = r0; r < r1; r += NB) {
             const int m = min(NB, r1 - r);
+            const int sb = slot(r);
             T tmp[NB];
+            if (sb + NB <= CAPR) {  // the rows are consecutive in the ring
+                const T *p = WR + sb * LDW + lane;
 #pragma unroll
-            for (int q = 0; q < NB; ++q) tmp[q] = WR[slot(min(r + q, r1 - 1)) * LDW + lane];
+                for (int q = 0; q < NB; ++q) tmp[q] = p[q * LDW];
+            } else {
+#pragma unroll
+                for (int q = 0; q < NB; ++q) tmp[q] = WR[(sb + q < CAPR ? sb + q : sb + q - CAPR) * LDW + lane];
+            }
             if (m == NB) {
 #pragma unroll
                 for (int q = 0; q < NB; ++q)
@@ -1072,7 +1088,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     int st_pub = -1;   // storer: watermark to publish once its stores are complete
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
-    T taup = 0;          // compute wave: the previous reflector of its sweep
+    T taup = 0;          // compute wave: the previous reflector of its sweep (tau, and
+    T vprev[16];         // v at this lane's columns h*16 .. h*16+15)
+#pragma unroll
+    for (int c = 0; c < 16; ++c) vprev[c] = 0;
     for (int t = 2 * s0;; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
@@ -1114,12 +1133,12 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 const int rb = slot(r0 + ci) * LDW;  // ring slot of row r0 + ci
                 const int e = rowok ? ci - h * 16 : -1;          // D column c of this lane is in the lower triangle iff c <= e
                 T *v = vsw[wv];
-                T o[16], dd[16], vp[16];
+                T o[16], dd[16];
+                T(&vp)[16] = vprev;  // the previous task's reflector, columns h*16 ..
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
                     dd[c] = WR[rb + ci - h * 16 - c];
                     o[c] = WR[rb + NB + ci - h * 16 - c];
-                    vp[c] = v[h * 16 + c];
                 }
                 const T xs = WR[rb + ci + 1];  // column s
                 const T dg = rowok ? WR[rb] : (T)0;
@@ -1150,9 +1169,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 T tau_k = 0, mu = 0, vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
-                    const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
-                    tau_k = 2 * v0 * v0 / (sigma + v0 * v0);
-                    vi = ci == 0 ? (T)1 : x / v0;
+                    const T v0 = x0 <= 0 ? x0 - mu : -sigma * recip(x0 + mu);
+                    const T iv0 = recip(v0);
+                    tau_k = (T)2 * recip((T)1 + sigma * iv0 * iv0);
+                    vi = ci == 0 ? (T)1 : x * iv0;
                 }
                 wave_sync();
                 if (h == 0) v[ci] = vi;
@@ -1173,10 +1193,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     if ((ci & 1) == 0) w2s[wv][h * 16 + (ci >> 1)] = pj;
                 }
                 wave_sync();
-                if (tau_k != 0) {
-                    T vr[16];
+                T vr[16];
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) vr[c] = v[h * 16 + c];
+                for (int c = 0; c < 16; ++c) vr[c] = v[h * 16 + c];
+                if (tau_k != 0) {
                     const T pcol = w2s[wv][ci];
                     if (k > 0) {
                         const T tv = tau_k * vi;
@@ -1211,6 +1231,8 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                         if (c <= e) WR[rb + ci - h * 16 - c] = dd[c];
                 }
                 taup = tau_k;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) vprev[c] = vr[c];
             }
         }
         __syncthreads();
