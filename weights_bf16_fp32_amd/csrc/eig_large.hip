@@ -92,52 +92,166 @@ __device__ __forceinline__ void static_for(F &&f)
 template <typename T, int NT>
 struct RegQr {
     static constexpr int NW = NT / 64;
-    T red[NW][NB];  // per-wave column sums
-    T dvec[NB];     // d_c of the current column
+    T red[NW][NB];   // per-wave column sums
+    T dvec[NW][NB];  // d_c of the current column (one copy per wave)
     T sig[NW];      // per-wave partial sigma of the next column
     T x0;           // P[k][k] of the next column
     T tau[NB];
     T Tl[NB * NB];
 };
 
+// Cross-lane moves without the LDS pipeline: DPP within rows of 16 lanes
+// (quad permutes 0xB1 = lane^1 and 0x4E = lane^2, half-row mirror 0x141,
+// row mirror 0x140) and the gfx950 row swaps (permlane16/32_swap), which
+// exchange the odd rows (16 lanes) or the upper half (32 lanes) of the first
+// operand with the even rows or the lower half of the second.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x)
+{
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
+                            __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
+}
+// (a, b) -> (a', b'): a' = a in even rows, b from the row below in odd rows;
+// b' = a from the row above in even rows, b in odd rows
+__device__ __forceinline__ void rowswap16(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void rowswap16(double &a, double &b)
+{
+    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
+    a = __hiloint2double((int)h[0], (int)l[0]);
+    b = __hiloint2double((int)h[1], (int)l[1]);
+}
+__device__ __forceinline__ void halfswap32(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void halfswap32(double &a, double &b)
+{
+    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
+    a = __hiloint2double((int)h[0], (int)l[0]);
+    b = __hiloint2double((int)h[1], (int)l[1]);
+}
+// x + x[lane ^ 32]
+template <typename T>
+__device__ __forceinline__ T pair32_sum(T x)
+{
+    T a = x, b = x;
+    halfswap32(a, b);
+    return a + b;
+}
+// in lanes 32..63 the value of lane - 32; lanes 0..31 keep their own
+template <typename T>
+__device__ __forceinline__ T from_lower_half(T x)
+{
+    T a = x, b = x;
+    halfswap32(a, b);
+    return a;
+}
+// sum over the 32 lanes of each half-wave
+template <typename T>
+__device__ __forceinline__ T half_sum(T x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    T a = x, b = x;
+    rowswap16(a, b);
+    return a + b;
+}
+
+// butterfly reduce-scatter within each half-wave: lane ci (0..31) returns the
+// sum over the half of q[ci >> 1].  Level by level the partner differs in bit
+// 4 (row swap), 3 (row mirror), 2 (half-row mirror), 1 and 0 (quad permutes)
+// of the lane index and shares the higher bits, and each lane keeps the half
+// of its values selected by that bit.
+template <typename T>
+__device__ __forceinline__ T reduce_scatter16(const T (&q)[16], int ci)
+{
+    T y8[8], y4[4], y2[2];
+    const bool b3 = ci & 8, b2 = ci & 4, b1 = ci & 2;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        T a = q[m], b = q[m + 8];
+        rowswap16(a, b);
+        y8[m] = a + b;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) y4[m] = (b3 ? y8[m + 4] : y8[m]) + dpp<0x140>(b3 ? y8[m] : y8[m + 4]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) y2[m] = (b2 ? y4[m + 2] : y4[m]) + dpp<0x141>(b2 ? y4[m] : y4[m + 2]);
+    const T y1 = (b1 ? y2[1] : y2[0]) + dpp<0x4E>(b1 ? y2[0] : y2[1]);
+    return y1 + dpp<0xB1>(y1);
+}
+
+// 1/x: hardware reciprocal with one Newton step in fp32 (within an ulp or so),
+// a correctly rounded division in fp64
+__device__ __forceinline__ float recip(float x)
+{
+    const float r = __builtin_amdgcn_rcpf(x);
+    return r * (2.f - x * r);
+}
+__device__ __forceinline__ double recip(double x) { return 1.0 / x; }
+
+__device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
+__device__ __forceinline__ double readlane0(double x)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 0), __builtin_amdgcn_readlane(__double2loint(x), 0));
+}
+
+// Orders LDS traffic between the lanes of one wave (a wave's LDS operations
+// complete in program order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// sum over the wave
 template <typename T>
 __device__ __forceinline__ T wave_sum64(T x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    return pair32_sum(half_sum(x));
 }
 
 // butterfly reduce-scatter: returns, in every lane, the sum over the wave of
-// x[lane % 32]
+// x[lane % 32].  Level by level the partner differs in bit 4 (row swap), 3
+// (row mirror), 2 (half-row mirror), 1 and 0 (quad permutes) of the lane index
+// and shares the higher bits; the two half-waves are added at the end.
 template <typename T>
 __device__ __forceinline__ T reduce_scatter32(const T (&x)[NB], int lane)
 {
     T y16[16], y8[8], y4[4], y2[2];
-    const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-        const T keep = b4 ? x[m + 16] : x[m], send = b4 ? x[m] : x[m + 16];
-        y16[m] = keep + __shfl_xor(send, 16, 64);
+        T a = x[m], b = x[m + 16];
+        rowswap16(a, b);
+        y16[m] = a + b;
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const T keep = b3 ? y16[m + 8] : y16[m], send = b3 ? y16[m] : y16[m + 8];
-        y8[m] = keep + __shfl_xor(send, 8, 64);
-    }
+    for (int m = 0; m < 8; ++m) y8[m] = (b3 ? y16[m + 8] : y16[m]) + dpp<0x140>(b3 ? y16[m] : y16[m + 8]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const T keep = b2 ? y8[m + 4] : y8[m], send = b2 ? y8[m] : y8[m + 4];
-        y4[m] = keep + __shfl_xor(send, 4, 64);
-    }
+    for (int m = 0; m < 4; ++m) y4[m] = (b2 ? y8[m + 4] : y8[m]) + dpp<0x141>(b2 ? y8[m] : y8[m + 4]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const T keep = b1 ? y4[m + 2] : y4[m], send = b1 ? y4[m] : y4[m + 2];
-        y2[m] = keep + __shfl_xor(send, 2, 64);
-    }
-    const T keep = b0 ? y2[1] : y2[0], send = b0 ? y2[0] : y2[1];
-    const T y1 = keep + __shfl_xor(send, 1, 64);
-    return y1 + __shfl_xor(y1, 32, 64);
+    for (int m = 0; m < 2; ++m) y2[m] = (b1 ? y4[m + 2] : y4[m]) + dpp<0x4E>(b1 ? y4[m] : y4[m + 2]);
+    const T y1 = (b0 ? y2[1] : y2[0]) + dpp<0xB1>(b0 ? y2[0] : y2[1]);
+    return pair32_sum(y1);
 }
 
 template <typename T, int NT>
@@ -168,24 +282,31 @@ __device__ __forceinline__ void reg_qr(T (&p)[NB], int rows, int kr, RegQr<T, NT
                 t = 2 * v0 * v0 / (sigma + v0 * v0);
                 scale = 1 / v0;
             }
+            const T v = live ? (tid > k ? scale * p[k] : (tid == k ? (T)1 : (T)0)) : (T)0;
             if (t != 0) {
-                const T v = live ? (tid > k ? scale * p[k] : (tid == k ? (T)1 : (T)0)) : (T)0;
+                // d_c = sum_i v_i P[i][c]: for c > k the update of column c, for c < k
+                // (where P holds the earlier Householder vectors below the diagonal)
+                // the inner products that form the new column of T
                 T x[NB];
 #pragma unroll
                 for (int c = 0; c < NB; ++c) x[c] = v * p[c];
                 const T dsum = reduce_scatter32<T>(x, lane);
-                __syncthreads();  // readers of the previous column's red/dvec are done
                 if (lane < NB) S.red[wv][lane] = dsum;
-                __syncthreads();
-                if (tid < NB) {
+            }
+            __syncthreads();  // the partial sums are complete; sig and x0 of column k have been read
+            if (t != 0) {
+                // every wave forms its own copy of d
+                if (lane < NB) {
                     T acc = 0;
 #pragma unroll
-                    for (int w = 0; w < NW; ++w) acc += S.red[w][tid];
-                    S.dvec[tid] = acc;
+                    for (int w = 0; w < NW; ++w) acc += S.red[w][lane];
+                    S.dvec[wv][lane] = acc;
                 }
-                __syncthreads();
+                wave_sync();
+                const T *dv = S.dvec[wv];
+                const T tv = t * v;
 #pragma unroll
-                for (int c = k + 1; c < NB; ++c) p[c] -= t * v * S.dvec[c];
+                for (int c = k + 1; c < NB; ++c) p[c] -= tv * dv[c];
                 if (tid == k) p[k] = mu;
                 if (tid > k) p[k] = v;
                 // T[i][k] = -t sum_{i <= j < k} T[i][j] d_j: thread (i, j mod 8), 8-lane sum
@@ -194,10 +315,10 @@ __device__ __forceinline__ void reg_qr(T (&p)[NB], int rows, int kr, RegQr<T, NT
                     T acc = 0;
 #pragma unroll
                     for (int j = jg; j < k; j += 8)
-                        if (j >= i) acc += S.Tl[i * NB + j] * S.dvec[j];
-                    acc += __shfl_xor(acc, 1, 64);
-                    acc += __shfl_xor(acc, 2, 64);
-                    acc += __shfl_xor(acc, 4, 64);
+                        if (j >= i) acc += S.Tl[i * NB + j] * dv[j];
+                    acc += dpp<0xB1>(acc);
+                    acc += dpp<0x4E>(acc);
+                    acc += dpp<0x141>(acc);
                     if (jg == 0 && i < k) S.Tl[i * NB + k] = -t * acc;
                 }
             }
@@ -206,7 +327,6 @@ __device__ __forceinline__ void reg_qr(T (&p)[NB], int rows, int kr, RegQr<T, NT
             if constexpr (k + 1 < NB) {
                 T part = (tid > k + 1 && live) ? p[k + 1] * p[k + 1] : (T)0;
                 part = wave_sum64(part);
-                __syncthreads();  // every thread has read sig/x0 of column k
                 if (lane == 0) S.sig[wv] = part;
                 if (tid == k + 1) S.x0 = p[k + 1];
                 __syncthreads();
@@ -790,126 +910,6 @@ __global__ __launch_bounds__(256) void k_band_copy(const T *__restrict__ A, int6
 
 __device__ __forceinline__ int ntasks_of(int64_t s, int64_t n) { return (int)((n - 2 - s) / NB) + 1; }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T x)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
-// Cross-lane moves without the LDS pipeline: DPP within rows of 16 lanes
-// (quad permutes 0xB1 = lane^1 and 0x4E = lane^2, half-row mirror 0x141,
-// row mirror 0x140) and the gfx950 row swaps (permlane16/32_swap), which
-// exchange the odd rows (16 lanes) or the upper half (32 lanes) of the first
-// operand with the even rows or the lower half of the second.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp(double x)
-{
-    const int lo = __double2loint(x), hi = __double2hiint(x);
-    return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
-                            __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
-}
-// (a, b) -> (a', b'): a' = a in even rows, b from the row below in odd rows;
-// b' = a from the row above in even rows, b in odd rows
-__device__ __forceinline__ void rowswap16(float &a, float &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void rowswap16(double &a, double &b)
-{
-    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
-    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
-    a = __hiloint2double((int)h[0], (int)l[0]);
-    b = __hiloint2double((int)h[1], (int)l[1]);
-}
-__device__ __forceinline__ void halfswap32(float &a, float &b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void halfswap32(double &a, double &b)
-{
-    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
-    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
-    a = __hiloint2double((int)h[0], (int)l[0]);
-    b = __hiloint2double((int)h[1], (int)l[1]);
-}
-// x + x[lane ^ 32]
-template <typename T>
-__device__ __forceinline__ T pair32_sum(T x)
-{
-    T a = x, b = x;
-    halfswap32(a, b);
-    return a + b;
-}
-// in lanes 32..63 the value of lane - 32; lanes 0..31 keep their own
-template <typename T>
-__device__ __forceinline__ T from_lower_half(T x)
-{
-    T a = x, b = x;
-    halfswap32(a, b);
-    return a;
-}
-// sum over the 32 lanes of each half-wave
-template <typename T>
-__device__ __forceinline__ T half_sum(T x)
-{
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    T a = x, b = x;
-    rowswap16(a, b);
-    return a + b;
-}
-
-// butterfly reduce-scatter within each half-wave: lane ci (0..31) returns the
-// sum over the half of q[ci >> 1].  Level by level the partner differs in bit
-// 4 (row swap), 3 (row mirror), 2 (half-row mirror), 1 and 0 (quad permutes)
-// of the lane index and shares the higher bits, and each lane keeps the half
-// of its values selected by that bit.
-template <typename T>
-__device__ __forceinline__ T reduce_scatter16(const T (&q)[16], int ci)
-{
-    T y8[8], y4[4], y2[2];
-    const bool b3 = ci & 8, b2 = ci & 4, b1 = ci & 2;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        T a = q[m], b = q[m + 8];
-        rowswap16(a, b);
-        y8[m] = a + b;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) y4[m] = (b3 ? y8[m + 4] : y8[m]) + dpp<0x140>(b3 ? y8[m] : y8[m + 4]);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) y2[m] = (b2 ? y4[m + 2] : y4[m]) + dpp<0x141>(b2 ? y4[m] : y4[m + 2]);
-    const T y1 = (b1 ? y2[1] : y2[0]) + dpp<0x4E>(b1 ? y2[0] : y2[1]);
-    return y1 + dpp<0xB1>(y1);
-}
-
-// 1/x: hardware reciprocal with one Newton step in fp32 (within an ulp or so),
-// a correctly rounded division in fp64
-__device__ __forceinline__ float recip(float x)
-{
-    const float r = __builtin_amdgcn_rcpf(x);
-    return r * (2.f - x * r);
-}
-__device__ __forceinline__ double recip(double x) { return 1.0 / x; }
-
-__device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
-__device__ __forceinline__ double readlane0(double x)
-{
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 0), __builtin_amdgcn_readlane(__double2loint(x), 0));
-}
 
 // Band rows are exchanged between workgroups on different XCDs.  Every such
 // access is a relaxed agent-scope atomic (a load or store that is coherent
@@ -928,14 +928,6 @@ __device__ __forceinline__ void cstore(T *p, T v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Orders LDS traffic between the lanes of one wave (a wave's LDS operations
-// complete in program order; this keeps the compiler from moving them).
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // One workgroup per group of G consecutive sweeps s0 .. s0+G-1: G compute
 // waves, a loader wave and a storer wave.  At time step t compute wave i runs
