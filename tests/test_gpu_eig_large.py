@@ -96,3 +96,25 @@ def test_eig_large_special(spec, kind):
         ref = np.sort(np.diag(A))[::-1]
         assert info == 0
         assert np.max(np.abs(w - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("n", [1024, 4096])
+def test_eig_large_f32_trace_preserved(spec, n):
+    """An orthogonal similarity keeps the trace.  In fp32 each of the O(n^2 / 32)
+    two-sided reflections moves it by rounding of either sign; a transformation
+    that is not orthogonal to working precision (tau rounded apart from its v)
+    shifts every eigenvalue the same way and the sum drifts by a multiple of
+    n eps lambda_max (about 4 n eps lambda_max with such a tau on the FFN-width
+    workload).  The unbiased reduction drifts by about n eps lambda_max / 10 on
+    these inputs; the bound is n eps lambda_max / 4."""
+    print_case("eig_large_f32_trace", n=n)
+    rng = np.random.default_rng(4000 + n)
+    Z = rng.standard_normal((2 * n, n)).astype(np.float32)
+    A = (Z.T.astype(np.float64) @ Z.astype(np.float64) / (2 * n)).astype(np.float32)
+    w, info = _run(spec, A, np.float32)
+    assert info == 0
+    tr = float(np.trace(A.astype(np.float64)))
+    drift = abs(float(w.sum()) - tr)
+    eps = float(np.finfo(np.float32).eps)
+    print(f"[trace] n={n} |sum(lambda) - tr(A)| = {drift:.3g}, n eps lambda_max = {n * eps * w[0]:.3g}", flush=True)
+    assert drift <= 0.25 * n * eps * float(w[0])

@@ -1161,10 +1161,13 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 T tau_k = 0, mu = 0, vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
-                    const T v0 = x0 <= 0 ? x0 - mu : -sigma * recip(x0 + mu);
-                    const T iv0 = recip(v0);
-                    tau_k = (T)2 * recip((T)1 + sigma * iv0 * iv0);
+                    const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
+                    const T iv0 = (T)1 / v0;
                     vi = ci == 0 ? (T)1 : x * iv0;
+                    // tau = 2 / v^T v of the v actually used, so that I - tau v v^T is
+                    // orthogonal to rounding (a tau from the formula, rounded
+                    // differently from v, drifts the trace over many applications)
+                    tau_k = (T)2 / ((T)1 + half_sum(ci >= 1 ? vi * vi : (T)0));
                 }
                 wave_sync();
                 if (h == 0) v[ci] = vi;
@@ -1257,7 +1260,8 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_tridiag_prep(const T *__restrict__ band, int64_t n, double *__restrict__ dd,
-                                                      double *__restrict__ ee2, double *__restrict__ bounds)
+                                                      double *__restrict__ ee2, double *__restrict__ bounds,
+                                                      float2 *__restrict__ de32)
 {
     __shared__ double rlo[256], rhi[256], remax[256];
     const int tid = threadIdx.x;
@@ -1268,6 +1272,7 @@ __global__ __launch_bounds__(256) void k_tridiag_prep(const T *__restrict__ band
         const double ep = i > 0 ? (double)band[i * BW + 1] : 0.0;           // A[i][i-1]
         dd[i] = d;
         ee2[i] = e * e;
+        if (de32 != nullptr) de32[i] = make_float2((float)d, (float)(ep * ep));  // (d_i, e_{i-1}^2)
         const double r = fabs(e) + fabs(ep);
         lo = fmin(lo, d - r);
         hi = fmax(hi, d + r);
@@ -1291,6 +1296,7 @@ __global__ __launch_bounds__(256) void k_tridiag_prep(const T *__restrict__ band
         bounds[0] = rlo[0] - pad;
         bounds[1] = rhi[0] + pad;
         bounds[2] = fmax(1.0, remax[0]) * 1e-300;  // pivmin
+        bounds[3] = fmax(1.0, remax[0]) * 1.1754943508222875e-38;  // pivmin of the fp32 recurrence
     }
 }
 
@@ -1347,6 +1353,79 @@ __global__ __launch_bounds__(64) void k_bisect(const double *__restrict__ dd, co
     if (live && j == 0) w[kidx] = (T)(0.5 * (a + b));
 }
 
+// Sturm count in fp32 for an fp32 matrix: q_i = (d_i - x) - e_{i-1}^2 / q_{i-1}
+// with the hardware reciprocal.  Each step perturbs d_i and e_{i-1}^2 by a few
+// ulps relative, so the count is exact for a matrix within a few ulps of T
+// entry by entry, and the eigenvalues found are within a small multiple of
+// eps ||T|| (Kahan's and Demmel's error analysis of the bisection count).  The
+// (d_i, e_{i-1}^2) pairs are the same for every lane and are read as scalars.
+__device__ __forceinline__ int sturm_below_f32(const float2 *__restrict__ de, int n, float x, float pivmin)
+{
+    int cnt = 0;
+    float q = 1.f;  // e_{-1}^2 = 0
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float2 p = de[i + u];
+            q = (p.x - x) - p.y * __builtin_amdgcn_rcpf(q);
+            q = fabsf(q) < pivmin ? -pivmin : q;
+            cnt += q < 0.f;
+        }
+    }
+    for (; i < n; ++i) {
+        const float2 p = de[i];
+        q = (p.x - x) - p.y * __builtin_amdgcn_rcpf(q);
+        q = fabsf(q) < pivmin ? -pivmin : q;
+        cnt += q < 0.f;
+    }
+    return cnt;
+}
+
+// fp32 multisection: 4 eigenvalues per wave, 16 lanes (15 interior points + 1)
+// each, down to 2 ulps of |lambda| or 1/16 ulp of ||T||, below the accuracy of
+// the count itself
+__global__ __launch_bounds__(64) void k_bisect_f32(const float2 *__restrict__ de, int n,
+                                                   const double *__restrict__ bounds, float *__restrict__ w)
+{
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, j = lane & 15;
+    const int kidx = blockIdx.x * 4 + g;  // descending index
+    const bool live = kidx < n;
+    const int target = n - 1 - (live ? kidx : 0);  // ascending index
+    // the fp64 Gershgorin bounds, rounded outwards, with a few ulps of slack
+    float a = (float)bounds[0], b = (float)bounds[1];
+    const float span = fmaxf(fabsf(a), fabsf(b));
+    a -= 4.f * 1.1920929e-7f * span;
+    b += 4.f * 1.1920929e-7f * span;
+    const float pivmin = (float)bounds[3];
+    const float atol = 0.0625f * 1.1920929e-7f * span;
+    for (int it = 0; it < 40; ++it) {
+        const float width = b - a;
+        const bool done = width <= fmaxf(atol, 2.f * 1.1920929e-7f * fmaxf(fabsf(a), fabsf(b)));
+        const float x = a + width * (float)(j + 1) * (1.f / 17.f);
+        const int cnt = (live && !done) ? sturm_below_f32(de, n, x, pivmin) : 0;
+        // new a = largest x_j with count <= target, new b = smallest x_j with count > target
+        const bool le = cnt <= target;
+        float na = le ? x : -INFINITY;
+        float nb = le ? INFINITY : x;
+        na = fmaxf(na, dpp<0xB1>(na));
+        nb = fminf(nb, dpp<0xB1>(nb));
+        na = fmaxf(na, dpp<0x4E>(na));
+        nb = fminf(nb, dpp<0x4E>(nb));
+        na = fmaxf(na, dpp<0x141>(na));
+        nb = fminf(nb, dpp<0x141>(nb));
+        na = fmaxf(na, dpp<0x140>(na));
+        nb = fminf(nb, dpp<0x140>(nb));
+        if (!done) {
+            if (na > a) a = na;
+            if (nb < b) b = nb;
+        }
+        if (__all(done || !live)) break;
+    }
+    if (live && j == 0) w[kidx] = 0.5f * (a + b);
+}
+
 __global__ void k_info(const int32_t *__restrict__ err, int32_t *__restrict__ info)
 {
     if (threadIdx.x == 0) info[0] = err[0] != 0 ? 1 : 0;
@@ -1373,6 +1452,7 @@ struct Bufs {
     T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Qt, *U, *Tm, *Mm, *Ppart;
     int32_t *prog;
     double *dd, *ee2, *bounds;
+    float2 *de32;
 };
 
 constexpr int KS_MAX = 8;
@@ -1401,6 +1481,7 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.dd = ws.take<double>((size_t)n);
     b.ee2 = ws.take<double>((size_t)n);
     b.bounds = ws.take<double>(4);
+    b.de32 = ws.take<float2>((size_t)n);
     return ws.off;
 }
 
@@ -1497,11 +1578,15 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         LAUNCH_OK();
     }
     // ---- stage 3: eigenvalues of the tridiagonal
-    hipLaunchKernelGGL(k_tridiag_prep<T>, dim3(1), dim3(256), 0, st, b.band, n, b.dd, b.ee2, b.bounds);
+    hipLaunchKernelGGL(k_tridiag_prep<T>, dim3(1), dim3(256), 0, st, b.band, n, b.dd, b.ee2, b.bounds,
+                       sizeof(T) == 4 ? b.de32 : nullptr);
     LAUNCH_OK();
-    const double rel_tol = sizeof(T) == 4 ? 1e-9 : 4e-16;
-    hipLaunchKernelGGL(k_bisect<T>, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds, rel_tol,
-                       w);
+    if constexpr (sizeof(T) == 4) {
+        hipLaunchKernelGGL(k_bisect_f32, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.de32, (int)n, b.bounds, w);
+    } else {
+        hipLaunchKernelGGL(k_bisect<T>, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds,
+                           4e-16, w);
+    }
     LAUNCH_OK();
     if (info != nullptr) {
         hipLaunchKernelGGL(k_info, dim3(1), dim3(64), 0, st, b.prog + n, info);
