@@ -207,6 +207,15 @@ __device__ __forceinline__ float recip(float x)
 }
 __device__ __forceinline__ double recip(double x) { return 1.0 / x; }
 
+__device__ __forceinline__ float readlane_t(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_t(double x, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                            __builtin_amdgcn_readlane(__double2loint(x), l));
+}
 __device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
 __device__ __forceinline__ double readlane0(double x)
 {
@@ -477,49 +486,55 @@ __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, con
 
 // ---- TSQR, step 4: Householder reconstruction from Q1's top block
 template <typename T>
-__global__ __launch_bounds__(256) void k_tsqr_recon(const T *__restrict__ Q1, const T *__restrict__ Rf,
-                                                    T *__restrict__ Pg, int64_t lda, T *__restrict__ V,
-                                                    T *__restrict__ Ug, T *__restrict__ Tm)
+__global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, const T *__restrict__ Rf,
+                                                   T *__restrict__ Pg, int64_t lda, T *__restrict__ V,
+                                                   T *__restrict__ Ug, T *__restrict__ Tm)
 {
-    __shared__ T M[NB * LDP];
-    __shared__ T S[NB];
-    const int tid = threadIdx.x;
-    for (int p = tid; p < NB * NB; p += 256) M[(p / NB) * LDP + p % NB] = Q1[p];
-    __syncthreads();
-    for (int k = 0; k < NB; ++k) {
-        if (tid == 0) {
-            const T s = M[k * LDP + k] >= 0 ? (T)-1 : (T)1;
-            S[k] = s;
-            M[k * LDP + k] -= s;
+    // one wave; lane i (and i + 32) holds row i of Q1 - S in registers, and the
+    // pivot rows reach the other lanes as scalars (readlane)
+    const int lane = threadIdx.x;
+    const int i = lane & 31;
+    T m[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) m[j] = Q1[i * NB + j];
+    T si = 0;  // S[i]
+    T sv[NB];  // S, the same in every lane
+    static_for<0, NB>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        const T mk = readlane_t(m[k], k);
+        const T s = mk >= 0 ? (T)-1 : (T)1;
+        sv[k] = s;
+        if (i == k) si = s;
+        const T piv = mk - s;
+        if (i == k) m[k] = piv;
+        T rowk[NB];
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) rowk[j] = readlane_t(m[j], k);
+        if (i > k) {
+            const T l = m[k] / piv;
+            m[k] = l;
+#pragma unroll
+            for (int j = k + 1; j < NB; ++j) m[j] -= l * rowk[j];
         }
-        __syncthreads();
-        const T piv = M[k * LDP + k];
-        for (int i = k + 1 + tid; i < NB; i += 256) M[i * LDP + k] /= piv;
-        __syncthreads();
-        for (int p = tid; p < NB * NB; p += 256) {
-            const int i = p / NB, j = p % NB;
-            if (i > k && j > k) M[i * LDP + j] -= M[i * LDP + k] * M[k * LDP + j];
-        }
-        __syncthreads();
-    }
-    // T = -(U S) Y1^{-T}: row i solves z Y1^T = -(U S)[i], by forward substitution
-    if (tid < NB) {
-        const int i = tid;
-        T z[NB];
+    });
+    // T = -(U S) Y1^{-T}: row i solves z Y1^T = -(U S)[i] by forward substitution,
+    // with Y1 unit lower (the multipliers below the diagonal)
+    T z[NB];
+    static_for<0, NB>([&](auto JC) {
+        constexpr int j = decltype(JC)::value;
+        T b = j >= i ? -m[j] * sv[j] : (T)0;
+#pragma unroll
+        for (int l = 0; l < j; ++l) b -= readlane_t(m[l], j) * z[l];
+        z[j] = b;
+    });
+    if (lane < NB) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            T b = j >= i ? -M[i * LDP + j] * S[j] : (T)0;
-            for (int l = 0; l < j; ++l) b -= M[j * LDP + l] * z[l];
-            z[j] = b;
+            Tm[i * NB + j] = z[j];
+            Ug[i * NB + j] = j >= i ? m[j] : (T)0;
+            V[i * NB + j] = i == j ? (T)1 : (i > j ? m[j] : (T)0);
+            if (i <= j) Pg[i * lda + j] = si * Rf[i * NB + j];  // R_panel = S R
         }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) Tm[i * NB + j] = z[j];
-    }
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int i = p / NB, j = p % NB;
-        Ug[p] = j >= i ? M[i * LDP + j] : (T)0;
-        V[p] = i == j ? (T)1 : (i > j ? M[i * LDP + j] : (T)0);
-        if (i <= j) Pg[i * lda + j] = S[i] * Rf[p];  // R_panel = S R
     }
 }
 
@@ -765,18 +780,41 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_mfin(const T *__restrict__ Ppart, int nblk, const T *__restrict__ Tm,
                                               T *__restrict__ Mm)
 {
-    __shared__ T P[NB * NB];
+    __shared__ T P[NB * LDP];
+    __shared__ T Ts[NB * LDP];
     const int tid = threadIdx.x;
-    for (int p = tid; p < NB * NB; p += 256) {
-        T s = 0;
-        for (int b = 0; b < nblk; ++b) s += Ppart[(int64_t)b * NB * NB + p];
-        P[p] = s;
+    constexpr int PER = NB * NB / 256;
+    // the partial sums of each element: 8 loads in flight at a time
+    T acc[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) acc[q] = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+        T part[8][PER];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                part[u][q] = b0 + u < nblk ? Ppart[(int64_t)(b0 + u) * NB * NB + tid + 256 * q] : (T)0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int q = 0; q < PER; ++q) acc[q] += part[u][q];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int p = tid + 256 * q;
+        P[(p / NB) * LDP + p % NB] = acc[q];
+        Ts[(p / NB) * LDP + p % NB] = Tm[p];
     }
     __syncthreads();
-    for (int p = tid; p < NB * NB; p += 256) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int p = tid + 256 * q;
         const int i = p / NB, c = p % NB;
         T s = 0;
-        for (int l = 0; l <= i; ++l) s += Tm[l * NB + i] * P[l * NB + c];  // T^T is lower
+#pragma unroll
+        for (int l = 0; l < NB; ++l)
+            if (l <= i) s += Ts[l * LDP + i] * P[l * LDP + c];  // T^T is lower
         Mm[p] = s;
     }
 }
@@ -848,6 +886,8 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
                 for (int qb = 0; qb < 2; ++qb)
                     acc[qa][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
         }
+        // all old values are loaded before the first store
+        float old[2][2][16];
 #pragma unroll
         for (int qa = 0; qa < 2; ++qa)
 #pragma unroll
@@ -856,7 +896,18 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int i = i0 + wm * 64 + qa * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                    if (i < m && j < m && i >= j) A[(int64_t)i * lda + j] -= acc[qa][qb][e];
+                    old[qa][qb][e] = i < m && j < m && i >= j ? A[(int64_t)i * lda + j] : 0.f;
+                }
+            }
+#pragma unroll
+        for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int j = j0 + wn * 64 + qb * 32 + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = i0 + wm * 64 + qa * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+                    if (i < m && j < m && i >= j) A[(int64_t)i * lda + j] = old[qa][qb][e] - acc[qa][qb][e];
                 }
             }
     } else {
@@ -874,6 +925,7 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
                 for (int qb = 0; qb < 4; ++qb)
                     acc[qa][qb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
         }
+        double old[4][4][4];
 #pragma unroll
         for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
@@ -882,7 +934,18 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = i0 + wm * 64 + qa * 16 + (lane >> 4) + 4 * e;
-                    if (i < m && j < m && i >= j) A[(int64_t)i * lda + j] -= acc[qa][qb][e];
+                    old[qa][qb][e] = i < m && j < m && i >= j ? A[(int64_t)i * lda + j] : 0.0;
+                }
+            }
+#pragma unroll
+        for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                const int j = j0 + wn * 64 + qb * 16 + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + wm * 64 + qa * 16 + (lane >> 4) + 4 * e;
+                    if (i < m && j < m && i >= j) A[(int64_t)i * lda + j] = old[qa][qb][e] - acc[qa][qb][e];
                 }
             }
     }
@@ -1536,7 +1599,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
                                b.Qt, (int)m, per, b.Q1);
             LAUNCH_OK();
-            hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(256), 0, st, b.Q1, b.Rf, P, lda, b.V, b.U, b.Tm);
+            hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, st, b.Q1, b.Rf, P, lda, b.V, b.U, b.Tm);
             LAUNCH_OK();
             hipLaunchKernelGGL(k_tsqr_y2<T>, dim3((unsigned)cdiv_h(m - NB, 256)), dim3(256), 0, st, b.Q1, b.U,
                                (int)m, b.V);

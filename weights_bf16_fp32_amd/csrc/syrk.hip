@@ -132,22 +132,41 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
     }
 
     if (!active) return;
+    // every old value of C is loaded before the first store, so the loads are in
+    // flight together instead of one read-modify-write round trip at a time
+    auto rc = [&](int a, int b, int e, int64_t &row, int64_t &col) {
+        col = j0 + wn * 64 + b * 32 + (lane & 31);
+        row = i0 + wm * 64 + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        return row < d && col < d && row >= col;
+    };
+    if (beta != 0.f) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    int64_t row, col;
+                    const float old = rc(a, b, e, row, col) ? C[row * ldc + col] : 0.f;
+                    acc[a][b][e] = alpha * acc[a][b][e] + beta * old;
+                }
+    } else {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] *= alpha;
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t col = j0 + wn * 64 + b * 32 + (lane & 31);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = i0 + wm * 64 + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                if (row < d && col < d && row >= col) {
-                    float *p = C + row * ldc + col;
-                    float val = alpha * acc[a][b][e];
-                    if (beta != 0.f) val += beta * *p;
-                    *p = val;
-                }
+                int64_t row, col;
+                if (rc(a, b, e, row, col)) C[row * ldc + col] = acc[a][b][e];
             }
-        }
 }
 
 // ---------------------------------------------------------------- fp64 MFMA
@@ -238,23 +257,32 @@ __global__ __launch_bounds__(256) void syrk_f64_mfma(const float *__restrict__ X
         cur ^= 1;
     }
     if (!active) return;
+    // v_mfma_f64_16x16x4f64 result: lane l holds column l % 16, rows l / 16 + 4 e.
+    // All old values are loaded before the first store.
+    auto rc = [&](int a, int b, int e, int64_t &row, int64_t &col) {
+        col = j0 + wn * 64 + b * 16 + (lane & 15);
+        row = i0 + wm * 64 + a * 16 + (lane >> 4) + 4 * e;
+        return row < d && col < d && row >= col;
+    };
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t col = j0 + wn * 64 + b * 16 + (lane & 15);
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // v_mfma_f64_16x16x4f64 result: lane l holds column l % 16, rows l / 16 + 4 e
-                const int64_t row = i0 + wm * 64 + a * 16 + (lane >> 4) + 4 * e;
-                if (row < d && col < d && row >= col) {
-                    double *p = C + row * ldc + col;
-                    double val = alpha * acc[a][b][e];
-                    if (beta != 0.0) val += beta * *p;
-                    *p = val;
-                }
+                int64_t row, col;
+                const double old = beta != 0.0 && rc(a, b, e, row, col) ? C[row * ldc + col] : 0.0;
+                acc[a][b][e] = alpha * acc[a][b][e] + beta * old;
             }
-        }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int64_t row, col;
+                if (rc(a, b, e, row, col)) C[row * ldc + col] = acc[a][b][e];
+            }
 }
 
 // ---------------------------------------------------------------- generic VALU
@@ -309,17 +337,22 @@ __global__ __launch_bounds__(256) void syrk_generic(const TIn *__restrict__ X, i
         }
         __syncthreads();
     }
+    // all old values are loaded before the first store
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            int64_t row = i0 + ty * 4 + p, col = j0 + tx * 4 + q;
-            if (row < d && col < d && row >= col) {
-                TAcc *ptr = C + row * ldc + col;
-                TAcc val = alpha * acc[p][q];
-                if (beta != (TAcc)0) val += beta * *ptr;
-                *ptr = val;
-            }
+            const int64_t row = i0 + ty * 4 + p, col = j0 + tx * 4 + q;
+            const bool in = row < d && col < d && row >= col;
+            const TAcc old = beta != (TAcc)0 && in ? C[row * ldc + col] : (TAcc)0;
+            acc[p][q] = alpha * acc[p][q] + beta * old;
+        }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = i0 + ty * 4 + p, col = j0 + tx * 4 + q;
+            if (row < d && col < d && row >= col) C[row * ldc + col] = acc[p][q];
         }
 }
 
