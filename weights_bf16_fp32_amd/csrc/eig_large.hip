@@ -23,12 +23,17 @@
 //   the diagonal block from both sides.  Task (s, k) may run once task
 //   (s-1, k+1) is done, so the tasks (s, t - 2s) of one time step t are
 //   independent.  A workgroup runs G consecutive sweeps, one wave each, a time
-//   step at a time, with their rows in an LDS ring; consecutive groups are
-//   ordered by a row watermark (rows below it are final and stored back),
-//   with a bounded wait.
+//   step at a time, with their rows in an LDS ring and each task's block in
+//   the wave's registers; a loader wave and a storer wave move band rows
+//   between the ring and global memory; consecutive groups are ordered by a
+//   row watermark (rows below it are final and stored back), with a bounded
+//   wait.  Each reflector's tau is 2 / v^T v of the v it is applied with, so
+//   every reflection is orthogonal to rounding.
 // Stage 3, eigenvalues of the tridiagonal: 16-section on the Sturm count
-//   (number of negative pivots of LDL^T(T - xI)) in fp64, 16 lanes per
-//   eigenvalue, from the Gershgorin interval; results in descending order.
+//   (number of negative pivots of LDL^T(T - xI)), 16 lanes per eigenvalue, from
+//   the Gershgorin interval; results in descending order.  An fp32 matrix is
+//   counted in fp32 (backward stable: exact for a matrix within a few ulps of T
+//   entry by entry), an fp64 one in fp64.
 #include <float.h>
 
 #include <algorithm>
