@@ -1636,8 +1636,8 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     LAUNCH_OK();
     if (n >= 3) {
         // G sweeps per workgroup (one wave each); the LDS ring holds >= (2G + 1) NB rows
-        constexpr int G = sizeof(T) == 4 ? 8 : 3;
-        constexpr int CAPR = sizeof(T) == 4 ? 576 : 256;
+        constexpr int G = sizeof(T) == 4 ? 4 : 3;
+        constexpr int CAPR = sizeof(T) == 4 ? 288 : 256;
         const int64_t nsw = n - 2;
         const int64_t ngroups = cdiv_h(nsw, G);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
