@@ -99,10 +99,12 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
                      float *out);
 
 /* ------------------------------------------------------------------------
- * A3  Batched small symmetric eigenvalues (n <= 64), cyclic Jacobi with a
- *     parallel (round-robin) ordering, one workgroup per matrix, matrix
- *     resident in LDS.  The pages call a library eigvalsh per window and flip
- *     it to descending order ([RMT] section 3.2 code).
+ * A3  Batched small symmetric eigenvalues (n <= 64), one 64-lane wave per
+ *     matrix: Householder reduction to tridiagonal form with the matrix in
+ *     registers, then bisection on Sturm counts (fp32).  The pages call a
+ *     library eigvalsh per window and flip it to descending order ([RMT]
+ *     section 3.2 code).  Every eigenvalue is within a small multiple of
+ *     eps_f32 * ||A|| of the exact one.
  *
  * Source of the matrices (fp32):
  *   SPEC_SRC_DENSE: matrix b is a[b*stride_a + i*lda + j]; the lower triangle is read.
@@ -111,9 +113,10 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
  *                   A[i][j] = scale * a[s*T*n + (w*stride + max(i,j))*n + |i-j|];
  *                   batch must equal streams * W.
  * w:    f32 [batch][n], eigenvalues descending.
- * info: int32 [batch] (may be NULL): sweeps used, or -1 if max_sweeps was reached
- *       before every off-diagonal element satisfied |a_pq| <= eps32 * sqrt(|a_pp a_qq|).
- * max_sweeps in [1, 100].
+ * info: int32 [batch] (may be NULL): the number of bisection rounds (>= 0), or -1
+ *       if the matrix has a non-finite entry (its eigenvalues are then NaN).
+ * max_sweeps in [1, 100]: validated and otherwise unused (the method is direct;
+ *       the argument keeps the call's shape for callers of iterative solvers).
  * ---------------------------------------------------------------------- */
 enum { SPEC_SRC_DENSE = 0, SPEC_SRC_BAND = 1 };
 

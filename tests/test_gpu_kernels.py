@@ -152,7 +152,7 @@ def test_gram_band_f32_and_dense(spec):
         assert np.max(np.abs(Dg[s] - G)) <= (d + 2) * EPS32 * np.max(np.abs(G)) * 4
 
 
-# ----------------------------------------------------------------- A3 batched Jacobi
+# ----------------------------------------------------------------- A3 batched small eigenvalues
 
 def _rand_sym_batch(rng, batch, n):
     A = rng.standard_normal((batch, n, n))
@@ -160,9 +160,9 @@ def _rand_sym_batch(rng, batch, n):
 
 
 @pytest.mark.parametrize("n", [1, 2, 5, 30, 31, 32, 33, 64])
-def test_jacobi_dense(spec, n):
+def test_batched_eig_dense(spec, n):
     torch = _torch()
-    print_case("jacobi_dense", n=n)
+    print_case("batched_eig_dense", n=n)
     rng = np.random.default_rng(100 + n)
     batch = 17
     A = _rand_sym_batch(rng, batch, n)
@@ -187,19 +187,51 @@ def test_jacobi_dense(spec, n):
     assert np.all(info.cpu().numpy() >= 0)
 
 
-def test_jacobi_reports_non_convergence(spec):
+@pytest.mark.parametrize("n", [30, 40])
+def test_batched_eig_flags_non_finite(spec, n):
+    """A matrix with a NaN or inf entry gets info -1 and NaN eigenvalues; the
+    other matrices of the batch are unaffected."""
     torch = _torch()
-    rng = np.random.default_rng(5)
-    A = _rand_sym_batch(rng, 4, 30)
-    w, info = spec.eigvalsh_batched_dense(dev(A), max_sweeps=1)
+    print_case("batched_eig_non_finite", n=n)
+    rng = np.random.default_rng(5 + n)
+    A = _rand_sym_batch(rng, 4, n)
+    A[1, 3, 2] = np.nan
+    A[2, n - 1, 0] = np.inf
+    w, info = spec.eigvalsh_batched_dense(dev(A))
     torch.cuda.synchronize()
-    assert np.all(info.cpu().numpy() == -1)
+    inf_ = info.cpu().numpy()
+    wg = w.cpu().numpy().astype(np.float64)
+    assert inf_[1] == -1 and inf_[2] == -1 and inf_[0] >= 0 and inf_[3] >= 0
+    assert np.all(np.isnan(wg[1])) and np.all(np.isnan(wg[2]))
+    ref, _ = oracle.eigvalsh_small(A[[0, 3]].astype(np.float64))
+    assert np.max(np.abs(wg[[0, 3]] - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
-def test_jacobi_band_windows(spec):
+def test_batched_eig_clustered_and_graded(spec):
+    """Clustered eigenvalues (a 10-fold one and pairs 1e-6 apart) and a graded
+    spectrum over 8 decades, n = 30: every eigenvalue within 1e-5 lambda_max
+    and the output non-increasing."""
+    torch = _torch()
+    n = 30
+    rng = np.random.default_rng(77)
+    lam = np.concatenate([np.full(10, 2.0), 1.0 + 1e-6 * np.arange(10), 10.0 ** -np.arange(10)])
+    A = np.empty((3, n, n), dtype=np.float32)
+    for b in range(3):
+        Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+        A[b] = ((Q * (lam if b < 2 else 10.0 ** -np.linspace(0, 8, n))) @ Q.T).astype(np.float32)
+    w, info = spec.eigvalsh_batched_dense(dev(A))
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    ref, _ = oracle.eigvalsh_small(A.astype(np.float64))
+    for b in range(3):
+        assert np.max(np.abs(wg[b] - ref[b])) <= 1e-5 * np.max(np.abs(ref[b])), b
+    assert np.all(np.diff(wg, axis=1) <= 0)
+
+
+def test_batched_eig_band_windows(spec):
     torch = _torch()
     S, T, d, N = 3, 90, 512, 30
-    print_case("jacobi_band", S=S, T=T, d=d, N=N)
+    print_case("batched_eig_band", S=S, T=T, d=d, N=N)
     H = synth.eigentrack(streams=S, T=T, d=d)
     band = spec.gram_window(dev_bf16(H), N=N)
     w, info = spec.eigvalsh_batched_band(band, n=N, scale=1.0 / N)

@@ -167,7 +167,8 @@ def _batched(src: BatchSrc, batch: int, n: int, w, info, max_sweeps: int, device
 
 
 def eigvalsh_batched_dense(A, w=None, info=None, max_sweeps: int = 15):
-    """Eigenvalues (descending) of A [batch, n, n] f32 (lower triangle read)."""
+    """Eigenvalues (descending) of A [batch, n, n] f32 (lower triangle read).
+    info[b] = bisection rounds, or -1 for a matrix with a non-finite entry."""
     if A.dim() == 2:
         A = A.unsqueeze(0)
     batch, n, _ = A.shape

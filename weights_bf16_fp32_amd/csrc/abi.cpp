@@ -83,7 +83,7 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
     } else {
         return SPEC_EINVAL;
     }
-    return from_hip(launch_jacobi_batched((hipStream_t)stream, src, batch, n, w, max_sweeps, info));
+    return from_hip(launch_eigvalsh_batched((hipStream_t)stream, src, batch, n, w, info));
 }
 
 int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes)

@@ -105,79 +105,6 @@ struct RegQr {
     T Tl[NB * NB];
 };
 
-// Cross-lane moves without the LDS pipeline: DPP within rows of 16 lanes
-// (quad permutes 0xB1 = lane^1 and 0x4E = lane^2, half-row mirror 0x141,
-// row mirror 0x140) and the gfx950 row swaps (permlane16/32_swap), which
-// exchange the odd rows (16 lanes) or the upper half (32 lanes) of the first
-// operand with the even rows or the lower half of the second.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp(double x)
-{
-    const int lo = __double2loint(x), hi = __double2hiint(x);
-    return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
-                            __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
-}
-// (a, b) -> (a', b'): a' = a in even rows, b from the row below in odd rows;
-// b' = a from the row above in even rows, b in odd rows
-__device__ __forceinline__ void rowswap16(float &a, float &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void rowswap16(double &a, double &b)
-{
-    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
-    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
-    a = __hiloint2double((int)h[0], (int)l[0]);
-    b = __hiloint2double((int)h[1], (int)l[1]);
-}
-__device__ __forceinline__ void halfswap32(float &a, float &b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void halfswap32(double &a, double &b)
-{
-    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false, false);
-    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false, false);
-    a = __hiloint2double((int)h[0], (int)l[0]);
-    b = __hiloint2double((int)h[1], (int)l[1]);
-}
-// x + x[lane ^ 32]
-template <typename T>
-__device__ __forceinline__ T pair32_sum(T x)
-{
-    T a = x, b = x;
-    halfswap32(a, b);
-    return a + b;
-}
-// in lanes 32..63 the value of lane - 32; lanes 0..31 keep their own
-template <typename T>
-__device__ __forceinline__ T from_lower_half(T x)
-{
-    T a = x, b = x;
-    halfswap32(a, b);
-    return a;
-}
-// sum over the 32 lanes of each half-wave
-template <typename T>
-__device__ __forceinline__ T half_sum(T x)
-{
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    T a = x, b = x;
-    rowswap16(a, b);
-    return a + b;
-}
 
 // butterfly reduce-scatter within each half-wave: lane ci (0..31) returns the
 // sum over the half of q[ci >> 1].  Level by level the partner differs in bit
@@ -212,29 +139,7 @@ __device__ __forceinline__ float recip(float x)
 }
 __device__ __forceinline__ double recip(double x) { return 1.0 / x; }
 
-__device__ __forceinline__ float readlane_t(float x, int l)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-__device__ __forceinline__ double readlane_t(double x, int l)
-{
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
-                            __builtin_amdgcn_readlane(__double2loint(x), l));
-}
-__device__ __forceinline__ float readlane0(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); }
-__device__ __forceinline__ double readlane0(double x)
-{
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 0), __builtin_amdgcn_readlane(__double2loint(x), 0));
-}
 
-// Orders LDS traffic between the lanes of one wave (a wave's LDS operations
-// complete in program order; this keeps the compiler from moving them).
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // sum over the wave
 template <typename T>

@@ -17,8 +17,8 @@ hipError_t launch_gram_band(hipStream_t stream, const void *H, int ht, int64_t s
 hipError_t launch_gram_dense(hipStream_t stream, const void *H, int ht, int64_t streams, int64_t T, int64_t d,
                              int64_t ld_t, int64_t ld_s, int N, int stride, float scale, float *out);
 
-hipError_t launch_jacobi_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
-                                 int max_sweeps, int32_t *info);
+hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
+                                   int32_t *info);
 
 size_t eig_large_workspace_bytes(int64_t n, int t);
 

@@ -1,0 +1,222 @@
+// Batched eigenvalues of small symmetric matrices (n <= 64), one 64-lane wave
+// per matrix: Householder reduction to tridiagonal form with the matrix in
+// registers, then bisection on Sturm counts.
+//
+// The pages take the spectrum of each EigenTrack window with a library
+// eigvalsh and flip it to descending order ("Random matrix theory spectral
+// methods" page, section 3.2 code); here each window's N x N Gram is reduced
+// directly:
+//   - lane i holds row i of the matrix (both triangles).  Step k builds the
+//     reflector that zeroes column k below the subdiagonal from the lanes'
+//     column-k entries (one wave reduction for the norm), forms p = tau A v
+//     and w = p - (tau/2)(p^T v) v with v and w broadcast through LDS, and
+//     applies A <- A - v w^T - w v^T to the trailing rows.  tau = 2 / v^T v
+//     of the v actually used, so every reflection is orthogonal to rounding.
+//   - the diagonal d and subdiagonal e of T = Q^T A Q end up the same in every
+//     lane; eigenvalue l (descending) is found by lanes l and l + 32 together
+//     (n <= 32): each counts the eigenvalues below one of two interior points
+//     of the current interval (Sturm count: negative pivots of LDL^T(T - xI),
+//     in fp32 with the hardware reciprocal), the pair exchange counts with a
+//     half-wave swap and keep the third that holds eigenvalue l.  For
+//     32 < n <= 64 every lane bisects its own eigenvalue.  The output is in
+//     descending order by construction.
+//   - Accuracy: the reduction is backward stable, and the fp32 count is exact
+//     for a tridiagonal within a few ulps of T entry by entry (Kahan's and
+//     Demmel's analysis of the bisection count), so the eigenvalues are within
+//     a small multiple of eps_f32 ||A||.  Intervals stop at 2 ulps of |lambda|
+//     or ||T|| / 2^24.
+#include <float.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ float wave_total(float x) { return pair32_sum(half_sum(x)); }
+
+// the same int in the partner lane (lane ^ 32)
+__device__ __forceinline__ int partner32(int x)
+{
+    float a = __int_as_float(x), b = a;
+    halfswap32(a, b);
+    // a: lanes 32..63 got lane - 32; b: lanes 0..31 got lane + 32
+    return __float_as_int((threadIdx.x & 32) ? a : b);
+}
+
+template <int NM>
+__global__ __launch_bounds__(64) void small_eig_batched(spec_batch_src src, int64_t batch, int n,
+                                                        float *__restrict__ w, int32_t *__restrict__ info)
+{
+    __shared__ __attribute__((aligned(16))) float vs[NM];
+    __shared__ __attribute__((aligned(16))) float wsh[NM];
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int i = lane;  // row of this lane; rows >= n are zero
+    const bool rowok = i < n;
+
+    // ---- row i, A[i][j] for every j (the source's lower triangle, mirrored)
+    float a[NM];
+    if (src.kind == SPEC_SRC_DENSE) {
+        const float *base = src.a + b * src.stride_a;
+#pragma unroll
+        for (int j = 0; j < NM; ++j)
+            a[j] = rowok && j < n ? base[(int64_t)max(i, j) * src.lda + min(i, j)] : 0.f;
+    } else {
+        const int64_t W = (src.T - n) / src.stride + 1;
+        const int64_t s = b / W, win = b % W;
+        const float *base = src.a + (s * src.T + win * src.stride) * n;  // step t of the window: base + t n
+#pragma unroll
+        for (int j = 0; j < NM; ++j)
+            a[j] = rowok && j < n ? src.scale * base[(int64_t)max(i, j) * n + abs(i - j)] : 0.f;
+    }
+    bool fin = true;
+#pragma unroll
+    for (int j = 0; j < NM; ++j) fin = fin && isfinite(a[j]);
+    if (!__all(fin)) {
+        if (lane < n) w[b * n + lane] = __int_as_float(0x7fc00000);
+        if (info != nullptr && lane == 0) info[b] = -1;
+        return;
+    }
+
+    // ---- Householder tridiagonalisation; e[k] = T[k+1][k], the same in every lane
+    float e[NM];
+    static_for<0, NM - 2>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        if (k < n - 2) {
+            const float x = a[k];  // A[i][k]
+            const float sig = wave_total(i > k + 1 ? x * x : 0.f);
+            const float x0 = readlane_t(x, k + 1);
+            float tau = 0.f, mu = x0, vi = 0.f;
+            if (sig > 0.f) {
+                mu = sqrtf(x0 * x0 + sig);
+                const float v0 = x0 <= 0.f ? x0 - mu : -sig / (x0 + mu);
+                vi = i == k + 1 ? 1.f : (i > k + 1 ? x / v0 : 0.f);
+                tau = 2.f / (1.f + wave_total(i > k + 1 ? vi * vi : 0.f));
+            }
+            e[k] = mu;
+            if (tau != 0.f) {
+                wave_sync();
+                if (lane < NM) vs[lane] = vi;
+                wave_sync();
+                float p = 0.f;
+#pragma unroll
+                for (int j = k + 1; j < NM; ++j) p += a[j] * vs[j];
+                p *= tau;
+                const float pv = wave_total(i > k ? p * vi : 0.f);
+                const float wi = p - 0.5f * tau * pv * vi;
+                if (lane < NM) wsh[lane] = wi;
+                wave_sync();
+                if (i > k) {
+#pragma unroll
+                    for (int j = k + 1; j < NM; ++j) a[j] -= vi * wsh[j] + wi * vs[j];
+                }
+            }
+        }
+    });
+    // diagonal, last subdiagonal entry, squares; rows past n are padded so that
+    // they never count (d = FLT_MAX, e = 0)
+    float d[NM], e2[NM];
+    static_for<0, NM>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        d[k] = k < n ? readlane_t(a[k], k) : FLT_MAX;
+        if constexpr (k + 1 < NM) {
+            if (k == n - 2) e[k] = readlane_t(a[k], k + 1);
+            e2[k] = k + 1 < n ? e[k] * e[k] : 0.f;
+        }
+    });
+    // Gershgorin interval and pivot guard
+    float lo = FLT_MAX, hi = -FLT_MAX, emax = 0.f;
+    static_for<0, NM>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        if (k < n) {
+            float r = 0.f;
+            if constexpr (k > 0) r += fabsf(e[k - 1]);
+            if constexpr (k + 1 < NM) {
+                if (k + 1 < n) {
+                    r += fabsf(e[k]);
+                    emax = fmaxf(emax, e2[k]);
+                }
+            }
+            lo = fminf(lo, d[k] - r);
+            hi = fmaxf(hi, d[k] + r);
+        }
+    });
+    const float span = fmaxf(fabsf(lo), fabsf(hi));
+    lo -= 4.f * FLT_EPSILON * span;
+    hi += 4.f * FLT_EPSILON * span;
+    const float pivmin = FLT_MIN * fmaxf(1.f, emax);
+    const float atol = 0.0625f * FLT_EPSILON * span;
+
+    auto below = [&](float x) {
+        int cnt = 0;
+        float q = 1.f;
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            q = (d[k] - x) - (k > 0 ? e2[k - 1] : 0.f) * __builtin_amdgcn_rcpf(q);
+            q = fabsf(q) < pivmin ? -pivmin : q;
+            cnt += q < 0.f;
+        }
+        return cnt;
+    };
+
+    // ---- eigenvalue l (descending), i.e. ascending index n - 1 - l
+    constexpr bool PAIR = NM <= 32;
+    const int l = PAIR ? (lane & 31) : lane;
+    const int target = n - 1 - min(l, n - 1);
+    float lo_l = lo, hi_l = hi;
+    int it = 0;
+    for (; it < 64; ++it) {
+        const float width = hi_l - lo_l;
+        const bool done = width <= fmaxf(atol, 2.f * FLT_EPSILON * fmaxf(fabsf(lo_l), fabsf(hi_l)));
+        if (__all(done || l >= n)) break;
+        if constexpr (PAIR) {
+            const float x1 = lo_l + width * (1.f / 3.f), x2 = lo_l + width * (2.f / 3.f);
+            const int cnt = below((lane & 32) ? x2 : x1);
+            const int other = partner32(cnt);
+            const int c1 = (lane & 32) ? other : cnt, c2 = (lane & 32) ? cnt : other;
+            if (!done) {
+                if (c1 > target) {
+                    hi_l = x1;
+                } else if (c2 > target) {
+                    lo_l = x1;
+                    hi_l = x2;
+                } else {
+                    lo_l = x2;
+                }
+            }
+        } else {
+            const float x = lo_l + 0.5f * width;
+            const int cnt = below(x);
+            if (!done) {
+                if (cnt > target)
+                    hi_l = x;
+                else
+                    lo_l = x;
+            }
+        }
+    }
+    if ((!PAIR || lane < 32) && l < n) w[b * n + l] = 0.5f * (lo_l + hi_l);
+    if (info != nullptr && lane == 0) info[b] = it;
+}
+
+}  // namespace
+
+hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
+                                   int32_t *info)
+{
+    if (batch == 0) return hipSuccess;
+    if (n <= 32)
+        hipLaunchKernelGGL(small_eig_batched<32>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, info);
+    else
+        hipLaunchKernelGGL(small_eig_batched<64>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, info);
+    return hipGetLastError();
+}
