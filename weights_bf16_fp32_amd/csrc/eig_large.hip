@@ -1053,10 +1053,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     int st_pub = -1;   // storer: watermark to publish once its stores are complete
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
-    T taup = 0;          // compute wave: the previous reflector of its sweep (tau, and
-    T vprev[16];         // v at this lane's columns h*16 .. h*16+15)
-#pragma unroll
-    for (int c = 0; c < 16; ++c) vprev[c] = 0;
+    T taup = 0;          // compute wave: tau of the previous reflector of its sweep
     for (int t = 2 * s0;; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
@@ -1098,12 +1095,12 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 const int rb = slot(r0 + ci) * LDW;  // ring slot of row r0 + ci
                 const int e = rowok ? ci - h * 16 : -1;          // D column c of this lane is in the lower triangle iff c <= e
                 T *v = vsw[wv];
-                T o[16], dd[16];
-                T(&vp)[16] = vprev;  // the previous task's reflector, columns h*16 ..
+                T o[16], dd[16], vp[16];
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
                     dd[c] = WR[rb + ci - h * 16 - c];
                     o[c] = WR[rb + NB + ci - h * 16 - c];
+                    vp[c] = v[h * 16 + c];  // the previous task's reflector
                 }
                 const T xs = WR[rb + ci + 1];  // column s
                 const T dg = rowok ? WR[rb] : (T)0;
@@ -1134,8 +1131,11 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 T tau_k = 0, mu = 0, vi = 0;
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
-                    const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
-                    const T iv0 = (T)1 / v0;
+                    // v_0 and 1/v_0 need not be exact: tau below is computed from the
+                    // v actually stored, so H stays orthogonal, and the column that H
+                    // annihilates is set to mu e_0 explicitly
+                    const T v0 = x0 <= 0 ? x0 - mu : -sigma * recip(x0 + mu);
+                    const T iv0 = recip(v0);
                     vi = ci == 0 ? (T)1 : x * iv0;
                     // tau = 2 / v^T v of the v actually used, so that I - tau v v^T is
                     // orthogonal to rounding (a tau from the formula, rounded
@@ -1199,8 +1199,6 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                         if (c <= e) WR[rb + ci - h * 16 - c] = dd[c];
                 }
                 taup = tau_k;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) vprev[c] = vr[c];
             }
         }
         __syncthreads();
