@@ -28,6 +28,39 @@ SPEC_DEVICE void tri_tile(int64_t t, int &ti, int &tj)
     tj = (int)(t - (int64_t)i * (i + 1) / 2);
 }
 
+// Lower-triangle tile enumeration in 8 x 8 super-blocks: linear index t ->
+// (ti, tj), ti >= tj, nt tiles per side.  The super-blocks (I, J), I >= J, come
+// in row order and the tiles of one super-block are consecutive (row order,
+// the triangle only on the diagonal), so a run of 64 consecutive indices
+// covers a compact block that shares 8 + 8 operand panels.
+SPEC_DEVICE void tri_tile_blocked(int64_t t, int nt, int &ti, int &tj)
+{
+    constexpr int SB = 8;
+    const int ns = (nt + SB - 1) / SB;
+    for (int I = 0; I < ns; ++I) {
+        const int rows = min(SB, nt - SB * I);
+        for (int J = 0; J <= I; ++J) {
+            const int cols = min(SB, nt - SB * J);
+            const int64_t cnt = I == J ? (int64_t)rows * (rows + 1) / 2 : (int64_t)rows * cols;
+            if (t < cnt) {
+                const int u = (int)t;
+                if (I == J) {
+                    int r = 0;
+                    while ((r + 1) * (r + 2) / 2 <= u) ++r;
+                    ti = SB * I + r;
+                    tj = SB * J + (u - r * (r + 1) / 2);
+                } else {
+                    ti = SB * I + u / cols;
+                    tj = SB * J + u % cols;
+                }
+                return;
+            }
+            t -= cnt;
+        }
+    }
+    ti = tj = 0;
+}
+
 // Remap a linear workgroup id so that consecutive logical tiles land on the
 // same XCD (the hardware deals workgroups round-robin over the 8 XCDs, each
 // with its own L2): logical = xcd * per_xcd + slot.

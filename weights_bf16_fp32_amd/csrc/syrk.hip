@@ -27,6 +27,15 @@
 
 namespace {
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 constexpr int SB_TILE = 128;  // C tile edge
 constexpr int SB_BK = 64;     // samples per K-step
 constexpr int SB_LDS_ROW = 72;  // uint16 per LDS row: 64 samples + 8 pad (144 B)
@@ -43,7 +52,7 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][SB_TILE * SB_LDS_ROW];
 
     int ti, tj;
-    tri_tile(xcd_remap(blockIdx.x, gridDim.x), ti, tj);
+    tri_tile_blocked(xcd_remap(blockIdx.x, gridDim.x), (int)((d + SB_TILE - 1) / SB_TILE), ti, tj);
     const int64_t i0 = (int64_t)ti * SB_TILE, j0 = (int64_t)tj * SB_TILE;
     const bool diag = ti == tj;
 
@@ -57,32 +66,41 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
     const int64_t fbase = (op == 0 ? i0 : j0) + fb * 8;
     const bool f_ok = fbase < d;  // d % 8 == 0: a block is wholly inside or outside
 
-    // v[e] holds samples (k0 + 8 kb + e), features fbase .. fbase + 7 (two per word)
-    u32x4_t v[8];
-    auto gload = [&](int64_t k0) {
+    // v[e] holds samples (k0 + 8 kb + e), features fbase .. fbase + 7 (two per word).
+    // Buffer loads from a resource that starts at sample k0 and ends at sample
+    // n: rows past the end read as zero, and a feature block past d gets an
+    // offset beyond every resource, so no load is predicated.
+    const uint32_t ldb = (uint32_t)(ldx * 2);  // bytes per sample
+    uint32_t voff[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int64_t k = k0 + kb * 8 + e;
-            if (loader && f_ok && k < n) {
-                v[e] = *reinterpret_cast<const u32x4_t *>(X + k * ldx + fbase);
-            } else {
-                v[e] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
+    for (int e = 0; e < 8; ++e)
+        voff[e] = f_ok && loader ? (uint32_t)(kb * 8 + e) * ldb + (uint32_t)fbase * 2u : 0xFFFFFFF0u;
+    // four register stages: the samples of step k + 3 are requested while step k
+    // runs on MFMA, and written to LDS two steps later, so a load has three
+    // steps to arrive
+    constexpr int PF = 4;
+    u32x4_t vb[PF][8];
+    auto gload = [&](u32x4_t (&v)[8], int64_t k0) {
+        const int64_t rem = (n - k0) * ldx * 2;  // bytes from sample k0 to the end (<= 0: none)
+        const int num = (int)(rem <= 0 ? 0 : (rem < 0x7FFFFFF0 ? rem : 0x7FFFFFF0));
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(X + (rem > 0 ? k0 : 0) * ldx), 0, num, 0x00020000);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[e], 0, 0));
     };
-    // transpose: LDS row (feature f) gets samples 8 kb .. 8 kb + 7 (two per word)
-    auto lstore = [&](int stage) {
-        if (!loader) return;
-        uint16_t *base = &lds[stage][op][0];
+    // transpose: LDS row (feature f) gets samples 8 kb .. 8 kb + 7 (two per word),
+    // each word one byte permute of two loaded words
+    auto lstore = [&](const u32x4_t (&v)[8], int stage) {
+        uint16_t *base = &lds[stage][op][0] + (fb * 8) * SB_LDS_ROW + kb * 8;
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             u32x4_t o;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t a = v[2 * p][f >> 1], b = v[2 * p + 1][f >> 1];
-                o[p] = (f & 1) ? pack_hi(a, b) : pack_lo(a, b);
-            }
-            *reinterpret_cast<u32x4_t *>(base + (fb * 8 + f) * SB_LDS_ROW + kb * 8) = o;
+            for (int p = 0; p < 4; ++p)
+                o[p] = __builtin_amdgcn_perm(v[2 * p + 1][f >> 1], v[2 * p][f >> 1],
+                                             (f & 1) ? 0x07060302u : 0x05040100u);
+            *reinterpret_cast<u32x4_t *>(base + f * SB_LDS_ROW) = o;
         }
     };
 
@@ -96,28 +114,35 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-    gload(0);
-    lstore(0);
+    // Every thread loads and stores unconditionally (straight-line code lets the
+    // compiler wait for exactly the stage it needs): the second operand's
+    // threads of a diagonal tile read zeros and write them to the operand half
+    // that tile never reads.
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p) gload(vb[p], p * SB_BK);
+    lstore(vb[0], 0);
     __syncthreads();
-    int cur = 0;
-    for (int64_t k0 = 0; k0 < n; k0 += SB_BK) {
-        const bool more = k0 + SB_BK < n;
-        if (more) gload(k0 + SB_BK);
-        if (active) {
-            const uint16_t *la = &lds[cur][0][0];
-            const uint16_t *lb = &lds[cur][diag ? 0 : 1][0];
+    // fragment rows of this lane in both operands (a diagonal tile reads its one operand twice)
+    const uint16_t *fa_base = &lds[0][0][0] + (wm * 64 + (lane & 31)) * SB_LDS_ROW + (lane >> 5) * 8;
+    const uint16_t *fb_base = &lds[0][diag ? 0 : 1][0] + (wn * 64 + (lane & 31)) * SB_LDS_ROW + (lane >> 5) * 8;
+    constexpr int STAGE = 2 * SB_TILE * SB_LDS_ROW;  // uint16 per stage
+    // steps past n read zeros and add nothing, so the step count is rounded up to PF
+    const int64_t nsteps = (n + SB_BK - 1) / SB_BK;
+    for (int64_t s0 = 0; s0 < nsteps; s0 += PF) {
+        static_for<0, PF>([&](auto UC) {
+            constexpr int u = decltype(UC)::value;
+            const int64_t k = s0 + u;
+            gload(vb[(u + PF - 1) % PF], (k + PF - 1) * SB_BK);
+            // every wave runs its MFMAs (the upper quadrant of a diagonal tile is
+            // computed and not stored), so the accumulators need no copies
+            const uint16_t *la = fa_base + (u & 1) * STAGE, *lb = fb_base + (u & 1) * STAGE;
 #pragma unroll
             for (int kk = 0; kk < SB_BK / 16; ++kk) {
                 bf16x8_t fa[2], fbv[2];
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    int row = wm * 64 + m * 32 + (lane & 31);
-                    fa[m] = *reinterpret_cast<const bf16x8_t *>(la + row * SB_LDS_ROW + kk * 16 + (lane >> 5) * 8);
-                }
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    int row = wn * 64 + m * 32 + (lane & 31);
-                    fbv[m] = *reinterpret_cast<const bf16x8_t *>(lb + row * SB_LDS_ROW + kk * 16 + (lane >> 5) * 8);
+                    fa[m] = *reinterpret_cast<const bf16x8_t *>(la + m * 32 * SB_LDS_ROW + kk * 16);
+                    fbv[m] = *reinterpret_cast<const bf16x8_t *>(lb + m * 32 * SB_LDS_ROW + kk * 16);
                 }
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
@@ -125,10 +150,9 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
                     for (int b = 0; b < 2; ++b)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fbv[b], acc[a][b], 0, 0, 0);
             }
-        }
-        if (more) lstore(cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
+            lstore(vb[(u + 1) % PF], (u + 1) & 1);
+            __syncthreads();
+        });
     }
 
     if (!active) return;
@@ -181,7 +205,7 @@ __global__ __launch_bounds__(256) void syrk_f64_mfma(const float *__restrict__ X
     __shared__ __attribute__((aligned(16))) double lds[2][2][SD_BK * SD_LDS_ROW];
 
     int ti, tj;
-    tri_tile(xcd_remap(blockIdx.x, gridDim.x), ti, tj);
+    tri_tile_blocked(xcd_remap(blockIdx.x, gridDim.x), (int)((d + SD_TILE - 1) / SD_TILE), ti, tj);
     const int64_t i0 = (int64_t)ti * SD_TILE, j0 = (int64_t)tj * SD_TILE;
     const bool diag = ti == tj;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
