@@ -304,13 +304,179 @@ __global__ __launch_bounds__(NT) void k_tsqr_local(const T *__restrict__ Pg, int
     for (int q = tid; q < NB * NB; q += NT) Tloc[(int64_t)b * NB * NB + q] = S.Tl[q];
 }
 
-// ---- TSQR, step 2: QR of the stacked R factors; Rf and Qt = Q_top [I; 0]
+// ---- TSQR, steps 1 and 2 in fp32: NW waves with four rows per lane (up to
+// 256 NW rows); wave w, lane l holds rows 256 w + l, + 64, + 128, + 192, so
+// row k < NB is slot 0 of wave 0's lane k.  The same Householder steps as
+// reg_qr: one wave needs no workgroup barrier (its sums are butterflies inside
+// the wave); with more, each column takes two (partial sigma, partial d).  As
+// the QR of the stacked R factors (one block, Kt not null) it also writes
+// K = T V[0:NB]^T, from which Q_top [I; 0] = [I; 0] - V K.
+template <typename T, int NW>
+__global__ __launch_bounds__(64 * NW) void k_tsqr_wave(const T *__restrict__ Pg, int64_t lda, int m, int per,
+                                                       T *__restrict__ Vloc, T *__restrict__ Tloc,
+                                                       T *__restrict__ Rstack, T *__restrict__ Kt)
+{
+    static_assert(std::is_same<T, float>::value, "rows of 32 fp32 columns in registers");
+    constexpr int RPL = 4;
+    __shared__ __attribute__((aligned(16))) T red[NW][NB];  // per-wave column sums
+    __shared__ T sig[2][NW], x0s[2];                         // per-wave partial sigma, P[k][k] (two buffers)
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x;
+    const int r0 = b * per;
+    const int rows = min(per, m - r0);
+    const int rb = wv * 64 * RPL + lane;  // row of slot 0
+    T p[RPL][NB];
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+        const int r = rb + q * 64;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) p[q][c] = r < rows ? Pg[(int64_t)(r0 + r) * lda + c] : (T)0;
+    }
+    T Tr[NB];  // wave 0, lane i < NB: row i of T (upper triangular)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) Tr[c] = 0;
+    static_for<0, NB>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        T part = 0;
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) part += rb + q * 64 > k ? p[q][k] * p[q][k] : (T)0;
+        part = wave_sum64(part);
+        T sigma, x0;
+        if constexpr (NW == 1) {
+            sigma = part;
+            x0 = readlane_t(p[0][k], k);
+        } else {
+            if (lane == 0) sig[k & 1][wv] = part;
+            if (tid == k) x0s[k & 1] = p[0][k];
+            __syncthreads();
+            sigma = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sigma += sig[k & 1][w];
+            x0 = x0s[k & 1];
+        }
+        T t = 0, scale = 0, mu = 0;
+        if (sigma > 0) {
+            mu = sqrt(x0 * x0 + sigma);
+            const T v0 = x0 <= 0 ? x0 - mu : -sigma / (x0 + mu);
+            t = 2 * v0 * v0 / (sigma + v0 * v0);
+            scale = 1 / v0;
+        }
+        T v[RPL];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+            const int r = rb + q * 64;
+            v[q] = r > k ? scale * p[q][k] : (r == k ? (T)1 : (T)0);
+        }
+        if (t != 0) {  // the same in every wave
+            // d_c = sum_r v_r P[r][c]: for c > k the update of column c, for c < k
+            // the inner products with the earlier Householder vectors (T's column)
+            T x[NB];
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                T a = 0;
+#pragma unroll
+                for (int q = 0; q < RPL; ++q) a += v[q] * p[q][c];
+                x[c] = a;
+            }
+            const T dsum = reduce_scatter32<T>(x, lane);
+            if constexpr (NW == 1) {
+                wave_sync();
+                red[0][lane & (NB - 1)] = dsum;
+                wave_sync();
+            } else {
+                if (lane < NB) red[wv][lane] = dsum;
+                __syncthreads();
+            }
+            T d[NB];
+#pragma unroll
+            for (int c4 = 0; c4 < NB / 4; ++c4) {
+                float4 q4 = reinterpret_cast<const float4 *>(red[0])[c4];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    const float4 o = reinterpret_cast<const float4 *>(red[w])[c4];
+                    q4.x += o.x;
+                    q4.y += o.y;
+                    q4.z += o.z;
+                    q4.w += o.w;
+                }
+                d[4 * c4] = q4.x;
+                d[4 * c4 + 1] = q4.y;
+                d[4 * c4 + 2] = q4.z;
+                d[4 * c4 + 3] = q4.w;
+            }
+#pragma unroll
+            for (int q = 0; q < RPL; ++q) {
+                const T tv = t * v[q];
+#pragma unroll
+                for (int c = k + 1; c < NB; ++c) p[q][c] -= tv * d[c];
+            }
+            // T[i][k] = -t sum_{i <= j < k} T[i][j] d_j (T[i][j] = 0 for j < i)
+            T acc = 0;
+#pragma unroll
+            for (int j = 0; j < k; ++j) acc += Tr[j] * d[j];
+            Tr[k] = lane < k ? -t * acc : (T)0;
+#pragma unroll
+            for (int q = 0; q < RPL; ++q) {
+                const int r = rb + q * 64;
+                if (r == k) p[q][k] = mu;
+                if (r > k) p[q][k] = v[q];
+            }
+        }
+        if (lane == k) Tr[k] = t;
+    });
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+        const int r = rb + q * 64;
+        if (r < rows) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                Vloc[(int64_t)(r0 + r) * NB + c] = r == c ? (T)1 : (r > c ? p[q][c] : (T)0);
+                if (r < NB) Rstack[(int64_t)b * NB * NB + r * NB + c] = r <= c ? p[q][c] : (T)0;
+            }
+        }
+    }
+    if (wv != 0) return;
+    if (lane < NB) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) Tloc[(int64_t)b * NB * NB + lane * NB + c] = Tr[c];
+    }
+    if (Kt != nullptr) {
+        // K[j][c] = sum_{j <= l <= c} T[j][l] V[c][l] (upper triangular): lane
+        // (j, c parity); V's top rows as LDS broadcasts, T's row j from lane j
+        constexpr int LV = NB + 4;
+        __shared__ __attribute__((aligned(16))) T Vs[NB * LV];
+        if (lane < NB) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) Vs[lane * LV + c] = lane == c ? (T)1 : (lane > c ? p[0][c] : (T)0);
+        }
+        T tj[NB];
+#pragma unroll
+        for (int l = 0; l < NB; ++l) {
+            T a = Tr[l], c2 = Tr[l];
+            halfswap32(a, c2);
+            tj[l] = (lane & 32) ? a : Tr[l];
+        }
+        wave_sync();
+        const int j = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            if ((c & 1) != h) continue;
+            T acc = 0;
+#pragma unroll
+            for (int l = 0; l <= c; ++l) acc += tj[l] * Vs[c * LV + l];
+            Kt[j * NB + c] = acc;
+        }
+    }
+}
+
+// ---- TSQR, step 2: QR of the stacked R factors; Rf, V_top and K = T V_top[0:NB]^T
+// (Q_top [I; 0] = [I; 0] - V_top K)
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_tsqr_top(const T *__restrict__ Rstack, int nblk, T *__restrict__ Rf,
-                                                 T *__restrict__ Qt)
+                                                 T *__restrict__ Vtop, T *__restrict__ Kt)
 {
     __shared__ RegQr<T, NT> S;
-    __shared__ T Vt[NB * LDP], K[NB * NB];
+    __shared__ T Vt[NB * LDP];
     const int tid = threadIdx.x;
     const int rows = nblk * NB;
     T p[NB];
@@ -330,29 +496,20 @@ __global__ __launch_bounds__(NT) void k_tsqr_top(const T *__restrict__ Rstack, i
         const int j = q / NB, c = q % NB;
         T acc = 0;
         for (int l = j; l <= c; ++l) acc += S.Tl[j * NB + l] * Vt[c * LDP + l];
-        K[q] = acc;
+        Kt[q] = acc;
     }
-    __syncthreads();
-    // Qt[r][c] = [r == c] - sum_j V[r][j] K[j][c]
     if (tid < rows) {
-        T q[NB];
 #pragma unroll
-        for (int c = 0; c < NB; ++c) q[c] = tid == c ? (T)1 : (T)0;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const T vrj = tid == j ? (T)1 : (tid > j ? p[j] : (T)0);
-#pragma unroll
-            for (int c = 0; c < NB; ++c) q[c] -= vrj * K[j * NB + c];
-        }
-#pragma unroll
-        for (int c = 0; c < NB; ++c) Qt[(int64_t)tid * NB + c] = q[c];
+        for (int c = 0; c < NB; ++c) Vtop[(int64_t)tid * NB + c] = tid == c ? (T)1 : (tid > c ? p[c] : (T)0);
     }
 }
 
-// ---- TSQR, step 3: Q1 rows of block b = [Qt_b; 0] - V_b (T_b V_b[0:NB]^T Qt_b)
+// ---- TSQR, step 3: Q1 rows of block b = [Qt_b; 0] - V_b (T_b V_b[0:NB]^T Qt_b),
+// with Qt_b = [I; 0]_b - V_top,b K_top, rows b NB .. b NB + NB of Q_top [I; 0]
 template <typename T>
 __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, const T *__restrict__ Tloc,
-                                                 const T *__restrict__ Qt, int m, int per, T *__restrict__ Q1)
+                                                 const T *__restrict__ Vtop, const T *__restrict__ Ktop, int m,
+                                                 int per, T *__restrict__ Q1)
 {
     __shared__ T Vt[NB * NB], Tb[NB * NB], Qb[NB * NB], Y[NB * NB], K[NB * NB];
     const int tid = threadIdx.x;
@@ -362,7 +519,15 @@ __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, con
     for (int p = tid; p < NB * NB; p += 256) {
         Vt[p] = Vloc[(int64_t)(r0 + p / NB) * NB + p % NB];
         Tb[p] = Tloc[(int64_t)b * NB * NB + p];
-        Qb[p] = Qt[(int64_t)b * NB * NB + p];
+        Y[p] = Vtop[(int64_t)b * NB * NB + p];
+        K[p] = Ktop[p];
+    }
+    __syncthreads();
+    for (int p = tid; p < NB * NB; p += 256) {
+        const int i = p / NB, c = p % NB;
+        T s = b * NB + i == c ? (T)1 : (T)0;
+        for (int j = 0; j < NB; ++j) s -= Y[i * NB + j] * K[j * NB + c];
+        Qb[p] = s;
     }
     __syncthreads();
     // Y = V_b[0:NB]^T Qt_b ; K = T_b Y
@@ -420,21 +585,31 @@ __global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, con
         T rowk[NB];
 #pragma unroll
         for (int j = k + 1; j < NB; ++j) rowk[j] = readlane_t(m[j], k);
+        const T rp = recip(piv);  // |piv| >= 1
         if (i > k) {
-            const T l = m[k] / piv;
+            const T l = m[k] * rp;
             m[k] = l;
 #pragma unroll
             for (int j = k + 1; j < NB; ++j) m[j] -= l * rowk[j];
         }
     });
     // T = -(U S) Y1^{-T}: row i solves z Y1^T = -(U S)[i] by forward substitution,
-    // with Y1 unit lower (the multipliers below the diagonal)
+    // with Y1 unit lower (the multipliers below the diagonal).  Y1 goes through
+    // LDS once and its rows are read back as broadcasts.
+    constexpr int LY = NB + 4;
+    __shared__ __attribute__((aligned(16))) T Y1s[NB * LY];
+    if (lane < NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) Y1s[i * LY + j] = j < i ? m[j] : (T)0;
+    }
+    wave_sync();
     T z[NB];
     static_for<0, NB>([&](auto JC) {
         constexpr int j = decltype(JC)::value;
         T b = j >= i ? -m[j] * sv[j] : (T)0;
 #pragma unroll
-        for (int l = 0; l < j; ++l) b -= readlane_t(m[l], j) * z[l];
+        for (int l = 0; l < j; ++l) b -= Y1s[j * LY + l] * z[l];
+        asm volatile("" : "+v"(b));  // computed here, not sunk into the stores below
         z[j] = b;
     });
     if (lane < NB) {
@@ -1420,7 +1595,7 @@ struct Ws {
 
 template <typename T>
 struct Bufs {
-    T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Qt, *U, *Tm, *Mm, *Ppart;
+    T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Mm, *Ppart;
     int32_t *prog;
     double *dd, *ee2, *bounds;
     float2 *de32;
@@ -1444,7 +1619,9 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.Tloc = ws.take<T>((size_t)32 * NB * NB);
     b.Rstack = ws.take<T>((size_t)32 * NB * NB);
     b.Rf = ws.take<T>((size_t)NB * NB);
-    b.Qt = ws.take<T>((size_t)32 * NB * NB);
+    b.Vtop = ws.take<T>((size_t)32 * NB * NB);
+    b.Ttop = ws.take<T>((size_t)NB * NB);
+    b.Ktop = ws.take<T>((size_t)NB * NB);
     b.U = ws.take<T>((size_t)NB * NB);
     b.Tm = ws.take<T>((size_t)NB * NB);
     b.Mm = ws.take<T>((size_t)NB * NB);
@@ -1487,25 +1664,53 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
             const int per = (int)cdiv_h(m, nblk);
             const int rows_top = nblk * NB;
-            if (per <= 256)
-                hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per, b.Vloc,
-                                   b.Tloc, b.Rstack);
-            else if (per <= 512)
-                hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, st, P, lda, (int)m, per, b.Vloc,
-                                   b.Tloc, b.Rstack);
-            else
-                hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, st, P, lda, (int)m, per,
-                                   b.Vloc, b.Tloc, b.Rstack);
-            LAUNCH_OK();
-            if (rows_top <= 256)
-                hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
-            else if (rows_top <= 512)
-                hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
-            else
-                hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, st, b.Rstack, nblk, b.Rf, b.Qt);
-            LAUNCH_OK();
+            // fp32: QRs with four rows per lane (one wave up to 256 rows, two up to 512,
+            // four up to 1024); fp64: one row per thread
+            if constexpr (std::is_same<T, float>::value) {
+                if (per <= 256)
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(nblk), dim3(64), 0, st, P, lda, (int)m, per, b.Vloc,
+                                       b.Tloc, b.Rstack, (T *)nullptr);
+                else if (per <= 512)
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(nblk), dim3(128), 0, st, P, lda, (int)m, per,
+                                       b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                else
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per,
+                                       b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                LAUNCH_OK();
+                if (rows_top <= 256)
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(1), dim3(64), 0, st, b.Rstack, (int64_t)NB, rows_top,
+                                       rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                else if (rows_top <= 512)
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(1), dim3(128), 0, st, b.Rstack, (int64_t)NB,
+                                       rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                else
+                    hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(1), dim3(256), 0, st, b.Rstack, (int64_t)NB,
+                                       rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                LAUNCH_OK();
+            } else {
+                if (per <= 256)
+                    hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per,
+                                       b.Vloc, b.Tloc, b.Rstack);
+                else if (per <= 512)
+                    hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, st, P, lda, (int)m, per,
+                                       b.Vloc, b.Tloc, b.Rstack);
+                else
+                    hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, st, P, lda, (int)m, per,
+                                       b.Vloc, b.Tloc, b.Rstack);
+                LAUNCH_OK();
+                if (rows_top <= 256)
+                    hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, st, b.Rstack, nblk, b.Rf, b.Vtop,
+                                       b.Ktop);
+                else if (rows_top <= 512)
+                    hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, st, b.Rstack, nblk, b.Rf, b.Vtop,
+                                       b.Ktop);
+                else
+                    hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, st, b.Rstack, nblk, b.Rf,
+                                       b.Vtop, b.Ktop);
+                LAUNCH_OK();
+            }
             hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
-                               b.Qt, (int)m, per, b.Q1);
+                               b.Vtop, b.Ktop, (int)m, per, b.Q1);
             LAUNCH_OK();
             hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, st, b.Q1, b.Rf, P, lda, b.V, b.U, b.Tm);
             LAUNCH_OK();
