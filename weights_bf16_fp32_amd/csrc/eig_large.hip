@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     __shared__ T vsw[G][NB];
     __shared__ T red[G][NB];
     __shared__ T w2s[G][NB];
-    __shared__ int abort_flag;
+    __shared__ int abort_flag[2];  // set at step t in entry t & 1, read by every wave after that step
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ci = lane & 31, h = lane >> 5;
     const int nn = (int)n;
@@ -1149,8 +1149,8 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     // rows loaded into the ring once the lead's task k has been fetched
     auto loaded_to = [&](int k) { return k < 0 ? s0 + 1 : lastrow(s0, min(k, ntl - 1)) + 1; };
 
-    // the loader's wait for the previous group; sets abort_flag on time-out
-    auto wait_rows = [&](int r1) {
+    // the loader's wait for the previous group; sets abort_flag[par] on time-out
+    auto wait_rows = [&](int r1, int par) {
         int ok = 1;
         if (g > 0 && lane == 0) {
             if (cload(wm + g - 1) <= r1) {
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
             }
             if (!ok) {
                 cstore(err, 1);
-                abort_flag = 1;
+                abort_flag[par] = 1;
             }
         }
         return __builtin_amdgcn_readfirstlane(ok);
@@ -1208,20 +1208,20 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
         }
     };
 
-    if (tid == 0) abort_flag = 0;
+    if (tid < 2) abort_flag[tid] = 0;
     __syncthreads();
     // ---- prologue: the lead's first LA chunks, synchronously
     if (wv == G) {
         for (int k = 0; k < LA && k < ntl; ++k) {
             const int lo = loaded_to(k - 1), hi = loaded_to(k);
-            if (!wait_rows(hi - 1)) break;
+            if (!wait_rows(hi - 1, 0)) break;
             T tmp[NB];
             load_chunk(lo, tmp);
             write_chunk(lo, tmp);
         }
     }
     __syncthreads();
-    if (abort_flag) return;
+    if (abort_flag[0]) return;
 
     T ld[NB];          // loader: the chunk in flight
     int ld_lo = -1;    // loader: its first row (-1: none)
@@ -1229,7 +1229,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
     T taup = 0;          // compute wave: tau of the previous reflector of its sweep
-    for (int t = 2 * s0;; ++t) {
+    int ab = 0;          // abort flag of the previous step
+    // the group's last sweep ends last: its last task is the group's last step
+    const int t_end = 2 * (s0 + Ge - 1) + ntasks(s0 + Ge - 1);
+    for (int t = 2 * s0; t < t_end; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
             // write the chunk requested at the previous step, request the next one
@@ -1238,21 +1241,31 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
             const int kn = k0 + LA;
             if (kn < ntl) {
                 const int lo = loaded_to(kn - 1), hi = loaded_to(kn);
-                if (wait_rows(hi - 1)) {
+                if (wait_rows(hi - 1, t & 1)) {
                     load_chunk(lo, ld);
                     ld_lo = lo;
                 }
             }
         } else if (wv == G + 1) {
-            // publish the watermark of the stores issued at the previous step
-            if (st_pub >= 0) {
-                __builtin_amdgcn_s_waitcnt(0);
-                if (lane == 0) cstore(wm + g, (int32_t)st_pub);
-                st_pub = -1;
-            }
+            // issue this step's row stores, then publish the watermark of the
+            // previous step's once they are complete.  Vector memory operations
+            // complete in issue order, so with a full chunk in flight the wait is
+            // for all but the NB newest (one store per row)
+            const int pub = st_pub;
+            int issued = 0;
+            st_pub = -1;
             if (wmk > wst) {
+                issued = wmk - wst;
                 store_rows(wst, wmk);
                 st_pub = wmk;
+            }
+            if (pub >= 0) {
+                static_assert(NB == 32, "vmcnt(32) below");
+                if (issued == NB)
+                    __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32)
+                else
+                    __builtin_amdgcn_s_waitcnt(0);
+                if (lane == 0) cstore(wm + g, (int32_t)pub);
             }
         } else {
             const int s = s0 + wv;
@@ -1376,22 +1389,23 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 taup = tau_k;
             }
         }
+        if (ab) return;  // every wave leaves at the same step
         __syncthreads();
-        if (abort_flag) return;
+        ab = abort_flag[t & 1];  // not written again before the next barrier
         // ---- uniform bookkeeping: the storer has taken [wst, wmk); rows below the
-        // first row of every remaining task, and already in the ring, are released
+        // first row of every remaining task, and already in the ring, are released.
+        // At step t + 1 sweep s0 + i is at task x - 2 i (x = t + 1 - 2 s0): the
+        // first sweep that has not started (i >= x / 2) starts at its row s0 + i + 1,
+        // and the started ones are further down (at least NB rows per task), so
+        // that row is the minimum; once all have started, the last sweep's task is.
         wst = max(wst, wmk);
-        int nwm = loaded_to(k0 + LA - 1);
-        bool more = false;
-        for (int i = 0; i < Ge; ++i) {
-            const int kk = t + 1 - 2 * (s0 + i);
-            if (kk < ntasks(s0 + i)) {
-                nwm = min(nwm, minrow(s0 + i, kk));
-                more = true;
-            }
+        {
+            const int x = t + 1 - 2 * s0;
+            const int iu = (x + 1) >> 1;
+            const int nt = iu < Ge ? s0 + iu + 1 : minrow(s0 + Ge - 1, x - 2 * (Ge - 1));
+            const int nwm = min(loaded_to(k0 + LA - 1), nt);
+            if (nwm > wmk) wmk = nwm;
         }
-        if (nwm > wmk) wmk = nwm;
-        if (!more) break;
     }
     // ---- epilogue: store what is left and publish the end
     if (wv == G + 1) {
