@@ -1088,9 +1088,9 @@ __device__ __forceinline__ void cstore(T *p, T v)
 //    passed them) and written into the ring at step t + 1, so no compute wave
 //    waits on a load.
 //  * storer: the rows no future task of the group touches (below the
-//    watermark) are stored at the step after their release; at the next step,
-//    once the stores are complete, the watermark is published for the next
-//    group.
+//    watermark) are stored at the step after their release, and once the
+//    stores are complete, in the same step, the watermark is published for
+//    the next group.
 // Band rows move between the ring and global memory as buffer loads and
 // stores (one instruction per row, row offsets in the instruction; rows past
 // the end of the band read as zero) with the same cache policy as cload/cstore.
@@ -1225,7 +1225,6 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
 
     T ld[NB];          // loader: the chunk in flight
     int ld_lo = -1;    // loader: its first row (-1: none)
-    int st_pub = -1;   // storer: watermark to publish once its stores are complete
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
     T taup = 0;          // compute wave: tau of the previous reflector of its sweep
@@ -1247,25 +1246,12 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 }
             }
         } else if (wv == G + 1) {
-            // issue this step's row stores, then publish the watermark of the
-            // previous step's once they are complete.  Vector memory operations
-            // complete in issue order, so with a full chunk in flight the wait is
-            // for all but the NB newest (one store per row)
-            const int pub = st_pub;
-            int issued = 0;
-            st_pub = -1;
+            // store the rows released at the previous step and publish their
+            // watermark once the stores are complete
             if (wmk > wst) {
-                issued = wmk - wst;
                 store_rows(wst, wmk);
-                st_pub = wmk;
-            }
-            if (pub >= 0) {
-                static_assert(NB == 32, "vmcnt(32) below");
-                if (issued == NB)
-                    __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32)
-                else
-                    __builtin_amdgcn_s_waitcnt(0);
-                if (lane == 0) cstore(wm + g, (int32_t)pub);
+                __builtin_amdgcn_s_waitcnt(0);
+                if (lane == 0) cstore(wm + g, (int32_t)wmk);
             }
         } else {
             const int s = s0 + wv;
