@@ -1084,9 +1084,9 @@ __device__ __forceinline__ void cstore(T *p, T v)
 // the G waves run them side by side.  The rows of the group stay in an LDS ring
 // (row r at slot r & (CAPR - 1), its band entries A[r][r - j] contiguous).
 //  * loader: the lead sweep s0 needs NB new rows per step.  The rows for step
-//    t + LA are requested at step t (after the previous group's watermark has
-//    passed them) and written into the ring at step t + 1, so no compute wave
-//    waits on a load.
+//    t + 1 are loaded at step t, as soon as the previous group's watermark has
+//    passed them, and written into the ring before the step ends, so no
+//    compute wave waits on a load.
 //  * storer: the rows no future task of the group touches (below the
 //    watermark) are stored at the step after their release, and once the
 //    stores are complete, in the same step, the watermark is published for
@@ -1118,7 +1118,7 @@ template <typename T, int G, int CAPR>
 __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
                                                         uint64_t spin_ticks)
 {
-    constexpr int LA = 2;  // loader lookahead in time steps
+    constexpr int LA = 2;  // the ring holds the lead's chunks up to the next step's (LA - 1 ahead)
     static_assert(CAPR % NB == 0 && (LA + 2 * G - 1) * NB <= CAPR, "ring too small");
     constexpr int LDW = BW + 1;
     constexpr int RB = BW * sizeof(T);  // bytes per band row
@@ -1210,9 +1210,9 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
 
     if (tid < 2) abort_flag[tid] = 0;
     __syncthreads();
-    // ---- prologue: the lead's first LA chunks, synchronously
+    // ---- prologue: the lead's first chunk
     if (wv == G) {
-        for (int k = 0; k < LA && k < ntl; ++k) {
+        for (int k = 0; k < LA - 1 && k < ntl; ++k) {
             const int lo = loaded_to(k - 1), hi = loaded_to(k);
             if (!wait_rows(hi - 1, 0)) break;
             T tmp[NB];
@@ -1223,8 +1223,6 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     __syncthreads();
     if (abort_flag[0]) return;
 
-    T ld[NB];          // loader: the chunk in flight
-    int ld_lo = -1;    // loader: its first row (-1: none)
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
     T taup = 0;          // compute wave: tau of the previous reflector of its sweep
@@ -1234,15 +1232,14 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     for (int t = 2 * s0; t < t_end; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
-            // write the chunk requested at the previous step, request the next one
-            if (ld_lo >= 0) write_chunk(ld_lo, ld);
-            ld_lo = -1;
-            const int kn = k0 + LA;
+            // the lead's chunk for the next step
+            const int kn = k0 + LA - 1;
             if (kn < ntl) {
                 const int lo = loaded_to(kn - 1), hi = loaded_to(kn);
                 if (wait_rows(hi - 1, t & 1)) {
+                    T ld[NB];
                     load_chunk(lo, ld);
-                    ld_lo = lo;
+                    write_chunk(lo, ld);
                 }
             }
         } else if (wv == G + 1) {
