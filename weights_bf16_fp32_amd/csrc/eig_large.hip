@@ -1082,7 +1082,7 @@ __device__ __forceinline__ void cstore(T *p, T v)
 // task (s0 + i, t - 2 (s0 + i)); the tasks of one time step touch disjoint rows
 // and depend only on tasks of earlier steps ("(s, k) after (s - 1, k + 1)"), so
 // the G waves run them side by side.  The rows of the group stay in an LDS ring
-// (row r at slot r & (CAPR - 1), its band entries A[r][r - j] contiguous).
+// (row r at slot (r - s0 - 1) mod CAPR, its band entries A[r][r - j] contiguous).
 //  * loader: the lead sweep s0 needs NB new rows per step.  The rows for step
 //    t + 1 are loaded at step t, as soon as the previous group's watermark has
 //    passed them, and written into the ring before the step ends, so no
@@ -1123,8 +1123,9 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     constexpr int LDW = BW + 1;
     constexpr int RB = BW * sizeof(T);  // bytes per band row
     constexpr int QI = 4096 / RB;       // rows reachable from one base through the instruction offset
-    __shared__ T WRbuf[NB + CAPR * LDW];
+    __shared__ T WRbuf[NB + CAPR * LDW + 64];
     T *const WR = WRbuf + NB;  // NB guard entries before the first ring row
+    constexpr int SINK = CAPR * LDW;  // 64 entries after the ring: target of masked-off stores
     __shared__ T vsw[G][NB];
     __shared__ T red[G][NB];
     __shared__ T w2s[G][NB];
@@ -1308,10 +1309,11 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma * recip(x0 + mu);
                     const T iv0 = recip(v0);
                     vi = ci == 0 ? (T)1 : x * iv0;
-                    // tau = 2 / v^T v of the v actually used, so that I - tau v v^T is
-                    // orthogonal to rounding (a tau from the formula, rounded
-                    // differently from v, drifts the trace over many applications)
-                    tau_k = (T)2 / ((T)1 + half_sum(ci >= 1 ? vi * vi : (T)0));
+                    // tau = 2 / v^T v with v^T v = 1 + sigma iv0^2, the same iv0 that
+                    // scales v: I - tau v v^T is orthogonal up to the rounding of the
+                    // entries (a tau from v0 alone, whose reciprocal is rounded
+                    // differently from iv0, drifts the trace over many applications)
+                    tau_k = (T)2 / ((T)1 + sigma * iv0 * iv0);
                 }
                 wave_sync();
                 if (h == 0) v[ci] = vi;
@@ -1365,9 +1367,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     }
                 }
                 if (tau_k != 0) {
+                    // entries above the block's diagonal go to the sink, so the 16
+                    // stores need no branches
 #pragma unroll
-                    for (int c = 0; c < 16; ++c)
-                        if (c <= e) WR[rb + ci - h * 16 - c] = dd[c];
+                    for (int c = 0; c < 16; ++c) WR[c <= e ? rb + ci - h * 16 - c : SINK + lane] = dd[c];
                 }
                 taup = tau_k;
             }
