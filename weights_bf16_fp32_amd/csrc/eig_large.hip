@@ -623,50 +623,48 @@ __global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, con
     }
 }
 
-// ---- TSQR, step 5: V rows NB.. = Q1 rows U^{-1}
+// ---- V rows r_q1.. = Q1 rows U^{-1} (TSQR step 5; rows below r_q1 are already
+// in V), then W = V T, one row per thread
+constexpr int VW_T = 128;
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_tsqr_y2(const T *__restrict__ Q1, const T *__restrict__ Ug, int m,
-                                                 T *__restrict__ V)
+__global__ __launch_bounds__(VW_T) void k_vw(const T *__restrict__ Q1, const T *__restrict__ Ug,
+                                             const T *__restrict__ Tm, int m, int r_q1, T *__restrict__ V,
+                                             T *__restrict__ W)
 {
-    __shared__ T U[NB * LDP];
+    __shared__ T U[NB * LDP], Ts[NB * LDP];
     const int tid = threadIdx.x;
-    for (int p = tid; p < NB * NB; p += 256) U[(p / NB) * LDP + p % NB] = Ug[p];
+    for (int p = tid; p < NB * NB; p += VW_T) {
+        U[(p / NB) * LDP + p % NB] = r_q1 < m ? Ug[p] : (T)0;
+        Ts[(p / NB) * LDP + p % NB] = Tm[p];
+    }
     __syncthreads();
-    const int64_t r = NB + blockIdx.x * 256 + tid;
+    const int64_t r = (int64_t)blockIdx.x * VW_T + tid;
     if (r >= m) return;
-    T q[NB], y[NB];
+    T y[NB];
+    if (r < r_q1) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) q[j] = Q1[r * NB + j];
+        for (int j = 0; j < NB; ++j) y[j] = V[r * NB + j];
+    } else {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        T s = q[j];
+        for (int j = 0; j < NB; ++j) y[j] = Q1[r * NB + j];
 #pragma unroll
-        for (int l = 0; l < j; ++l) s -= y[l] * U[l * LDP + j];
-        y[j] = s / U[j * LDP + j];
+        for (int j = 0; j < NB; ++j) {
+            T s = y[j];
+#pragma unroll
+            for (int l = 0; l < j; ++l) s -= y[l] * U[l * LDP + j];
+            y[j] = s / U[j * LDP + j];
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) V[r * NB + j] = y[j];
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) V[r * NB + j] = y[j];
-}
-
-// ---- W = V T (m x NB)
-template <typename T>
-__global__ __launch_bounds__(256) void k_make_w(const T *__restrict__ V, const T *__restrict__ Tm, int m,
-                                                T *__restrict__ W)
-{
-    __shared__ T Ts[NB * NB];
-    const int tid = threadIdx.x;
-    for (int p = tid; p < NB * NB; p += 256) Ts[p] = Tm[p];
-    __syncthreads();
-    const int64_t r = blockIdx.x * 8 + (tid >> 5);
-    const int c = tid & 31;
-    if (r >= m) return;
-    T vrow[NB];
+    for (int c = 0; c < NB; ++c) {
+        T s = 0;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) vrow[j] = V[r * NB + j];
-    T s = 0;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) s += vrow[j] * Ts[j * NB + c];  // T is upper: terms j > c vanish
-    W[r * NB + c] = s;
+        for (int j = 0; j <= c; ++j) s += y[j] * Ts[j * LDP + c];  // T is upper triangular
+        W[r * NB + c] = s;
+    }
 }
 
 // ---- X partials = A22[rows, jrange] W[jrange]  (A22 lower-stored symmetric)
@@ -860,16 +858,17 @@ __global__ __launch_bounds__(256) void k_xreduce(const T *__restrict__ Xpart, in
     }
 }
 
-// ---- M = T^T sum(Ppart)
+// ---- M = T^T sum(Ppart) (every workgroup forms its own copy), then Z = X - V M / 2
+// in place in X for the workgroup's rows
+constexpr int MZ_BLOCKS = 64;
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_mfin(const T *__restrict__ Ppart, int nblk, const T *__restrict__ Tm,
-                                              T *__restrict__ Mm)
+__global__ __launch_bounds__(256) void k_mz(const T *__restrict__ Ppart, int nblk, const T *__restrict__ Tm,
+                                            T *__restrict__ X, const T *__restrict__ V, int m)
 {
-    __shared__ T P[NB * LDP];
-    __shared__ T Ts[NB * LDP];
+    __shared__ T P[NB * LDP], Ts[NB * LDP], Ms[NB * NB];
     const int tid = threadIdx.x;
     constexpr int PER = NB * NB / 256;
-    // the partial sums of each element: 8 loads in flight at a time
     T acc[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) acc[q] = 0;
@@ -900,29 +899,30 @@ __global__ __launch_bounds__(256) void k_mfin(const T *__restrict__ Ppart, int n
 #pragma unroll
         for (int l = 0; l < NB; ++l)
             if (l <= i) s += Ts[l * LDP + i] * P[l * LDP + c];  // T^T is lower
-        Mm[p] = s;
+        Ms[p] = s;
     }
-}
-
-// ---- Z = X - V M / 2  (in place in X)
-template <typename T>
-__global__ __launch_bounds__(256) void k_zform(T *__restrict__ X, const T *__restrict__ V, const T *__restrict__ Mm,
-                                               int m)
-{
-    __shared__ T Ms[NB * NB];
-    const int tid = threadIdx.x;
-    for (int p = tid; p < NB * NB; p += 256) Ms[p] = Mm[p];
     __syncthreads();
-    const int64_t r = blockIdx.x * 8 + (tid >> 5);
+    // rows in batches of four, their loads in flight together
     const int c = tid & 31;
-    if (r >= m) return;
-    T vrow[NB];
+    const int64_t stride = (int64_t)gridDim.x * 8;
+    for (int64_t r0 = (int64_t)blockIdx.x * 8 + (tid >> 5); r0 < m; r0 += 4 * stride) {
+        T vrow[4][NB], x[4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) vrow[j] = V[r * NB + j];
-    T s = 0;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t r = r0 + u * stride;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) s += vrow[j] * Ms[j * NB + c];
-    X[r * NB + c] -= (T)0.5 * s;
+            for (int j = 0; j < NB; ++j) vrow[u][j] = r < m ? V[r * NB + j] : (T)0;
+            x[u] = r < m ? X[r * NB + c] : (T)0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t r = r0 + u * stride;
+            T s = 0;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) s += vrow[u][j] * Ms[j * NB + c];
+            if (r < m) X[r * NB + c] = x[u] - (T)0.5 * s;
+        }
+    }
 }
 
 // ---- A22 -= V Z^T + Z V^T on lower 128 x 128 tiles
@@ -1595,7 +1595,7 @@ struct Ws {
 
 template <typename T>
 struct Bufs {
-    T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Mm, *Ppart;
+    T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Ppart;
     int32_t *prog;
     double *dd, *ee2, *bounds;
     float2 *de32;
@@ -1624,7 +1624,6 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.Ktop = ws.take<T>((size_t)NB * NB);
     b.U = ws.take<T>((size_t)NB * NB);
     b.Tm = ws.take<T>((size_t)NB * NB);
-    b.Mm = ws.take<T>((size_t)NB * NB);
     b.Ppart = ws.take<T>((size_t)cdiv_h(n, XR) * NB * NB);
     b.dd = ws.take<double>((size_t)n);
     b.ee2 = ws.take<double>((size_t)n);
@@ -1714,11 +1713,10 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             LAUNCH_OK();
             hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, st, b.Q1, b.Rf, P, lda, b.V, b.U, b.Tm);
             LAUNCH_OK();
-            hipLaunchKernelGGL(k_tsqr_y2<T>, dim3((unsigned)cdiv_h(m - NB, 256)), dim3(256), 0, st, b.Q1, b.U,
-                               (int)m, b.V);
-            LAUNCH_OK();
         }
-        hipLaunchKernelGGL(k_make_w<T>, dim3((unsigned)cdiv_h(m, 8)), dim3(256), 0, st, b.V, b.Tm, (int)m, b.W);
+        // V rows below the reconstructed top block (TSQR), then W = V T
+        hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_T)), dim3(VW_T), 0, st, b.Q1, b.U, b.Tm, (int)m,
+                           m <= DIRECT_ROWS ? (int)m : NB, b.V, b.W);
         LAUNCH_OK();
         const int nrb = (int)cdiv_h(m, SY_RB);
         int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
@@ -1729,9 +1727,8 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         const int nxb = (int)cdiv_h(m, XR);
         hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, b.V, b.X, b.Ppart);
         LAUNCH_OK();
-        hipLaunchKernelGGL(k_mfin<T>, dim3(1), dim3(256), 0, st, b.Ppart, nxb, b.Tm, b.Mm);
-        LAUNCH_OK();
-        hipLaunchKernelGGL(k_zform<T>, dim3((unsigned)cdiv_h(m, 8)), dim3(256), 0, st, b.X, b.V, b.Mm, (int)m);
+        hipLaunchKernelGGL(k_mz<T>, dim3((unsigned)std::min<int64_t>(MZ_BLOCKS, cdiv_h(m, 8))), dim3(256), 0, st,
+                           b.Ppart, nxb, b.Tm, b.X, b.V, (int)m);
         LAUNCH_OK();
         const int64_t nt = cdiv_h(m, S2_T);
         hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A22, lda, (int)m, b.V,
