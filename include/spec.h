@@ -152,7 +152,8 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
  * info: int32 [1] device (may be NULL): 0 on success, 1 if the bulge-chasing
  *       pipeline hit its bounded wait (results invalid).
  * Calls sharing one workspace must be ordered on one stream.
- * Requires 1 <= n <= 32768 (SPEC_F32) or n <= 8192 (SPEC_F64), lda >= n.
+ * Requires 1 <= n <= 32768 (SPEC_F32) or n <= 8192 (SPEC_F64), n <= lda < 2^22
+ * (offsets inside a 128-row tile of A are 32-bit); otherwise SPEC_EINVAL.
  * ---------------------------------------------------------------------- */
 int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes);
 

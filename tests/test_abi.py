@@ -107,6 +107,7 @@ def test_large_validation(L):
     assert f(None, FAKE, spec.F64, 512, 512, FAKE, FAKE, b.value - 1, None) == EWORKSPACE
     assert f(None, FAKE, spec.F64, 512, 512, FAKE, None, b.value, None) == EWORKSPACE
     assert f(None, FAKE, spec.F64, 512, 500, FAKE, FAKE, b.value, None) == EINVAL
+    assert f(None, FAKE, spec.F64, 512, 1 << 22, FAKE, FAKE, b.value, None) == EINVAL  # lda too large
 
 
 def test_descriptors_validation(L):

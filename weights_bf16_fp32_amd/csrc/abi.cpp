@@ -101,7 +101,7 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
     size_t need = 0;
     int st = spec_eigvalsh_large_workspace(n, t, &need);
     if (st != SPEC_OK) return st;
-    if (A == nullptr || w == nullptr || lda < n) return SPEC_EINVAL;
+    if (A == nullptr || w == nullptr || lda < n || lda >= ((int64_t)1 << 22)) return SPEC_EINVAL;
     if (!aligned(A, 16) || !aligned(w, elt_size(t)) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
     if (ws == nullptr || ws_bytes < need) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;

@@ -940,22 +940,54 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
     const int i0 = ti * S2_T, j0 = tj * S2_T;
     const bool diag = ti == tj;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // L = [V | Z] rows i0.., R = [Z | V] rows j0..
-#pragma unroll
-    for (int q = 0; q < S2_T * NB / 256; ++q) {
-        const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
-        const int i = i0 + r, j = j0 + r;
-        const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
-        const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
-        Ls[r * (S2_K + 1) + c] = vi;
-        Ls[r * (S2_K + 1) + NB + c] = zi;
-        Rs[r * (S2_K + 1) + c] = zj;
-        Rs[r * (S2_K + 1) + NB + c] = vj;
-    }
-    __syncthreads();
     const int wm = wave >> 1, wn = wave & 1;
-    if (diag && wm == 0 && wn == 1) return;
+    const bool live = !(diag && wm == 0 && wn == 1);  // the strictly upper quadrant of a diagonal tile
     if constexpr (sizeof(T) == 4) {
+        // The tile through a buffer resource that starts at A[i0][j0] and ends
+        // after A[m-1][m-1]: rows past m read as zero and take no stores, and a
+        // masked element gets an offset past every resource.  Offsets inside
+        // the tile are 32-bit (lda < 2^22), one VGPR per element instead of a
+        // 64-bit address, so two workgroups fit a CU.
+        const int64_t corner = (int64_t)i0 * lda + j0;
+        const int64_t span = ((int64_t)(m - 1) * lda + (m - 1) - corner + 1) * 4;  // > 0: the tile starts above m
+        const int64_t extent = ((int64_t)(S2_T - 1) * lda + S2_T) * 4;               // the whole tile, < 2^31
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(A + corner, 0, (int)(span < extent ? span : extent), 0x00020000);
+        const int rl = wm * 64 + (lane >> 5) * 4, cl = wn * 64 + (lane & 31);  // lane's first row and column
+        const uint32_t vbase = (uint32_t)(rl * (int)lda + cl) * 4u;
+        // element (qa, qb, e): row rl + qa*32 + (e>>2)*8 + (e&3), column cl + qb*32
+        auto eoff = [&](int qa, int qb, int e) {
+            const int dr = qa * 32 + (e >> 2) * 8 + (e & 3);
+            const bool ok = !diag || rl + dr >= cl + qb * 32;
+            return ok ? vbase + (uint32_t)(dr * (int)lda + qb * 32) * 4u : 0x80000000u;
+        };
+        // the old values are requested first: their loads are in flight while
+        // the panel blocks are staged and the MFMAs run
+        float old[2][2][16];
+        if (live) {
+#pragma unroll
+            for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        old[qa][qb][e] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)eoff(qa, qb, e), 0, 0));
+        }
+        // L = [V | Z] rows i0.., R = [Z | V] rows j0..
+#pragma unroll
+        for (int q = 0; q < S2_T * NB / 256; ++q) {
+            const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
+            const int i = i0 + r, j = j0 + r;
+            const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
+            const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
+            Ls[r * (S2_K + 1) + c] = vi;
+            Ls[r * (S2_K + 1) + NB + c] = zi;
+            Rs[r * (S2_K + 1) + c] = zj;
+            Rs[r * (S2_K + 1) + NB + c] = vj;
+        }
+        __syncthreads();
+        if (!live) return;
         f32x16_t acc[2][2] = {};
 #pragma unroll 4
         for (int kk = 0; kk < S2_K; kk += 2) {
@@ -971,31 +1003,29 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
                 for (int qb = 0; qb < 2; ++qb)
                     acc[qa][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
         }
-        // all old values are loaded before the first store
-        float old[2][2][16];
 #pragma unroll
         for (int qa = 0; qa < 2; ++qa)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int j = j0 + wn * 64 + qb * 32 + (lane & 31);
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int i = i0 + wm * 64 + qa * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                    old[qa][qb][e] = i < m && j < m && i >= j ? A[(int64_t)i * lda + j] : 0.f;
-                }
-            }
-#pragma unroll
-        for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int j = j0 + wn * 64 + qb * 32 + (lane & 31);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int i = i0 + wm * 64 + qa * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                    if (i < m && j < m && i >= j) A[(int64_t)i * lda + j] = old[qa][qb][e] - acc[qa][qb][e];
-                }
-            }
+                for (int e = 0; e < 16; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, old[qa][qb][e] - acc[qa][qb][e]), rs, (int)eoff(qa, qb, e), 0, 0);
     } else {
+        // L = [V | Z] rows i0.., R = [Z | V] rows j0..
+#pragma unroll
+        for (int q = 0; q < S2_T * NB / 256; ++q) {
+            const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
+            const int i = i0 + r, j = j0 + r;
+            const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
+            const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
+            Ls[r * (S2_K + 1) + c] = vi;
+            Ls[r * (S2_K + 1) + NB + c] = zi;
+            Rs[r * (S2_K + 1) + c] = zj;
+            Rs[r * (S2_K + 1) + NB + c] = vj;
+        }
+        __syncthreads();
+        if (!live) return;
         f64x4_t acc[4][4] = {};
         for (int kk = 0; kk < S2_K; kk += 4) {
             double a[4], b[4];
@@ -1010,6 +1040,7 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
                 for (int qb = 0; qb < 4; ++qb)
                     acc[qa][qb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
         }
+        // every old value is loaded before the first store
         double old[4][4][4];
 #pragma unroll
         for (int qa = 0; qa < 4; ++qa)
