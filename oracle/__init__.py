@@ -24,6 +24,11 @@ What it computes, each function citing the passage it follows:
   eigengap, MP edge and outlier count, W1 distance to MP (RMT page, section
   2.3), top-20 % energy share, tail level and small-sigma count (S3 page,
   sections 1 and 2).
+* :func:`smooth_descriptors` exponential smoothing of descriptor time series
+  (RMT page, section 3.2).
+* :func:`robust_stats`    median and winsorised sigma^2 estimates, MAD outlier
+  count (RMT page, section 4.2), log-eigenvalue mean and spread (section 3.2)
+  and the KL form of the MP deviation over a histogram (section 2.3).
 
 All arithmetic is fp64.  bf16 inputs arrive as uint16 bit patterns and are
 widened exactly.
@@ -367,3 +372,124 @@ def descriptors(w, *, mode: int = EIG, n_samples: int = 1, p_dim: int = 1, k: in
     out["sigma1"] = float(sig[0])
     out["n_small"] = int(np.sum(sig < small_rel * sig[0]))
     return out
+
+
+# ---------------------------------------------------------------- descriptor post-processing
+
+SIGMA2_WINSOR = 3
+#: the fp64 fields of a descriptor record, smoothed as time series
+SMOOTH_FIELDS = ["S", "H", "erank", "m1", "gk", "g1", "sigma2", "lambda_plus", "mp_w1",
+                 "top_energy", "top_sigma_share", "tail_head", "tail_min", "sigma1"]
+FLAG_HELD = 8
+
+
+def smooth_series(x, alpha: float) -> np.ndarray:
+    """Exponential smoothing of one descriptor time series ("Random matrix
+    theory spectral methods" page, section 3.2: the descriptor series are
+    exponentially smoothed): y_0 = x_0, y_t = alpha x_t + (1 - alpha) y_{t-1}.
+
+    Reading (the page gives no rule for gaps): a non-finite x_t leaves the state
+    as it was (y_t = y_{t-1}); before the first finite value y_t is NaN."""
+    y = np.empty(len(x), dtype=np.float64)
+    state, have = float("nan"), False
+    for t, v in enumerate(x):
+        v = float(v)
+        if math.isfinite(v):
+            state = v if not have else alpha * v + (1.0 - alpha) * state
+            have = True
+        y[t] = state if have else float("nan")
+    return y
+
+
+def smooth_descriptors(rec: np.ndarray, alpha: float) -> np.ndarray:
+    """rec: structured records [streams, W] with the fields of a descriptor
+    record.  Every field in SMOOTH_FIELDS is smoothed along W (smooth_series);
+    counts are copied; flags gain FLAG_HELD where a record has a non-finite
+    smoothed field."""
+    out = rec.copy()
+    for s in range(rec.shape[0]):
+        held = np.zeros(rec.shape[1], dtype=bool)
+        for f in SMOOTH_FIELDS:
+            out[f][s] = smooth_series(rec[f][s], alpha)
+            held |= ~np.isfinite(rec[f][s].astype(np.float64))
+        out["flags"][s] = rec["flags"][s] | np.where(held, FLAG_HELD, 0)
+    return out
+
+
+def mp_bin_masses(sigma2: float, c: float, bins: int) -> np.ndarray:
+    """MP probability of each of `bins` equal-width bins of [lambda_-, lambda_+]
+    (differences of mp_cdf at the bin edges)."""
+    lm, lp = mp_edges(sigma2, c)
+    edges = [lm + (lp - lm) * b / bins for b in range(bins + 1)]
+    F = [0.0] + [mp_cdf(x, sigma2, c) for x in edges[1:-1]] + [1.0]
+    return np.diff(np.asarray(F, dtype=np.float64))
+
+
+def robust_stats(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma2_mode: int = SIGMA2_GIVEN,
+                 winsor_frac: float = 0.05, mad_k: float = 3.0, bins: int = 16) -> dict:
+    """Robust and log-domain statistics of one spectrum (negative round-off
+    clamped to 0):
+
+    * median, and sigma2_winsor = (sum of the winsorised spectrum) / p: the q =
+      floor(winsor_frac r) largest values set to the (q+1)-th largest and the q
+      smallest to the (q+1)-th smallest (q <= (r-1)/2), the MEAN estimate of
+      sigma^2 made robust to extreme eigenvalues; mad = median |lambda - median|
+      and n_mad = #{|lambda - median| > mad_k * 1.4826 * mad} (outliers by the
+      median absolute deviation, 1.4826 its normal-consistency factor) -- RMT
+      page, section 4.2 (median rather than mean for sigma^2, winsorised
+      extremes, MAD anomaly detection)
+    * log_mean, log_std: mean and (population) standard deviation of ln lambda
+      over the positive eigenvalues -- section 3.2 (log transform of the
+      eigenvalues)
+    * kl_mp = sum_b p_b ln(p_b / q_b): KL divergence of the spectrum's histogram
+      over `bins` equal-width bins of [lambda_-, lambda_+] (values outside
+      counted in the end bins) from the MP bin masses q_b -- section 2.3 (KL form
+      of the MP deviation); sigma^2 by sigma2_mode (GIVEN, MEDIAN, MEAN = S/p,
+      WINSOR = sigma2_winsor) and the companion form for p > n as in mp_w1.
+    Undefined values are NaN (flags: 1 non-finite input, 4 no positive value)."""
+    raw = np.asarray(w, dtype=np.float64)
+    flags = 0 if np.all(np.isfinite(raw)) else 1
+    lam = np.sort(np.maximum(raw, 0.0))[::-1]
+    r = lam.size
+    med = float(np.median(lam))
+    asc = lam[::-1]
+    q = min(int(math.floor(winsor_frac * r)), (r - 1) // 2)
+    wz = np.clip(asc, asc[q], asc[r - 1 - q])
+    s2w = float(np.sum(wz)) / p_dim
+    dev = np.abs(lam - med)
+    mad = float(np.median(dev))
+    n_mad = int(np.sum(dev > mad_k * 1.4826 * mad))
+    pos = lam[lam > 0]
+    if pos.size:
+        lg = np.log(pos)
+        log_mean = float(np.mean(lg))
+        log_std = float(math.sqrt(np.mean((lg - log_mean) ** 2)))
+    else:
+        log_mean = log_std = float("nan")
+        flags |= 4
+    S = float(np.sum(lam))
+    if sigma2_mode == SIGMA2_MEDIAN:
+        s2 = med
+    elif sigma2_mode == SIGMA2_MEAN:
+        s2 = S / p_dim
+    elif sigma2_mode == SIGMA2_WINSOR:
+        s2 = s2w
+    else:
+        s2 = float(sigma2)
+    kl = float("nan")
+    if s2 > 0 and flags & 1 == 0:
+        if p_dim <= n_samples:
+            mu, cc = lam, p_dim / n_samples
+        else:
+            mu, cc = (n_samples / p_dim) * lam, n_samples / p_dim
+        lm, lp = mp_edges(s2, cc)
+        qb = mp_bin_masses(s2, cc, bins)
+        cnt = np.zeros(bins, dtype=np.int64)
+        for v in mu:
+            b = int(math.floor((v - lm) / (lp - lm) * bins))
+            cnt[min(max(b, 0), bins - 1)] += 1
+        pb = cnt / r
+        nz = pb > 0
+        kl = float(np.sum(pb[nz] * np.log(pb[nz] / qb[nz])))
+    return {"median": med, "sigma2_winsor": s2w, "mad": mad, "log_mean": log_mean, "log_std": log_std,
+            "sigma2": s2, "kl_mp": kl, "n_mad": n_mad, "flags": flags}

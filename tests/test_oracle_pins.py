@@ -307,3 +307,98 @@ def test_jacobi_reports_non_convergence():
     A = _sym(rng, 30)
     w, sweeps = oracle.eigvalsh_small(A, max_sweeps=1)
     assert sweeps < 0
+
+
+# ------------------------------------------------------------- descriptor post-processing
+
+def test_smooth_closed_forms():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(40)
+    assert np.array_equal(oracle.smooth_series(x, 1.0), x)  # alpha = 1: no smoothing
+    assert np.allclose(oracle.smooth_series(np.full(30, 2.5), 0.3), 2.5, rtol=0, atol=1e-15)
+    # step response from 0: y_t = 1 - (1 - a)^t
+    a = 0.25
+    y = oracle.smooth_series(np.r_[0.0, np.ones(20)], a)
+    assert np.allclose(y[1:], 1.0 - (1.0 - a) ** np.arange(1, 21), rtol=0, atol=1e-15)
+    # impulse after a zero start: y_t = a (1 - a)^(t - 1)
+    y = oracle.smooth_series(np.r_[0.0, 1.0, np.zeros(10)], a)
+    assert np.allclose(y[1:], a * (1.0 - a) ** np.arange(11), rtol=0, atol=1e-15)
+    # linear in the series
+    z = rng.standard_normal(40)
+    assert np.allclose(oracle.smooth_series(2 * x - 3 * z, a),
+                       2 * oracle.smooth_series(x, a) - 3 * oracle.smooth_series(z, a), atol=1e-13)
+    # gaps: a non-finite value holds the state; NaN until the first finite value
+    y = oracle.smooth_series([np.nan, 4.0, np.inf, 8.0], 0.5)
+    assert np.isnan(y[0]) and y[1] == 4.0 and y[2] == 4.0 and y[3] == 6.0
+
+
+def test_robust_stats_by_hand():
+    # lambda = 9, 4, 3, 2, 1: median 3; |lambda - 3| = 6, 1, 0, 1, 2 -> MAD 1; with
+    # k = 3 the cut is 4.4478, so one outlier; winsorising one value at each end
+    # gives 4, 4, 3, 2, 2 (sum 15); ln: 0, ln 2, ln 3, ln 4, ln 9
+    r = oracle.robust_stats([9, 4, 3, 2, 1], n_samples=10, p_dim=5, winsor_frac=0.2, mad_k=3.0)
+    assert r["median"] == 3.0 and r["mad"] == 1.0 and r["n_mad"] == 1
+    assert r["sigma2_winsor"] == 15.0 / 5
+    lg = np.log([9.0, 4.0, 3.0, 2.0, 1.0])
+    assert abs(r["log_mean"] - math.log(216.0) / 5) <= 1e-15
+    assert abs(r["log_std"] - math.sqrt(np.mean((lg - lg.mean()) ** 2))) <= 1e-15
+    # even count: the median is the mean of the two middle values
+    r = oracle.robust_stats([10, 6, 2, 0], n_samples=8, p_dim=4)
+    assert r["median"] == 4.0 and r["mad"] == 3.0  # deviations 6, 2, 2, 4, sorted 2, 2, 4, 6
+    # no winsorising: the MEAN estimate S / p
+    lam = np.random.default_rng(2).uniform(0, 3, 101)
+    r = oracle.robust_stats(lam, n_samples=400, p_dim=101, winsor_frac=0.0)
+    assert abs(r["sigma2_winsor"] - lam.sum() / 101) <= 1e-14 * lam.sum()
+    # all zero: no positive value, no MP reference
+    r = oracle.robust_stats(np.zeros(6), n_samples=10, p_dim=6, sigma2_mode=oracle.SIGMA2_MEDIAN)
+    assert r["flags"] == 4 and math.isnan(r["log_mean"]) and math.isnan(r["kl_mp"])
+
+
+def test_mad_normal_consistency():
+    # 1.4826 MAD estimates the standard deviation of a normal sample
+    x = 12.0 + 2.0 * np.random.default_rng(4).standard_normal(200001)
+    assert x.min() > 0  # the clamp to zero is a no-op
+    r = oracle.robust_stats(x, n_samples=10 ** 6, p_dim=x.size)
+    assert abs(1.4826 * r["mad"] - 2.0) < 0.02
+    # and about 0.27 % of a normal sample lies beyond 3 of them
+    assert abs(r["n_mad"] / x.size - 0.0027) < 0.0006
+
+
+@pytest.mark.parametrize("c", [0.1, 0.5, 1.0])
+def test_mp_bin_masses_by_quadrature(c):
+    lm, lp = oracle.mp_edges(1.7, c)
+    q = oracle.mp_bin_masses(1.7, c, 12)
+    assert abs(q.sum() - 1.0) <= 1e-12
+    edges = np.linspace(lm, lp, 13)
+    for b in range(12):
+        ref, _ = scipy.integrate.quad(lambda x: float(oracle.mp_density(np.array([x]), 1.7, c)[0]),
+                                      edges[b], edges[b + 1], limit=200)
+        assert abs(q[b] - ref) <= 1e-7, (b, q[b], ref)
+
+
+def test_kl_pins():
+    s2, n, p, B = 1.0, 1000, 250, 10  # c = 0.25
+    lm, lp = oracle.mp_edges(s2, p / n)
+    q = oracle.mp_bin_masses(s2, p / n, B)
+    # every value in one bin: KL = -ln q_b
+    for b in (0, 4, 9):
+        v = lm + (lp - lm) * (b + 0.5) / B
+        r = oracle.robust_stats(np.full(p, v), n_samples=n, p_dim=p, bins=B)
+        assert abs(r["kl_mp"] + math.log(q[b])) <= 1e-12
+    # values outside the support count in the end bins
+    r = oracle.robust_stats([2 * lp, 0.5 * lm], n_samples=n, p_dim=p, bins=B)
+    assert abs(r["kl_mp"] - (0.5 * math.log(0.5 / q[-1]) + 0.5 * math.log(0.5 / q[0]))) <= 1e-12
+    # the MP quantiles themselves: the histogram matches the bin masses to 1/r
+    rr = 20000
+    mu = oracle.mp_quantiles(s2, 0.5, rr)
+    r = oracle.robust_stats(mu, n_samples=2 * rr, p_dim=rr, bins=B)
+    assert 0.0 <= r["kl_mp"] < 1e-6
+    # non-negative on arbitrary spectra; the companion form for p > n scales by n / p
+    rng = np.random.default_rng(9)
+    for _ in range(5):
+        lam = rng.uniform(0, 4, 64)
+        assert oracle.robust_stats(lam, n_samples=100, p_dim=64, bins=8)["kl_mp"] >= 0.0
+    lam = rng.uniform(0, 40, 30)
+    a = oracle.robust_stats(lam, n_samples=30, p_dim=300, bins=8)["kl_mp"]
+    b = oracle.robust_stats(lam * 0.1, n_samples=300, p_dim=30, bins=8)["kl_mp"]
+    assert abs(a - b) <= 1e-12
