@@ -208,6 +208,45 @@ def main():
     roof = dict(rows[dominant])
     roof["kernel"] = dominant
 
+    # descriptor post-processing (a row beyond the hot path, timed on its own):
+    # smoothing of the window descriptor series, robust / log / KL statistics of
+    # the window spectra and of the 4096 spectrum
+    sm_out = torch.empty_like(desc_win)
+    rb_win = torch.empty((S * W, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+    rb_big = torch.empty((1, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+    post = {
+        "desc_smooth": lambda: spec.desc_smooth(desc_win, streams=S, W=W, alpha=0.2, out=sm_out, to_host=False),
+        "robust_windows": lambda: spec.spectrum_robust(w_win, n_samples=N, p_dim=ET["d"],
+                                                       sigma2_mode=spec.SIGMA2_MEDIAN, bins=8, out=rb_win,
+                                                       to_host=False),
+        "robust_4096": lambda: spec.spectrum_robust(w_big, n_samples=n_total, p_dim=d,
+                                                    sigma2_mode=spec.SIGMA2_WINSOR, bins=32, out=rb_big,
+                                                    to_host=False),
+    }
+    post_ms = {}
+    for name, fn in post.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        post_ms[name] = e0.elapsed_time(e1) / 10
+    smooth_bytes = 2 * S * W * spec.DESC_DTYPE.itemsize
+    robust_bytes = S * W * (N * 4 + spec.ROBUST_DTYPE.itemsize)
+    post_rows = {
+        "desc_smooth": {"ms": post_ms["desc_smooth"], "records": S * W, "bound": "hbm",
+                        "achieved_GBs": smooth_bytes / (post_ms["desc_smooth"] / 1e3) / 1e9},
+        "robust_windows": {"ms": post_ms["robust_windows"], "spectra": S * W, "bound": "hbm",
+                           "achieved_GBs": robust_bytes / (post_ms["robust_windows"] / 1e3) / 1e9},
+        "robust_4096": {"ms": post_ms["robust_4096"], "spectra": 1},
+    }
+    for r in post_rows.values():
+        if "achieved_GBs" in r:
+            r["frac"] = r["achieved_GBs"] * 1e9 / PEAK_HBM
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
@@ -228,6 +267,7 @@ def main():
         "window_mean_bisection_rounds": mean_rounds,
         "roofline": roof,
         "roofline_all": rows,
+        "postproc": post_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -220,6 +220,68 @@ int spec_descriptors_workspace(int64_t r, size_t *bytes);
 int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                      const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------------------
+ * Post-processing of descriptor series and spectra ("Random matrix theory
+ * spectral methods" page, sections 3.2 and 4.2; section 2.3 for the KL form).
+ *
+ * spec_desc_smooth: exponential smoothing of descriptor time series.
+ *   in, out: device spec_desc records [streams][W] (window index fastest;
+ *   out must not overlap in).  Each of the 14 fp64 fields (S .. sigma1) is
+ *   smoothed along W: y_0 = x_0, y_t = alpha x_t + (1 - alpha) y_{t-1}.  A
+ *   non-finite x_t leaves the state unchanged and sets SPEC_FLAG_HELD in that
+ *   record's flags; until the first finite value the output is NaN.  Counts
+ *   (n_above, n_small, r_pos) are copied.
+ *   Requires 0 < alpha <= 1, streams >= 0, W >= 1; else SPEC_EINVAL.
+ *
+ * spec_spectrum_robust: per spectrum (w[b*ldw + i], i < r, sorted DESCENDING,
+ *   negative values clamped to 0; wt = SPEC_F32 or SPEC_F64), in fp64:
+ *     median         the median of the r values
+ *     sigma2_winsor  sum of the spectrum winsorised at q = floor(winsor_frac r)
+ *                    values per end (q <= (r-1)/2), divided by p_dim: the
+ *                    trace estimate of sigma^2 with extreme eigenvalues clipped
+ *     mad            median |lambda - median|;  n_mad = #{|lambda - median| >
+ *                    mad_k * 1.4826 * mad} (MAD outlier count)
+ *     log_mean, log_std  mean and population standard deviation of ln lambda
+ *                    over the positive values (log transform)
+ *     sigma2         the sigma^2 of the MP reference: sigma2_mode GIVEN, MEDIAN,
+ *                    MEAN (sum / p_dim) or WINSOR (sigma2_winsor)
+ *     kl_mp          sum_b p_b ln(p_b / q_b) over `bins` equal-width bins of the
+ *                    MP support [lambda_-, lambda_+] of that sigma^2 and ratio c
+ *                    = p/n (if p_dim > n_samples: mu = (n/p) lambda and ratio n/p,
+ *                    as for mp_w1); values outside the support count in the end
+ *                    bins; p_b the fraction of values in bin b, q_b its MP mass
+ *   flags: SPEC_FLAG_NONFINITE (a NaN or Inf value: median, sigma2_winsor, mad,
+ *   kl_mp and a sigma2 not GIVEN are NaN; the log statistics use the finite
+ *   values), SPEC_FLAG_S_ZERO (no finite positive value: log statistics NaN);
+ *   kl_mp is NaN when sigma2 <= 0.
+ *   out: device array of `batch` spec_robust records.
+ *   Requires r >= 2, ldw >= r, 1 <= bins <= 64, 0 <= winsor_frac <= 0.5,
+ *   mad_k > 0, n_samples, p_dim >= 1, sigma2_mode in 0..3 and sigma2 > 0 when
+ *   it is GIVEN; else SPEC_EINVAL (SPEC_EUNSUPPORTED for other wt).
+ * ---------------------------------------------------------------------- */
+enum { SPEC_SIGMA2_WINSOR = 3 };
+enum { SPEC_FLAG_HELD = 8 }; /* spec_desc_smooth: a non-finite field was held */
+
+typedef struct {
+    int32_t sigma2_mode; /* SPEC_SIGMA2_GIVEN, _MEDIAN, _MEAN, _WINSOR */
+    int32_t bins;        /* histogram bins for kl_mp (1..64) */
+    double sigma2;       /* used when sigma2_mode == SPEC_SIGMA2_GIVEN */
+    int64_t n_samples;   /* n */
+    int64_t p_dim;       /* p */
+    double winsor_frac;  /* fraction clipped at each end, e.g. 0.05 */
+    double mad_k;        /* outlier cut in robust standard deviations, e.g. 3 */
+} spec_robust_params;
+
+typedef struct {
+    double median, sigma2_winsor, mad, log_mean, log_std, sigma2, kl_mp;
+    int64_t n_mad, flags;
+} spec_robust; /* 72 bytes */
+
+int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t W, double alpha, spec_desc *out);
+
+int spec_spectrum_robust(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                         const spec_robust_params *p, spec_robust *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,3 +123,24 @@ def test_descriptors_validation(L):
         assert f(None, FAKE, spec.F32, 1, 32, 32, ctypes.byref(q), FAKE, FAKE, 4096) == EINVAL, field
     assert f(None, FAKE, spec.BF16, 1, 32, 32, ctypes.byref(p), FAKE, FAKE, 4096) == EUNSUPPORTED
     assert f(None, FAKE, spec.F32, 1, 1, 1, ctypes.byref(p), FAKE, FAKE, 4096) == EINVAL
+
+
+def test_postproc_validation(L):
+    f = L.spec_desc_smooth
+    assert f(None, FAKE, 4, 10, 0.0, FAKE + 4096 * 144) == EINVAL  # alpha = 0
+    assert f(None, FAKE, 4, 10, 1.5, FAKE + 4096 * 144) == EINVAL  # alpha > 1
+    assert f(None, FAKE, 4, 0, 0.5, FAKE + 4096 * 144) == EINVAL   # W = 0
+    assert f(None, FAKE, 4, 10, 0.5, FAKE + 144) == EINVAL         # out overlaps in
+    assert f(None, None, 4, 10, 0.5, FAKE) == EINVAL
+    g = L.spec_spectrum_robust
+    ok = dict(sigma2_mode=0, bins=16, sigma2=1.0, n_samples=64, p_dim=32, winsor_frac=0.05, mad_k=3.0)
+    for field, val in [("bins", 0), ("bins", 65), ("winsor_frac", 0.6), ("winsor_frac", -0.1), ("mad_k", 0.0),
+                       ("sigma2_mode", 4), ("sigma2", 0.0), ("n_samples", 0), ("p_dim", 0)]:
+        kw = dict(ok)
+        kw[field] = val
+        p = spec.RobustParams(*[kw[k] for k, _ in spec.RobustParams._fields_])
+        assert g(None, FAKE, spec.F32, 1, 32, 32, ctypes.byref(p), FAKE) == EINVAL, field
+    p = spec.RobustParams(*[ok[k] for k, _ in spec.RobustParams._fields_])
+    assert g(None, FAKE, spec.BF16, 1, 32, 32, ctypes.byref(p), FAKE) == EUNSUPPORTED
+    assert g(None, FAKE, spec.F32, 1, 1, 1, ctypes.byref(p), FAKE) == EINVAL   # r < 2
+    assert g(None, FAKE, spec.F32, 1, 32, 31, ctypes.byref(p), FAKE) == EINVAL  # ldw < r

@@ -11,6 +11,8 @@ fallback of any kind.
     w, info = spec.eigvalsh_batched_band(band, n=30, scale=1/30)
     w = spec.eigvalsh_large(C)                                # destroys C
     rec = spec.descriptors(w, n_samples=n, p_dim=d, k=1)      # structured numpy array
+    sm = spec.desc_smooth(raw_records, streams=S, W=W, alpha=0.3)  # smoothed descriptor series
+    rb = spec.spectrum_robust(w, n_samples=n, p_dim=d)        # median/MAD/winsor/log/KL statistics
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import numpy as np
 __all__ = [
     "SpecError", "lib", "cov_accumulate", "gram_window", "eigvalsh_batched_dense",
     "eigvalsh_batched_band", "eigvalsh_large", "eigvalsh_large_workspace", "descriptors",
-    "descriptors_workspace", "DESC_DTYPE",
+    "descriptors_workspace", "DESC_DTYPE", "desc_smooth", "spectrum_robust", "ROBUST_DTYPE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,14 +34,17 @@ BF16, F32, F64 = 0, 1, 2
 GRAM_BAND, GRAM_DENSE = 0, 1
 SRC_DENSE, SRC_BAND = 0, 1
 MODE_EIG, MODE_SINGULAR = 0, 1
-SIGMA2_GIVEN, SIGMA2_MEDIAN, SIGMA2_MEAN = 0, 1, 2
-FLAG_NONFINITE, FLAG_GK_UNDEF, FLAG_S_ZERO = 1, 2, 4
+SIGMA2_GIVEN, SIGMA2_MEDIAN, SIGMA2_MEAN, SIGMA2_WINSOR = 0, 1, 2, 3
+FLAG_NONFINITE, FLAG_GK_UNDEF, FLAG_S_ZERO, FLAG_HELD = 1, 2, 4, 8
 
 _DESC_FIELDS_F = ["S", "H", "erank", "m1", "gk", "g1", "sigma2", "lambda_plus", "mp_w1",
                   "top_energy", "top_sigma_share", "tail_head", "tail_min", "sigma1"]
 _DESC_FIELDS_I = ["n_above", "n_small", "r_pos", "flags"]
 DESC_DTYPE = np.dtype([(f, "<f8") for f in _DESC_FIELDS_F] + [(f, "<i8") for f in _DESC_FIELDS_I])
 assert DESC_DTYPE.itemsize == 144
+_ROBUST_FIELDS_F = ["median", "sigma2_winsor", "mad", "log_mean", "log_std", "sigma2", "kl_mp"]
+ROBUST_DTYPE = np.dtype([(f, "<f8") for f in _ROBUST_FIELDS_F] + [("n_mad", "<i8"), ("flags", "<i8")])
+assert ROBUST_DTYPE.itemsize == 72
 
 
 class SpecError(RuntimeError):
@@ -61,9 +66,15 @@ class DescParams(ctypes.Structure):
                 ("tail_frac", ctypes.c_double)]
 
 
+class RobustParams(ctypes.Structure):
+    _fields_ = [("sigma2_mode", ctypes.c_int32), ("bins", ctypes.c_int32), ("sigma2", ctypes.c_double),
+                ("n_samples", ctypes.c_int64), ("p_dim", ctypes.c_int64), ("winsor_frac", ctypes.c_double),
+                ("mad_k", ctypes.c_double)]
+
+
 EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_window",
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
-           "spec_descriptors_workspace", "spec_descriptors"]
+           "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust"]
 
 _lib = None
 
@@ -89,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.spec_descriptors_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
         L.spec_descriptors.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp, vp,
                                        ctypes.c_size_t]
+        L.spec_desc_smooth.argtypes = [vp, vp, i64, i64, dbl, vp]
+        L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
         _lib = L
@@ -237,3 +250,39 @@ def descriptors(w, *, n_samples: int, p_dim: int, k: int = 1, mode: int = MODE_E
     if not to_host:
         return out
     return out.cpu().numpy().view(DESC_DTYPE).reshape(batch)
+
+
+def desc_smooth(rec, *, streams: int, W: int, alpha: float, out=None, to_host: bool = True):
+    """Exponential smoothing along W of the descriptor records rec (a device uint8
+    buffer of streams * W records, as descriptors(..., to_host=False) returns).
+    Returns a numpy structured array [streams, W] of DESC_DTYPE (or the device
+    buffer if to_host is False)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((streams * W, DESC_DTYPE.itemsize), dtype=torch.uint8, device=rec.device)
+    _check(lib().spec_desc_smooth(_stream(), _dev(rec), streams, W, float(alpha), _dev(out)))
+    if not to_host:
+        return out
+    return out.cpu().numpy().view(DESC_DTYPE).reshape(streams, W)
+
+
+def spectrum_robust(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma2_mode: int = SIGMA2_GIVEN,
+                    winsor_frac: float = 0.05, mad_k: float = 3.0, bins: int = 16, out=None,
+                    to_host: bool = True):
+    """Median, winsorised sigma^2, MAD and MAD outlier count, log-eigenvalue mean
+    and spread, and the KL form of the MP deviation of each row of w [batch, r]
+    (sorted descending).  Returns a numpy structured array of ROBUST_DTYPE (or
+    the device buffer if to_host is False)."""
+    torch = _torch()
+    if w.dim() == 1:
+        w = w.unsqueeze(0)
+    batch, r = w.shape
+    if out is None:
+        out = torch.empty((batch, ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=w.device)
+    p = RobustParams(int(sigma2_mode), int(bins), float(sigma2), int(n_samples), int(p_dim), float(winsor_frac),
+                     float(mad_k))
+    _check(lib().spec_spectrum_robust(_stream(), _dev(w), _dt(w), batch, r, w.stride(0), ctypes.byref(p),
+                                      _dev(out)))
+    if not to_host:
+        return out
+    return out.cpu().numpy().view(ROBUST_DTYPE).reshape(batch)

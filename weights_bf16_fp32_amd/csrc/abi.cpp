@@ -133,4 +133,30 @@ int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t
     return from_hip(launch_descriptors((hipStream_t)stream, w, wt, batch, r, ldw, p, out, ws));
 }
 
+int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t W, double alpha, spec_desc *out)
+{
+    if (in == nullptr || out == nullptr || streams < 0 || streams > ((int64_t)1 << 31) - 1 || W < 1) return SPEC_EINVAL;
+    if (!(alpha > 0.0 && alpha <= 1.0)) return SPEC_EINVAL;
+    if (!aligned(in, 8) || !aligned(out, 8)) return SPEC_EINVAL;
+    const char *a = (const char *)in, *b = (const char *)out;
+    const size_t bytes = (size_t)streams * (size_t)W * sizeof(spec_desc);
+    if (a < b + bytes && b < a + bytes) return SPEC_EINVAL;  // overlapping
+    return from_hip(launch_desc_smooth((hipStream_t)stream, in, streams, W, alpha, out));
+}
+
+int spec_spectrum_robust(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                         const spec_robust_params *p, spec_robust *out)
+{
+    if (w == nullptr || p == nullptr || out == nullptr) return SPEC_EINVAL;
+    if (wt != SPEC_F32 && wt != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if (batch < 0 || batch > ((int64_t)1 << 31) - 1 || r < 2 || ldw < r) return SPEC_EINVAL;
+    if (p->bins < 1 || p->bins > 64 || p->n_samples < 1 || p->p_dim < 1) return SPEC_EINVAL;
+    if (!(p->winsor_frac >= 0.0 && p->winsor_frac <= 0.5) || !(p->mad_k > 0.0 && isfinite(p->mad_k)))
+        return SPEC_EINVAL;
+    if (p->sigma2_mode < SPEC_SIGMA2_GIVEN || p->sigma2_mode > SPEC_SIGMA2_WINSOR) return SPEC_EINVAL;
+    if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
+    if (!aligned(w, elt_size(wt)) || !aligned(out, 8)) return SPEC_EINVAL;
+    return from_hip(launch_spectrum_robust((hipStream_t)stream, w, wt, batch, r, ldw, p, out));
+}
+
 }  // extern "C"

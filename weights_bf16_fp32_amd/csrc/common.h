@@ -179,3 +179,19 @@ SPEC_DEVICE void wave_sync()
         hipError_t e__ = hipGetLastError();                                  \
         if (e__ != hipSuccess) return e__;                                   \
     } while (0)
+
+// Marchenko-Pastur distribution function with sigma^2 = 1 and ratio 0 < c <= 1
+// in the angle phi of lambda = (1 + c) - 2 sqrt(c) cos(phi): the antiderivative
+// of h^2 sin^2(phi) / (2 pi c lambda(phi)), h = 2 sqrt c, with
+// kappa = (1 + sqrt c) / (1 - sqrt c) ("Random matrix theory spectral methods"
+// page, section 2.1, the MP density).  F(0) = 0, F(pi) = 1.
+__device__ inline double mp_cdf_phi(double phi, double c)
+{
+    const double sc = sqrt(c);
+    double third = 0.0;
+    if (c < 1.0) {
+        const double kappa = (1.0 + sc) / (1.0 - sc);
+        third = ((1.0 - c) / c) * atan2(kappa * sin(0.5 * phi), cos(0.5 * phi));
+    }
+    return (sin(phi) / sc + (1.0 + c) * phi / (2.0 * c) - third) / M_PI;
+}

@@ -21,21 +21,12 @@
 //   reduction.
 #include <float.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace {
-
-__device__ double mp_cdf_phi(double phi, double c)
-{
-    const double sc = sqrt(c);
-    double third = 0.0;
-    if (c < 1.0) {
-        const double kappa = (1.0 + sc) / (1.0 - sc);
-        third = ((1.0 - c) / c) * atan2(kappa * sin(0.5 * phi), cos(0.5 * phi));
-    }
-    return (sin(phi) / sc + (1.0 + c) * phi / (2.0 * c) - third) / M_PI;
-}
 
 __global__ void mp_table(double c, int64_t r, double *__restrict__ q)
 {
@@ -57,27 +48,19 @@ __global__ void mp_table(double c, int64_t r, double *__restrict__ q)
     q[i] = lminus + 4.0 * sc * s * s;  // = m - h cos(phi)
 }
 
-__device__ __forceinline__ double wsum(double x)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
+// sums over the wave, in every lane: DPP and row swaps, no LDS round trips;
+// counts (< 2^53) go through fp64 exactly
+__device__ __forceinline__ double wsum(double x) { return pair32_sum(half_sum(x)); }
 
-__device__ __forceinline__ int64_t wsum_i(int64_t x)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
+__device__ __forceinline__ int64_t wsum_i(int64_t x) { return (int64_t)pair32_sum(half_sum((double)x)); }
 
+// the descriptors of spectrum b, by one wave
 template <typename T>
-__global__ __launch_bounds__(64) void descriptors_kernel(const T *__restrict__ w, int64_t batch, int64_t r,
-                                                         int64_t ldw, spec_desc_params p,
-                                                         const double *__restrict__ qtab, spec_desc *__restrict__ out)
+__device__ __forceinline__ void desc_one(const T *__restrict__ w, int64_t b, int64_t r, int64_t ldw,
+                                         const spec_desc_params &p, const double *__restrict__ qtab,
+                                         spec_desc *__restrict__ out)
 {
-    const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const T *wb = w + b * ldw;
     auto lam = [&](int64_t i) -> double {
         double v = (double)wb[i];
@@ -182,6 +165,20 @@ __global__ __launch_bounds__(64) void descriptors_kernel(const T *__restrict__ w
     }
 }
 
+// four waves per workgroup, each taking spectra b = 4 g + wave, + 4 G, ...: a
+// workgroup per short spectrum would be limited by the dispatch rate
+constexpr int DW = 4;
+
+template <typename T>
+__global__ __launch_bounds__(64 * DW) void descriptors_kernel(const T *__restrict__ w, int64_t batch, int64_t r,
+                                                              int64_t ldw, spec_desc_params p,
+                                                              const double *__restrict__ qtab,
+                                                              spec_desc *__restrict__ out)
+{
+    for (int64_t b = (int64_t)blockIdx.x * DW + (threadIdx.x >> 6); b < batch; b += (int64_t)gridDim.x * DW)
+        desc_one<T>(w, b, r, ldw, p, qtab, out);
+}
+
 }  // namespace
 
 size_t descriptors_workspace_bytes(int64_t r) { return (size_t)((r + 31) / 32 * 32) * sizeof(double); }
@@ -196,11 +193,12 @@ hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (batch == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((batch + DW - 1) / DW, 8192);
     if (wt == SPEC_F32)
-        hipLaunchKernelGGL(descriptors_kernel<float>, dim3((unsigned)batch), dim3(64), 0, stream, (const float *)w,
+        hipLaunchKernelGGL(descriptors_kernel<float>, dim3(grid), dim3(64 * DW), 0, stream, (const float *)w,
                            batch, r, ldw, *p, q, out);
     else
-        hipLaunchKernelGGL(descriptors_kernel<double>, dim3((unsigned)batch), dim3(64), 0, stream, (const double *)w,
+        hipLaunchKernelGGL(descriptors_kernel<double>, dim3(grid), dim3(64 * DW), 0, stream, (const double *)w,
                            batch, r, ldw, *p, q, out);
     return hipGetLastError();
 }

@@ -29,3 +29,9 @@ size_t descriptors_workspace_bytes(int64_t r);
 
 hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                               const spec_desc_params *p, spec_desc *out, void *ws);
+
+hipError_t launch_desc_smooth(hipStream_t stream, const spec_desc *in, int64_t streams, int64_t W, double alpha,
+                              spec_desc *out);
+
+hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                                  const spec_robust_params *p, spec_robust *out);
