@@ -439,14 +439,15 @@ def robust_stats(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma2_m
       page, section 4.2 (median rather than mean for sigma^2, winsorised
       extremes, MAD anomaly detection)
     * log_mean, log_std: mean and (population) standard deviation of ln lambda
-      over the positive eigenvalues -- section 3.2 (log transform of the
+      over the finite positive eigenvalues -- section 3.2 (log transform of the
       eigenvalues)
     * kl_mp = sum_b p_b ln(p_b / q_b): KL divergence of the spectrum's histogram
       over `bins` equal-width bins of [lambda_-, lambda_+] (values outside
       counted in the end bins) from the MP bin masses q_b -- section 2.3 (KL form
       of the MP deviation); sigma^2 by sigma2_mode (GIVEN, MEDIAN, MEAN = S/p,
       WINSOR = sigma2_winsor) and the companion form for p > n as in mp_w1.
-    Undefined values are NaN (flags: 1 non-finite input, 4 no positive value)."""
+    Undefined values are NaN (flags: 1 non-finite input, which makes every
+    order statistic, sum and sigma^2 estimate NaN; 4 no finite positive value)."""
     raw = np.asarray(w, dtype=np.float64)
     flags = 0 if np.all(np.isfinite(raw)) else 1
     lam = np.sort(np.maximum(raw, 0.0))[::-1]
@@ -459,7 +460,7 @@ def robust_stats(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma2_m
     dev = np.abs(lam - med)
     mad = float(np.median(dev))
     n_mad = int(np.sum(dev > mad_k * 1.4826 * mad))
-    pos = lam[lam > 0]
+    pos = lam[(lam > 0) & np.isfinite(lam)]
     if pos.size:
         lg = np.log(pos)
         log_mean = float(np.mean(lg))
