@@ -208,6 +208,163 @@ __global__ __launch_bounds__(64) void small_eig_batched(spec_batch_src src, int6
     if (info != nullptr && lane == 0) info[b] = it;
 }
 
+// Two matrices per wave for n <= 32: half h = lane / 32 takes matrix 2 g + h
+// and lane i = lane % 32 its row i.  Every sum is a half-wave butterfly, the
+// broadcasts go through per-half LDS rows, and each lane finds its own
+// eigenvalue, counting at both interior points of its interval in one pass
+// (two independent Sturm recurrences).  The arithmetic is that of
+// small_eig_batched, value for value.
+__global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t batch, int n,
+                                                     float *__restrict__ w, int32_t *__restrict__ info)
+{
+    constexpr int NM = 32;
+    __shared__ __attribute__((aligned(16))) float vs[2][NM];
+    __shared__ __attribute__((aligned(16))) float wsh[2][NM];
+    __shared__ __attribute__((aligned(16))) float dsh[2][NM + 1];
+    const int lane = threadIdx.x, h = lane >> 5, i = lane & 31;
+    const int64_t b = 2 * (int64_t)blockIdx.x + h;
+    const bool live = b < batch;
+    const bool rowok = live && i < n;
+
+    float a[NM];
+    if (src.kind == SPEC_SRC_DENSE) {
+        const float *base = src.a + (live ? b : 0) * src.stride_a;
+#pragma unroll
+        for (int j = 0; j < NM; ++j)
+            a[j] = rowok && j < n ? base[(int64_t)max(i, j) * src.lda + min(i, j)] : 0.f;
+    } else {
+        const int64_t W = (src.T - n) / src.stride + 1;
+        const int64_t bb = live ? b : 0;
+        const int64_t s = bb / W, win = bb % W;
+        const float *base = src.a + (s * src.T + win * src.stride) * n;
+#pragma unroll
+        for (int j = 0; j < NM; ++j)
+            a[j] = rowok && j < n ? src.scale * base[(int64_t)max(i, j) * n + abs(i - j)] : 0.f;
+    }
+    bool fin = true;
+#pragma unroll
+    for (int j = 0; j < NM; ++j) fin = fin && isfinite(a[j]);
+    const uint64_t badm = __ballot(!fin);
+    const bool bad = (h ? (badm >> 32) : (badm & 0xffffffffull)) != 0;
+    if (bad) {  // this half reports NaN; its lanes go on with zeros
+#pragma unroll
+        for (int j = 0; j < NM; ++j) a[j] = 0.f;
+    }
+
+    // ---- Householder tridiagonalisation, the two halves side by side
+    float e[NM];
+    static_for<0, NM - 2>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        if (k < n - 2) {
+            const float x = a[k];  // A[i][k]
+            const float sig = half_sum(i > k + 1 ? x * x : 0.f);
+            const float x0 = half_sum(i == k + 1 ? x : 0.f);
+            const bool go = sig > 0.f;
+            const float mu = go ? sqrtf(x0 * x0 + sig) : x0;
+            const float v0 = go ? (x0 <= 0.f ? x0 - mu : -sig / (x0 + mu)) : 1.f;
+            const float vi = go ? (i == k + 1 ? 1.f : (i > k + 1 ? x / v0 : 0.f)) : 0.f;
+            const float vv = half_sum(i > k + 1 ? vi * vi : 0.f);
+            const float tau = go ? 2.f / (1.f + vv) : 0.f;
+            e[k] = mu;
+            wave_sync();
+            vs[h][i] = vi;
+            wave_sync();
+            float p = 0.f;
+#pragma unroll
+            for (int j = k + 1; j < NM; ++j) p += a[j] * vs[h][j];
+            p *= tau;
+            const float pv = half_sum(i > k ? p * vi : 0.f);
+            const float wi = p - 0.5f * tau * pv * vi;
+            wsh[h][i] = wi;
+            wave_sync();
+            if (i > k) {
+#pragma unroll
+                for (int j = k + 1; j < NM; ++j) a[j] -= vi * wsh[h][j] + wi * vs[h][j];
+            }
+        }
+    });
+    // the diagonal and the last subdiagonal entry through LDS
+    {
+        float diag = 0.f;
+#pragma unroll
+        for (int j = 0; j < NM; ++j) diag = i == j ? a[j] : diag;
+        float last = 0.f;
+#pragma unroll
+        for (int j = 0; j < NM; ++j) last = j == n - 2 ? a[j] : last;
+        wave_sync();
+        dsh[h][i] = diag;
+        if (n >= 2 && i == n - 1) dsh[h][NM] = last;
+        wave_sync();
+    }
+    float d[NM], e2[NM];
+    const float elast = n >= 2 ? dsh[h][NM] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+        d[k] = k < n ? dsh[h][k] : FLT_MAX;
+        if (k + 1 < NM) {
+            if (k == n - 2) e[k] = elast;
+            e2[k] = k + 1 < n ? e[k] * e[k] : 0.f;
+        }
+    }
+    // Gershgorin interval and pivot guard
+    float lo = FLT_MAX, hi = -FLT_MAX, emax = 0.f;
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+        if (k < n) {
+            float r = 0.f;
+            if (k > 0) r += fabsf(e[k - 1]);
+            if (k + 1 < NM && k + 1 < n) {
+                r += fabsf(e[k]);
+                emax = fmaxf(emax, e2[k]);
+            }
+            lo = fminf(lo, d[k] - r);
+            hi = fmaxf(hi, d[k] + r);
+        }
+    }
+    const float span = fmaxf(fabsf(lo), fabsf(hi));
+    lo -= 4.f * FLT_EPSILON * span;
+    hi += 4.f * FLT_EPSILON * span;
+    const float pivmin = FLT_MIN * fmaxf(1.f, emax);
+    const float atol = 0.0625f * FLT_EPSILON * span;
+
+    // ---- eigenvalue l = i (descending), ascending index n - 1 - l: trisection,
+    // the counts below both interior points in one pass
+    const int l = i;
+    const int target = n - 1 - min(l, n - 1);
+    float lo_l = lo, hi_l = hi;
+    int it = 0;
+    for (; it < 64; ++it) {
+        const float width = hi_l - lo_l;
+        const bool done = width <= fmaxf(atol, 2.f * FLT_EPSILON * fmaxf(fabsf(lo_l), fabsf(hi_l)));
+        if (__all(done || l >= n || !live)) break;
+        const float x1 = lo_l + width * (1.f / 3.f), x2 = lo_l + width * (2.f / 3.f);
+        int c1 = 0, c2 = 0;
+        float q1 = 1.f, q2 = 1.f;
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            const float ek = k > 0 ? e2[k - 1] : 0.f;
+            q1 = (d[k] - x1) - ek * __builtin_amdgcn_rcpf(q1);
+            q2 = (d[k] - x2) - ek * __builtin_amdgcn_rcpf(q2);
+            q1 = fabsf(q1) < pivmin ? -pivmin : q1;
+            q2 = fabsf(q2) < pivmin ? -pivmin : q2;
+            c1 += q1 < 0.f;
+            c2 += q2 < 0.f;
+        }
+        if (!done) {
+            if (c1 > target) {
+                hi_l = x1;
+            } else if (c2 > target) {
+                lo_l = x1;
+                hi_l = x2;
+            } else {
+                lo_l = x2;
+            }
+        }
+    }
+    if (live && l < n) w[b * n + l] = bad ? __int_as_float(0x7fc00000) : 0.5f * (lo_l + hi_l);
+    if (live && info != nullptr && i == 0) info[b] = bad ? -1 : it;
+}
+
 }  // namespace
 
 hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
@@ -215,7 +372,8 @@ hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src
 {
     if (batch == 0) return hipSuccess;
     if (n <= 32)
-        hipLaunchKernelGGL(small_eig_batched<32>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, info);
+        hipLaunchKernelGGL(small_eig_pair, dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src, batch, n, w,
+                           info);
     else
         hipLaunchKernelGGL(small_eig_batched<64>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, info);
     return hipGetLastError();
