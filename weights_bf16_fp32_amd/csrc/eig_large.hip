@@ -511,50 +511,93 @@ __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, con
                                                  const T *__restrict__ Vtop, const T *__restrict__ Ktop, int m,
                                                  int per, T *__restrict__ Q1)
 {
-    __shared__ T Vt[NB * NB], Tb[NB * NB], Qb[NB * NB], Y[NB * NB], K[NB * NB];
+    constexpr int L = NB + 1;  // padded rows: a lane per row reads without bank conflicts
+    __shared__ T Vt[NB * L], Tb[NB * L], Qb[NB * L], Y[NB * L], K[NB * L];
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
     const int r0 = b * per;
     const int rows = min(per, m - r0);
     for (int p = tid; p < NB * NB; p += 256) {
-        Vt[p] = Vloc[(int64_t)(r0 + p / NB) * NB + p % NB];
-        Tb[p] = Tloc[(int64_t)b * NB * NB + p];
-        Y[p] = Vtop[(int64_t)b * NB * NB + p];
-        K[p] = Ktop[p];
+        const int q = (p / NB) * L + p % NB;
+        Vt[q] = Vloc[(int64_t)(r0 + p / NB) * NB + p % NB];
+        Tb[q] = Tloc[(int64_t)b * NB * NB + p];
+        Y[q] = Vtop[(int64_t)b * NB * NB + p];
+        K[q] = Ktop[p];
     }
     __syncthreads();
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int i = p / NB, c = p % NB;
-        T s = b * NB + i == c ? (T)1 : (T)0;
-        for (int j = 0; j < NB; ++j) s -= Y[i * NB + j] * K[j * NB + c];
-        Qb[p] = s;
-    }
-    __syncthreads();
-    // Y = V_b[0:NB]^T Qt_b ; K = T_b Y
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int j = p / NB, c = p % NB;
-        T s = 0;
-        for (int l = j; l < NB; ++l) s += Vt[l * NB + j] * Qb[l * NB + c];
-        Y[p] = s;
-    }
-    __syncthreads();
-    for (int p = tid; p < NB * NB; p += 256) {
-        const int j = p / NB, c = p % NB;
-        T s = 0;
-        for (int l = j; l < NB; ++l) s += Tb[j * NB + l] * Y[l * NB + c];
-        K[p] = s;
+    if constexpr (sizeof(T) == 4) {
+        // three 32 x 32 x 32 products on MFMA by wave 0:
+        //   Qb = [I; 0]_b - Y K,  Y = V_b[0:NB]^T Qb,  K = T_b Y
+        // (lane l supplies A[l % 32][k + l / 32] and B[k + l / 32][l % 32]; the
+        // result element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32)
+        if (tid < 64) {
+            const int lane = tid, cl = lane & 31, hl = lane >> 5;
+            auto product = [&](const T *Am, bool a_rows, const T *Bm) {
+                f32x16_t acc = {};
+#pragma unroll
+                for (int kk = 0; kk < NB; kk += 2) {
+                    // a_rows: A[i][k] stored at Am[i][k]; else stored transposed, Am[k][i]
+                    const float a = a_rows ? Am[cl * L + kk + hl] : Am[(kk + hl) * L + cl];
+                    const float bv = Bm[(kk + hl) * L + cl];
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, acc, 0, 0, 0);
+                }
+                return acc;
+            };
+            auto row_of = [&](int e) { return (e >> 2) * 8 + hl * 4 + (e & 3); };
+            f32x16_t acc = product(Y, true, K);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = row_of(e);
+                Qb[r * L + cl] = (b * NB + r == cl ? 1.f : 0.f) - acc[e];
+            }
+            wave_sync();
+            acc = product(Vt, false, Qb);  // V_b^T: A[j][l] = Vt[l][j]
+            wave_sync();
+#pragma unroll
+            for (int e = 0; e < 16; ++e) Y[row_of(e) * L + cl] = acc[e];
+            wave_sync();
+            acc = product(Tb, true, Y);
+            wave_sync();
+#pragma unroll
+            for (int e = 0; e < 16; ++e) K[row_of(e) * L + cl] = acc[e];
+        }
+    } else {
+        for (int p = tid; p < NB * NB; p += 256) {
+            const int i = p / NB, c = p % NB;
+            T s = b * NB + i == c ? (T)1 : (T)0;
+            for (int j = 0; j < NB; ++j) s -= Y[i * L + j] * K[j * L + c];
+            Qb[i * L + c] = s;
+        }
+        __syncthreads();
+        // Y = V_b[0:NB]^T Qt_b ; K = T_b Y
+        T yv[NB * NB / 256];
+        for (int p = tid, u = 0; p < NB * NB; p += 256, ++u) {
+            const int jj = p / NB, c = p % NB;
+            T s = 0;
+            for (int l = jj; l < NB; ++l) s += Vt[l * L + jj] * Qb[l * L + c];
+            yv[u] = s;
+        }
+        __syncthreads();
+        for (int p = tid, u = 0; p < NB * NB; p += 256, ++u) Y[(p / NB) * L + p % NB] = yv[u];
+        __syncthreads();
+        for (int p = tid; p < NB * NB; p += 256) {
+            const int jj = p / NB, c = p % NB;
+            T s = 0;
+            for (int l = jj; l < NB; ++l) s += Tb[jj * L + l] * Y[l * L + c];
+            K[jj * L + c] = s;
+        }
     }
     __syncthreads();
     const int i = blockIdx.x * 8 + (tid >> 5);  // row within the block
     const int c = tid & 31;
     if (i < rows) {
-        T s = i < NB ? Qb[i * NB + c] : (T)0;
+        T s = i < NB ? Qb[i * L + c] : (T)0;
         const T *vr = Vloc + (int64_t)(r0 + i) * NB;
         T vrow[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) vrow[j] = vr[j];
+        for (int jj = 0; jj < NB; ++jj) vrow[jj] = vr[jj];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) s -= vrow[j] * K[j * NB + c];
+        for (int jj = 0; jj < NB; ++jj) s -= vrow[jj] * K[jj * L + c];
         Q1[(int64_t)(r0 + i) * NB + c] = s;
     }
 }
