@@ -402,3 +402,53 @@ def test_kl_pins():
     a = oracle.robust_stats(lam, n_samples=30, p_dim=300, bins=8)["kl_mp"]
     b = oracle.robust_stats(lam * 0.1, n_samples=300, p_dim=30, bins=8)["kl_mp"]
     assert abs(a - b) <= 1e-12
+
+
+# ------------------------------------------------------------- randomised top eigenvalues
+
+def _spd_with_spectrum(rng, lam):
+    d = lam.size
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    return (Q * lam) @ Q.T
+
+
+def test_topk_exact_on_low_rank():
+    # rank 20 < 32 columns: the range finder captures the whole range, so the
+    # Ritz values are the 20 nonzero eigenvalues followed by zeros
+    rng = np.random.default_rng(21)
+    lam = np.r_[np.linspace(10.0, 1.0, 20), np.zeros(280)]
+    A = _spd_with_spectrum(rng, lam)
+    r = oracle.topk_ritz(A, rng.standard_normal((300, 32)), q=0)
+    assert np.max(np.abs(r[:20] - lam[:20])) <= 1e-11 * 10
+    assert np.max(np.abs(r[20:])) <= 1e-11 * 10
+
+
+def test_topk_interlacing_and_convergence():
+    rng = np.random.default_rng(22)
+    d = 400
+    lam = 0.7 ** np.arange(d) * 5.0 + 1e-3  # fast decay
+    A = _spd_with_spectrum(rng, lam)
+    Om = rng.standard_normal((d, 32))
+    ref = np.sort(np.linalg.eigvalsh(A))[::-1]
+    prev = None
+    for q in range(4):
+        r = oracle.topk_ritz(A, Om, q)
+        # Cauchy interlacing: each Ritz value is at most the eigenvalue of that rank
+        assert np.all(r <= ref[:32] + 1e-12)
+        err = np.max(np.abs(r[:10] - ref[:10]) / ref[:10])
+        if prev is not None:
+            assert err <= prev + 1e-15  # more iterations never hurt here
+        prev = err
+    assert prev <= 1e-10
+
+
+def test_topk_depends_on_the_span_only():
+    # Omega R spans the same space for an invertible R: the same Ritz values
+    rng = np.random.default_rng(23)
+    d = 200
+    A = _spd_with_spectrum(rng, rng.uniform(0, 3, d))
+    Om = rng.standard_normal((d, 32))
+    R = rng.standard_normal((32, 32)) + 8 * np.eye(32)
+    a = oracle.topk_ritz(A, Om, 1)
+    b = oracle.topk_ritz(A, Om @ R, 1)
+    assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(a))
