@@ -161,6 +161,29 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
                         size_t ws_bytes, int32_t *info);
 
 /* ------------------------------------------------------------------------
+ * Leading eigenvalues by random projection ("Random matrix theory spectral
+ * methods" page, section 3.2: top-k eigenvalues from a random projection in
+ * O(k d^2) rather than O(d^3)): the randomised range finder with q steps of
+ * subspace iteration and Rayleigh-Ritz,
+ *     Y = A Omega, Q = orth(Y);  q times: Q = orth(A Q);  w = eig(Q^T A Q),
+ * orth a Householder QR.  Returns all 32 Ritz values, descending; the leading
+ * k < 32 approximate the k largest eigenvalues of A (the other columns are
+ * oversampling).
+ *
+ * A:     [n][lda] f32 device, symmetric, LOWER triangle read; not modified.
+ * Omega: [n][32] f32 device (row-major, contiguous): the caller's random test
+ *        matrix (e.g. standard normal entries).
+ * w:     f32 [32] device, Ritz values descending.
+ * ws:    device workspace of spec_eigvalsh_large_workspace(n, SPEC_F32) bytes
+ *        (256-byte aligned); calls sharing one workspace must be ordered on
+ *        one stream.
+ * Requires t == SPEC_F32 (else SPEC_EUNSUPPORTED), 64 <= n <= 32768,
+ * n <= lda < 2^22, 0 <= q <= 16; else SPEC_EINVAL.
+ * ---------------------------------------------------------------------- */
+int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
+                       void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * A5  Spectral descriptors of `batch` spectra of r values each
  *     (w[b*ldw + i], i < r, sorted DESCENDING; type wt = SPEC_F32 or SPEC_F64).
  *

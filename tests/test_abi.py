@@ -144,3 +144,15 @@ def test_postproc_validation(L):
     assert g(None, FAKE, spec.BF16, 1, 32, 32, ctypes.byref(p), FAKE) == EUNSUPPORTED
     assert g(None, FAKE, spec.F32, 1, 1, 1, ctypes.byref(p), FAKE) == EINVAL   # r < 2
     assert g(None, FAKE, spec.F32, 1, 32, 31, ctypes.byref(p), FAKE) == EINVAL  # ldw < r
+
+
+def test_topk_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.spec_eigvalsh_large_workspace(512, spec.F32, ctypes.byref(b)) == 0
+    f = L.spec_eigvalsh_topk
+    assert f(None, FAKE, spec.F64, 512, 512, FAKE, 2, FAKE, FAKE, b.value) == EUNSUPPORTED
+    assert f(None, FAKE, spec.F32, 32, 32, FAKE, 2, FAKE, FAKE, b.value) == EINVAL     # n < 64
+    assert f(None, FAKE, spec.F32, 512, 500, FAKE, 2, FAKE, FAKE, b.value) == EINVAL   # lda < n
+    assert f(None, FAKE, spec.F32, 512, 512, FAKE, 17, FAKE, FAKE, b.value) == EINVAL  # q > 16
+    assert f(None, FAKE, spec.F32, 512, 512, None, 2, FAKE, FAKE, b.value) == EINVAL
+    assert f(None, FAKE, spec.F32, 512, 512, FAKE, 2, FAKE, FAKE, b.value - 1) == EWORKSPACE

@@ -1,0 +1,71 @@
+"""Parity of the randomised leading eigenvalues (random projection, subspace
+iteration, Rayleigh-Ritz) with the fp64 oracle on the same f32 matrix and the
+same seeded test matrix, through the C ABI.
+
+Bound: every Ritz value within 1e-4 * lambda_max (the eigenvalue tolerance of
+the large solver); the Ritz values of an exactly low-rank matrix are its
+eigenvalues, and no Ritz value exceeds the eigenvalue of its rank (interlacing).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import dev, print_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spec():
+    import weights_bf16_fp32_amd as spec
+    spec.lib()
+    return spec
+
+
+def _cov(rng, n_rows, d, spikes):
+    X = rng.standard_normal((n_rows, d))
+    U, _ = np.linalg.qr(rng.standard_normal((d, len(spikes))))
+    X += (rng.standard_normal((n_rows, len(spikes))) * np.sqrt(spikes)) @ U.T
+    return ((X.T @ X) / n_rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("d,q", [(300, 0), (1000, 1), (1000, 3), (4096, 2)])
+def test_topk_parity(spec, d, q):
+    import torch
+    print_case("topk", d=d, q=q)
+    rng = np.random.default_rng(d + q)
+    A = _cov(rng, 2 * d if d < 4096 else 4096, d, spikes=np.geomspace(50, 2, 12))
+    Om = rng.standard_normal((d, 32)).astype(np.float32)
+    Ad = dev(A)
+    Au = Ad.clone()
+    iu = np.triu_indices(d, 1)
+    Au[iu[0], iu[1]] = 1e30  # the upper triangle is never read
+    w = spec.eigvalsh_topk(Au, dev(Om), q=q)
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    ref = oracle.topk_ritz(A.astype(np.float64), Om, q)
+    lmax = ref[0]
+    err = np.max(np.abs(wg - ref))
+    print(f"[topk] d={d} q={q} max |dtheta| {err:.3g} lambda_max {lmax:.4g}", flush=True)
+    assert err <= 1e-4 * lmax
+    assert np.all(np.diff(wg) <= 0)
+    # A was only read
+    assert torch.equal(Au[iu[1], iu[0]], Ad[iu[1], iu[0]])
+
+
+def test_topk_low_rank_exact(spec):
+    import torch
+    print_case("topk_low_rank")
+    rng = np.random.default_rng(3)
+    d = 512
+    lam = np.r_[np.linspace(9.0, 1.0, 20), np.zeros(d - 20)]
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    A = ((Q * lam) @ Q.T).astype(np.float32)
+    Om = rng.standard_normal((d, 32)).astype(np.float32)
+    w = spec.eigvalsh_topk(dev(A), dev(Om), q=1)
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    ev = np.sort(np.linalg.eigvalsh(A.astype(np.float64)))[::-1]
+    assert np.max(np.abs(wg[:20] - ev[:20])) <= 1e-4 * ev[0]
+    assert np.max(np.abs(wg[20:])) <= 1e-4 * ev[0]
+    assert np.all(wg <= ev[:32] + 1e-4 * ev[0])

@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "SpecError", "lib", "cov_accumulate", "gram_window", "eigvalsh_batched_dense",
     "eigvalsh_batched_band", "eigvalsh_large", "eigvalsh_large_workspace", "descriptors",
-    "descriptors_workspace", "DESC_DTYPE", "desc_smooth", "spectrum_robust", "ROBUST_DTYPE",
+    "descriptors_workspace", "DESC_DTYPE", "desc_smooth", "spectrum_robust", "ROBUST_DTYPE", "eigvalsh_topk",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,7 +74,8 @@ class RobustParams(ctypes.Structure):
 
 EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_window",
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
-           "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust"]
+           "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
+           "spec_eigvalsh_topk"]
 
 _lib = None
 
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.spec_descriptors.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp, vp,
                                        ctypes.c_size_t]
         L.spec_desc_smooth.argtypes = [vp, vp, i64, i64, dbl, vp]
+        L.spec_eigvalsh_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
@@ -286,3 +288,20 @@ def spectrum_robust(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma
     if not to_host:
         return out
     return out.cpu().numpy().view(ROBUST_DTYPE).reshape(batch)
+
+
+def eigvalsh_topk(A, Omega, q: int = 2, w=None, ws=None):
+    """The 32 Ritz values (descending) of the symmetric A [n, n] (lower triangle
+    read, A kept) on the range of A Omega after q subspace iterations; Omega is
+    the caller's random test matrix [n, 32] (float32, contiguous)."""
+    torch = _torch()
+    n = A.shape[0]
+    if A.stride(1) != 1 or not Omega.is_contiguous() or tuple(Omega.shape) != (n, 32):
+        raise SpecError(-1, "A must be row-major and Omega a contiguous [n, 32] tensor")
+    if w is None:
+        w = torch.empty((32,), dtype=torch.float32, device=A.device)
+    if ws is None:
+        ws = torch.empty((eigvalsh_large_workspace(n, torch.float32),), dtype=torch.uint8, device=A.device)
+    _check(lib().spec_eigvalsh_topk(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(Omega), int(q), _dev(w),
+                                    _dev(ws), ws.numel()))
+    return w

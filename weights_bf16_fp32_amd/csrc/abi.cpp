@@ -133,6 +133,19 @@ int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t
     return from_hip(launch_descriptors((hipStream_t)stream, w, wt, batch, r, ldw, p, out, ws));
 }
 
+int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
+                       void *ws, size_t ws_bytes)
+{
+    if (t != SPEC_F32) return SPEC_EUNSUPPORTED;
+    if (A == nullptr || Omega == nullptr || w == nullptr) return SPEC_EINVAL;
+    if (n < 64 || n > 32768 || lda < n || lda >= ((int64_t)1 << 22) || q < 0 || q > 16) return SPEC_EINVAL;
+    if (!aligned(A, 16) || !aligned(Omega, 16) || !aligned(w, 4)) return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < eig_large_workspace_bytes(n, SPEC_F32)) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    return from_hip(launch_topk_ritz((hipStream_t)stream, (const float *)A, n, lda, (const float *)Omega, q,
+                                     (float *)w, ws));
+}
+
 int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t W, double alpha, spec_desc *out)
 {
     if (in == nullptr || out == nullptr || streams < 0 || streams > ((int64_t)1 << 31) - 1 || W < 1) return SPEC_EINVAL;

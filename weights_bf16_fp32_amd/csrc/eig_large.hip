@@ -1842,6 +1842,91 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     return hipSuccess;
 }
 
+// ---- sum of the XR-row partial products: B = sum_blk Ppart[blk] (NB x NB)
+__global__ __launch_bounds__(256) void k_psum(const float *__restrict__ Ppart, int nblk, float *__restrict__ B)
+{
+    for (int q = threadIdx.x; q < NB * NB; q += 256) {
+        float acc = 0.f;
+        for (int b = 0; b < nblk; ++b) acc += Ppart[(int64_t)b * NB * NB + q];
+        B[q] = acc;
+    }
+}
+
+// Leading eigenvalues by random projection ("Random matrix theory spectral
+// methods" page, section 3.2): Y = A Omega, Q = orth(Y), q times Q = orth(A Q),
+// then the NB Ritz values eig(Q^T A Q), descending.  The products are the
+// reduction's SYMM (lower-stored A, split over column chunks) and partial sums;
+// orth is the TSQR of the reduction with its explicit Q1; Q^T A Q is the sum of
+// the per-block products Q_blk^T (A Q)_blk; its eigenvalues come from the
+// batched small solver.  A is read, not written.
+hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, const float *Omega, int q, float *w,
+                    void *ws)
+{
+    Bufs<float> b;
+    layout<float>(n, (char *)ws, b);
+    const int m = (int)n;
+    constexpr int TOP_BLOCKS = Cfg<float>::RB / NB;
+    auto symm = [&](const float *Wm) -> hipError_t {
+        const int nrb = (int)cdiv_h(m, SY_RB);
+        int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
+        const int chunk = (int)(cdiv_h(cdiv_h(m, ks), SY_JB) * SY_JB);
+        ks = (int)cdiv_h(m, chunk);
+        hipLaunchKernelGGL(k_symm<float>, dim3(nrb, ks), dim3(256), 0, st, A, lda, m, Wm, b.Xpart, chunk);
+        LAUNCH_OK();
+        const int nxb = (int)cdiv_h(m, XR);
+        hipLaunchKernelGGL(k_xreduce<float>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, m, Wm, b.X, b.Ppart);
+        return hipGetLastError();
+    };
+    auto orth = [&]() -> hipError_t {  // Q1 = the first NB columns of the Q of X = QR
+        const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
+        const int per = (int)cdiv_h(m, nblk);
+        const int rows_top = nblk * NB;
+        if (per <= 256)
+            hipLaunchKernelGGL((k_tsqr_wave<float, 1>), dim3(nblk), dim3(64), 0, st, b.X, (int64_t)NB, m, per,
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+        else if (per <= 512)
+            hipLaunchKernelGGL((k_tsqr_wave<float, 2>), dim3(nblk), dim3(128), 0, st, b.X, (int64_t)NB, m, per,
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+        else
+            hipLaunchKernelGGL((k_tsqr_wave<float, 4>), dim3(nblk), dim3(256), 0, st, b.X, (int64_t)NB, m, per,
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+        LAUNCH_OK();
+        if (rows_top <= 256)
+            hipLaunchKernelGGL((k_tsqr_wave<float, 1>), dim3(1), dim3(64), 0, st, b.Rstack, (int64_t)NB, rows_top,
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+        else if (rows_top <= 512)
+            hipLaunchKernelGGL((k_tsqr_wave<float, 2>), dim3(1), dim3(128), 0, st, b.Rstack, (int64_t)NB, rows_top,
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+        else
+            hipLaunchKernelGGL((k_tsqr_wave<float, 4>), dim3(1), dim3(256), 0, st, b.Rstack, (int64_t)NB, rows_top,
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_tsqr_q1<float>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
+                           b.Vtop, b.Ktop, m, per, b.Q1);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    if ((e = symm(Omega)) != hipSuccess) return e;
+    if ((e = orth()) != hipSuccess) return e;
+    for (int it = 0; it < q; ++it) {
+        if ((e = symm(b.Q1)) != hipSuccess) return e;
+        if ((e = orth()) != hipSuccess) return e;
+    }
+    if ((e = symm(b.Q1)) != hipSuccess) return e;  // X = A Q and the blocks of Q^T X
+    hipLaunchKernelGGL(k_psum, dim3(1), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), b.U);
+    LAUNCH_OK();
+    spec_batch_src src;
+    src.kind = SPEC_SRC_DENSE;
+    src.a = b.U;
+    src.lda = NB;
+    src.stride_a = NB * NB;
+    src.streams = 0;
+    src.T = 0;
+    src.stride = 1;
+    src.scale = 1.f;
+    return launch_eigvalsh_batched(st, &src, 1, NB, w, nullptr);
+}
+
 }  // namespace
 
 size_t eig_large_workspace_bytes(int64_t n, int t)
@@ -1859,4 +1944,10 @@ hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64
 {
     if (t == SPEC_F32) return run<float>(stream, (float *)A, n, lda, (float *)w, ws, info);
     return run<double>(stream, (double *)A, n, lda, (double *)w, ws, info);
+}
+
+hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
+                            float *w, void *ws)
+{
+    return run_topk(stream, A, n, lda, Omega, q, w, ws);
 }

@@ -35,3 +35,6 @@ hipError_t launch_desc_smooth(hipStream_t stream, const spec_desc *in, int64_t s
 
 hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                                   const spec_robust_params *p, spec_robust *out);
+
+hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
+                            float *w, void *ws);
