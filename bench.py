@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-postproc", action="store_true",
+                    help="skip the timing of the rows beyond the hot path (post-processing, top-k)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -208,56 +210,58 @@ def main():
     roof = dict(rows[dominant])
     roof["kernel"] = dominant
 
-    # descriptor post-processing (a row beyond the hot path, timed on its own):
-    # smoothing of the window descriptor series, robust / log / KL statistics of
-    # the window spectra and of the 4096 spectrum
-    sm_out = torch.empty_like(desc_win)
-    rb_win = torch.empty((S * W, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    rb_big = torch.empty((1, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    post = {
-        "desc_smooth": lambda: spec.desc_smooth(desc_win, streams=S, W=W, alpha=0.2, out=sm_out, to_host=False),
-        "robust_windows": lambda: spec.spectrum_robust(w_win, n_samples=N, p_dim=ET["d"],
-                                                       sigma2_mode=spec.SIGMA2_MEDIAN, bins=8, out=rb_win,
-                                                       to_host=False),
-        "robust_4096": lambda: spec.spectrum_robust(w_big, n_samples=n_total, p_dim=d,
-                                                    sigma2_mode=spec.SIGMA2_WINSOR, bins=32, out=rb_big,
-                                                    to_host=False),
-    }
-    # leading eigenvalues of the 4096 covariance by random projection (q = 2), on
-    # the covariance rebuilt by the SYRK chunks (the eigensolve overwrote it)
-    for k in range(SW["chunks"]):
-        spec.cov_accumulate(Xd[k], C, alpha=1.0, beta=0.0 if k == 0 else 1.0)
-    Om = torch.from_numpy(np.random.default_rng(2024).standard_normal((d, 32)).astype(np.float32)).to(dev)
-    w_top = torch.empty((32,), dtype=torch.float32, device=dev)
-    post["topk_4096_q2"] = lambda: spec.eigvalsh_topk(C, Om, q=2, w=w_top, ws=ws_big)
-    post_ms = {}
-    for name, fn in post.items():
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
+    post_rows = None
+    if not args.no_postproc:
+        # descriptor post-processing (a row beyond the hot path, timed on its own):
+        # smoothing of the window descriptor series, robust / log / KL statistics of
+        # the window spectra and of the 4096 spectrum
+        sm_out = torch.empty_like(desc_win)
+        rb_win = torch.empty((S * W, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        rb_big = torch.empty((1, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        post = {
+            "desc_smooth": lambda: spec.desc_smooth(desc_win, streams=S, W=W, alpha=0.2, out=sm_out, to_host=False),
+            "robust_windows": lambda: spec.spectrum_robust(w_win, n_samples=N, p_dim=ET["d"],
+                                                           sigma2_mode=spec.SIGMA2_MEDIAN, bins=8, out=rb_win,
+                                                           to_host=False),
+            "robust_4096": lambda: spec.spectrum_robust(w_big, n_samples=n_total, p_dim=d,
+                                                        sigma2_mode=spec.SIGMA2_WINSOR, bins=32, out=rb_big,
+                                                        to_host=False),
+        }
+        # leading eigenvalues of the 4096 covariance by random projection (q = 2), on
+        # the covariance rebuilt by the SYRK chunks (the eigensolve overwrote it)
+        for k in range(SW["chunks"]):
+            spec.cov_accumulate(Xd[k], C, alpha=1.0, beta=0.0 if k == 0 else 1.0)
+        Om = torch.from_numpy(np.random.default_rng(2024).standard_normal((d, 32)).astype(np.float32)).to(dev)
+        w_top = torch.empty((32,), dtype=torch.float32, device=dev)
+        post["topk_4096_q2"] = lambda: spec.eigvalsh_topk(C, Om, q=2, w=w_top, ws=ws_big)
+        post_ms = {}
+        for name, fn in post.items():
             fn()
-        e1.record()
-        torch.cuda.synchronize()
-        post_ms[name] = e0.elapsed_time(e1) / 10
-    smooth_bytes = 2 * S * W * spec.DESC_DTYPE.itemsize
-    robust_bytes = S * W * (N * 4 + spec.ROBUST_DTYPE.itemsize)
-    post_rows = {
-        "desc_smooth": {"ms": post_ms["desc_smooth"], "records": S * W, "bound": "hbm",
-                        "achieved_GBs": smooth_bytes / (post_ms["desc_smooth"] / 1e3) / 1e9},
-        "robust_windows": {"ms": post_ms["robust_windows"], "spectra": S * W, "bound": "hbm",
-                           "achieved_GBs": robust_bytes / (post_ms["robust_windows"] / 1e3) / 1e9},
-        "robust_4096": {"ms": post_ms["robust_4096"], "spectra": 1},
-        # 4 products A Q (2 n^2 32 flop each, the symmetric half read twice) + 3 TSQRs
-        "topk_4096_q2": {"ms": post_ms["topk_4096_q2"], "ritz_values": 32, "bound": "mfma",
-                         "achieved_TFLOPs": 4 * 2.0 * d * d * 32 / (post_ms["topk_4096_q2"] / 1e3) / 1e12},
-    }
-    for r in post_rows.values():
-        if "achieved_GBs" in r:
-            r["frac"] = r["achieved_GBs"] * 1e9 / PEAK_HBM
-        if "achieved_TFLOPs" in r:
-            r["frac"] = r["achieved_TFLOPs"] * 1e12 / PEAK_F32_MFMA
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            post_ms[name] = e0.elapsed_time(e1) / 10
+        smooth_bytes = 2 * S * W * spec.DESC_DTYPE.itemsize
+        robust_bytes = S * W * (N * 4 + spec.ROBUST_DTYPE.itemsize)
+        post_rows = {
+            "desc_smooth": {"ms": post_ms["desc_smooth"], "records": S * W, "bound": "hbm",
+                            "achieved_GBs": smooth_bytes / (post_ms["desc_smooth"] / 1e3) / 1e9},
+            "robust_windows": {"ms": post_ms["robust_windows"], "spectra": S * W, "bound": "hbm",
+                               "achieved_GBs": robust_bytes / (post_ms["robust_windows"] / 1e3) / 1e9},
+            "robust_4096": {"ms": post_ms["robust_4096"], "spectra": 1},
+            # 4 products A Q (2 n^2 32 flop each, the symmetric half read twice) + 3 TSQRs
+            "topk_4096_q2": {"ms": post_ms["topk_4096_q2"], "ritz_values": 32, "bound": "mfma",
+                             "achieved_TFLOPs": 4 * 2.0 * d * d * 32 / (post_ms["topk_4096_q2"] / 1e3) / 1e12},
+        }
+        for r in post_rows.values():
+            if "achieved_GBs" in r:
+                r["frac"] = r["achieved_GBs"] * 1e9 / PEAK_HBM
+            if "achieved_TFLOPs" in r:
+                r["frac"] = r["achieved_TFLOPs"] * 1e12 / PEAK_F32_MFMA
 
     cpu = None
     if not args.no_cpu_baseline:
