@@ -30,7 +30,9 @@ What it computes, each function citing the passage it follows:
   count (RMT page, section 4.2), log-eigenvalue mean and spread (section 3.2)
   and the KL form of the MP deviation over a histogram (section 2.3).
 * :func:`topk_ritz`       leading eigenvalues by random projection (RMT page,
-  section 3.2): range finder, subspace iteration, Rayleigh-Ritz.
+  section 3.2): range finder, subspace iteration, Rayleigh-Ritz;
+  :func:`topk_ritz_vectors` also returns the Ritz vectors (the signal-subspace
+  basis of RMT page, section 4.1).
 
 All arithmetic is fp64.  bf16 inputs arrive as uint16 bit patterns and are
 widened exactly.
@@ -518,3 +520,21 @@ def topk_ritz(A: np.ndarray, Omega: np.ndarray, q: int) -> np.ndarray:
     B = Q.T @ A @ Q
     B = 0.5 * (B + B.T)
     return np.sort(np.linalg.eigvalsh(B))[::-1]
+
+
+def topk_ritz_vectors(A: np.ndarray, Omega: np.ndarray, q: int):
+    """Ritz values (descending) and Ritz vectors P = Q U of topk_ritz: the
+    columns of P are orthonormal and span the range found by the projection;
+    column i belongs to Ritz value i.  The leading columns approximate the
+    leading eigenvectors; those with a Ritz value above the MP edge are the
+    signal subspace (RMT page, section 4.1: the eigenvectors
+    beyond lambda_plus span it, P = [u_1 .. u_k])."""
+    A = np.asarray(A, dtype=np.float64)
+    Q, _ = np.linalg.qr(A @ np.asarray(Omega, dtype=np.float64))
+    for _ in range(q):
+        Q, _ = np.linalg.qr(A @ Q)
+    B = Q.T @ A @ Q
+    B = 0.5 * (B + B.T)
+    th, U = np.linalg.eigh(B)
+    order = np.argsort(th)[::-1]
+    return th[order], Q @ U[:, order]

@@ -452,3 +452,23 @@ def test_topk_depends_on_the_span_only():
     a = oracle.topk_ritz(A, Om, 1)
     b = oracle.topk_ritz(A, Om @ R, 1)
     assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(a))
+
+
+def test_topk_vectors_pins():
+    rng = np.random.default_rng(31)
+    d = 300
+    lam = np.r_[np.linspace(12.0, 3.0, 10), rng.uniform(0.0, 0.5, d - 10)]
+    A = _spd_with_spectrum(rng, lam)
+    Om = rng.standard_normal((d, 32))
+    th, P = oracle.topk_ritz_vectors(A, Om, 3)
+    assert np.allclose(th, oracle.topk_ritz(A, Om, 3), rtol=0, atol=1e-12 * th[0])
+    assert np.max(np.abs(P.T @ P - np.eye(32))) <= 1e-12           # orthonormal
+    R = P.T @ A @ P
+    assert np.max(np.abs(R - np.diag(th))) <= 1e-11 * th[0]        # Rayleigh-Ritz: P^T A P diagonal
+    # the leading Ritz vectors approach the leading eigenvectors: the rest of
+    # the spectrum is below 0.5, so each iteration shrinks the angle by <= 1/6
+    w, V = np.linalg.eigh(A)
+    V = V[:, ::-1]
+    _, P6 = oracle.topk_ritz_vectors(A, Om, 6)
+    for i in range(10):
+        assert abs(abs(P6[:, i] @ V[:, i]) - 1.0) <= 1e-10, i
