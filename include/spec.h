@@ -184,6 +184,28 @@ int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t ld
                        void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Ritz vectors of the random projection: the signal-subspace basis
+ * ("Random matrix theory spectral methods" page, section 4.1: the
+ * eigenvectors whose eigenvalues lie beyond the MP edge lambda_plus span the
+ * signal subspace, P = [u_1 .. u_k]).  The same range finder as
+ * spec_eigvalsh_topk, then the eigenvectors U of B = Q^T A Q (32 x 32, cyclic
+ * Jacobi in one wave) and P = Q U.  Column i of P is the Ritz vector of w[i]
+ * (w descending); the columns are orthonormal to f32 rounding, each with an
+ * arbitrary sign.  The caller keeps the leading columns whose Ritz value
+ * exceeds its lambda_plus.
+ *
+ * A, Omega, t, n, lda, q, ws, ws_bytes: as for spec_eigvalsh_topk.
+ * w:   f32 [32] device, Ritz values descending (the same values as
+ *      spec_eigvalsh_topk up to the rounding of the small eigensolver).
+ * P:   f32 [n][ldp] device, row-major; columns 0..31 of each row written,
+ *      the rest untouched.  Must not overlap A, Omega, w or ws.
+ * Requires 32 <= ldp < 2^22 and the conditions of spec_eigvalsh_topk;
+ * else SPEC_EINVAL (SPEC_EUNSUPPORTED for t != SPEC_F32).
+ * ---------------------------------------------------------------------- */
+int spec_eigvecs_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
+                      void *P, int64_t ldp, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * A5  Spectral descriptors of `batch` spectra of r values each
  *     (w[b*ldw + i], i < r, sorted DESCENDING; type wt = SPEC_F32 or SPEC_F64).
  *

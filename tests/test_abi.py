@@ -156,3 +156,24 @@ def test_topk_validation(L):
     assert f(None, FAKE, spec.F32, 512, 512, FAKE, 17, FAKE, FAKE, b.value) == EINVAL  # q > 16
     assert f(None, FAKE, spec.F32, 512, 512, None, 2, FAKE, FAKE, b.value) == EINVAL
     assert f(None, FAKE, spec.F32, 512, 512, FAKE, 2, FAKE, FAKE, b.value - 1) == EWORKSPACE
+
+
+def test_eigvecs_topk_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.spec_eigvalsh_large_workspace(512, spec.F32, ctypes.byref(b)) == 0
+    f = L.spec_eigvecs_topk
+    ok = (None, FAKE, spec.F32, 512, 512, FAKE, 2, FAKE, FAKE, 32, FAKE, b.value)
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=spec.F64) == EUNSUPPORTED
+    assert call(a3=32, a4=32) == EINVAL          # n < 64
+    assert call(a4=500) == EINVAL                # lda < n
+    assert call(a6=17) == EINVAL                 # q > 16
+    assert call(a6=-1) == EINVAL
+    assert call(a8=None) == EINVAL               # no P
+    assert call(a9=31) == EINVAL                 # ldp < 32
+    assert call(a9=1 << 22) == EINVAL
+    assert call(a11=b.value - 1) == EWORKSPACE

@@ -69,3 +69,70 @@ def test_topk_low_rank_exact(spec):
     assert np.max(np.abs(wg[:20] - ev[:20])) <= 1e-4 * ev[0]
     assert np.max(np.abs(wg[20:])) <= 1e-4 * ev[0]
     assert np.all(wg <= ev[:32] + 1e-4 * ev[0])
+
+
+@pytest.mark.parametrize("d,q", [(300, 0), (1000, 3), (4096, 2)])
+def test_eigvecs_parity(spec, d, q):
+    """Ritz vectors: values as above; P^T P = I and the Rayleigh quotients
+    p_i^T A p_i = theta_i to 1e-4 (f32 rounding of Q and P); columns whose Ritz
+    value is separated from the others by gap_i >= 1e-2 lambda_max match the
+    oracle's up to sign, within 1e-4 lambda_max / gap_i + 1e-4 (the
+    perturbation bound of an eigenvector over its gap)."""
+    import torch
+    print_case("eigvecs_topk", d=d, q=q)
+    rng = np.random.default_rng(10 * d + q)
+    A = _cov(rng, 2 * d if d < 4096 else 4096, d, spikes=np.geomspace(50, 2, 12))
+    Om = rng.standard_normal((d, 32)).astype(np.float32)
+    Ad = dev(A)
+    Au = Ad.clone()
+    iu = np.triu_indices(d, 1)
+    Au[iu[0], iu[1]] = 1e30  # the upper triangle is never read
+    ldp = 40
+    Pbuf = torch.full((d, ldp), 7.0, dtype=torch.float32, device=Ad.device)
+    w, P = spec.eigvecs_topk(Au, dev(Om), q=q, P=Pbuf)
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    Pb = P.cpu().numpy().astype(np.float64)
+    assert np.all(Pb[:, 32:] == 7.0)  # columns past 32 untouched
+    Pg = Pb[:, :32]
+    tr, Pr = oracle.topk_ritz_vectors(A.astype(np.float64), Om, q)
+    lmax = tr[0]
+    err = np.max(np.abs(wg - tr))
+    orth = np.max(np.abs(Pg.T @ Pg - np.eye(32)))
+    A64 = A.astype(np.float64)
+    rq = np.einsum("ij,ij->j", Pg, A64 @ Pg)
+    rq_err = np.max(np.abs(rq - wg))
+    gap = np.array([np.min(np.abs(np.delete(tr, i) - tr[i])) for i in range(32)])
+    sel = np.nonzero(gap >= 1e-2 * lmax)[0]
+    dots = np.einsum("ij,ij->j", Pg[:, sel], Pr[:, sel])
+    vec_err = np.linalg.norm(Pg[:, sel] - np.sign(dots) * Pr[:, sel], axis=0)
+    bound = 1e-4 * lmax / gap[sel] + 1e-4
+    print(f"[eigvecs] d={d} q={q} |dtheta| {err:.3g} orth {orth:.3g} rq {rq_err:.3g} "
+          f"compared {sel.size} cols, max err/bound {np.max(vec_err / bound):.3g}", flush=True)
+    assert err <= 1e-4 * lmax
+    assert np.all(np.diff(wg) <= 0)
+    assert orth <= 1e-4
+    assert rq_err <= 1e-4 * lmax
+    assert sel.size >= 4
+    assert np.all(vec_err <= bound)
+    assert torch.equal(Au[iu[1], iu[0]], Ad[iu[1], iu[0]])
+
+
+def test_eigvecs_low_rank_subspace(spec):
+    """Exactly rank 6 with distinct eigenvalues: the 6 leading Ritz vectors are
+    the eigenvectors (up to sign) and span the column space of A."""
+    import torch
+    print_case("eigvecs_low_rank")
+    rng = np.random.default_rng(11)
+    d = 768
+    lam = np.r_[[12.0, 9.0, 6.5, 4.0, 2.5, 1.0], np.zeros(d - 6)]
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    A = ((Q * lam) @ Q.T).astype(np.float32)
+    Om = rng.standard_normal((d, 32)).astype(np.float32)
+    w, P = spec.eigvecs_topk(dev(A), dev(Om), q=1)
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    Pg = P.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(wg[:6] - lam[:6])) <= 1e-4 * lam[0]
+    dots = np.abs(np.einsum("ij,ij->j", Pg[:, :6], Q[:, :6]))
+    assert np.all(dots >= 1 - 1e-4), dots

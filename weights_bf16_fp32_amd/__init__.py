@@ -25,6 +25,7 @@ __all__ = [
     "SpecError", "lib", "cov_accumulate", "gram_window", "eigvalsh_batched_dense",
     "eigvalsh_batched_band", "eigvalsh_large", "eigvalsh_large_workspace", "descriptors",
     "descriptors_workspace", "DESC_DTYPE", "desc_smooth", "spectrum_robust", "ROBUST_DTYPE", "eigvalsh_topk",
+    "eigvecs_topk",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,7 +76,7 @@ class RobustParams(ctypes.Structure):
 EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_window",
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
-           "spec_eigvalsh_topk"]
+           "spec_eigvalsh_topk", "spec_eigvecs_topk"]
 
 _lib = None
 
@@ -103,6 +104,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t]
         L.spec_desc_smooth.argtypes = [vp, vp, i64, i64, dbl, vp]
         L.spec_eigvalsh_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, ctypes.c_size_t]
+        L.spec_eigvecs_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, i64, vp, ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
@@ -305,3 +307,25 @@ def eigvalsh_topk(A, Omega, q: int = 2, w=None, ws=None):
     _check(lib().spec_eigvalsh_topk(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(Omega), int(q), _dev(w),
                                     _dev(ws), ws.numel()))
     return w
+
+
+def eigvecs_topk(A, Omega, q: int = 2, w=None, P=None, ws=None):
+    """Ritz values (descending, [32]) and Ritz vectors P [n, 32] (column i for
+    value i, orthonormal columns, arbitrary signs) of the same projection as
+    eigvalsh_topk; the columns with a value above the MP edge span the signal
+    subspace."""
+    torch = _torch()
+    n = A.shape[0]
+    if A.stride(1) != 1 or not Omega.is_contiguous() or tuple(Omega.shape) != (n, 32):
+        raise SpecError(-1, "A must be row-major and Omega a contiguous [n, 32] tensor")
+    if w is None:
+        w = torch.empty((32,), dtype=torch.float32, device=A.device)
+    if P is None:
+        P = torch.empty((n, 32), dtype=torch.float32, device=A.device)
+    if P.dim() != 2 or P.shape[0] != n or P.shape[1] < 32 or P.stride(1) != 1 or P.dtype != torch.float32:
+        raise SpecError(-1, "P must be a row-major float32 [n, >= 32] tensor")
+    if ws is None:
+        ws = torch.empty((eigvalsh_large_workspace(n, torch.float32),), dtype=torch.uint8, device=A.device)
+    _check(lib().spec_eigvecs_topk(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(Omega), int(q), _dev(w),
+                                   _dev(P), P.stride(0), _dev(ws), ws.numel()))
+    return w, P

@@ -143,7 +143,21 @@ int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t ld
     if (ws == nullptr || ws_bytes < eig_large_workspace_bytes(n, SPEC_F32)) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_topk_ritz((hipStream_t)stream, (const float *)A, n, lda, (const float *)Omega, q,
-                                     (float *)w, ws));
+                                     (float *)w, nullptr, 0, ws));
+}
+
+int spec_eigvecs_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
+                      void *P, int64_t ldp, void *ws, size_t ws_bytes)
+{
+    if (t != SPEC_F32) return SPEC_EUNSUPPORTED;
+    if (A == nullptr || Omega == nullptr || w == nullptr || P == nullptr) return SPEC_EINVAL;
+    if (n < 64 || n > 32768 || lda < n || lda >= ((int64_t)1 << 22) || q < 0 || q > 16) return SPEC_EINVAL;
+    if (ldp < 32 || ldp >= ((int64_t)1 << 22)) return SPEC_EINVAL;
+    if (!aligned(A, 16) || !aligned(Omega, 16) || !aligned(w, 4) || !aligned(P, 4)) return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < eig_large_workspace_bytes(n, SPEC_F32)) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    return from_hip(launch_topk_ritz((hipStream_t)stream, (const float *)A, n, lda, (const float *)Omega, q,
+                                     (float *)w, (float *)P, ldp, ws));
 }
 
 int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t W, double alpha, spec_desc *out)

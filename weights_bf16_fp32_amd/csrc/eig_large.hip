@@ -1845,11 +1845,154 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
 // ---- sum of the XR-row partial products: B = sum_blk Ppart[blk] (NB x NB)
 __global__ __launch_bounds__(256) void k_psum(const float *__restrict__ Ppart, int nblk, float *__restrict__ B)
 {
-    for (int q = threadIdx.x; q < NB * NB; q += 256) {
-        float acc = 0.f;
-        for (int b = 0; b < nblk; ++b) acc += Ppart[(int64_t)b * NB * NB + q];
-        B[q] = acc;
+    const int q = blockIdx.x * 256 + threadIdx.x;  // grid NB * NB / 256
+    float acc = 0.f;
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) acc += Ppart[(int64_t)b * NB * NB + q];
+    B[q] = acc;
+}
+
+// ---- eigenvectors of the small Rayleigh quotient B = sum of the nblk partial
+// blocks Ppart (NB x NB, symmetrised) by parallel Jacobi: in step r of a sweep
+// the indices are paired by the round-robin tournament (31 with r, and i with
+// (2r - i) mod 31), which covers every pair once in NB - 1 steps, and the 16
+// disjoint rotations of a step are applied together as B <- J^T B J,
+// V <- V J.  Each rotation zeroes its b_pq with tan from tau = (b_qq - b_pp) /
+// (2 b_pq); a pair is left alone when |b_pq| <= max(2e-6 sqrt(|b_pp b_qq|),
+// 1e-7 max|b_ij|) (2e-6 ~ NB times the f32 unit roundoff, the level at which
+// rounding keeps re-creating off-diagonal mass), a step with no rotation is
+// skipped, and the sweeps stop when none rotates (at most 30).
+// J has two non-zeros per column: column j of B J is al_j col_j + be_j
+// col_partner(j), so every new element is a 4-term sum of the old B (double
+// buffered in LDS).  Output: w descending and U with column r the vector of w[r].
+__global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ Ppart, int nblk, float *__restrict__ w,
+                                                     float *__restrict__ U)
+{
+    constexpr int L = NB + 1, EPT = NB * NB / 256;
+    __shared__ float Bs[2][NB * L], Vs[2][NB * L];
+    __shared__ float4 cf[NB];  // per index: (al, be, new diagonal, 1 if its pair rotates)
+    __shared__ float red[8];
+    __shared__ int step_on;
+    const int tid = threadIdx.x;
+    float bmax = 0.f;
+    {
+        float acc[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
+        for (int b = 0; b < nblk; ++b) {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) acc[k] += Ppart[(int64_t)b * NB * NB + tid + 256 * k];
+        }
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int e = tid + 256 * k, r = e / NB, c = e % NB;
+            Bs[1][r * L + c] = acc[k];
+            Vs[0][r * L + c] = r == c ? 1.f : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int e = tid + 256 * k, r = e / NB, c = e % NB;
+            const float v = 0.5f * (Bs[1][r * L + c] + Bs[1][c * L + r]);
+            Bs[0][r * L + c] = v;
+            bmax = fmaxf(bmax, fabsf(v));
+        }
+        for (int o = 32; o > 0; o >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+        if ((tid & 63) == 0) red[tid >> 6] = bmax;
+        __syncthreads();
+        bmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     }
+    const float floor_abs = 1e-7f * bmax;
+    int cur = 0;
+    for (int sweep = 0; sweep < 30; ++sweep) {
+        int any = 0;
+        for (int r = 0; r < NB - 1; ++r) {
+            auto partner = [r](int i) { return i == NB - 1 ? r : (i == r ? NB - 1 : (2 * r - i + 2 * (NB - 1)) % (NB - 1)); };
+            int on = 0;
+            if (tid < NB) {  // the rotation of index tid's pair (both members compute it alike)
+                const int i = tid, j = partner(i), p = min(i, j), q = max(i, j);
+                const float *B = Bs[cur];
+                const float apq = B[p * L + q], app = B[p * L + p], aqq = B[q * L + q];
+                float a = 1.f, bb = 0.f, d = B[i * L + i];
+                if (fabsf(apq) > fmaxf(2e-6f * sqrtf(fabsf(app * aqq)), floor_abs)) {
+                    // hardware reciprocal and reciprocal square root (about 1 ulp):
+                    // c^2 + s^2 = 1 to a few ulp, which is all the rotation needs
+                    const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+                    const float at = fabsf(tau);
+                    const float t = copysignf(at > 1e18f ? __builtin_amdgcn_rcpf(2.f * at)
+                                                         : __builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(1.f + tau * tau)),
+                                              tau);
+                    const float c = __builtin_amdgcn_rsqf(1.f + t * t), sn = t * c;
+                    a = c;
+                    bb = i == p ? -sn : sn;
+                    d = i == p ? app - t * apq : aqq + t * apq;
+                    on = 1;
+                }
+                cf[i] = make_float4(a, bb, d, on ? 1.f : 0.f);
+                any |= on;
+                const int flag = __ballot(on) != 0;
+                if (tid == 0) step_on = flag;
+            }
+            __syncthreads();
+            if (!step_on) {  // no pair rotates in this step
+                __syncthreads();  // every read of step_on precedes its next write
+                continue;
+            }
+            const float *B = Bs[cur];
+            const float *V = Vs[cur];
+            float *Bn = Bs[cur ^ 1];
+            float *Vn = Vs[cur ^ 1];
+            const int j = tid % NB, pj = partner(j);  // the same column in every k
+            const float4 cj = cf[j];
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int i = tid / NB + (256 / NB) * k, pi = partner(i);
+                const float4 ci = cf[i];
+                const float b00 = B[i * L + j], b01 = B[i * L + pj], b10 = B[pi * L + j], b11 = B[pi * L + pj];
+                const float v0 = V[i * L + j], v1 = V[i * L + pj];
+                float v = ci.x * (cj.x * b00 + cj.y * b01) + ci.y * (cj.x * b10 + cj.y * b11);
+                v = (pi == j && ci.w != 0.f) ? 0.f : v;  // the rotated pair's b_pq
+                v = i == j ? ci.z : v;
+                Bn[i * L + j] = v;
+                Vn[i * L + j] = cj.x * v0 + cj.y * v1;
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+        if (!__syncthreads_or(any)) break;
+    }
+    // rank of eigenvalue i among the diagonal (descending, ties by index)
+    if (tid < NB) {
+        const int i = tid;
+        const float li = Bs[cur][i * L + i];
+        int r = 0;
+        for (int j = 0; j < NB; ++j) {
+            const float lj = Bs[cur][j * L + j];
+            r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        w[r] = li;
+        for (int k = 0; k < NB; ++k) U[k * NB + r] = Vs[cur][k * L + i];
+    }
+}
+
+// ---- P = Q1 U (m x NB): the Ritz vectors
+__global__ __launch_bounds__(256) void k_ritz_vectors(const float *__restrict__ Q, int m, const float *__restrict__ U,
+                                                      float *__restrict__ P, int64_t ldp)
+{
+    __shared__ float Us[NB * NB];
+    const int tid = threadIdx.x;
+    for (int q = tid; q < NB * NB; q += 256) Us[q] = U[q];
+    __syncthreads();
+    const int64_t r = (int64_t)blockIdx.x * 8 + (tid >> 5);
+    const int c = tid & 31;
+    if (r >= m) return;
+    float qrow[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) qrow[j] = Q[r * NB + j];
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc += qrow[j] * Us[j * NB + c];
+    P[r * ldp + c] = acc;
 }
 
 // Leading eigenvalues by random projection ("Random matrix theory spectral
@@ -1860,7 +2003,7 @@ __global__ __launch_bounds__(256) void k_psum(const float *__restrict__ Ppart, i
 // the per-block products Q_blk^T (A Q)_blk; its eigenvalues come from the
 // batched small solver.  A is read, not written.
 hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, const float *Omega, int q, float *w,
-                    void *ws)
+                    float *P, int64_t ldp, void *ws)
 {
     Bufs<float> b;
     layout<float>(n, (char *)ws, b);
@@ -1913,7 +2056,13 @@ hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, cons
         if ((e = orth()) != hipSuccess) return e;
     }
     if ((e = symm(b.Q1)) != hipSuccess) return e;  // X = A Q and the blocks of Q^T X
-    hipLaunchKernelGGL(k_psum, dim3(1), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), b.U);
+    if (P != nullptr) {  // Ritz values and vectors: Jacobi on B, then P = Q U
+        hipLaunchKernelGGL(k_ritz_jacobi, dim3(1), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), w, b.Tm);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_ritz_vectors, dim3((unsigned)cdiv_h(m, 8)), dim3(256), 0, st, b.Q1, m, b.Tm, P, ldp);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_psum, dim3(NB * NB / 256), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), b.U);
     LAUNCH_OK();
     spec_batch_src src;
     src.kind = SPEC_SRC_DENSE;
@@ -1947,7 +2096,7 @@ hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64
 }
 
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
-                            float *w, void *ws)
+                            float *w, float *P, int64_t ldp, void *ws)
 {
-    return run_topk(stream, A, n, lda, Omega, q, w, ws);
+    return run_topk(stream, A, n, lda, Omega, q, w, P, ldp, ws);
 }

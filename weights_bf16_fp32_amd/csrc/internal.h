@@ -37,4 +37,4 @@ hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int
                                   const spec_robust_params *p, spec_robust *out);
 
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
-                            float *w, void *ws);
+                            float *w, float *P, int64_t ldp, void *ws);
