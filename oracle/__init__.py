@@ -33,6 +33,8 @@ What it computes, each function citing the passage it follows:
   section 3.2): range finder, subspace iteration, Rayleigh-Ritz;
   :func:`topk_ritz_vectors` also returns the Ritz vectors (the signal-subspace
   basis of RMT page, section 4.1).
+* :func:`project_weight`  the compressed weight W' = P^T W P of a d x d weight
+  on a d x k basis (RMT page, section 4.1) and the low-rank factor W P.
 
 All arithmetic is fp64.  bf16 inputs arrive as uint16 bit patterns and are
 widened exactly.
@@ -538,3 +540,22 @@ def topk_ritz_vectors(A: np.ndarray, Omega: np.ndarray, q: int):
     th, U = np.linalg.eigh(B)
     order = np.argsort(th)[::-1]
     return th[order], Q @ U[:, order]
+
+
+def project_weight(W, P):
+    """Projection compression of a square weight (RMT page, section 4.1: with
+    the signal-subspace basis P = [u_1 .. u_k] in R^{d x k}, the d x d layer
+    weight W becomes W' = P^T W P in R^{k x k}).  Returns (W', X) with the
+    right factor X = W P in R^{d x k}, the factor of the rank-k map
+    W P P^T (W kept on the span of P).
+
+    W: [d, d] float (bf16 as uint16 bit patterns, widened exactly); P: [d, k].
+    Both products are plain fp64 matrix products, first X = W P, then
+    W' = P^T X."""
+    W = np.asarray(W)
+    if W.dtype == np.uint16:
+        W = (W.astype(np.uint32) << 16).view(np.float32)
+    W = W.astype(np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    X = W @ P
+    return P.T @ X, X

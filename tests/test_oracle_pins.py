@@ -472,3 +472,40 @@ def test_topk_vectors_pins():
     _, P6 = oracle.topk_ritz_vectors(A, Om, 6)
     for i in range(10):
         assert abs(abs(P6[:, i] @ V[:, i]) - 1.0) <= 1e-10, i
+
+
+def test_project_weight_pins():
+    rng = np.random.default_rng(41)
+    d, k = 40, 7
+    W = rng.standard_normal((d, d))
+    # the first k unit vectors: W' is the leading k x k block, X the first k columns
+    E = np.eye(d)[:, :k]
+    Wp, X = oracle.project_weight(W, E)
+    assert np.array_equal(Wp, W[:k, :k]) and np.array_equal(X, W[:, :k])
+    # brute force on a tiny case: W'_ab = sum_ij P_ia W_ij P_jb
+    P = rng.standard_normal((d, k))
+    Wp, X = oracle.project_weight(W, P)
+    bf = np.zeros((k, k))
+    for a in range(k):
+        for b in range(k):
+            bf[a, b] = sum(P[i, a] * W[i, j] * P[j, b] for i in range(d) for j in range(d))
+    assert np.max(np.abs(Wp - bf)) <= 1e-11 * np.max(np.abs(bf))
+    # a non-symmetric W keeps its orientation: (P^T W P)^T = P^T W^T P
+    Wt, _ = oracle.project_weight(W.T.copy(), P)
+    assert np.allclose(Wt, Wp.T, rtol=0, atol=1e-12 * np.max(np.abs(Wp)))
+    # symmetric W = Q diag(s) Q^T on its own leading eigenvectors: W' = diag(s_1..s_k)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    s = np.sort(rng.uniform(0.1, 5.0, d))[::-1]
+    Wp, _ = oracle.project_weight((Q * s) @ Q.T, Q[:, :k])
+    assert np.max(np.abs(Wp - np.diag(s[:k]))) <= 1e-12 * s[0]
+    # Eckart-Young: with the k leading right singular vectors, ||W P||_F^2 is the
+    # sum of the k largest sigma^2 and ||W - W P P^T||_F^2 the sum of the rest,
+    # the least error of any rank-k approximation
+    U, sig, Vt = np.linalg.svd(W)
+    _, X = oracle.project_weight(W, Vt[:k].T)
+    assert abs(np.sum(X ** 2) - np.sum(sig[:k] ** 2)) <= 1e-11 * np.sum(sig ** 2)
+    assert abs(np.sum((W - X @ Vt[:k]) ** 2) - np.sum(sig[k:] ** 2)) <= 1e-11 * np.sum(sig ** 2)
+    # bf16 bit patterns are widened exactly
+    Wb = (rng.standard_normal((d, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(oracle.project_weight(Wb, P)[0], oracle.project_weight(Wf, P)[0])
