@@ -236,6 +236,13 @@ def main():
         post["topk_4096_q2"] = lambda: spec.eigvalsh_topk(C, Om, q=2, w=w_top, ws=ws_big)
         P_top = torch.empty((d, 32), dtype=torch.float32, device=dev)
         post["eigvecs_topk_4096_q2"] = lambda: spec.eigvecs_topk(C, Om, q=2, w=w_top, P=P_top, ws=ws_big)
+        Wb = torch.from_numpy((np.random.default_rng(2025).standard_normal((d, d)).astype(np.float32)
+                               / np.sqrt(d))).to(dev).to(torch.bfloat16)
+        Wp_out = torch.empty((32, 32), dtype=torch.float32, device=dev)
+        X_out = torch.empty((d, 32), dtype=torch.float32, device=dev)
+        ws_proj = torch.empty((spec.project_weight_workspace(d),), dtype=torch.uint8, device=dev)
+        post["project_weight_4096_bf16_k32"] = lambda: spec.project_weight(Wb, P_top, k=32, Wp=Wp_out, X=X_out,
+                                                                           ws=ws_proj)
         post_ms = {}
         for name, fn in post.items():
             fn()
@@ -260,6 +267,11 @@ def main():
                              "achieved_TFLOPs": 4 * 2.0 * d * d * 32 / (post_ms["topk_4096_q2"] / 1e3) / 1e12},
             # the same plus the 32 x 32 Jacobi and P = Q U (signal-subspace basis)
             "eigvecs_topk_4096_q2": {"ms": post_ms["eigvecs_topk_4096_q2"], "ritz_vectors": 32},
+            # W' = P^T W P and W P: the bf16 weight read once (2 d^2 bytes), 2 d^2 32 flop
+            "project_weight_4096_bf16_k32": {
+                "ms": post_ms["project_weight_4096_bf16_k32"], "bound": "hbm",
+                "achieved_GBs": 2.0 * d * d / (post_ms["project_weight_4096_bf16_k32"] / 1e3) / 1e9,
+                "achieved_TFLOPs_f32": 2.0 * d * d * 32 / (post_ms["project_weight_4096_bf16_k32"] / 1e3) / 1e12},
         }
         for r in post_rows.values():
             if "achieved_GBs" in r:

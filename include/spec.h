@@ -206,6 +206,32 @@ int spec_eigvecs_topk(void *stream, const void *A, int t, int64_t n, int64_t lda
                       void *P, int64_t ldp, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Projection compression of a square weight ("Random matrix theory spectral
+ * methods" page, section 4.1: with the signal-subspace basis P = [u_1 .. u_k]
+ * in R^{d x k}, the d x d layer weight W is compressed to W' = P^T W P in
+ * R^{k x k}).  Also returns, when X != NULL, the right factor X = W P, so that
+ * X P^T is W kept on the span of P (a rank-k factorisation).
+ * Products in f32 (MFMA) with f32 accumulation; bf16 weights widen exactly.
+ *
+ * W:  [d][ldw] device, type wt = SPEC_BF16 or SPEC_F32 (else
+ *     SPEC_EUNSUPPORTED), row-major, 16-byte aligned, ldw a multiple of 8
+ *     (bf16) or 4 (f32); not modified.
+ * P:  [d][ldp] f32 device, row-major: the k basis columns (e.g. the leading
+ *     columns of spec_eigvecs_topk's output).
+ * Wp: [k][ldo] f32 device, row-major: W' (columns k.. of each row untouched).
+ * X:  [d][ldx] f32 device or NULL: W P (columns k.. untouched).
+ * ws: device workspace of spec_project_weight_workspace(d) bytes (256-byte
+ *     aligned); calls sharing one workspace must be ordered on one stream.
+ * Outputs must not overlap the inputs or ws.
+ * Requires 1 <= k <= min(d, 32), d <= 65536, ldw >= d, ldp, ldo >= k and
+ * ldx >= k when X is given; else SPEC_EINVAL.
+ * ---------------------------------------------------------------------- */
+int spec_project_weight_workspace(int64_t d, size_t *bytes);
+
+int spec_project_weight(void *stream, const void *W, int wt, int64_t d, int64_t ldw, const void *P, int64_t ldp, int k,
+                        void *Wp, int64_t ldo, void *X, int64_t ldx, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * A5  Spectral descriptors of `batch` spectra of r values each
  *     (w[b*ldw + i], i < r, sorted DESCENDING; type wt = SPEC_F32 or SPEC_F64).
  *

@@ -177,3 +177,30 @@ def test_eigvecs_topk_validation(L):
     assert call(a9=31) == EINVAL                 # ldp < 32
     assert call(a9=1 << 22) == EINVAL
     assert call(a11=b.value - 1) == EWORKSPACE
+
+
+def test_project_weight_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.spec_project_weight_workspace(4096, ctypes.byref(b)) == 0 and b.value > 4096 * 32 * 4
+    assert L.spec_project_weight_workspace(0, ctypes.byref(b)) == EINVAL
+    assert L.spec_project_weight_workspace(512, ctypes.byref(b)) == 0  # the size for d = 512 below
+    f = L.spec_project_weight
+    ok = [None, FAKE, spec.BF16, 512, 512, FAKE, 32, 32, FAKE, 32, FAKE, 32, FAKE, b.value]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=spec.F64) == EUNSUPPORTED
+    assert call(a1=None) == EINVAL
+    assert call(a3=0) == EINVAL                   # d < 1
+    assert call(a7=0) == EINVAL                   # k < 1
+    assert call(a7=33) == EINVAL                  # k > 32
+    assert call(a3=16, a4=16, a7=17) == EINVAL    # k > d
+    assert call(a4=500) == EINVAL                 # ldw < d
+    assert call(a4=516) == EINVAL                 # bf16 rows not 16-byte multiples
+    assert call(a6=31) == EINVAL                  # ldp < k
+    assert call(a9=31) == EINVAL                  # ldo < k
+    assert call(a11=31) == EINVAL                 # ldx < k with X given
+    assert call(a1=FAKE + 8) == EINVAL            # W not 16-byte aligned
+    assert call(a13=b.value - 1) == EWORKSPACE

@@ -25,7 +25,7 @@ __all__ = [
     "SpecError", "lib", "cov_accumulate", "gram_window", "eigvalsh_batched_dense",
     "eigvalsh_batched_band", "eigvalsh_large", "eigvalsh_large_workspace", "descriptors",
     "descriptors_workspace", "DESC_DTYPE", "desc_smooth", "spectrum_robust", "ROBUST_DTYPE", "eigvalsh_topk",
-    "eigvecs_topk",
+    "eigvecs_topk", "project_weight", "project_weight_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,7 +76,8 @@ class RobustParams(ctypes.Structure):
 EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_window",
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
-           "spec_eigvalsh_topk", "spec_eigvecs_topk"]
+           "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
+           "spec_project_weight"]
 
 _lib = None
 
@@ -105,6 +106,9 @@ def lib() -> ctypes.CDLL:
         L.spec_desc_smooth.argtypes = [vp, vp, i64, i64, dbl, vp]
         L.spec_eigvalsh_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, ctypes.c_size_t]
         L.spec_eigvecs_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, i64, vp, ctypes.c_size_t]
+        L.spec_project_weight_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.spec_project_weight.argtypes = [vp, vp, i32, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp,
+                                          ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
@@ -329,3 +333,36 @@ def eigvecs_topk(A, Omega, q: int = 2, w=None, P=None, ws=None):
     _check(lib().spec_eigvecs_topk(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(Omega), int(q), _dev(w),
                                    _dev(P), P.stride(0), _dev(ws), ws.numel()))
     return w, P
+
+
+def project_weight_workspace(d: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().spec_project_weight_workspace(d, ctypes.byref(b)))
+    return b.value
+
+
+def project_weight(W, P, k=None, Wp=None, X=None, want_factor: bool = True, ws=None):
+    """W' = P^T W P ([k, k]) and, if want_factor, X = W P ([d, k]) for a square
+    weight W [d, d] (bf16 or float32, row-major) and the basis P [d, >= k]
+    (float32, row-major; the first k columns are used)."""
+    torch = _torch()
+    d = W.shape[0]
+    if W.dim() != 2 or W.shape[1] != d or W.stride(1) != 1:
+        raise SpecError(-1, "W must be a row-major square tensor")
+    if P.dim() != 2 or P.shape[0] != d or P.stride(1) != 1 or P.dtype != torch.float32:
+        raise SpecError(-1, "P must be a row-major float32 [d, k] tensor")
+    k = P.shape[1] if k is None else int(k)
+    if k > P.shape[1]:
+        raise SpecError(-1, "k exceeds the columns of P")
+    if Wp is None:
+        Wp = torch.empty((k, k), dtype=torch.float32, device=W.device)
+    if want_factor and X is None:
+        X = torch.empty((d, k), dtype=torch.float32, device=W.device)
+    if not want_factor:
+        X = None
+    if ws is None:
+        ws = torch.empty((project_weight_workspace(d),), dtype=torch.uint8, device=W.device)
+    _check(lib().spec_project_weight(_stream(), _dev(W), _dt(W), d, W.stride(0), _dev(P), P.stride(0), k, _dev(Wp),
+                                     Wp.stride(0), None if X is None else _dev(X), 0 if X is None else X.stride(0),
+                                     _dev(ws), ws.numel()))
+    return Wp, X

@@ -187,3 +187,26 @@ int spec_spectrum_robust(void *stream, const void *w, int wt, int64_t batch, int
 }
 
 }  // extern "C"
+
+int spec_project_weight_workspace(int64_t d, size_t *bytes)
+{
+    if (bytes == nullptr || d < 1 || d > 65536) return SPEC_EINVAL;
+    *bytes = project_weight_workspace_bytes(d);
+    return SPEC_OK;
+}
+
+int spec_project_weight(void *stream, const void *W, int wt, int64_t d, int64_t ldw, const void *P, int64_t ldp, int k,
+                        void *Wp, int64_t ldo, void *X, int64_t ldx, void *ws, size_t ws_bytes)
+{
+    if (wt != SPEC_BF16 && wt != SPEC_F32) return SPEC_EUNSUPPORTED;
+    if (W == nullptr || P == nullptr || Wp == nullptr) return SPEC_EINVAL;
+    if (d < 1 || d > 65536 || k < 1 || k > 32 || k > d) return SPEC_EINVAL;
+    if (ldw < d || ldp < k || ldo < k || (X != nullptr && ldx < k)) return SPEC_EINVAL;
+    const int64_t vec = wt == SPEC_BF16 ? 8 : 4;  // 16-byte rows
+    if (!aligned(W, 16) || ldw % vec != 0) return SPEC_EINVAL;
+    if (!aligned(P, 4) || !aligned(Wp, 4) || (X != nullptr && !aligned(X, 4))) return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < project_weight_workspace_bytes(d)) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    return from_hip(launch_project_weight((hipStream_t)stream, W, wt, d, ldw, (const float *)P, ldp, k, (float *)Wp,
+                                          ldo, (float *)X, ldx, ws));
+}

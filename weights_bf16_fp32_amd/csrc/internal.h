@@ -38,3 +38,8 @@ hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int
 
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
                             float *w, float *P, int64_t ldp, void *ws);
+
+size_t project_weight_workspace_bytes(int64_t d);
+
+hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int64_t d, int64_t ldw, const float *P,
+                                 int64_t ldp, int k, float *Wp, int64_t ldo, float *X, int64_t ldx, void *ws);
