@@ -8,7 +8,7 @@
 //                per workgroup; the P chunk is staged transposed in LDS so a
 //                lane takes its 8 consecutive k-values with two 16-byte reads.
 //   k_wp_reduce  X = sum_c X_c (written when asked: the right factor W P) and the
-//                partial P[rows]^T X[rows] of 128 rows.
+//                partial P[rows]^T X[rows] of 32 rows.
 //   k_wp_gsum    W' = the sum of the partials.
 // The k columns are padded to 32 with zeros (P's columns k..31 read as 0).
 #include <hip/hip_runtime.h>
@@ -19,39 +19,72 @@
 namespace {
 
 constexpr int KP = 32;          // padded basis width
-constexpr int JC = 256;         // columns of W per chunk (a multiple of 64)
+constexpr int JC = 256;         // columns of W per chunk (a multiple of 16)
 constexpr int RB = 128;         // rows of W per workgroup (4 waves x 32)
+constexpr int RR = 32;          // rows per workgroup of the reduction
 constexpr int PL = JC + 4;      // padded LDS row of the transposed P chunk
 
 int64_t cdiv_h(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 8 consecutive weights of a row as raw registers (zero past column d), widened
+// to f32 only when used, so that a whole chunk's loads are issued at once.
+struct RawBF16 {
+    uint4 u;
+};
+struct RawF32 {
+    float4 a, b;
+};
 template <typename T>
-SPEC_DEVICE void load8(const T *__restrict__ row, int64_t j, int64_t d, bool vec, float (&v)[8]);
-
+struct RawOf;
 template <>
-SPEC_DEVICE void load8<uint16_t>(const uint16_t *__restrict__ row, int64_t j, int64_t d, bool vec, float (&v)[8])
+struct RawOf<uint16_t> {
+    using type = RawBF16;
+};
+template <>
+struct RawOf<float> {
+    using type = RawF32;
+};
+
+SPEC_DEVICE RawBF16 load_raw(const uint16_t *__restrict__ row, int64_t j, int64_t d)
 {
-    if (vec) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(row + j);
-        v[0] = bf16_lo(u.x), v[1] = bf16_hi(u.x), v[2] = bf16_lo(u.y), v[3] = bf16_hi(u.y);
-        v[4] = bf16_lo(u.z), v[5] = bf16_hi(u.z), v[6] = bf16_lo(u.w), v[7] = bf16_hi(u.w);
+    RawBF16 r;
+    if (j + 8 <= d) {
+        r.u = *reinterpret_cast<const uint4 *>(row + j);
     } else {
+        uint32_t w[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = j + t < d ? bf16_to_f32(row[j + t]) : 0.f;
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = j + 2 * t < d ? row[j + 2 * t] : 0u;
+            const uint32_t hi = j + 2 * t + 1 < d ? row[j + 2 * t + 1] : 0u;
+            w[t] = lo | (hi << 16);
+        }
+        r.u = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    return r;
 }
-
-template <>
-SPEC_DEVICE void load8<float>(const float *__restrict__ row, int64_t j, int64_t d, bool vec, float (&v)[8])
+SPEC_DEVICE RawF32 load_raw(const float *__restrict__ row, int64_t j, int64_t d)
 {
-    if (vec) {
-        const float4 a = *reinterpret_cast<const float4 *>(row + j);
-        const float4 b = *reinterpret_cast<const float4 *>(row + j + 4);
-        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    RawF32 r;
+    if (j + 8 <= d) {
+        r.a = *reinterpret_cast<const float4 *>(row + j);
+        r.b = *reinterpret_cast<const float4 *>(row + j + 4);
     } else {
+        float v[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] = j + t < d ? row[j + t] : 0.f;
+        r.a = make_float4(v[0], v[1], v[2], v[3]);
+        r.b = make_float4(v[4], v[5], v[6], v[7]);
     }
+    return r;
+}
+SPEC_DEVICE void widen(const RawBF16 &r, float (&v)[8])
+{
+    v[0] = bf16_lo(r.u.x), v[1] = bf16_hi(r.u.x), v[2] = bf16_lo(r.u.y), v[3] = bf16_hi(r.u.y);
+    v[4] = bf16_lo(r.u.z), v[5] = bf16_hi(r.u.z), v[6] = bf16_lo(r.u.w), v[7] = bf16_hi(r.u.w);
+}
+SPEC_DEVICE void widen(const RawF32 &r, float (&v)[8])
+{
+    v[0] = r.a.x, v[1] = r.a.y, v[2] = r.a.z, v[3] = r.a.w, v[4] = r.b.x, v[5] = r.b.y, v[6] = r.b.z, v[7] = r.b.w;
 }
 
 // grid (cdiv(d, RB), cdiv(d, JC)), 256 threads.  Xpart[c][r][0..31].
@@ -61,42 +94,43 @@ __global__ __launch_bounds__(256) void k_wp_part(const T *__restrict__ W, int64_
                                                  float *__restrict__ Xpart)
 {
     __shared__ __align__(16) float Pt[KP * PL];  // Pt[c][j - j_begin]
+    constexpr int NG = JC / 16;                   // 16-column groups per chunk
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t jb = (int64_t)blockIdx.y * JC;
     const int jn = (int)min<int64_t>(JC, d - jb);
-    for (int q = tid; q < KP * JC; q += 256) {
-        const int j = q / KP, c = q % KP;  // coalesced over c
-        Pt[c * PL + j] = (j < jn && c < k) ? P[(jb + j) * ldp + c] : 0.f;
-    }
-    __syncthreads();
     const int64_t row = (int64_t)blockIdx.x * RB + wv * 32 + (lane & 31);
     const int h = lane >> 5, c = lane & 31;
     const bool row_ok = row < d;
     const T *wr = W + (row_ok ? row : 0) * ldw;
+    // this lane's 8 columns of each group, all loads issued before the P staging
+    typename RawOf<T>::type raw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int64_t j = jb + 16 * g + 8 * h;
+        if (row_ok)
+            raw[g] = load_raw(wr, j, d);
+        else
+            raw[g] = load_raw(wr, d, d);  // reads nothing: all zero
+    }
+#pragma unroll
+    for (int q = tid; q < KP * JC; q += 256) {
+        const int j = q / KP, cc = q % KP;  // coalesced over cc
+        Pt[cc * PL + j] = (j < jn && cc < k) ? P[(jb + j) * ldp + cc] : 0.f;
+    }
+    __syncthreads();
     f32x16_t acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < jn; j0 += 64) {  // 4 groups of 16 columns: 4 loads in flight per lane
-        float wv8[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = jb + j0 + 16 * u + 8 * h;  // this lane's 8 columns of W (zero past d)
-            if (row_ok)
-                load8<T>(wr, j, d, j + 8 <= d, wv8[u]);
-            else {
+    for (int g = 0; g < NG; ++g) {
+        float wv8[8];
+        widen(raw[g], wv8);
+        const float *pt = &Pt[c * PL + 16 * g + 8 * h];  // 16 g + 8 h + 7 < JC
+        const float4 p0 = *reinterpret_cast<const float4 *>(pt);
+        const float4 p1 = *reinterpret_cast<const float4 *>(pt + 4);
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-                for (int t = 0; t < 8; ++t) wv8[u][t] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float *pt = &Pt[c * PL + j0 + 16 * u + 8 * h];  // j0 + 16 u + 8 h + 7 < JC
-            const float4 p0 = *reinterpret_cast<const float4 *>(pt);
-            const float4 p1 = *reinterpret_cast<const float4 *>(pt + 4);
-            const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wv8[u][t], pv[t], acc, 0, 0, 0);
-        }
+        for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wv8[t], pv[t], acc, 0, 0, 0);
     }
     float *xp = Xpart + (int64_t)blockIdx.y * d * KP;
     const int64_t r0 = (int64_t)blockIdx.x * RB + wv * 32;
@@ -107,20 +141,21 @@ __global__ __launch_bounds__(256) void k_wp_part(const T *__restrict__ W, int64_
     }
 }
 
-// grid cdiv(d, RB), 256 threads: X rows of this block summed over the chunks,
+// grid cdiv(d, RR), 256 threads: X rows of this block summed over the chunks,
 // then Gpart[block][a][b] = sum_r P[r][a] X[r][b].
 __global__ __launch_bounds__(256) void k_wp_reduce(const float *__restrict__ Xpart, int nchunk, int64_t d,
                                                    const float *__restrict__ P, int64_t ldp, int k,
                                                    float *__restrict__ X, int64_t ldx, float *__restrict__ Gpart)
 {
-    __shared__ float Xs[RB * (KP + 1)], Ps[RB * (KP + 1)];
+    __shared__ float Xs[RR * (KP + 1)], Ps[RR * (KP + 1)];
     const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * RB;
-    for (int q = tid; q < RB * KP; q += 256) {
+    const int64_t r0 = (int64_t)blockIdx.x * RR;
+    for (int q = tid; q < RR * KP; q += 256) {
         const int rr = q / KP, c = q % KP;
         const int64_t r = r0 + rr;
         float x = 0.f, p = 0.f;
         if (r < d) {
+#pragma unroll 4
             for (int ch = 0; ch < nchunk; ++ch) x += Xpart[((int64_t)ch * d + r) * KP + c];
             if (c < k) {
                 p = P[r * ldp + c];
@@ -134,7 +169,8 @@ __global__ __launch_bounds__(256) void k_wp_reduce(const float *__restrict__ Xpa
     for (int q = tid; q < KP * KP; q += 256) {
         const int a = q / KP, b = q % KP;
         float g = 0.f;
-        for (int rr = 0; rr < RB; ++rr) g += Ps[rr * (KP + 1) + a] * Xs[rr * (KP + 1) + b];
+#pragma unroll 8
+        for (int rr = 0; rr < RR; ++rr) g += Ps[rr * (KP + 1) + a] * Xs[rr * (KP + 1) + b];
         Gpart[(int64_t)blockIdx.x * KP * KP + q] = g;
     }
 }
@@ -145,7 +181,7 @@ __global__ __launch_bounds__(256) void k_wp_gsum(const float *__restrict__ Gpart
 {
     const int q = blockIdx.x * 256 + threadIdx.x, a = q / KP, b = q % KP;
     float g = 0.f;
-#pragma unroll 8
+#pragma unroll 16
     for (int i = 0; i < nblk; ++i) g += Gpart[(int64_t)i * KP * KP + q];
     if (a < k && b < k) Wp[a * ldo + b] = g;
 }
@@ -155,14 +191,14 @@ __global__ __launch_bounds__(256) void k_wp_gsum(const float *__restrict__ Gpart
 size_t project_weight_workspace_bytes(int64_t d)
 {
     const size_t xpart = (size_t)cdiv_h(d, JC) * (size_t)d * KP * sizeof(float);
-    const size_t gpart = (size_t)cdiv_h(d, RB) * KP * KP * sizeof(float);
+    const size_t gpart = (size_t)cdiv_h(d, RR) * KP * KP * sizeof(float);
     return ((xpart + 255) / 256) * 256 + gpart;
 }
 
 hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int64_t d, int64_t ldw, const float *P,
                                  int64_t ldp, int k, float *Wp, int64_t ldo, float *X, int64_t ldx, void *ws)
 {
-    const int nchunk = (int)cdiv_h(d, JC), nrb = (int)cdiv_h(d, RB);
+    const int nchunk = (int)cdiv_h(d, JC), nrb = (int)cdiv_h(d, RB), nrr = (int)cdiv_h(d, RR);
     float *Xpart = (float *)ws;
     float *Gpart = (float *)((char *)ws + (((size_t)nchunk * (size_t)d * KP * sizeof(float) + 255) / 256) * 256);
     const dim3 g1((unsigned)nrb, (unsigned)nchunk);
@@ -172,9 +208,9 @@ hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int6
     else
         hipLaunchKernelGGL(k_wp_part<float>, g1, dim3(256), 0, stream, (const float *)W, ldw, d, P, ldp, k, Xpart);
     SPEC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_wp_reduce, dim3((unsigned)nrb), dim3(256), 0, stream, Xpart, nchunk, d, P, ldp, k, X, ldx,
+    hipLaunchKernelGGL(k_wp_reduce, dim3((unsigned)nrr), dim3(256), 0, stream, Xpart, nchunk, d, P, ldp, k, X, ldx,
                        Gpart);
     SPEC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_wp_gsum, dim3(KP * KP / 256), dim3(256), 0, stream, Gpart, nrb, k, Wp, ldo);
+    hipLaunchKernelGGL(k_wp_gsum, dim3(KP * KP / 256), dim3(256), 0, stream, Gpart, nrr, k, Wp, ldo);
     return hipGetLastError();
 }
