@@ -120,3 +120,39 @@ def test_project_signal_subspace_end_to_end(spec):
     # the spectrum of W to that relative level
     assert np.max(np.abs(ev - np.sort(s))) <= 0.05 * np.max(np.abs(s))
     assert abs(np.linalg.norm(wp) - np.linalg.norm(s)) <= 0.05 * np.linalg.norm(s)
+
+
+def test_low_rank_factor_eckart_young(spec):
+    """Swift-SVD-style rank-k factors from the library alone: C = W^T W
+    (SYRK), the top Ritz vectors P of C (random projection), X = W P; then
+    ||W - X P^T||_F^2 is within 1 % of the Eckart-Young optimum
+    sum_{i > k} sigma_i^2, known here by construction (W = U diag(sigma) V^T
+    with seeded orthogonal U, V)."""
+    import torch
+    print_case("low_rank_eckart_young")
+    rng = np.random.default_rng(2)
+    d, k = 1024, 16
+    sig = 10.0 * 0.7 ** np.arange(d) + 1e-3
+    U, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    V, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    W = ((U * sig) @ V.T).astype(np.float32)
+    W64 = W.astype(np.float64)
+    s_true = np.linalg.svd(W64, compute_uv=False)  # of the f32-rounded W actually used
+    opt = float(np.sum(s_true[k:] ** 2))
+    Wd = dev(W)
+    C = torch.zeros((d, d), dtype=torch.float32, device=Wd.device)
+    spec.cov_accumulate(Wd, C, alpha=1.0, beta=0.0)
+    w, P = spec.eigvecs_topk(C, dev(rng.standard_normal((d, 32)).astype(np.float32)), q=2)
+    Wp, X = spec.project_weight(Wd, P, k=k)
+    torch.cuda.synchronize()
+    Pk = P.cpu().numpy().astype(np.float64)[:, :k]
+    Xk = X.cpu().numpy().astype(np.float64)
+    err = float(np.sum((W64 - Xk @ Pk.T) ** 2))
+    print(f"[eckart-young] k={k} error {err:.6g} optimum {opt:.6g} ratio {err / opt:.6f}", flush=True)
+    assert opt <= err * (1 + 1e-9) + 1e-12  # no rank-k factor beats the optimum
+    assert err <= 1.01 * opt
+    # W' of the same basis against its fp64 value on the GPU's own P (a property
+    # of the output, not an oracle input), within the f32 bound used above
+    ref = Pk.T @ W64 @ Pk
+    bound = 2 * (d + 2) * EPS32 * (np.abs(Pk).T @ np.abs(W64) @ np.abs(Pk))
+    assert np.all(np.abs(Wp.cpu().numpy().astype(np.float64) - ref) <= bound)
