@@ -45,10 +45,11 @@ struct RawOf<float> {
     using type = RawF32;
 };
 
+template <bool FULL>
 SPEC_DEVICE RawBF16 load_raw(const uint16_t *__restrict__ row, int64_t j, int64_t d)
 {
     RawBF16 r;
-    if (j + 8 <= d) {
+    if (FULL) {
         r.u = *reinterpret_cast<const uint4 *>(row + j);
     } else {
         uint32_t w[4];
@@ -62,10 +63,11 @@ SPEC_DEVICE RawBF16 load_raw(const uint16_t *__restrict__ row, int64_t j, int64_
     }
     return r;
 }
+template <bool FULL>
 SPEC_DEVICE RawF32 load_raw(const float *__restrict__ row, int64_t j, int64_t d)
 {
     RawF32 r;
-    if (j + 8 <= d) {
+    if (FULL) {
         r.a = *reinterpret_cast<const float4 *>(row + j);
         r.b = *reinterpret_cast<const float4 *>(row + j + 4);
     } else {
@@ -87,35 +89,21 @@ SPEC_DEVICE void widen(const RawF32 &r, float (&v)[8])
     v[0] = r.a.x, v[1] = r.a.y, v[2] = r.a.z, v[3] = r.a.w, v[4] = r.b.x, v[5] = r.b.y, v[6] = r.b.z, v[7] = r.b.w;
 }
 
-// grid (cdiv(d, RB), cdiv(d, JC)), 256 threads.  Xpart[c][r][0..31].
-template <typename T>
-__global__ __launch_bounds__(256) void k_wp_part(const T *__restrict__ W, int64_t ldw, int64_t d,
-                                                 const float *__restrict__ P, int64_t ldp, int k,
-                                                 float *__restrict__ Xpart)
+// One 32-row tile of X_c for this lane's wave: W loads, basis chunk to LDS,
+// then the MFMAs group by group.  FULL: the chunk lies inside the matrix.
+template <typename T, bool FULL>
+SPEC_DEVICE f32x16_t wp_chunk(const T *__restrict__ wr, int64_t jb, int64_t d, int h, int c,
+                              const float (&pst)[KP * JC / 256], float *Pt)
 {
-    __shared__ __align__(16) float Pt[KP * PL];  // Pt[c][j - j_begin]
-    constexpr int NG = JC / 16;                   // 16-column groups per chunk
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t jb = (int64_t)blockIdx.y * JC;
-    const int jn = (int)min<int64_t>(JC, d - jb);
-    const int64_t row = (int64_t)blockIdx.x * RB + wv * 32 + (lane & 31);
-    const int h = lane >> 5, c = lane & 31;
-    const bool row_ok = row < d;
-    const T *wr = W + (row_ok ? row : 0) * ldw;
-    // this lane's 8 columns of each group, all loads issued before the P staging
+    constexpr int NG = JC / 16;  // 16-column groups per chunk
+    const int tid = threadIdx.x;
     typename RawOf<T>::type raw[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int64_t j = jb + 16 * g + 8 * h;
-        if (row_ok)
-            raw[g] = load_raw(wr, j, d);
-        else
-            raw[g] = load_raw(wr, d, d);  // reads nothing: all zero
-    }
+    for (int g = 0; g < NG; ++g) raw[g] = load_raw<FULL>(wr, jb + 16 * g + 8 * h, d);
 #pragma unroll
-    for (int q = tid; q < KP * JC; q += 256) {
-        const int j = q / KP, cc = q % KP;  // coalesced over cc
-        Pt[cc * PL + j] = (j < jn && cc < k) ? P[(jb + j) * ldp + cc] : 0.f;
+    for (int i = 0; i < KP * JC / 256; ++i) {
+        const int q = tid + 256 * i, j = q / KP, cc = q % KP;
+        Pt[cc * PL + j] = pst[i];
     }
     __syncthreads();
     f32x16_t acc;
@@ -132,6 +120,38 @@ __global__ __launch_bounds__(256) void k_wp_part(const T *__restrict__ W, int64_
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wv8[t], pv[t], acc, 0, 0, 0);
     }
+    return acc;
+}
+
+// grid (cdiv(d, RB), cdiv(d, JC)), 256 threads.  Xpart[c][r][0..31].
+template <typename T>
+__global__ __launch_bounds__(256) void k_wp_part(const T *__restrict__ W, int64_t ldw, int64_t d,
+                                                 const float *__restrict__ P, int64_t ldp, int k,
+                                                 float *__restrict__ Xpart)
+{
+    __shared__ __align__(16) float Pt[KP * PL];  // Pt[c][j - j_begin]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t jb = (int64_t)blockIdx.y * JC;
+    const int jn = (int)min<int64_t>(JC, d - jb);
+    const int64_t row = (int64_t)blockIdx.x * RB + wv * 32 + (lane & 31);
+    const int h = lane >> 5, c = lane & 31;
+    // rows past d read row d - 1 (valid memory); their outputs are never stored
+    const T *wr = W + min<int64_t>(row, d - 1) * ldw;
+    // Load order matters: memory counters retire in issue order, so the basis
+    // chunk is loaded first (the LDS stores wait for it alone), then this
+    // lane's 8 columns of every group of W, whose MFMAs each wait only for
+    // their own group while the later groups are still in flight.  The full
+    // and the ragged chunk run separate straight-line bodies: a loaded value
+    // merged across a branch would make every load wait for the previous one.
+    constexpr int PPT = KP * JC / 256;  // basis values per thread
+    float pst[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int q = tid + 256 * i, j = q / KP, cc = q % KP;  // coalesced over cc
+        pst[i] = (j < jn && cc < k) ? P[(jb + j) * ldp + cc] : 0.f;
+    }
+    const f32x16_t acc = jn == JC ? wp_chunk<T, true>(wr, jb, d, h, c, pst, Pt)
+                                  : wp_chunk<T, false>(wr, jb, d, h, c, pst, Pt);
     float *xp = Xpart + (int64_t)blockIdx.y * d * KP;
     const int64_t r0 = (int64_t)blockIdx.x * RB + wv * 32;
 #pragma unroll
@@ -155,7 +175,7 @@ __global__ __launch_bounds__(256) void k_wp_reduce(const float *__restrict__ Xpa
         const int64_t r = r0 + rr;
         float x = 0.f, p = 0.f;
         if (r < d) {
-#pragma unroll 4
+#pragma unroll 16
             for (int ch = 0; ch < nchunk; ++ch) x += Xpart[((int64_t)ch * d + r) * KP + c];
             if (c < k) {
                 p = P[r * ldp + c];
@@ -175,15 +195,24 @@ __global__ __launch_bounds__(256) void k_wp_reduce(const float *__restrict__ Xpa
     }
 }
 
-// grid KP * KP / 256, 256 threads
+// grid KP * KP / 16, 256 threads: 16 outputs per workgroup, each summed by 16
+// threads over interleaved partials, then combined in LDS
 __global__ __launch_bounds__(256) void k_wp_gsum(const float *__restrict__ Gpart, int nblk, int k,
                                                  float *__restrict__ Wp, int64_t ldo)
 {
-    const int q = blockIdx.x * 256 + threadIdx.x, a = q / KP, b = q % KP;
+    __shared__ float part[16][17];
+    const int o = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int q = blockIdx.x * 16 + o, a = q / KP, b = q % KP;
     float g = 0.f;
-#pragma unroll 16
-    for (int i = 0; i < nblk; ++i) g += Gpart[(int64_t)i * KP * KP + q];
-    if (a < k && b < k) Wp[a * ldo + b] = g;
+#pragma unroll 8
+    for (int i = sl; i < nblk; i += 16) g += Gpart[(int64_t)i * KP * KP + q];
+    part[sl][o] = g;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        float t = 0.f;
+        for (int i = 0; i < 16; ++i) t += part[i][o];
+        if (a < k && b < k) Wp[a * ldo + b] = t;
+    }
 }
 
 }  // namespace
@@ -211,6 +240,6 @@ hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int6
     hipLaunchKernelGGL(k_wp_reduce, dim3((unsigned)nrr), dim3(256), 0, stream, Xpart, nchunk, d, P, ldp, k, X, ldx,
                        Gpart);
     SPEC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_wp_gsum, dim3(KP * KP / 256), dim3(256), 0, stream, Gpart, nrr, k, Wp, ldo);
+    hipLaunchKernelGGL(k_wp_gsum, dim3(KP * KP / 16), dim3(256), 0, stream, Gpart, nrr, k, Wp, ldo);
     return hipGetLastError();
 }
