@@ -612,9 +612,13 @@ __global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, con
     // pivot rows reach the other lanes as scalars (readlane)
     const int lane = threadIdx.x;
     const int i = lane & 31;
-    T m[NB];
+    T m[NB], rf[NB];  // row i of Q1 and of the stacked R, both loaded up front:
+                      // a load under the store loop's branch would wait for
+                      // every store before it
 #pragma unroll
     for (int j = 0; j < NB; ++j) m[j] = Q1[i * NB + j];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) rf[j] = Rf[i * NB + j];
     T si = 0;  // S[i]
     T sv[NB];  // S, the same in every lane
     static_for<0, NB>([&](auto KC) {
@@ -661,7 +665,7 @@ __global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, con
             Tm[i * NB + j] = z[j];
             Ug[i * NB + j] = j >= i ? m[j] : (T)0;
             V[i * NB + j] = i == j ? (T)1 : (i > j ? m[j] : (T)0);
-            if (i <= j) Pg[i * lda + j] = si * Rf[i * NB + j];  // R_panel = S R
+            if (i <= j) Pg[i * lda + j] = si * rf[j];  // R_panel = S R
         }
     }
 }
