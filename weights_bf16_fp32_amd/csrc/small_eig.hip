@@ -226,20 +226,30 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
     const bool live = b < batch;
     const bool rowok = live && i < n;
 
+    // Every load is unconditional, at indices clamped into the matrix (row and
+    // column n - 1 at most), and masked afterwards: a load under a branch
+    // would wait for the one before it.
     float a[NM];
+    const int ic = min(i, n - 1);
     if (src.kind == SPEC_SRC_DENSE) {
         const float *base = src.a + (live ? b : 0) * src.stride_a;
 #pragma unroll
-        for (int j = 0; j < NM; ++j)
-            a[j] = rowok && j < n ? base[(int64_t)max(i, j) * src.lda + min(i, j)] : 0.f;
+        for (int j = 0; j < NM; ++j) {
+            const int jc = min(j, n - 1);
+            const float v = base[(int64_t)max(ic, jc) * src.lda + min(ic, jc)];
+            a[j] = rowok && j < n ? v : 0.f;
+        }
     } else {
         const int64_t W = (src.T - n) / src.stride + 1;
         const int64_t bb = live ? b : 0;
         const int64_t s = bb / W, win = bb % W;
         const float *base = src.a + (s * src.T + win * src.stride) * n;
 #pragma unroll
-        for (int j = 0; j < NM; ++j)
-            a[j] = rowok && j < n ? src.scale * base[(int64_t)max(i, j) * n + abs(i - j)] : 0.f;
+        for (int j = 0; j < NM; ++j) {
+            const int jc = min(j, n - 1);
+            const float v = base[(int64_t)max(ic, jc) * n + abs(ic - jc)];
+            a[j] = rowok && j < n ? src.scale * v : 0.f;
+        }
     }
     bool fin = true;
 #pragma unroll
