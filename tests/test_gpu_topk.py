@@ -136,3 +136,40 @@ def test_eigvecs_low_rank_subspace(spec):
     assert np.max(np.abs(wg[:6] - lam[:6])) <= 1e-4 * lam[0]
     dots = np.abs(np.einsum("ij,ij->j", Pg[:, :6], Q[:, :6]))
     assert np.all(dots >= 1 - 1e-4), dots
+
+
+@pytest.mark.parametrize("case", ["min64", "ragged777", "zero", "identity"])
+def test_eigvecs_edge_cases(spec, case):
+    """The smallest size, a ragged size with a wider P, and two degenerate
+    matrices: A = 0 (every Ritz value 0; P must still be orthonormal and
+    finite) and A = I (every Ritz value 1, any orthonormal P is right)."""
+    import torch
+    print_case("eigvecs_edge", case=case)
+    rng = np.random.default_rng({"min64": 64, "ragged777": 777, "zero": 5, "identity": 6}[case])
+    d = {"min64": 64, "ragged777": 777, "zero": 256, "identity": 256}[case]
+    if case == "zero":
+        A = np.zeros((d, d), np.float32)
+    elif case == "identity":
+        A = np.eye(d, dtype=np.float32)
+    else:
+        A = _cov(rng, 2 * d, d, spikes=np.geomspace(30, 3, 6))
+    Om = rng.standard_normal((d, 32)).astype(np.float32)
+    ldp = 48 if case == "ragged777" else 32
+    Pbuf = torch.full((d, ldp), 5.0, dtype=torch.float32, device="cuda")
+    w, P = spec.eigvecs_topk(dev(A), dev(Om), q=2, P=Pbuf[:, :32])
+    torch.cuda.synchronize()
+    wg = w.cpu().numpy().astype(np.float64)
+    Pb = Pbuf.cpu().numpy().astype(np.float64)
+    Pg = Pb[:, :32]
+    assert np.all(np.isfinite(wg)) and np.all(np.isfinite(Pg))
+    assert np.all(Pb[:, 32:] == 5.0)
+    assert np.max(np.abs(Pg.T @ Pg - np.eye(32))) <= 1e-4
+    if case == "zero":
+        assert np.all(wg == 0.0)
+    elif case == "identity":
+        assert np.max(np.abs(wg - 1.0)) <= 1e-5
+    else:
+        tr, Pr = oracle.topk_ritz_vectors(A.astype(np.float64), Om, 2)
+        assert np.max(np.abs(wg - tr)) <= 1e-4 * tr[0]
+        rq = np.einsum("ij,ij->j", Pg, A.astype(np.float64) @ Pg)
+        assert np.max(np.abs(rq - wg)) <= 1e-4 * tr[0]
