@@ -1008,26 +1008,17 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
             const bool ok = !diag || rl + dr >= cl + qb * 32;
             return ok ? vbase + (uint32_t)(dr * (int)lda + qb * 32) * 4u : 0x80000000u;
         };
-        // the old values are requested first: their loads are in flight while
-        // the panel blocks are staged and the MFMAs run
-        float old[2][2][16];
-        if (live) {
-#pragma unroll
-            for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        old[qa][qb][e] = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)eoff(qa, qb, e), 0, 0));
-        }
         // L = [V | Z] rows i0.., R = [Z | V] rows j0..
 #pragma unroll
         for (int q = 0; q < S2_T * NB / 256; ++q) {
             const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
             const int i = i0 + r, j = j0 + r;
-            const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
-            const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
+            // rows clamped to m - 1 and masked: unconditional loads stay in flight
+            // together (a load under a branch would wait for all before it)
+            const int64_t ic = min(i, m - 1), jc = min(j, m - 1);
+            const T v_i = V[ic * NB + c], z_i = Z[ic * NB + c], v_j = V[jc * NB + c], z_j = Z[jc * NB + c];
+            const T vi = i < m ? v_i : (T)0, zi = i < m ? z_i : (T)0;
+            const T vj = j < m ? v_j : (T)0, zj = j < m ? z_j : (T)0;
             Ls[r * (S2_K + 1) + c] = vi;
             Ls[r * (S2_K + 1) + NB + c] = zi;
             Rs[r * (S2_K + 1) + c] = zj;
@@ -1035,6 +1026,18 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
         }
         __syncthreads();
         if (!live) return;
+        // the old values are requested after the staging (memory counters
+        // retire in issue order, so earlier they would hold up the LDS stores)
+        // and are in flight while the MFMAs run
+        float old[2][2][16];
+#pragma unroll
+        for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    old[qa][qb][e] =
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)eoff(qa, qb, e), 0, 0));
         f32x16_t acc[2][2] = {};
 #pragma unroll 4
         for (int kk = 0; kk < S2_K; kk += 2) {
@@ -1064,8 +1067,12 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
         for (int q = 0; q < S2_T * NB / 256; ++q) {
             const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
             const int i = i0 + r, j = j0 + r;
-            const T vi = i < m ? V[(int64_t)i * NB + c] : (T)0, zi = i < m ? Z[(int64_t)i * NB + c] : (T)0;
-            const T vj = j < m ? V[(int64_t)j * NB + c] : (T)0, zj = j < m ? Z[(int64_t)j * NB + c] : (T)0;
+            // rows clamped to m - 1 and masked: unconditional loads stay in flight
+            // together (a load under a branch would wait for all before it)
+            const int64_t ic = min(i, m - 1), jc = min(j, m - 1);
+            const T v_i = V[ic * NB + c], z_i = Z[ic * NB + c], v_j = V[jc * NB + c], z_j = Z[jc * NB + c];
+            const T vi = i < m ? v_i : (T)0, zi = i < m ? z_i : (T)0;
+            const T vj = j < m ? v_j : (T)0, zj = j < m ? z_j : (T)0;
             Ls[r * (S2_K + 1) + c] = vi;
             Ls[r * (S2_K + 1) + NB + c] = zi;
             Rs[r * (S2_K + 1) + c] = zj;
