@@ -865,16 +865,27 @@ __global__ __launch_bounds__(256) void k_xreduce(const T *__restrict__ Xpart, in
         const int idx = tid + 256 * q;
         vv[q] = idx / NB < rows ? V[(int64_t)r0 * NB + idx] : (T)0;
     }
-    for (int p = 0; p < ks; ++p) {
-        const T *src = Xpart + (int64_t)p * m * NB + (int64_t)r0 * NB;
-        T part[PER];
+    // four partitions per round, every load unconditional (partition and row
+    // clamped, the value masked): one round trip per four partitions instead
+    // of one per partition
+    for (int p = 0; p < ks; p += 4) {
+        T part[4][PER];
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int idx = tid + 256 * q;
-            part[q] = idx / NB < rows ? src[idx] : (T)0;
+        for (int u = 0; u < 4; ++u) {
+            const T *src = Xpart + (int64_t)min(p + u, ks - 1) * m * NB + (int64_t)r0 * NB;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int idx = tid + 256 * q;
+                part[u][q] = src[idx / NB < rows ? idx : (rows - 1) * NB + idx % NB];
+            }
         }
 #pragma unroll
-        for (int q = 0; q < PER; ++q) acc[q] += part[q];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int idx = tid + 256 * q;
+                acc[q] += (p + u < ks && idx / NB < rows) ? part[u][q] : (T)0;
+            }
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
