@@ -930,17 +930,19 @@ __global__ __launch_bounds__(256) void k_mz(const T *__restrict__ Ppart, int nbl
     T acc[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) acc[q] = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 8) {
-        T part[8][PER];
+    // 16 partial blocks per round, every load unconditional (block index
+    // clamped, the value masked) so that a round is one round trip
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+        T part[16][PER];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
 #pragma unroll
             for (int q = 0; q < PER; ++q)
-                part[u][q] = b0 + u < nblk ? Ppart[(int64_t)(b0 + u) * NB * NB + tid + 256 * q] : (T)0;
+                part[u][q] = Ppart[(int64_t)min(b0 + u, nblk - 1) * NB * NB + tid + 256 * q];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
 #pragma unroll
-            for (int q = 0; q < PER; ++q) acc[q] += part[u][q];
+            for (int q = 0; q < PER; ++q) acc[q] += b0 + u < nblk ? part[u][q] : (T)0;
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -968,9 +970,11 @@ __global__ __launch_bounds__(256) void k_mz(const T *__restrict__ Ppart, int nbl
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t r = r0 + u * stride;
+            const int64_t rc = r < m ? r : m - 1;  // clamped: unconditional loads (the
+                                                   // values of a row past m are never stored)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) vrow[u][j] = r < m ? V[r * NB + j] : (T)0;
-            x[u] = r < m ? X[r * NB + c] : (T)0;
+            for (int j = 0; j < NB; ++j) vrow[u][j] = V[rc * NB + j];
+            x[u] = X[rc * NB + c];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
