@@ -671,8 +671,12 @@ __global__ __launch_bounds__(64) void k_tsqr_recon(const T *__restrict__ Q1, con
 }
 
 // ---- V rows r_q1.. = Q1 rows U^{-1} (TSQR step 5; rows below r_q1 are already
-// in V), then W = V T, one row per thread
-constexpr int VW_T = 128;
+// in V), then W = V T.  32 lanes per row (lane c owns column c), two rows per
+// wave: the forward substitution and the product walk j = 0..31, y_j reaching
+// every lane of its row by readlane (lane j, or j + 32 for the upper row), so
+// a panel of m rows runs m / 2 waves instead of m / 64.
+constexpr int VW_T = 256;
+constexpr int VW_R = VW_T / NB;  // rows per workgroup
 
 template <typename T>
 __global__ __launch_bounds__(VW_T) void k_vw(const T *__restrict__ Q1, const T *__restrict__ Ug,
@@ -686,32 +690,43 @@ __global__ __launch_bounds__(VW_T) void k_vw(const T *__restrict__ Q1, const T *
         Ts[(p / NB) * LDP + p % NB] = Tm[p];
     }
     __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * VW_T + tid;
-    if (r >= m) return;
-    T y[NB];
-    if (r < r_q1) {
+    const int c = tid & 31, hi = (tid >> 5) & 1;
+    const int64_t r = (int64_t)blockIdx.x * VW_R + (tid >> 5);
+    const bool ok = r < m;
+    const int64_t rc = ok ? r : m - 1;  // rows past m repeat row m - 1 and store nothing
+    T tcol[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) y[j] = V[r * NB + j];
+    for (int j = 0; j < NB; ++j) tcol[j] = Ts[j * LDP + c];
+    T yc;
+    // r_q1 is m (every row, the repeated ones too, takes the first side) or NB,
+    // which is even: the two rows of a wave, 2w and 2w + 1, take the same side
+    if (rc < r_q1) {
+        yc = V[rc * NB + c];
     } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) y[j] = Q1[r * NB + j];
+        T ucol[NB], udg[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            T s = y[j];
-#pragma unroll
-            for (int l = 0; l < j; ++l) s -= y[l] * U[l * LDP + j];
-            y[j] = s / U[j * LDP + j];
+            ucol[j] = U[j * LDP + c];
+            udg[j] = U[j * LDP + j];
         }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) V[r * NB + j] = y[j];
+        T sc = Q1[rc * NB + c];
+        yc = 0;
+        static_for<0, NB>([&](auto JC) {
+            constexpr int j = decltype(JC)::value;
+            const T lo = readlane_t(sc, j), up = readlane_t(sc, j + 32);
+            const T yj = (hi ? up : lo) / udg[j];
+            if (c == j) yc = yj;
+            if (c > j) sc -= yj * ucol[j];
+        });
+        if (ok) V[r * NB + c] = yc;
     }
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-        T s = 0;
-#pragma unroll
-        for (int j = 0; j <= c; ++j) s += y[j] * Ts[j * LDP + c];  // T is upper triangular
-        W[r * NB + c] = s;
-    }
+    T wc = 0;
+    static_for<0, NB>([&](auto JC) {
+        constexpr int j = decltype(JC)::value;
+        const T lo = readlane_t(yc, j), up = readlane_t(yc, j + 32);
+        if (j <= c) wc += (hi ? up : lo) * tcol[j];  // T is upper triangular
+    });
+    if (ok) W[r * NB + c] = wc;
 }
 
 // ---- X partials = A22[rows, jrange] W[jrange]  (A22 lower-stored symmetric)
@@ -1815,7 +1830,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             LAUNCH_OK();
         }
         // V rows below the reconstructed top block (TSQR), then W = V T
-        hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_T)), dim3(VW_T), 0, st, b.Q1, b.U, b.Tm, (int)m,
+        hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_R)), dim3(VW_T), 0, st, b.Q1, b.U, b.Tm, (int)m,
                            m <= DIRECT_ROWS ? (int)m : NB, b.V, b.W);
         LAUNCH_OK();
         const int nrb = (int)cdiv_h(m, SY_RB);
