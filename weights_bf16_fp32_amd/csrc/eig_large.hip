@@ -1911,9 +1911,8 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
 {
     constexpr int L = NB + 1, EPT = NB * NB / 256;
     __shared__ float Bs[2][NB * L], Vs[2][NB * L];
-    __shared__ float4 cf[NB];  // per index: (al, be, new diagonal, 1 if its pair rotates)
+    __shared__ float4 cf[4][NB];  // per wave, per index: (al, be, new diagonal, 1 if its pair rotates)
     __shared__ float red[8];
-    __shared__ int step_on;
     const int tid = threadIdx.x;
     float bmax = 0.f;
     {
@@ -1945,13 +1944,18 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
     }
     const float floor_abs = 1e-7f * bmax;
     int cur = 0;
+    const int wv = tid >> 6, lane = tid & 63;
     for (int sweep = 0; sweep < 30; ++sweep) {
         int any = 0;
         for (int r = 0; r < NB - 1; ++r) {
             auto partner = [r](int i) { return i == NB - 1 ? r : (i == r ? NB - 1 : (2 * r - i + 2 * (NB - 1)) % (NB - 1)); };
+            // Every wave computes the step's rotations itself (lanes 0-31, one
+            // index each) into its own slot: all waves read the same B, so their
+            // coefficients and their skip decision agree, and one workgroup
+            // barrier per step (after the update) is enough.
             int on = 0;
-            if (tid < NB) {  // the rotation of index tid's pair (both members compute it alike)
-                const int i = tid, j = partner(i), p = min(i, j), q = max(i, j);
+            if (lane < NB) {  // the rotation of index lane's pair (both members compute it alike)
+                const int i = lane, j = partner(i), p = min(i, j), q = max(i, j);
                 const float *B = Bs[cur];
                 const float apq = B[p * L + q], app = B[p * L + p], aqq = B[q * L + q];
                 float a = 1.f, bb = 0.f, d = B[i * L + i];
@@ -1969,26 +1973,22 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
                     d = i == p ? app - t * apq : aqq + t * apq;
                     on = 1;
                 }
-                cf[i] = make_float4(a, bb, d, on ? 1.f : 0.f);
-                any |= on;
-                const int flag = __ballot(on) != 0;
-                if (tid == 0) step_on = flag;
+                cf[wv][i] = make_float4(a, bb, d, on ? 1.f : 0.f);
             }
-            __syncthreads();
-            if (!step_on) {  // no pair rotates in this step
-                __syncthreads();  // every read of step_on precedes its next write
-                continue;
-            }
+            const bool step_on = __ballot(on) != 0;  // the same in every wave
+            if (!step_on) continue;                  // B unchanged: nothing to order
+            any = 1;
+            wave_sync();  // this wave's coefficients are in LDS
             const float *B = Bs[cur];
             const float *V = Vs[cur];
             float *Bn = Bs[cur ^ 1];
             float *Vn = Vs[cur ^ 1];
             const int j = tid % NB, pj = partner(j);  // the same column in every k
-            const float4 cj = cf[j];
+            const float4 cj = cf[wv][j];
 #pragma unroll
             for (int k = 0; k < EPT; ++k) {
                 const int i = tid / NB + (256 / NB) * k, pi = partner(i);
-                const float4 ci = cf[i];
+                const float4 ci = cf[wv][i];
                 const float b00 = B[i * L + j], b01 = B[i * L + pj], b10 = B[pi * L + j], b11 = B[pi * L + pj];
                 const float v0 = V[i * L + j], v1 = V[i * L + pj];
                 float v = ci.x * (cj.x * b00 + cj.y * b01) + ci.y * (cj.x * b10 + cj.y * b11);
@@ -1998,9 +1998,9 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
                 Vn[i * L + j] = cj.x * v0 + cj.y * v1;
             }
             cur ^= 1;
-            __syncthreads();
+            __syncthreads();  // the new B and V are complete; the old ones are no longer read
         }
-        if (!__syncthreads_or(any)) break;
+        if (!any) break;  // the same in every wave
     }
     // rank of eigenvalue i among the diagonal (descending, ties by index)
     if (tid < NB) {
