@@ -7,6 +7,7 @@ wrong sign, a wrong index or a transposed operand in the oracle fails one of
 them.  No test here needs a GPU.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -209,6 +210,47 @@ def test_descriptors_diagonal_identity_rank1():
     assert Dn["r_pos"] == 2 and Dn["tail_min"] == 0.0
 
 
+def test_descriptors_sigma2_mean_from_the_data():
+    # MEAN: sigma^2 = tr C / p.  For C = alpha X^T X that is alpha ||X||_F^2 / p,
+    # computed here from X itself, whatever the number r of eigenvalues handed
+    # over: the n nonzero eigenvalues of the Gram (r = n < p) or all p of them.
+    rng = np.random.default_rng(31)
+    for n, p, alpha in [(30, 200, 1.0 / 30), (500, 60, 1.0), (64, 32, 1.0 / 64)]:
+        X = rng.standard_normal((n, p)) * 1.5
+        fro2 = float(np.sum(X * X))
+        if n < p:
+            w = np.linalg.eigvalsh(alpha * (X @ X.T))  # r = n values
+        else:
+            w = np.linalg.eigvalsh(alpha * (X.T @ X))  # r = p values
+        assert w.size != p or n >= p
+        D = oracle.descriptors(w, n_samples=n, p_dim=p, k=1, sigma2_mode=oracle.SIGMA2_MEAN)
+        s2 = alpha * fro2 / p
+        assert abs(D["sigma2"] - s2) <= 1e-12 * s2
+        lp = s2 * (1.0 + math.sqrt(p / n)) ** 2
+        assert abs(D["lambda_plus"] - lp) <= 1e-12 * lp
+        assert D["n_above"] == int(np.sum(w > lp))
+    # a spectrum with one value far out: sigma^2 = 23 / 4, lambda_plus = 5.75 (1 + 1)^2 = 23,
+    # so 20 is below the edge and only a value above 23 would count
+    D = oracle.descriptors([20.0, 1.0, 1.0, 1.0], n_samples=4, p_dim=4, sigma2_mode=oracle.SIGMA2_MEAN)
+    assert D["sigma2"] == 23.0 / 4 and D["lambda_plus"] == 23.0 and D["n_above"] == 0
+
+
+def test_descriptors_sigma2_median_by_hand():
+    # odd r: median of (5, 1, 3) is 3; c = 3 / 12 -> lambda_plus = 3 (1 + 1/2)^2 = 6.75
+    D = oracle.descriptors([5.0, 1.0, 3.0], n_samples=12, p_dim=3, sigma2_mode=oracle.SIGMA2_MEDIAN)
+    assert D["sigma2"] == 3.0 and D["lambda_plus"] == 6.75 and D["n_above"] == 0
+    # even r: the mean of the two middle values, (6 + 2) / 2 = 4; c = 1 -> lambda_plus = 16
+    D = oracle.descriptors([8.0, 0.0, 6.0, 2.0, 17.0, 1.0], n_samples=6, p_dim=6,
+                           sigma2_mode=oracle.SIGMA2_MEDIAN)
+    assert D["sigma2"] == (6.0 + 2.0) / 2 and D["lambda_plus"] == 16.0 and D["n_above"] == 1
+    # negative round-off is clamped before the median: (-1e-9, 0, 0, 7) -> (0 + 0) / 2
+    D = oracle.descriptors([-1e-9, 0.0, 0.0, 7.0], n_samples=8, p_dim=4, sigma2_mode=oracle.SIGMA2_MEDIAN)
+    assert D["sigma2"] == 0.0 and math.isnan(D["mp_w1"])
+    # GIVEN ignores the spectrum
+    D = oracle.descriptors([5.0, 1.0, 3.0], n_samples=12, p_dim=3, sigma2=0.5)
+    assert D["sigma2"] == 0.5 and D["lambda_plus"] == 0.5 * 2.25
+
+
 def test_descriptors_singular_mode_counts():
     d = 4096
     sig = synth.s3_sigma(d)
@@ -404,6 +446,31 @@ def test_kl_pins():
     assert abs(a - b) <= 1e-12
 
 
+def test_kl_sigma2_modes_by_hand():
+    # lambda = 9, 3, 1, 1, 1 with p = 5, n = 20 (c = 0.25) and 10 bins: the MP support
+    # is [0.25, 2.25] sigma^2 and a value v falls in bin floor((v / sigma^2 - 0.25) / 0.2),
+    # clamped to [0, 9].  By hand, per sigma^2 mode:
+    #   MEDIAN  sigma^2 = 1:                       1 -> 3.75 (bin 3); 3, 9 -> bin 9
+    #   MEAN    sigma^2 = 15 / 5 = 3:              1 -> 0.42 (bin 0); 3 -> 3.75 (bin 3); 9 -> bin 9
+    #   WINSOR  (q = 1: 1,1,1,3,3) sigma^2 = 1.8:  1 -> 1.53 (bin 1); 3 -> 7.08 (bin 7); 9 -> bin 9
+    #   GIVEN   sigma^2 = 0.5:                     1 -> 8.75 (bin 8); 3, 9 -> bin 9
+    # The MP bin masses depend on c only (sigma^2 scales the support), pinned by
+    # quadrature in test_mp_bin_masses_by_quadrature.
+    lam = [9.0, 3.0, 1.0, 1.0, 1.0]
+    q = oracle.mp_bin_masses(1.0, 0.25, 10)
+    assert np.allclose(oracle.mp_bin_masses(3.7, 0.25, 10), q, rtol=0, atol=1e-13)
+    cases = [(oracle.SIGMA2_MEDIAN, 1.0, {3: 0.6, 9: 0.4}),
+             (oracle.SIGMA2_MEAN, 3.0, {0: 0.6, 3: 0.2, 9: 0.2}),
+             (oracle.SIGMA2_WINSOR, 1.8, {1: 0.6, 7: 0.2, 9: 0.2}),
+             (oracle.SIGMA2_GIVEN, 0.5, {8: 0.6, 9: 0.4})]
+    for mode, s2, bins in cases:
+        r = oracle.robust_stats(lam, n_samples=20, p_dim=5, sigma2=0.5, sigma2_mode=mode,
+                                winsor_frac=0.2, bins=10)
+        assert abs(r["sigma2"] - s2) <= 1e-15 * s2, mode
+        kl = sum(pb * math.log(pb / q[b]) for b, pb in bins.items())
+        assert abs(r["kl_mp"] - kl) <= 1e-12 * abs(kl), (mode, r["kl_mp"], kl)
+
+
 # ------------------------------------------------------------- randomised top eigenvalues
 
 def _spd_with_spectrum(rng, lam):
@@ -509,3 +576,42 @@ def test_project_weight_pins():
     Wb = (rng.standard_normal((d, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(oracle.project_weight(Wb, P)[0], oracle.project_weight(Wf, P)[0])
+
+
+# ------------------------------------------------------------- P3 at the full sizes
+
+def test_swiftsvd_golden_vs_lapack():
+    """The stored oracle spectrum of the 4096 Swift-SVD covariance (the values the
+    GPU parity test compares with) against LAPACK's eigvalsh of the same fp64
+    matrix, rebuilt here chunk by chunk with the oracle's covariance."""
+    import json
+    import os
+    z = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "swiftsvd.npz"))
+    d = 4096
+    acc = np.zeros((d, d))
+    hashes = []
+    for k in range(32):
+        X = synth.swiftsvd_chunk(k)
+        hashes.append(synth.sha256(X))
+        acc = oracle.covariance(X, "bf16", 1.0, C0=acc, beta=1.0)
+    assert ",".join(hashes) == str(z["sha256"])
+    assert abs(np.trace(acc) - float(z["trace"])) <= 1e-13 * float(z["trace"])
+    ref = np.linalg.eigvalsh(acc)[::-1]
+    eig = z["eig"]
+    assert np.max(np.abs(eig - ref)) <= 1e-12 * ref[0]
+    assert json.loads(str(z["desc_json"]))["S"] == pytest.approx(float(np.sum(ref)), rel=1e-12)
+
+
+@pytest.mark.skipif(not os.environ.get("SPEC_HEAVY_PINS"),
+                    reason="minutes of CPU and ~6 GB of memory; set SPEC_HEAVY_PINS=1 to run")
+def test_ffn_golden_vs_lapack():
+    """The stored oracle spectrum of the 14336 FFN covariance against LAPACK's
+    eigvalsh of the same fp64 matrix (C = X^T X / 65536 of the regenerated input)."""
+    z = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "ffn.npz"))
+    X = synth.ffn()
+    assert synth.sha256(X) == str(z["sha256"])
+    C = oracle.covariance(X, "bf16", 1.0 / 65536)
+    del X
+    ref = np.linalg.eigvalsh(C)[::-1]
+    assert np.max(np.abs(z["eig"] - ref)) <= 1e-12 * ref[0]
+    assert int(z["n_above_inertia"]) == int(np.sum(ref > oracle.mp_edges(1.0, 14336 / 65536)[1]))
