@@ -14,7 +14,12 @@
  *     error the call returns a negative spec_status and enqueues nothing.  A
  *     failed kernel launch returns SPEC_EHIP.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
- *   - Device pointers must be 16-byte aligned (4-byte for int32 outputs).
+ *   - Alignment: every device pointer must be aligned to its element size (2 bytes
+ *     for bf16, 4 for f32 and int32, 8 for f64 and the descriptor records);
+ *     workspaces must be 256-byte aligned; entry points that need more say so.
+ *     A violation returns SPEC_EINVAL.  Where a pointer is 16-byte aligned and
+ *     its leading dimension a multiple of 16 bytes, a faster kernel is chosen
+ *     (spec_cov_accumulate); otherwise a general one computes the same result.
  *   - The library holds no state between calls and is thread-safe; calls that
  *     share output or workspace buffers on different streams race, as any
  *     stream-ordered work does.
@@ -115,8 +120,7 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
  * w:    f32 [batch][n], eigenvalues descending.
  * info: int32 [batch] (may be NULL): the number of bisection rounds (>= 0), or -1
  *       if the matrix has a non-finite entry (its eigenvalues are then NaN).
- * max_sweeps in [1, 100]: validated and otherwise unused (the method is direct;
- *       the argument keeps the call's shape for callers of iterative solvers).
+ * The method is direct (no sweep limit to choose).
  * ---------------------------------------------------------------------- */
 enum { SPEC_SRC_DENSE = 0, SPEC_SRC_BAND = 1 };
 
@@ -132,7 +136,7 @@ typedef struct {
 } spec_batch_src;
 
 int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w,
-                          int max_sweeps, int32_t *info);
+                          int32_t *info);
 
 /* ------------------------------------------------------------------------
  * A4  Large symmetric eigenvalues (the single eigendecomposition of the
@@ -188,8 +192,9 @@ int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t ld
  * ("Random matrix theory spectral methods" page, section 4.1: the
  * eigenvectors whose eigenvalues lie beyond the MP edge lambda_plus span the
  * signal subspace, P = [u_1 .. u_k]).  The same range finder as
- * spec_eigvalsh_topk, then the eigenvectors U of B = Q^T A Q (32 x 32, cyclic
- * Jacobi in one wave) and P = Q U.  Column i of P is the Ritz vector of w[i]
+ * spec_eigvalsh_topk, then the eigenvectors U of B = Q^T A Q (32 x 32, Jacobi
+ * with round-robin pair ordering, 16 disjoint rotations per step, in one
+ * workgroup) and P = Q U.  Column i of P is the Ritz vector of w[i]
  * (w descending); the columns are orthonormal to f32 rounding, each with an
  * arbitrary sign.  The caller keeps the leading columns whose Ritz value
  * exceeds its lambda_plus.
@@ -199,11 +204,16 @@ int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t ld
  *      spec_eigvalsh_topk up to the rounding of the small eigensolver).
  * P:   f32 [n][ldp] device, row-major; columns 0..31 of each row written,
  *      the rest untouched.  Must not overlap A, Omega, w or ws.
+ * info: int32 [1] device (may be NULL): 0 when the Jacobi sweeps converged;
+ *      1 when Q^T A Q has a NaN or Inf entry (non-finite A or Omega): every
+ *      value of w and of P's 32 columns is then NaN; 2 when the sweep limit
+ *      (30) was reached first (the values and vectors are the last iterate).
+ *      Every slot of w and P is written in all three cases.
  * Requires 32 <= ldp < 2^22 and the conditions of spec_eigvalsh_topk;
  * else SPEC_EINVAL (SPEC_EUNSUPPORTED for t != SPEC_F32).
  * ---------------------------------------------------------------------- */
 int spec_eigvecs_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
-                      void *P, int64_t ldp, void *ws, size_t ws_bytes);
+                      void *P, int64_t ldp, void *ws, size_t ws_bytes, int32_t *info);
 
 /* ------------------------------------------------------------------------
  * Projection compression of a square weight ("Random matrix theory spectral
@@ -352,6 +362,39 @@ int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t
 
 int spec_spectrum_robust(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                          const spec_robust_params *p, spec_robust *out);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing for measurement tools (not part of the computation).
+ *
+ * spec_timing_enable(mask): from now on, every launch of a kernel whose bit
+ *   (1 << SPEC_KT_*) is set in `mask` is bracketed by two HIP events recorded
+ *   on the stream it is launched on; earlier records are discarded.  mask = 0
+ *   stops recording.  The first non-zero call creates a pool of 16384 event
+ *   pairs (host-side HIP objects; no device memory), kept until the process
+ *   ends; launches beyond the pool are not timed.  Returns SPEC_EHIP if the
+ *   events cannot be created.
+ * spec_timing_read(kernel, &total_ms, &launches): waits for the recorded end
+ *   events of that kernel (the one call here that blocks the host) and returns
+ *   the summed device time in milliseconds and the number of timed launches;
+ *   SPEC_EWORKSPACE when some launches were not timed for lack of events.
+ * Not thread-safe with respect to concurrent measurement sessions.
+ * ---------------------------------------------------------------------- */
+enum {
+    SPEC_KT_SYRK = 0,      /* spec_cov_accumulate's kernel */
+    SPEC_KT_GRAM = 1,      /* spec_gram_window's kernel */
+    SPEC_KT_SMALL_EIG = 2, /* spec_eigvalsh_batched's kernel */
+    SPEC_KT_DESC = 3,      /* spec_descriptors' record kernel */
+    SPEC_KT_SYMM = 4,      /* spec_eigvalsh_large, stage 1: A (V T) products */
+    SPEC_KT_SYR2K = 5,     /* stage 1: rank-2k trailing updates */
+    SPEC_KT_PANEL = 6,     /* stage 1: panel factorisations (TSQR, reconstruction, V/W, M/Z) */
+    SPEC_KT_BULGE = 7,     /* stage 2: bulge chasing */
+    SPEC_KT_TRIDIAG = 8,   /* stage 3: tridiagonal eigenvalues */
+    SPEC_KT_COUNT = 9
+};
+
+int spec_timing_enable(unsigned kernels);
+
+int spec_timing_read(int kernel, double *total_ms, int64_t *launches);
 
 #ifdef __cplusplus
 }

@@ -86,13 +86,41 @@ def test_gram_validation(L):
 def test_batched_validation(L):
     f = L.spec_eigvalsh_batched
     src = spec.BatchSrc(spec.SRC_DENSE, FAKE, 30, 900, 0, 0, 1, 1.0)
-    assert f(None, ctypes.byref(src), 4, 65, FAKE, 15, None) == EUNSUPPORTED
-    assert f(None, ctypes.byref(src), 4, 0, FAKE, 15, None) == EINVAL
-    assert f(None, ctypes.byref(src), 4, 30, FAKE, 0, None) == EINVAL
-    assert f(None, ctypes.byref(src), 4, 31, FAKE, 15, None) == EINVAL  # lda < n
+    assert f(None, ctypes.byref(src), 4, 65, FAKE, None) == EUNSUPPORTED
+    assert f(None, ctypes.byref(src), 4, 0, FAKE, None) == EINVAL
+    assert f(None, ctypes.byref(src), 4, 31, FAKE, None) == EINVAL  # lda < n
     band = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 100, 1, 1 / 30)
-    assert f(None, ctypes.byref(band), 2 * 70, 30, FAKE, 15, None) == EINVAL  # batch != S * W
-    assert f(None, None, 4, 30, FAKE, 15, None) == EINVAL
+    assert f(None, ctypes.byref(band), 2 * 70, 30, FAKE, None) == EINVAL  # batch != S * W
+    assert f(None, None, 4, 30, FAKE, None) == EINVAL
+
+
+def test_alignment_codes(L):
+    """Every device pointer must be aligned to its element size, workspaces to 256
+    bytes, and the large eigensolver's A to 16 bytes; anything less is SPEC_EINVAL."""
+    cov = L.spec_cov_accumulate
+    assert cov(None, FAKE + 1, spec.BF16, 10, 8, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL  # bf16 X, odd
+    assert cov(None, FAKE + 2, spec.F32, 10, 8, 8, FAKE, spec.F32, 8, 1.0, 0.0) == EINVAL   # f32 X, 2 bytes
+    assert cov(None, FAKE, spec.F32, 10, 8, 8, FAKE + 4, spec.F64, 8, 1.0, 0.0) == EINVAL   # f64 C, 4 bytes
+    gram = L.spec_gram_window
+    assert gram(None, FAKE + 1, spec.BF16, 2, 100, 64, 64, 6400, 30, 1, 1.0, spec.GRAM_BAND, FAKE) == EINVAL
+    assert gram(None, FAKE, spec.BF16, 2, 100, 64, 64, 6400, 30, 1, 1.0, spec.GRAM_BAND, FAKE + 2) == EINVAL
+    bat = L.spec_eigvalsh_batched
+    src = spec.BatchSrc(spec.SRC_DENSE, FAKE + 2, 30, 900, 0, 0, 1, 1.0)
+    assert bat(None, ctypes.byref(src), 4, 30, FAKE, None) == EINVAL
+    src = spec.BatchSrc(spec.SRC_DENSE, FAKE, 30, 900, 0, 0, 1, 1.0)
+    assert bat(None, ctypes.byref(src), 4, 30, FAKE, FAKE + 2) == EINVAL  # info
+    b = ctypes.c_size_t(0)
+    L.spec_eigvalsh_large_workspace(512, spec.F32, ctypes.byref(b))
+    big = L.spec_eigvalsh_large
+    assert big(None, FAKE + 4, spec.F32, 512, 512, FAKE, FAKE, b.value, None) == EINVAL   # A: 16 bytes
+    assert big(None, FAKE, spec.F32, 512, 512, FAKE + 2, FAKE, b.value, None) == EINVAL   # w
+    assert big(None, FAKE, spec.F32, 512, 512, FAKE, FAKE + 128, b.value, None) == EINVAL  # ws: 256 bytes
+    p = spec.DescParams(0, 0, 1.0, 64, 32, 1, 0.2, 1e-2, 0.7)
+    L.spec_descriptors_workspace(32, ctypes.byref(b))
+    desc = L.spec_descriptors
+    assert desc(None, FAKE + 4, spec.F64, 1, 32, 32, ctypes.byref(p), FAKE, FAKE, b.value) == EINVAL  # w
+    assert desc(None, FAKE, spec.F64, 1, 32, 32, ctypes.byref(p), FAKE + 4, FAKE, b.value) == EINVAL  # out
+    assert desc(None, FAKE, spec.F64, 1, 32, 32, ctypes.byref(p), FAKE, FAKE + 8, b.value) == EINVAL  # ws
 
 
 def test_large_validation(L):
@@ -162,7 +190,7 @@ def test_eigvecs_topk_validation(L):
     b = ctypes.c_size_t(0)
     assert L.spec_eigvalsh_large_workspace(512, spec.F32, ctypes.byref(b)) == 0
     f = L.spec_eigvecs_topk
-    ok = (None, FAKE, spec.F32, 512, 512, FAKE, 2, FAKE, FAKE, 32, FAKE, b.value)
+    ok = (None, FAKE, spec.F32, 512, 512, FAKE, 2, FAKE, FAKE, 32, FAKE, b.value, None)
     def call(**kw):
         a = list(ok)
         for i, v in kw.items():
@@ -177,6 +205,7 @@ def test_eigvecs_topk_validation(L):
     assert call(a9=31) == EINVAL                 # ldp < 32
     assert call(a9=1 << 22) == EINVAL
     assert call(a11=b.value - 1) == EWORKSPACE
+    assert call(a12=FAKE + 2) == EINVAL          # info not 4-byte aligned
 
 
 def test_project_weight_validation(L):

@@ -55,6 +55,30 @@ def test_syrk_bf16(spec, n, d):
     assert np.all(np.isnan(Cg[U]))  # the strict upper triangle is never written
 
 
+@pytest.mark.parametrize("ldx", [(1 << 24) - 8, 1 << 24, (1 << 24) + 64])
+def test_syrk_bf16_huge_row_stride(spec, ldx):
+    """Row strides at and beyond what the MFMA kernel's 32-bit buffer offsets
+    reach (64 samples x ldx x 2 bytes): the larger ones take the general kernel;
+    every one gives the oracle's covariance."""
+    torch = _torch()
+    n, d = 70, 64
+    print_case("syrk_bf16_huge_ldx", n=n, d=d, ldx=ldx)
+    rng = np.random.default_rng(ldx % 1000)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    flat = torch.zeros(((n - 1) * ldx + d,), dtype=torch.bfloat16, device="cuda")
+    X = torch.as_strided(flat, (n, d), (ldx, 1))
+    X.copy_(dev_bf16(bits))
+    C = torch.full((d, d), float("nan"), dtype=torch.float32, device="cuda")
+    spec.cov_accumulate(X, C, alpha=1.0 / n, beta=0.0)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy().astype(np.float64)
+    ref = oracle.covariance(bits, "bf16", 1.0 / n)
+    bound = syrk_bound(np.abs(oracle.widen(bits, "bf16")), 1.0 / n, EPS32)
+    L = np.tril_indices(d)
+    assert np.all(np.abs(Cg[L] - ref[L]) <= bound[L])
+    del flat, X
+
+
 def test_syrk_bf16_accumulate(spec):
     torch = _torch()
     print_case("syrk_bf16_accumulate")

@@ -173,3 +173,29 @@ def test_eigvecs_edge_cases(spec, case):
         assert np.max(np.abs(wg - tr)) <= 1e-4 * tr[0]
         rq = np.einsum("ij,ij->j", Pg, A.astype(np.float64) @ Pg)
         assert np.max(np.abs(rq - wg)) <= 1e-4 * tr[0]
+
+
+def test_eigvecs_non_finite_input_writes_every_output(spec):
+    """A NaN in A makes Q^T A Q non-finite: info reports it and every value of w
+    and of P's 32 columns is written (NaN), nothing left uninitialised; a finite
+    input on the same buffers reports convergence."""
+    import torch
+    print_case("eigvecs_nonfinite")
+    rng = np.random.default_rng(17)
+    d = 256
+    A = _cov(rng, 2 * d, d, spikes=np.geomspace(20, 3, 4))
+    Om = dev(rng.standard_normal((d, 32)).astype(np.float32))
+    info = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((32,), 3.0, dtype=torch.float32, device="cuda")
+    Pbuf = torch.full((d, 40), 3.0, dtype=torch.float32, device="cuda")
+    spec.eigvecs_topk(dev(A), Om, q=2, w=w, P=Pbuf[:, :32], info=info)
+    torch.cuda.synchronize()
+    assert int(info.cpu()[0]) == 0
+    assert np.all(np.isfinite(w.cpu().numpy()))
+    A[17, 3] = np.nan
+    spec.eigvecs_topk(dev(A), Om, q=2, w=w, P=Pbuf[:, :32], info=info)
+    torch.cuda.synchronize()
+    assert int(info.cpu()[0]) == 1
+    assert np.all(np.isnan(w.cpu().numpy()))
+    Pb = Pbuf.cpu().numpy()
+    assert np.all(np.isnan(Pb[:, :32])) and np.all(Pb[:, 32:] == 3.0)

@@ -48,6 +48,26 @@ ROBUST_DTYPE = np.dtype([(f, "<f8") for f in _ROBUST_FIELDS_F] + [("n_mad", "<i8
 assert ROBUST_DTYPE.itemsize == 72
 
 
+KT = {"syrk": 0, "gram": 1, "small_eig": 2, "desc": 3, "symm": 4, "syr2k": 5, "panel": 6, "bulge": 7,
+      "tridiag": 8}
+
+
+def timing_enable(kernels) -> None:
+    """Start timing every launch of the named kernels (keys of KT) with HIP
+    events on their own stream; an empty list stops."""
+    m = 0
+    for k in kernels:
+        m |= 1 << KT[k]
+    _check(lib().spec_timing_enable(m))
+
+
+def timing_read(kernel: str):
+    """(total device ms, timed launches) of one kernel since timing_enable."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().spec_timing_read(KT[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
 class SpecError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"spec status {status}: {msg}")
@@ -77,7 +97,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
-           "spec_project_weight"]
+           "spec_project_weight", "spec_timing_enable", "spec_timing_read"]
 
 _lib = None
 
@@ -97,7 +117,7 @@ def lib() -> ctypes.CDLL:
         L.spec_version.restype = ctypes.c_char_p
         L.spec_cov_accumulate.argtypes = [vp, vp, i32, i64, i64, i64, vp, i32, i64, dbl, dbl]
         L.spec_gram_window.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, dbl, i32, vp]
-        L.spec_eigvalsh_batched.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, i32, vp]
+        L.spec_eigvalsh_batched.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, vp]
         L.spec_eigvalsh_large_workspace.argtypes = [i64, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.spec_eigvalsh_large.argtypes = [vp, vp, i32, i64, i64, vp, vp, ctypes.c_size_t, vp]
         L.spec_descriptors_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -105,11 +125,13 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t]
         L.spec_desc_smooth.argtypes = [vp, vp, i64, i64, dbl, vp]
         L.spec_eigvalsh_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, ctypes.c_size_t]
-        L.spec_eigvecs_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, i64, vp, ctypes.c_size_t]
+        L.spec_eigvecs_topk.argtypes = [vp, vp, i32, i64, i64, vp, i32, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.spec_project_weight_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
         L.spec_project_weight.argtypes = [vp, vp, i32, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp,
                                           ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
+        L.spec_timing_enable.argtypes = [ctypes.c_uint]
+        L.spec_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
         _lib = L
@@ -176,36 +198,34 @@ def gram_window(H, N: int, stride: int = 1, scale: float = 1.0, layout: int = GR
     return out
 
 
-def _batched(src: BatchSrc, batch: int, n: int, w, info, max_sweeps: int, device):
+def _batched(src: BatchSrc, batch: int, n: int, w, info, device):
     torch = _torch()
     if w is None:
         w = torch.empty((batch, n), dtype=torch.float32, device=device)
     if info is None:
         info = torch.empty((batch,), dtype=torch.int32, device=device)
-    _check(lib().spec_eigvalsh_batched(_stream(), ctypes.byref(src), batch, n, _dev(w), max_sweeps,
-                                       _dev(info)))
+    _check(lib().spec_eigvalsh_batched(_stream(), ctypes.byref(src), batch, n, _dev(w), _dev(info)))
     return w, info
 
 
-def eigvalsh_batched_dense(A, w=None, info=None, max_sweeps: int = 15):
+def eigvalsh_batched_dense(A, w=None, info=None):
     """Eigenvalues (descending) of A [batch, n, n] f32 (lower triangle read).
     info[b] = bisection rounds, or -1 for a matrix with a non-finite entry."""
     if A.dim() == 2:
         A = A.unsqueeze(0)
     batch, n, _ = A.shape
     src = BatchSrc(SRC_DENSE, _dev(A), A.stride(1), A.stride(0), 0, 0, 1, 1.0)
-    return _batched(src, batch, n, w, info, max_sweeps, A.device)
+    return _batched(src, batch, n, w, info, A.device)
 
 
-def eigvalsh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, info=None,
-                          max_sweeps: int = 15):
+def eigvalsh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, info=None):
     """Eigenvalues of every window's Gram scale * G_w from the band [S, T, n] of gram_window."""
     S, T, N = band.shape
     if N != n or not band.is_contiguous():
         raise SpecError(-1, "band must be a contiguous [streams, T, n] tensor")
     batch = S * ((T - n) // stride + 1)
     src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
-    return _batched(src, batch, n, w, info, max_sweeps, band.device)
+    return _batched(src, batch, n, w, info, band.device)
 
 
 def eigvalsh_large_workspace(n: int, dtype) -> int:
@@ -313,11 +333,12 @@ def eigvalsh_topk(A, Omega, q: int = 2, w=None, ws=None):
     return w
 
 
-def eigvecs_topk(A, Omega, q: int = 2, w=None, P=None, ws=None):
+def eigvecs_topk(A, Omega, q: int = 2, w=None, P=None, ws=None, info=None):
     """Ritz values (descending, [32]) and Ritz vectors P [n, 32] (column i for
     value i, orthonormal columns, arbitrary signs) of the same projection as
     eigvalsh_topk; the columns with a value above the MP edge span the signal
-    subspace."""
+    subspace.  ``info`` (int32 [1] device tensor, optional) receives 0
+    (converged), 1 (non-finite input) or 2 (sweep limit reached)."""
     torch = _torch()
     n = A.shape[0]
     if A.stride(1) != 1 or not Omega.is_contiguous() or tuple(Omega.shape) != (n, 32):
@@ -331,7 +352,7 @@ def eigvecs_topk(A, Omega, q: int = 2, w=None, P=None, ws=None):
     if ws is None:
         ws = torch.empty((eigvalsh_large_workspace(n, torch.float32),), dtype=torch.uint8, device=A.device)
     _check(lib().spec_eigvecs_topk(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(Omega), int(q), _dev(w),
-                                   _dev(P), P.stride(0), _dev(ws), ws.numel()))
+                                   _dev(P), P.stride(0), _dev(ws), ws.numel(), _dev(info) if info is not None else None))
     return w, P
 
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspec.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "syrk.hip", "gram.hip", "small_eig.hip", "descriptors.hip", "postproc.hip", "eig_large.hip",
+SOURCES = ["abi.cpp", "timing.cpp", "syrk.hip", "gram.hip", "small_eig.hip", "descriptors.hip", "postproc.hip", "eig_large.hip",
            "project.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -44,6 +44,7 @@ int spec_cov_accumulate(void *stream, const void *X, int xt, int64_t n, int64_t 
     if (!pair_ok) return SPEC_EUNSUPPORTED;
     if (!aligned(C, elt_size(ct)) || (X != nullptr && !aligned(X, elt_size(xt)))) return SPEC_EINVAL;
     if (d > (int64_t)1 << 20 || n > ((int64_t)1 << 40)) return SPEC_EUNSUPPORTED;
+    KTimer kt((hipStream_t)stream, SPEC_KT_SYRK);
     return from_hip(launch_syrk((hipStream_t)stream, X, xt, n, d, ldx, C, ct, ldc, alpha, beta));
 }
 
@@ -56,6 +57,7 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
     if (ld_t < d || ld_s < T * ld_t) return SPEC_EINVAL;
     if (!aligned(H, elt_size(ht)) || !aligned(out, 4)) return SPEC_EINVAL;
     if (!isfinite(scale)) return SPEC_EINVAL;
+    KTimer kt((hipStream_t)stream, SPEC_KT_GRAM);
     if (layout == SPEC_GRAM_BAND)
         return from_hip(launch_gram_band((hipStream_t)stream, H, ht, streams, T, d, ld_t, ld_s, N, out));
     if (layout == SPEC_GRAM_DENSE) {
@@ -66,13 +68,11 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
     return SPEC_EINVAL;
 }
 
-int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int max_sweeps,
-                          int32_t *info)
+int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info)
 {
     if (src == nullptr || w == nullptr || src->a == nullptr) return SPEC_EINVAL;
     if (n < 1 || n > 64) return n > 64 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
     if (batch < 0 || batch > ((int64_t)1 << 31) - 1) return SPEC_EINVAL;
-    if (max_sweeps < 1 || max_sweeps > 100) return SPEC_EINVAL;
     if (!aligned(w, 4) || !aligned(src->a, 4) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
     if (src->kind == SPEC_SRC_DENSE) {
         if (src->lda < n || src->stride_a < (int64_t)n * src->lda) return SPEC_EINVAL;
@@ -83,6 +83,7 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
     } else {
         return SPEC_EINVAL;
     }
+    KTimer kt((hipStream_t)stream, SPEC_KT_SMALL_EIG);
     return from_hip(launch_eigvalsh_batched((hipStream_t)stream, src, batch, n, w, info));
 }
 
@@ -129,7 +130,7 @@ int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t
     if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
     if (!aligned(w, elt_size(wt)) || !aligned(out, 8)) return SPEC_EINVAL;
     if (ws == nullptr || ws_bytes < descriptors_workspace_bytes(r)) return SPEC_EWORKSPACE;
-    if (!aligned(ws, 8)) return SPEC_EINVAL;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_descriptors((hipStream_t)stream, w, wt, batch, r, ldw, p, out, ws));
 }
 
@@ -143,21 +144,22 @@ int spec_eigvalsh_topk(void *stream, const void *A, int t, int64_t n, int64_t ld
     if (ws == nullptr || ws_bytes < eig_large_workspace_bytes(n, SPEC_F32)) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_topk_ritz((hipStream_t)stream, (const float *)A, n, lda, (const float *)Omega, q,
-                                     (float *)w, nullptr, 0, ws));
+                                     (float *)w, nullptr, 0, ws, nullptr));
 }
 
 int spec_eigvecs_topk(void *stream, const void *A, int t, int64_t n, int64_t lda, const void *Omega, int q, void *w,
-                      void *P, int64_t ldp, void *ws, size_t ws_bytes)
+                      void *P, int64_t ldp, void *ws, size_t ws_bytes, int32_t *info)
 {
     if (t != SPEC_F32) return SPEC_EUNSUPPORTED;
     if (A == nullptr || Omega == nullptr || w == nullptr || P == nullptr) return SPEC_EINVAL;
     if (n < 64 || n > 32768 || lda < n || lda >= ((int64_t)1 << 22) || q < 0 || q > 16) return SPEC_EINVAL;
     if (ldp < 32 || ldp >= ((int64_t)1 << 22)) return SPEC_EINVAL;
     if (!aligned(A, 16) || !aligned(Omega, 16) || !aligned(w, 4) || !aligned(P, 4)) return SPEC_EINVAL;
+    if (info != nullptr && !aligned(info, 4)) return SPEC_EINVAL;
     if (ws == nullptr || ws_bytes < eig_large_workspace_bytes(n, SPEC_F32)) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_topk_ritz((hipStream_t)stream, (const float *)A, n, lda, (const float *)Omega, q,
-                                     (float *)w, (float *)P, ldp, ws));
+                                     (float *)w, (float *)P, ldp, ws, info));
 }
 
 int spec_desc_smooth(void *stream, const spec_desc *in, int64_t streams, int64_t W, double alpha, spec_desc *out)
@@ -186,8 +188,6 @@ int spec_spectrum_robust(void *stream, const void *w, int wt, int64_t batch, int
     return from_hip(launch_spectrum_robust((hipStream_t)stream, w, wt, batch, r, ldw, p, out));
 }
 
-}  // extern "C"
-
 int spec_project_weight_workspace(int64_t d, size_t *bytes)
 {
     if (bytes == nullptr || d < 1 || d > 65536) return SPEC_EINVAL;
@@ -210,3 +210,5 @@ int spec_project_weight(void *stream, const void *W, int wt, int64_t d, int64_t 
     return from_hip(launch_project_weight((hipStream_t)stream, W, wt, d, ldw, (const float *)P, ldp, k, (float *)Wp,
                                           ldo, (float *)X, ldx, ws));
 }
+
+}  // extern "C"

@@ -194,6 +194,7 @@ hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t
     if (e != hipSuccess) return e;
     if (batch == 0) return hipSuccess;
     const unsigned grid = (unsigned)std::min<int64_t>((batch + DW - 1) / DW, 8192);
+    KTimer kt(stream, SPEC_KT_DESC);
     if (wt == SPEC_F32)
         hipLaunchKernelGGL(descriptors_kernel<float>, dim3(grid), dim3(64 * DW), 0, stream, (const float *)w,
                            batch, r, ldw, *p, q, out);

@@ -1769,6 +1769,8 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         if (m < 2) break;
         T *P = A + r0 * lda + c0;
         T *A22 = A + r0 * lda + r0;
+        {
+        KTimer kt_panel(st, SPEC_KT_PANEL);
         if (m <= DIRECT_ROWS) {
             hipLaunchKernelGGL(k_panel_direct<T>, dim3(1), dim3(256), 0, st, P, lda, (int)m, b.V, b.Tm);
             LAUNCH_OK();
@@ -1833,21 +1835,30 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_R)), dim3(VW_T), 0, st, b.Q1, b.U, b.Tm, (int)m,
                            m <= DIRECT_ROWS ? (int)m : NB, b.V, b.W);
         LAUNCH_OK();
+        }
         const int nrb = (int)cdiv_h(m, SY_RB);
         int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
         int chunk = (int)(cdiv_h(cdiv_h(m, ks), SY_JB) * SY_JB);
         ks = (int)cdiv_h(m, chunk);
-        hipLaunchKernelGGL(k_symm<T>, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart, chunk);
+        {
+            KTimer kt(st, SPEC_KT_SYMM);
+            hipLaunchKernelGGL(k_symm<T>, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart, chunk);
+        }
         LAUNCH_OK();
         const int nxb = (int)cdiv_h(m, XR);
-        hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, b.V, b.X, b.Ppart);
-        LAUNCH_OK();
-        hipLaunchKernelGGL(k_mz<T>, dim3((unsigned)std::min<int64_t>(MZ_BLOCKS, cdiv_h(m, 8))), dim3(256), 0, st,
-                           b.Ppart, nxb, b.Tm, b.X, b.V, (int)m);
+        {
+            KTimer kt(st, SPEC_KT_PANEL);
+            hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, b.V, b.X, b.Ppart);
+            hipLaunchKernelGGL(k_mz<T>, dim3((unsigned)std::min<int64_t>(MZ_BLOCKS, cdiv_h(m, 8))), dim3(256), 0, st,
+                               b.Ppart, nxb, b.Tm, b.X, b.V, (int)m);
+        }
         LAUNCH_OK();
         const int64_t nt = cdiv_h(m, S2_T);
-        hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A22, lda, (int)m, b.V,
-                           b.X);
+        {
+            KTimer kt(st, SPEC_KT_SYR2K);
+            hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A22, lda, (int)m,
+                               b.V, b.X);
+        }
         LAUNCH_OK();
     }
     // ---- stage 2: band -> tridiagonal
@@ -1861,11 +1872,16 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         const int64_t nsw = n - 2;
         const int64_t ngroups = cdiv_h(nsw, G);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
-        hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * (G + 2)), 0, st, b.band, n,
-                           b.prog, spin_ticks);
+        {
+            KTimer kt(st, SPEC_KT_BULGE);
+            hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * (G + 2)), 0, st, b.band, n,
+                               b.prog, spin_ticks);
+        }
         LAUNCH_OK();
     }
     // ---- stage 3: eigenvalues of the tridiagonal
+    {
+    KTimer kt_s3(st, SPEC_KT_TRIDIAG);
     hipLaunchKernelGGL(k_tridiag_prep<T>, dim3(1), dim3(256), 0, st, b.band, n, b.dd, b.ee2, b.bounds,
                        sizeof(T) == 4 ? b.de32 : nullptr);
     LAUNCH_OK();
@@ -1874,6 +1890,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     } else {
         hipLaunchKernelGGL(k_bisect<T>, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds,
                            4e-16, w);
+    }
     }
     LAUNCH_OK();
     if (info != nullptr) {
@@ -1907,7 +1924,7 @@ __global__ __launch_bounds__(256) void k_psum(const float *__restrict__ Ppart, i
 // col_partner(j), so every new element is a 4-term sum of the old B (double
 // buffered in LDS).  Output: w descending and U with column r the vector of w[r].
 __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ Ppart, int nblk, float *__restrict__ w,
-                                                     float *__restrict__ U)
+                                                     float *__restrict__ U, int32_t *__restrict__ info)
 {
     constexpr int L = NB + 1, EPT = NB * NB / 256;
     __shared__ float Bs[2][NB * L], Vs[2][NB * L];
@@ -1942,8 +1959,23 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
         __syncthreads();
         bmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     }
+    // a NaN or Inf in B (fmaxf skips NaN, so test every entry): no rotation is
+    // meaningful; every output is written as NaN and info says why
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) bad |= !isfinite(Bs[0][((tid + 256 * k) / NB) * L + (tid + 256 * k) % NB]);
+    bad = __syncthreads_or(bad);
+    if (bad) {
+        if (tid < NB) {
+            w[tid] = __builtin_nanf("");
+            for (int k = 0; k < NB; ++k) U[k * NB + tid] = __builtin_nanf("");
+        }
+        if (tid == 0 && info != nullptr) *info = 1;
+        return;
+    }
     const float floor_abs = 1e-7f * bmax;
     int cur = 0;
+    int converged = 0;
     const int wv = tid >> 6, lane = tid & 63;
     for (int sweep = 0; sweep < 30; ++sweep) {
         int any = 0;
@@ -2000,20 +2032,28 @@ __global__ __launch_bounds__(256) void k_ritz_jacobi(const float *__restrict__ P
             cur ^= 1;
             __syncthreads();  // the new B and V are complete; the old ones are no longer read
         }
-        if (!any) break;  // the same in every wave
+        if (!any) {  // the same in every wave
+            converged = 1;
+            break;
+        }
     }
-    // rank of eigenvalue i among the diagonal (descending, ties by index)
+    // rank of eigenvalue i among the diagonal: descending, ties by index, a NaN
+    // (from rounding overflow) after every number, so the ranks are a permutation
+    // and every slot of w and U is written
     if (tid < NB) {
         const int i = tid;
         const float li = Bs[cur][i * L + i];
         int r = 0;
         for (int j = 0; j < NB; ++j) {
             const float lj = Bs[cur][j * L + j];
-            r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+            const bool ni = isnan(li), nj = isnan(lj);
+            const bool before = (ni || nj) ? (ni && (!nj || j < i)) : (lj > li || (lj == li && j < i));
+            r += before ? 1 : 0;
         }
         w[r] = li;
         for (int k = 0; k < NB; ++k) U[k * NB + r] = Vs[cur][k * L + i];
     }
+    if (tid == 0 && info != nullptr) *info = converged ? 0 : 2;
 }
 
 // ---- P = Q1 U (m x NB): the Ritz vectors
@@ -2044,7 +2084,7 @@ __global__ __launch_bounds__(256) void k_ritz_vectors(const float *__restrict__ 
 // the per-block products Q_blk^T (A Q)_blk; its eigenvalues come from the
 // batched small solver.  A is read, not written.
 hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, const float *Omega, int q, float *w,
-                    float *P, int64_t ldp, void *ws)
+                    float *P, int64_t ldp, void *ws, int32_t *info)
 {
     Bufs<float> b;
     layout<float>(n, (char *)ws, b);
@@ -2098,7 +2138,7 @@ hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, cons
     }
     if ((e = symm(b.Q1)) != hipSuccess) return e;  // X = A Q and the blocks of Q^T X
     if (P != nullptr) {  // Ritz values and vectors: Jacobi on B, then P = Q U
-        hipLaunchKernelGGL(k_ritz_jacobi, dim3(1), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), w, b.Tm);
+        hipLaunchKernelGGL(k_ritz_jacobi, dim3(1), dim3(256), 0, st, b.Ppart, (int)cdiv_h(m, XR), w, b.Tm, info);
         LAUNCH_OK();
         hipLaunchKernelGGL(k_ritz_vectors, dim3((unsigned)cdiv_h(m, 8)), dim3(256), 0, st, b.Q1, m, b.Tm, P, ldp);
         return hipGetLastError();
@@ -2137,7 +2177,7 @@ hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64
 }
 
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
-                            float *w, float *P, int64_t ldp, void *ws)
+                            float *w, float *P, int64_t ldp, void *ws, int32_t *info)
 {
-    return run_topk(stream, A, n, lda, Omega, q, w, P, ldp, ws);
+    return run_topk(stream, A, n, lda, Omega, q, w, P, ldp, ws, info);
 }

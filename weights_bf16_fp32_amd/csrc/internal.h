@@ -37,9 +37,21 @@ hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int
                                   const spec_robust_params *p, spec_robust *out);
 
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
-                            float *w, float *P, int64_t ldp, void *ws);
+                            float *w, float *P, int64_t ldp, void *ws, int32_t *info);
 
 size_t project_weight_workspace_bytes(int64_t d);
 
 hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int64_t d, int64_t ldw, const float *P,
                                  int64_t ldp, int k, float *Wp, int64_t ldo, float *X, int64_t ldx, void *ws);
+
+// Kernel timing brackets (timing.cpp): ktimer_begin returns a slot (or -1 when
+// the kernel is not being timed); ktimer_end records the matching end event.
+int ktimer_begin(hipStream_t stream, int id);
+void ktimer_end(hipStream_t stream, int slot);
+
+struct KTimer {
+    hipStream_t s;
+    int slot;
+    KTimer(hipStream_t stream, int id) : s(stream), slot(ktimer_begin(stream, id)) {}
+    ~KTimer() { ktimer_end(s, slot); }
+};

@@ -388,7 +388,9 @@ hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int
                        int64_t ldc, double alpha, double beta)
 {
     if (xt == SPEC_BF16 && ct == SPEC_F32) {
-        if (d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0) {
+        // the MFMA kernel addresses 64 samples from one buffer base with 32-bit
+        // offsets: 64 * ldx * 2 bytes must stay below the resource limit
+        if (d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0 && ldx <= ((int64_t)1 << 24) - 8) {
             int64_t tiles = tri_count((d + SB_TILE - 1) / SB_TILE);
             hipLaunchKernelGGL(syrk_bf16_mfma, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint16_t *)X, n, d,
                                ldx, (float *)C, ldc, (float)alpha, (float)beta);
