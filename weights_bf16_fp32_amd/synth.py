@@ -208,5 +208,27 @@ def s3(layers: int = 32, d: int = 4096, sigma_min: float = 1e-3) -> np.ndarray:
     return out
 
 
+def s3_layers_device(layers: int = 32, d: int = 4096, sigma_min: float = 1e-3, device="cuda", seed: int = 0):
+    """The S3 weight workload drawn on the GPU with torch (for timing runs, where
+    64 host QRs of d x d would take minutes): the same recipe as s3_layer --
+    Haar U, V from QR of N(0,1) fp64 matrices with the signs of diag(R) folded
+    in, W = U diag(sigma) V^T in fp64, rounded to f32 -- from torch's seeded
+    device generator, so the values differ from s3_layer's while the planted
+    spectrum is the same.  Returns a [layers, d, d] float32 device tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    sig = torch.from_numpy(s3_sigma(d, sigma_min)).to(device)
+    out = torch.empty((layers, d, d), dtype=torch.float32, device=device)
+    for l in range(layers):
+        hs = []
+        for _ in range(2):
+            q, r = torch.linalg.qr(torch.randn((d, d), dtype=torch.float64, device=device, generator=g))
+            hs.append(q * torch.sign(torch.diagonal(r)))
+        out[l] = ((hs[0] * sig) @ hs[1].T).to(torch.float32)
+        del hs, q, r
+    return out
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
