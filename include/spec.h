@@ -302,6 +302,21 @@ int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t
                      const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * spec_descriptors_static: spec_descriptors for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same records, computed by the same kernels, with
+ * the MP quantile table held in the library's own device memory (one 256 KiB
+ * table per GPU, kept until the process ends) instead of a caller workspace.
+ * Allocates nothing.  Every call rewrites the table of its stream's GPU before
+ * reading it; calls that overlap on one GPU (different streams, or threads)
+ * race on it.
+ * Requires r <= 32768 (else SPEC_EUNSUPPORTED) and the conditions of
+ * spec_descriptors; SPEC_EHIP if the table's address cannot be obtained.
+ * ---------------------------------------------------------------------- */
+int spec_descriptors_static(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                            const spec_desc_params *p, spec_desc *out);
+
+/* ------------------------------------------------------------------------
  * Post-processing of descriptor series and spectra ("Random matrix theory
  * spectral methods" page, sections 3.2 and 4.2; section 2.3 for the KL form).
  *

@@ -97,7 +97,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
-           "spec_project_weight", "spec_timing_enable", "spec_timing_read"]
+           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static"]
 
 _lib = None
 
@@ -130,6 +130,7 @@ def lib() -> ctypes.CDLL:
         L.spec_project_weight.argtypes = [vp, vp, i32, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp,
                                           ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
+        L.spec_descriptors_static.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp]
         L.spec_timing_enable.argtypes = [ctypes.c_uint]
         L.spec_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in EXPORTS[2:]:
@@ -275,6 +276,26 @@ def descriptors(w, *, n_samples: int, p_dim: int, k: int = 1, mode: int = MODE_E
                    float(small_rel), float(tail_frac))
     _check(lib().spec_descriptors(_stream(), _dev(w), _dt(w), batch, r, w.stride(0), ctypes.byref(p),
                                   _dev(out), _dev(ws), ws.numel()))
+    if not to_host:
+        return out
+    return out.cpu().numpy().view(DESC_DTYPE).reshape(batch)
+
+
+def descriptors_static(w, *, n_samples: int, p_dim: int, k: int = 1, mode: int = MODE_EIG,
+                       sigma2: float = 1.0, sigma2_mode: int = SIGMA2_GIVEN, top_frac: float = 0.2,
+                       small_rel: float = 1e-2, tail_frac: float = 0.7, out=None, to_host: bool = True):
+    """descriptors() without a workspace: the library's own per-GPU table is used
+    (spec_descriptors_static; r <= 32768; overlapping calls on one GPU race)."""
+    torch = _torch()
+    if w.dim() == 1:
+        w = w.unsqueeze(0)
+    batch, r = w.shape
+    if out is None:
+        out = torch.empty((batch, DESC_DTYPE.itemsize), dtype=torch.uint8, device=w.device)
+    p = DescParams(mode, sigma2_mode, float(sigma2), int(n_samples), int(p_dim), int(k), float(top_frac),
+                   float(small_rel), float(tail_frac))
+    _check(lib().spec_descriptors_static(_stream(), _dev(w), _dt(w), batch, r, w.stride(0), ctypes.byref(p),
+                                         _dev(out)))
     if not to_host:
         return out
     return out.cpu().numpy().view(DESC_DTYPE).reshape(batch)

@@ -15,6 +15,23 @@ inline int from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_EHIP
 
 inline size_t elt_size(int t) { return t == SPEC_BF16 ? 2 : (t == SPEC_F32 ? 4 : 8); }
 
+// the checks spec_descriptors and spec_descriptors_static share
+int check_descriptors(const void *w, int wt, int64_t batch, int64_t r, int64_t ldw, const spec_desc_params *p,
+                      spec_desc *out)
+{
+    if (w == nullptr || p == nullptr || out == nullptr) return SPEC_EINVAL;
+    if (wt != SPEC_F32 && wt != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if (batch < 0 || batch > ((int64_t)1 << 31) - 1 || r < 2 || ldw < r) return SPEC_EINVAL;
+    if (p->k < 1 || p->k >= r || p->n_samples < 1 || p->p_dim < 1) return SPEC_EINVAL;
+    if (!(p->top_frac >= 0.0 && p->top_frac <= 1.0) || !(p->tail_frac >= 0.0 && p->tail_frac <= 1.0) ||
+        !(p->small_rel >= 0.0))
+        return SPEC_EINVAL;
+    if (p->sigma2_mode < SPEC_SIGMA2_GIVEN || p->sigma2_mode > SPEC_SIGMA2_MEAN) return SPEC_EINVAL;
+    if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
+    if (!aligned(w, elt_size(wt)) || !aligned(out, 8)) return SPEC_EINVAL;
+    return SPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,19 +133,20 @@ int spec_descriptors_workspace(int64_t r, size_t *bytes)
     return SPEC_OK;
 }
 
+int spec_descriptors_static(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                            const spec_desc_params *p, spec_desc *out)
+{
+    const int st = check_descriptors(w, wt, batch, r, ldw, p, out);
+    if (st != SPEC_OK) return st;
+    if (r > DESC_SCRATCH_MAX_R) return SPEC_EUNSUPPORTED;
+    return from_hip(launch_descriptors_static((hipStream_t)stream, w, wt, batch, r, ldw, p, out));
+}
+
 int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                      const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes)
 {
-    if (w == nullptr || p == nullptr || out == nullptr) return SPEC_EINVAL;
-    if (wt != SPEC_F32 && wt != SPEC_F64) return SPEC_EUNSUPPORTED;
-    if (batch < 0 || batch > ((int64_t)1 << 31) - 1 || r < 2 || ldw < r) return SPEC_EINVAL;
-    if (p->k < 1 || p->k >= r || p->n_samples < 1 || p->p_dim < 1) return SPEC_EINVAL;
-    if (!(p->top_frac >= 0.0 && p->top_frac <= 1.0) || !(p->tail_frac >= 0.0 && p->tail_frac <= 1.0) ||
-        !(p->small_rel >= 0.0))
-        return SPEC_EINVAL;
-    if (p->sigma2_mode < SPEC_SIGMA2_GIVEN || p->sigma2_mode > SPEC_SIGMA2_MEAN) return SPEC_EINVAL;
-    if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
-    if (!aligned(w, elt_size(wt)) || !aligned(out, 8)) return SPEC_EINVAL;
+    const int st = check_descriptors(w, wt, batch, r, ldw, p, out);
+    if (st != SPEC_OK) return st;
     if (ws == nullptr || ws_bytes < descriptors_workspace_bytes(r)) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_descriptors((hipStream_t)stream, w, wt, batch, r, ldw, p, out, ws));

@@ -22,6 +22,7 @@
 #include <float.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -179,6 +180,43 @@ __global__ __launch_bounds__(64 * DW) void descriptors_kernel(const T *__restric
         desc_one<T>(w, b, r, ldw, p, qtab, out);
 }
 
+// The MP quantile table of spec_descriptors_static: one per GPU, in the
+// library's own device memory, for callers that cannot allocate a workspace.
+// Every call on a GPU rewrites it before reading it; calls that overlap on one
+// GPU race on it.
+static __device__ __align__(256) double scratch[DESC_SCRATCH_MAX_R];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+double *scratch_ptr[MAX_DEVICES];  // device address of `scratch` on each GPU, once looked up
+
+// the address of `scratch` on the device `stream` belongs to: looked up once per
+// device with that device current (the host-side name is only a stand-in)
+hipError_t scratch_on(hipStream_t stream, double **out)
+{
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = (double *)p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 size_t descriptors_workspace_bytes(int64_t r) { return (size_t)((r + 31) / 32 * 32) * sizeof(double); }
@@ -202,4 +240,14 @@ hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t
         hipLaunchKernelGGL(descriptors_kernel<double>, dim3(grid), dim3(64 * DW), 0, stream, (const double *)w,
                            batch, r, ldw, *p, q, out);
     return hipGetLastError();
+}
+
+hipError_t launch_descriptors_static(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                                     const spec_desc_params *p, spec_desc *out)
+{
+    if (r > DESC_SCRATCH_MAX_R) return hipErrorInvalidValue;
+    double *q = nullptr;
+    hipError_t e = scratch_on(stream, &q);
+    if (e != hipSuccess) return e;
+    return launch_descriptors(stream, w, wt, batch, r, ldw, p, out, q);
 }

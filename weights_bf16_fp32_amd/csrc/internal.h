@@ -27,6 +27,12 @@ hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64
 
 size_t descriptors_workspace_bytes(int64_t r);
 
+// spectra lengths the library-held MP table of spec_descriptors_static covers
+constexpr int64_t DESC_SCRATCH_MAX_R = 32768;
+
+hipError_t launch_descriptors_static(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
+                                     const spec_desc_params *p, spec_desc *out);
+
 hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                               const spec_desc_params *p, spec_desc *out, void *ws);
 
