@@ -79,6 +79,37 @@ def test_syrk_bf16_huge_row_stride(spec, ldx):
     del flat, X
 
 
+@pytest.mark.parametrize("n,d,beta", [(300, 5888, 0.0), (97, 6000, 0.0), (64, 6000, 1.0)])
+def test_syrk_bf16_large_d(spec, n, d, beta):
+    """d large enough for the 256 x 256 tile kernel (>= 256 tiles): a ragged d
+    (6000 = 23 full tiles + 112), a sample count that is not a multiple of the
+    32-sample step, and beta = 1 on a random old C; every lower-triangle entry
+    against the oracle within the (n + 2) u bound, the strict upper triangle
+    untouched."""
+    torch = _torch()
+    print_case("syrk_bf16_large_d", n=n, d=d, beta=beta)
+    rng = np.random.default_rng(n + d)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32) * 2)
+    X = dev_bf16(bits)
+    C0 = rng.standard_normal((d, d)).astype(np.float32) if beta else None
+    C = torch.from_numpy(C0).cuda() if beta else torch.full((d, d), float("nan"), dtype=torch.float32, device="cuda")
+    if beta:
+        up = torch.triu(torch.ones((d, d), dtype=torch.bool, device="cuda"), 1)
+        C[up] = float("nan")
+    alpha = 1.0 / n
+    spec.cov_accumulate(X, C, alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy().astype(np.float64)
+    del C
+    ref = oracle.covariance(bits, "bf16", alpha, C0=C0, beta=beta)
+    bound = syrk_bound(np.abs(oracle.widen(bits, "bf16")), alpha, EPS32,
+                       C0abs=np.abs(C0.astype(np.float64)) if beta else None, beta=beta)
+    L = np.tril_indices(d)
+    assert np.all(np.abs(Cg[L] - ref[L]) <= bound[L])
+    U = np.triu_indices(d, 1)
+    assert np.all(np.isnan(Cg[U]))
+
+
 def test_syrk_bf16_accumulate(spec):
     torch = _torch()
     print_case("syrk_bf16_accumulate")

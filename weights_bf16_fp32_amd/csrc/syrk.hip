@@ -22,6 +22,8 @@
 //   syrk_generic    any of the above pairs plus f32 -> f32, plain VALU FMAs on
 //                   64x64 tiles; used for f32 -> f32 and for shapes the MFMA
 //                   kernels do not take (d or ldx not a multiple of 8).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -191,6 +193,178 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
                 int64_t row, col;
                 if (rc(a, b, e, row, col)) C[row * ldc + col] = acc[a][b][e];
             }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA, 256 x 256 tiles
+//
+// syrk_bf16_big: the same product for large d.  A 128 x 128 tile reads two
+// 128-feature strips of X per 128^2 outputs, and at d = 14336 the concurrent
+// tiles of an XCD hit its L2 only a quarter of the time, so the kernel streamed
+// X from HBM ~77 times.  Here a tile is 256 x 256 (4 waves of 128 x 128, 16
+// accumulator blocks of 32 x 32 each, all in AGPRs), which halves the strip
+// reads per output.  One workgroup per CU runs at a time (all 512 registers
+// of a lane), so the tiles run in rounds of one workgroup per CU, started
+// together and of equal cost; in round r, workgroup b (dealt to XCD b % 8)
+// takes tile r * R + (b % 8) * (R / 8) + (b mod R) / 8 of the blocked
+// triangle order (R = CUs per round), so the 32 tiles an XCD runs together
+// form a 4 x 8 block of one 8 x 8 super-block (12 strips) and advance through
+// the samples in step.
+// LDS: per operand and stage, sample group g (8 samples, 16 bytes per feature)
+// holds 256 features with a 16-byte gap after every 8: the 16-byte writes of
+// 8 consecutive feature blocks and the operand reads of 8 consecutive
+// features both fall on distinct banks.
+constexpr int BG_TILE = 256;
+constexpr int BG_BK = 32;                               // samples per K-step
+constexpr int BG_GROUP_U16 = (BG_TILE + BG_TILE / 8) * 8;  // uint16 per sample group (4608 B)
+constexpr int BG_OP_U16 = (BG_BK / 8) * BG_GROUP_U16;      // one operand, one stage
+constexpr int BG_PF = 3;                                 // register stages of prefetch
+
+__device__ __forceinline__ int bg_slot(int f) { return (f + (f >> 3)) * 8; }  // uint16 offset of feature f
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void syrk_bf16_big(const uint16_t *__restrict__ X, int64_t n, int64_t d,
+                                                     int64_t ldx, float *__restrict__ C, int64_t ldc, float alpha,
+                                                     float beta, int64_t ntiles, int round)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BG_OP_U16];
+    const int nt = (int)((d + BG_TILE - 1) / BG_TILE);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    // loader: operand op, 8-feature block fb (0..31), 8-sample group kb (0..3)
+    const int fb = tid & 31, kb = (tid >> 5) & 3, op = tid >> 7;
+    const uint32_t ldb = (uint32_t)(ldx * 2);
+    const int64_t nsteps = (n + BG_BK - 1) / BG_BK;
+    // rounds of `round` consecutive workgroups run together (one per CU); in a
+    // full round, the hardware deals workgroup b to XCD b % 8, and that XCD's
+    // round/8 workgroups take consecutive tiles of the blocked order
+    const int64_t b = blockIdx.x;
+    const int64_t r0 = b / round * round;
+    const int64_t t = r0 + round <= ntiles ? r0 + (b % 8) * (round / 8) + (b - r0) / 8 : b;
+    {
+        int ti, tj;
+        tri_tile_blocked(t, nt, ti, tj);
+        const int64_t i0 = (int64_t)ti * BG_TILE, j0 = (int64_t)tj * BG_TILE;
+        const bool diag = ti == tj;
+        const bool loader = !(diag && op == 1);
+        const int64_t fbase = (op == 0 ? i0 : j0) + fb * 8;
+        uint32_t voff[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            voff[e] = fbase < d && loader ? (uint32_t)(kb * 8 + e) * ldb + (uint32_t)fbase * 2u : 0xFFFFFFF0u;
+        u32x4_t vb[BG_PF][8];
+        auto gload = [&](u32x4_t (&v)[8], int64_t k0) {
+            const int64_t rem = (n - k0) * ldx * 2;
+            const int num = (int)(rem <= 0 ? 0 : (rem < 0x7FFFFFF0 ? rem : 0x7FFFFFF0));
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(X + (rem > 0 ? k0 : 0) * ldx), 0, num, 0x00020000);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[e], 0, 0));
+        };
+        auto lstore = [&](const u32x4_t (&v)[8], int stage) {
+            uint16_t *base = &lds[stage][op][0] + kb * BG_GROUP_U16;
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                u32x4_t o;
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    o[p] = __builtin_amdgcn_perm(v[2 * p + 1][f >> 1], v[2 * p][f >> 1],
+                                                 (f & 1) ? 0x07060302u : 0x05040100u);
+                *reinterpret_cast<u32x4_t *>(base + bg_slot(fb * 8 + f)) = o;
+            }
+        };
+        f32x16_t acc[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+        const bool active = !(diag && wm == 0 && wn == 1);
+#pragma unroll
+        for (int p = 0; p < BG_PF - 1; ++p) gload(vb[p], p * BG_BK);
+        lstore(vb[0], 0);
+        __syncthreads();
+        // operand rows of this lane: A rows wm*128 + a*32 + l%32, B rows wn*128 + b*32 + l%32;
+        // sample group 2 kk + l / 32 of the K-step
+        const int gsel = (lane >> 5) * BG_GROUP_U16;
+        for (int64_t s0 = 0; s0 < nsteps; s0 += BG_PF) {
+            static_for<0, BG_PF>([&](auto UC) {
+                constexpr int u = decltype(UC)::value;
+                const int64_t k = s0 + u;
+                gload(vb[(u + BG_PF - 1) % BG_PF], (k + BG_PF - 1) * BG_BK);
+                const int st = (int)(k & 1);
+                const uint16_t *la = &lds[st][0][0] + gsel;
+                const uint16_t *lb = &lds[st][diag ? 0 : 1][0] + gsel;
+                if (active) {
+#pragma unroll
+                    for (int kk = 0; kk < BG_BK / 16; ++kk) {
+                        bf16x8_t fa[4], fbv[4];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            fa[m] = *reinterpret_cast<const bf16x8_t *>(
+                                la + 2 * kk * BG_GROUP_U16 + bg_slot(wm * 128 + m * 32 + (lane & 31)));
+                            fbv[m] = *reinterpret_cast<const bf16x8_t *>(
+                                lb + 2 * kk * BG_GROUP_U16 + bg_slot(wn * 128 + m * 32 + (lane & 31)));
+                        }
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fbv[b], acc[a][b], 0, 0, 0);
+                    }
+                }
+                lstore(vb[(u + 1) % BG_PF], st ^ 1);
+                __syncthreads();
+            });
+        }
+        if (active) {
+            // C through a buffer resource from the tile's corner to the end of the
+            // matrix: 32-bit offsets (ldc < 2^21 is checked by the launcher), one
+            // VGPR per element; an element outside the lower triangle or past d
+            // gets an offset beyond every resource (its load reads 0, its store
+            // is dropped).  Four accumulator blocks at a time, their old values
+            // all loaded before the first store.
+            const int64_t corner = i0 * ldc + j0;
+            const int64_t span = ((d - 1) * ldc + d - corner) * 4;
+            const __amdgpu_buffer_rsrc_t rc =
+                __builtin_amdgcn_make_buffer_rsrc(C + corner, 0, (int)(span < 0x7FFFFFF0 ? span : 0x7FFFFFF0),
+                                                  0x00020000);
+            const int ldc4 = (int)ldc * 4;
+            const int rl = wm * 128 + (lane >> 5) * 4, cl = wn * 128 + (lane & 31);
+            const uint32_t lane_off = (uint32_t)(rl * ldc4 + cl * 4);
+            const int rlim = (int)min<int64_t>(d - i0, BG_TILE), clim = (int)min<int64_t>(d - j0, BG_TILE);
+            // one 32 x 32 block at a time: its 16 old values (beta != 0) are loaded
+            // before its 16 stores
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    uint32_t off[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int dr = a * 32 + (e >> 2) * 8 + (e & 3);
+                        const int row = rl + dr, col = cl + b * 32;  // within the tile
+                        const bool ok = row < rlim && col < clim && (!diag || row >= col);
+                        off[e] = ok ? lane_off + (uint32_t)(dr * ldc4 + b * 128) : 0x80000000u;
+                    }
+                    float v[16];
+                    if (beta != 0.f) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, (int)off[e], 0, 0));
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) v[e] = alpha * acc[a][b][e] + beta * v[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) v[e] = alpha * acc[a][b][e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[e]), rc, (int)off[e], 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);  // one block's values live at a time
+                }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- fp64 MFMA
@@ -390,7 +564,18 @@ hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int
     if (xt == SPEC_BF16 && ct == SPEC_F32) {
         // the MFMA kernel addresses 64 samples from one buffer base with 32-bit
         // offsets: 64 * ldx * 2 bytes must stay below the resource limit
-        if (d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0 && ldx <= ((int64_t)1 << 24) - 8) {
+        const bool vec = d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0 && ldx <= ((int64_t)1 << 24) - 8;
+        const int64_t big_tiles = tri_count((d + BG_TILE - 1) / BG_TILE);
+        if (vec && big_tiles >= 256 && ldc < ((int64_t)1 << 21)) {
+            // large d: 256 x 256 tiles in rounds of one workgroup per CU
+            hipDevice_t dev = 0;
+            int cus = 256;
+            if (hipStreamGetDevice(stream, &dev) == hipSuccess)
+                (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            const int round = cus >= 8 ? cus / 8 * 8 : 8;
+            hipLaunchKernelGGL(syrk_bf16_big, dim3((unsigned)big_tiles), dim3(256), 0, stream, (const uint16_t *)X, n,
+                               d, ldx, (float *)C, ldc, (float)alpha, (float)beta, big_tiles, round);
+        } else if (vec) {
             int64_t tiles = tri_count((d + SB_TILE - 1) / SB_TILE);
             hipLaunchKernelGGL(syrk_bf16_mfma, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint16_t *)X, n, d,
                                ldx, (float *)C, ldc, (float)alpha, (float)beta);
