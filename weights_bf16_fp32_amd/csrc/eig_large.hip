@@ -37,6 +37,7 @@
 #include <float.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -859,6 +860,157 @@ __global__ __launch_bounds__(256) void k_symm(const T *__restrict__ A, int64_t l
     }
 }
 
+// ---- the same partial products in fp32 with 16-byte loads.  Tiles of A wholly
+// below the diagonal are read row by row (float4 along j) into a row-major LDS
+// tile; tiles wholly above it come from the stored lower triangle as rows j of
+// A (float4 along i) and stay k-major in LDS (no transpose); the few tiles that
+// cross the diagonal are read element by element into the row-major form.  W
+// stays row-major.  The two k-slots of a lane's MFMAs walk columns h * 32 + q
+// (h = lane / 32, q = 0..31; the sum over k is the same in any order), so on a
+// row-major tile one ds_read_b128 gives the A operands of four
+// v_mfma_f32_32x32x2f32; the other operands are 32-bit reads of 32 consecutive
+// words per half-wave, and rows h * 32 + q of the k-major tile and of W are
+// skewed so that the two halves fall on opposite banks.  One LDS buffer and
+// one register stage: the loads of K-step k + 1 are in flight during step k's
+// MFMAs; 43 KB of LDS and fewer than 168 VGPRs let three workgroups share a CU
+// and cover each other's waits.
+constexpr int SQ_LD = SY_JB + 4;   // row-major A tile: stride 68 floats (16-byte rows, b128 reads)
+constexpr int SQ_LT = SY_RB + 4;   // k-major A tile: stride 132 floats, rows >= 32 skewed by 32 words
+constexpr int SQ_LW = NB + 1;      // W: stride 33 floats (the halves 32 rows apart differ by 32 banks)
+
+__device__ __forceinline__ int sq_trow(int k) { return k * SQ_LT + (k >= 32 ? 32 : 0); }
+
+__global__ __launch_bounds__(256) void k_symm_f32(const float *__restrict__ A, int64_t lda, int m,
+                                                  const float *__restrict__ W, float *__restrict__ Xpart, int chunk)
+{
+    static_assert(SY_JB * SQ_LT + 32 <= SY_RB * SQ_LD, "the k-major tile fits the row-major one's space");
+    __shared__ __attribute__((aligned(16))) float As[SY_RB * SQ_LD];
+    __shared__ float Ws[SY_JB * SQ_LW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i0 = blockIdx.x * SY_RB;
+    const int jlo = blockIdx.y * chunk, jhi = min(m, jlo + chunk);
+    const int64_t end = (int64_t)(m - 1) * lda + m;  // one past A22[m-1][m-1], in elements
+    float4 ra[8], rw[2];
+    // tile kind of the K-step at column j0: 0 below the diagonal, 1 above, 2 crossing
+    auto kind = [&](int j0) __attribute__((always_inline)) {
+        return j0 + SY_JB - 1 <= i0 ? 0 : (i0 + SY_RB - 1 < j0 ? 1 : 2);
+    };
+    auto rsrc = [&](int64_t corner) __attribute__((always_inline)) {
+        const int64_t span = (end - corner) * 4;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(A + corner), 0,
+                                                 (int)(span < 0x7FFFFFF0 ? (span > 0 ? span : 0) : 0x7FFFFFF0),
+                                                 0x00020000);
+    };
+    auto gload = [&](float4 (&va)[8], float4 (&vw)[2], int j0) __attribute__((always_inline)) {
+        const int kd = kind(j0);
+        if (kd == 0) {  // rows i0 + r, columns j0 + c4 .. + 3; columns past jhi masked on store
+            const __amdgpu_buffer_rsrc_t rs = rsrc((int64_t)i0 * lda + j0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * q, r = idx >> 4, c4 = (idx & 15) * 4;
+                va[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rs, (int)(((int64_t)r * lda + c4) * 4), 0, 0));
+            }
+        } else if (kd == 1) {  // stored rows j0 + jr, columns i0 + i4 .. + 3
+            const __amdgpu_buffer_rsrc_t rs = rsrc((int64_t)j0 * lda + i0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * q, jr = idx >> 5, i4 = (idx & 31) * 4;
+                va[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rs, (int)(((int64_t)jr * lda + i4) * 4), 0, 0));
+            }
+        } else {  // crossing the diagonal: element by element from the lower triangle
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * q, r = idx >> 4, c4 = (idx & 15) * 4;
+                const int i = i0 + r;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + c4 + e;
+                    v[e] = i < m && j < jhi ? (i >= j ? A[(int64_t)i * lda + j] : A[(int64_t)j * lda + i]) : 0.f;
+                }
+                va[q] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {  // W rows j0 + k (k < 64), columns c4 .. + 3
+            const int idx = tid + 256 * q, k = idx >> 3, c4 = (idx & 7) * 4;
+            const int j = min(j0 + k, m - 1);  // clamped (a row past jhi is masked on store)
+            vw[q] = *reinterpret_cast<const float4 *>(W + (int64_t)j * NB + c4);
+        }
+    };
+    auto lstore = [&](const float4 (&va)[8], const float4 (&vw)[2], int j0) __attribute__((always_inline)) {
+        if (kind(j0) == 1) {  // k-major: row jr holds column j0 + jr of the tile (rows past jhi zero)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * q, jr = idx >> 5, i4 = (idx & 31) * 4;
+                const bool ok = j0 + jr < jhi;
+                *reinterpret_cast<float4 *>(&As[sq_trow(jr) + i4]) = ok ? va[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * q, r = idx >> 4, c4 = (idx & 15) * 4;
+                const int j = j0 + c4;
+                float4 v = va[q];
+                v.x = j < jhi ? v.x : 0.f;
+                v.y = j + 1 < jhi ? v.y : 0.f;
+                v.z = j + 2 < jhi ? v.z : 0.f;
+                v.w = j + 3 < jhi ? v.w : 0.f;
+                *reinterpret_cast<float4 *>(&As[r * SQ_LD + c4]) = v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int idx = tid + 256 * q, k = idx >> 3, c4 = (idx & 7) * 4;
+            const bool ok = j0 + k < jhi;
+            float *wr = &Ws[k * SQ_LW + c4];
+            wr[0] = ok ? vw[q].x : 0.f;
+            wr[1] = ok ? vw[q].y : 0.f;
+            wr[2] = ok ? vw[q].z : 0.f;
+            wr[3] = ok ? vw[q].w : 0.f;
+        }
+    };
+    f32x16_t acc = {};
+    const int h = lane >> 5, c = lane & 31;
+    const float *fa = &As[(wave * 32 + c) * SQ_LD + h * 32];  // row-major: row wave*32 + c, columns h*32..
+    const float *ft = &As[sq_trow(h * 32) + wave * 32 + c];  // k-major: rows h*32.., column wave*32 + c
+    const float *fw = &Ws[(h * 32) * SQ_LW + c];               // W rows h*32.., column c
+    if (jlo < jhi) {
+        gload(ra, rw, jlo);
+        lstore(ra, rw, jlo);
+    }
+    __syncthreads();
+    for (int jc = jlo; jc < jhi; jc += SY_JB) {
+        const bool more = jc + SY_JB < jhi;
+        if (more) gload(ra, rw, jc + SY_JB);  // in flight during this step's MFMAs
+        if (kind(jc) == 1) {
+#pragma unroll
+            for (int q = 0; q < 32; ++q)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ft[q * SQ_LT], fw[q * SQ_LW], acc, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(fa + q4 * 4);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, fw[(q4 * 4 + 0) * SQ_LW], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, fw[(q4 * 4 + 1) * SQ_LW], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, fw[(q4 * 4 + 2) * SQ_LW], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, fw[(q4 * 4 + 3) * SQ_LW], acc, 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (more) lstore(ra, rw, jc + SY_JB);
+        __syncthreads();
+    }
+    float *Xp = Xpart + (int64_t)blockIdx.y * m * NB;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int r = i0 + wave * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (r < m) Xp[(int64_t)r * NB + (lane & 31)] = acc[e];
+    }
+}
+
 // ---- X = sum of partials; Ppart[blk] = V_blk^T X_blk (XR-row blocks)
 constexpr int XR = 128;
 
@@ -999,6 +1151,42 @@ __global__ __launch_bounds__(256) void k_mz(const T *__restrict__ Ppart, int nbl
             for (int j = 0; j < NB; ++j) s += vrow[u][j] * Ms[j * NB + c];
             if (r < m) X[r * NB + c] = x[u] - (T)0.5 * s;
         }
+    }
+}
+
+// ---- the same update on the first NB columns of A22 only (every row i >= j):
+// the block column of the next panel, updated before that panel is factored.
+// SC_ROWS rows per workgroup, four threads per row, eight columns each.
+constexpr int SC_ROWS = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_syr2k_cols(T *__restrict__ A, int64_t lda, int m, const T *__restrict__ V,
+                                                    const T *__restrict__ Z)
+{
+    __shared__ T Vj[NB * LDP], Zj[NB * LDP];
+    const int tid = threadIdx.x;
+    for (int q = tid; q < NB * NB; q += 256) {
+        const int r = q / NB, c = q % NB;
+        const bool ok = r < m;
+        Vj[r * LDP + c] = ok ? V[q] : (T)0;
+        Zj[r * LDP + c] = ok ? Z[q] : (T)0;
+    }
+    __syncthreads();
+    const int i = blockIdx.x * SC_ROWS + (tid >> 2), cg = (tid & 3) * 8;
+    const int ic = min(i, m - 1);  // clamped: unconditional loads, nothing stored past m
+    T vi[NB], zi[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        vi[k] = V[(int64_t)ic * NB + k];
+        zi[k] = Z[(int64_t)ic * NB + k];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int j = cg + c;
+        T sum = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) sum += vi[k] * Zj[j * LDP + k] + zi[k] * Vj[j * LDP + k];
+        if (i < m && i >= j) A[(int64_t)i * lda + j] -= sum;
     }
 }
 
@@ -1710,7 +1898,7 @@ struct Ws {
 
 template <typename T>
 struct Bufs {
-    T *band, *V, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Ppart;
+    T *band, *V, *V2, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Ppart;
     int32_t *prog;
     double *dd, *ee2, *bounds;
     float2 *de32;
@@ -1726,6 +1914,7 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.band = ws.take<T>((size_t)n * BW);
     b.prog = ws.take<int32_t>((size_t)n + 1);
     b.V = ws.take<T>((size_t)n * NB);
+    b.V2 = ws.take<T>((size_t)n * NB);
     b.W = ws.take<T>((size_t)n * NB);
     b.X = ws.take<T>((size_t)n * NB);
     b.Xpart = ws.take<T>((size_t)KS_MAX * n * NB);
@@ -1747,6 +1936,47 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     return ws.off;
 }
 
+// The helper stream of stage 1 (one per device, default priority, created on
+// first use) and the two events that order it with the caller's stream.
+struct Aux {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+constexpr int AUX_DEVICES = 64;
+Aux aux_dev[AUX_DEVICES];
+std::mutex aux_init_mu;
+
+hipError_t aux_for(hipStream_t st, Aux **out)
+{
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= AUX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(aux_init_mu);
+    Aux &a = aux_dev[dev];
+    if (a.s == nullptr) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (cur != dev) {
+            hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        a.fork = f;
+        a.join = j;
+        a.s = s;
+    }
+    *out = &a;
+    return hipSuccess;
+}
+
 #define LAUNCH_OK()                                     \
     do {                                                \
         hipError_t e_ = hipGetLastError();              \
@@ -1763,103 +1993,151 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     constexpr int DIRECT_ROWS = 256;
     static_assert(DIRECT_ROWS <= RB, "direct panel must fit");
     // ---- stage 1: dense -> band
+    // Panel p's trailing update is split: the next panel's block column (NB
+    // columns, all rows) first, then the rest of the trailing matrix; the next
+    // panel is factored on a helper stream while the main stream runs that
+    // rest, and the main stream waits for it before the next SYMM.  The two
+    // touch disjoint parts of A; V alternates between two buffers (the running
+    // SYR2K reads panel p's V while panel p + 1's is written).
+    Aux *aux = nullptr;
+    hipError_t ae = aux_for(st, &aux);
+    if (ae != hipSuccess) return ae;
+    std::lock_guard<std::mutex> aux_lock(aux->mu);  // one call at a time on the helper stream and its events
+    T *Vbuf[2] = {b.V, b.V2};
+    // factorisation of the panel at column c0 on stream s: V (into Vout), T, W = V T, R into A
+    auto factor = [&](hipStream_t s, int64_t c0, T *Vout) -> hipError_t {
+        const int64_t r0 = c0 + NB;
+        const int64_t m = n - r0;
+        T *P = A + r0 * lda + c0;
+        KTimer kt_panel(s, SPEC_KT_PANEL);
+            if (m <= DIRECT_ROWS) {
+                hipLaunchKernelGGL(k_panel_direct<T>, dim3(1), dim3(256), 0, s, P, lda, (int)m, Vout, b.Tm);
+                LAUNCH_OK();
+            } else {
+                // row blocks of about 256 rows, at most TOP_BLOCKS of them (the stacked R
+                // factors of all blocks are factored by one workgroup)
+                const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
+                const int per = (int)cdiv_h(m, nblk);
+                const int rows_top = nblk * NB;
+                // fp32: QRs with four rows per lane (one wave up to 256 rows, two up to 512,
+                // four up to 1024); fp64: one row per thread
+                if constexpr (std::is_same<T, float>::value) {
+                    if (per <= 256)
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(nblk), dim3(64), 0, s, P, lda, (int)m, per, b.Vloc,
+                                           b.Tloc, b.Rstack, (T *)nullptr);
+                    else if (per <= 512)
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(nblk), dim3(128), 0, s, P, lda, (int)m, per,
+                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                    else
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(nblk), dim3(256), 0, s, P, lda, (int)m, per,
+                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                    LAUNCH_OK();
+                    if (rows_top <= 256)
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(1), dim3(64), 0, s, b.Rstack, (int64_t)NB, rows_top,
+                                           rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                    else if (rows_top <= 512)
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(1), dim3(128), 0, s, b.Rstack, (int64_t)NB,
+                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                    else
+                        hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(1), dim3(256), 0, s, b.Rstack, (int64_t)NB,
+                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                    LAUNCH_OK();
+                } else {
+                    if (per <= 256)
+                        hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, s, P, lda, (int)m, per,
+                                           b.Vloc, b.Tloc, b.Rstack);
+                    else if (per <= 512)
+                        hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, s, P, lda, (int)m, per,
+                                           b.Vloc, b.Tloc, b.Rstack);
+                    else
+                        hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, s, P, lda, (int)m, per,
+                                           b.Vloc, b.Tloc, b.Rstack);
+                    LAUNCH_OK();
+                    if (rows_top <= 256)
+                        hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, s, b.Rstack, nblk, b.Rf, b.Vtop,
+                                           b.Ktop);
+                    else if (rows_top <= 512)
+                        hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, s, b.Rstack, nblk, b.Rf, b.Vtop,
+                                           b.Ktop);
+                    else
+                        hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, s, b.Rstack, nblk, b.Rf,
+                                           b.Vtop, b.Ktop);
+                    LAUNCH_OK();
+                }
+                hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, s, b.Vloc, b.Tloc,
+                                   b.Vtop, b.Ktop, (int)m, per, b.Q1);
+                LAUNCH_OK();
+                hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, s, b.Q1, b.Rf, P, lda, Vout, b.U, b.Tm);
+                LAUNCH_OK();
+            }
+            // V rows below the reconstructed top block (TSQR), then W = V T
+            hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_R)), dim3(VW_T), 0, s, b.Q1, b.U, b.Tm, (int)m,
+                               m <= DIRECT_ROWS ? (int)m : NB, Vout, b.W);
+            LAUNCH_OK();
+        return hipSuccess;
+    };
+    if (n - NB >= 2) {
+        hipError_t e = factor(st, 0, Vbuf[0]);
+        if (e != hipSuccess) return e;
+    }
     for (int64_t c0 = 0;; c0 += NB) {
         const int64_t r0 = c0 + NB;
         const int64_t m = n - r0;
         if (m < 2) break;
-        T *P = A + r0 * lda + c0;
         T *A22 = A + r0 * lda + r0;
-        {
-        KTimer kt_panel(st, SPEC_KT_PANEL);
-        if (m <= DIRECT_ROWS) {
-            hipLaunchKernelGGL(k_panel_direct<T>, dim3(1), dim3(256), 0, st, P, lda, (int)m, b.V, b.Tm);
-            LAUNCH_OK();
-        } else {
-            // row blocks of about 256 rows, at most TOP_BLOCKS of them (the stacked R
-            // factors of all blocks are factored by one workgroup)
-            const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
-            const int per = (int)cdiv_h(m, nblk);
-            const int rows_top = nblk * NB;
-            // fp32: QRs with four rows per lane (one wave up to 256 rows, two up to 512,
-            // four up to 1024); fp64: one row per thread
-            if constexpr (std::is_same<T, float>::value) {
-                if (per <= 256)
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(nblk), dim3(64), 0, st, P, lda, (int)m, per, b.Vloc,
-                                       b.Tloc, b.Rstack, (T *)nullptr);
-                else if (per <= 512)
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(nblk), dim3(128), 0, st, P, lda, (int)m, per,
-                                       b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
-                else
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per,
-                                       b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
-                LAUNCH_OK();
-                if (rows_top <= 256)
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(1), dim3(64), 0, st, b.Rstack, (int64_t)NB, rows_top,
-                                       rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
-                else if (rows_top <= 512)
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(1), dim3(128), 0, st, b.Rstack, (int64_t)NB,
-                                       rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
-                else
-                    hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(1), dim3(256), 0, st, b.Rstack, (int64_t)NB,
-                                       rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
-                LAUNCH_OK();
-            } else {
-                if (per <= 256)
-                    hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, st, P, lda, (int)m, per,
-                                       b.Vloc, b.Tloc, b.Rstack);
-                else if (per <= 512)
-                    hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, st, P, lda, (int)m, per,
-                                       b.Vloc, b.Tloc, b.Rstack);
-                else
-                    hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, st, P, lda, (int)m, per,
-                                       b.Vloc, b.Tloc, b.Rstack);
-                LAUNCH_OK();
-                if (rows_top <= 256)
-                    hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, st, b.Rstack, nblk, b.Rf, b.Vtop,
-                                       b.Ktop);
-                else if (rows_top <= 512)
-                    hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, st, b.Rstack, nblk, b.Rf, b.Vtop,
-                                       b.Ktop);
-                else
-                    hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, st, b.Rstack, nblk, b.Rf,
-                                       b.Vtop, b.Ktop);
-                LAUNCH_OK();
-            }
-            hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
-                               b.Vtop, b.Ktop, (int)m, per, b.Q1);
-            LAUNCH_OK();
-            hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, st, b.Q1, b.Rf, P, lda, b.V, b.U, b.Tm);
-            LAUNCH_OK();
-        }
-        // V rows below the reconstructed top block (TSQR), then W = V T
-        hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_R)), dim3(VW_T), 0, st, b.Q1, b.U, b.Tm, (int)m,
-                           m <= DIRECT_ROWS ? (int)m : NB, b.V, b.W);
-        LAUNCH_OK();
-        }
+        T *Vc = Vbuf[(c0 / NB) & 1];
         const int nrb = (int)cdiv_h(m, SY_RB);
         int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
         int chunk = (int)(cdiv_h(cdiv_h(m, ks), SY_JB) * SY_JB);
         ks = (int)cdiv_h(m, chunk);
         {
             KTimer kt(st, SPEC_KT_SYMM);
-            hipLaunchKernelGGL(k_symm<T>, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart, chunk);
+            if constexpr (std::is_same<T, float>::value)
+                hipLaunchKernelGGL(k_symm_f32, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart,
+                                   chunk);
+            else
+                hipLaunchKernelGGL(k_symm<T>, dim3(nrb, ks), dim3(256), 0, st, A22, lda, (int)m, b.W, b.Xpart,
+                                   chunk);
         }
         LAUNCH_OK();
         const int nxb = (int)cdiv_h(m, XR);
         {
             KTimer kt(st, SPEC_KT_PANEL);
-            hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, b.V, b.X, b.Ppart);
+            hipLaunchKernelGGL(k_xreduce<T>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, (int)m, Vc, b.X, b.Ppart);
             hipLaunchKernelGGL(k_mz<T>, dim3((unsigned)std::min<int64_t>(MZ_BLOCKS, cdiv_h(m, 8))), dim3(256), 0, st,
-                               b.Ppart, nxb, b.Tm, b.X, b.V, (int)m);
+                               b.Ppart, nxb, b.Tm, b.X, Vc, (int)m);
         }
         LAUNCH_OK();
-        const int64_t nt = cdiv_h(m, S2_T);
-        {
-            KTimer kt(st, SPEC_KT_SYR2K);
-            hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A22, lda, (int)m,
-                               b.V, b.X);
+        if (m - NB >= 2) {
+            // the next panel's block column, then its factorisation beside the rest
+            {
+                KTimer kt(st, SPEC_KT_SYR2K);
+                hipLaunchKernelGGL(k_syr2k_cols<T>, dim3((unsigned)cdiv_h(m, SC_ROWS)), dim3(256), 0, st, A22, lda,
+                                   (int)m, Vc, b.X);
+            }
+            LAUNCH_OK();
+            if ((ae = hipEventRecord(aux->fork, st)) != hipSuccess) return ae;
+            if ((ae = hipStreamWaitEvent(aux->s, aux->fork, 0)) != hipSuccess) return ae;
+            if ((ae = factor(aux->s, c0 + NB, Vbuf[(c0 / NB + 1) & 1])) != hipSuccess) return ae;
+            if ((ae = hipEventRecord(aux->join, aux->s)) != hipSuccess) return ae;
+            const int64_t mr = m - NB;
+            const int64_t nt = cdiv_h(mr, S2_T);
+            {
+                KTimer kt(st, SPEC_KT_SYR2K);
+                hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st,
+                                   A22 + NB * lda + NB, lda, (int)mr, Vc + NB * NB, b.X + NB * NB);
+            }
+            LAUNCH_OK();
+            if ((ae = hipStreamWaitEvent(st, aux->join, 0)) != hipSuccess) return ae;
+        } else {
+            const int64_t nt = cdiv_h(m, S2_T);
+            {
+                KTimer kt(st, SPEC_KT_SYR2K);
+                hipLaunchKernelGGL(k_syr2k<T>, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A22, lda,
+                                   (int)m, Vc, b.X);
+            }
+            LAUNCH_OK();
         }
-        LAUNCH_OK();
     }
     // ---- stage 2: band -> tridiagonal
     hipLaunchKernelGGL(k_band_copy<T>, dim3((unsigned)cdiv_h(n * BW + 1, 256)), dim3(256), 0, st, A, lda, n, b.band,
@@ -2095,7 +2373,7 @@ hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, cons
         int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
         const int chunk = (int)(cdiv_h(cdiv_h(m, ks), SY_JB) * SY_JB);
         ks = (int)cdiv_h(m, chunk);
-        hipLaunchKernelGGL(k_symm<float>, dim3(nrb, ks), dim3(256), 0, st, A, lda, m, Wm, b.Xpart, chunk);
+        hipLaunchKernelGGL(k_symm_f32, dim3(nrb, ks), dim3(256), 0, st, A, lda, m, Wm, b.Xpart, chunk);
         LAUNCH_OK();
         const int nxb = (int)cdiv_h(m, XR);
         hipLaunchKernelGGL(k_xreduce<float>, dim3(nxb), dim3(256), 0, st, b.Xpart, ks, m, Wm, b.X, b.Ppart);

@@ -210,16 +210,17 @@ __global__ __launch_bounds__(256) void syrk_bf16_mfma(const uint16_t *__restrict
 // form a 4 x 8 block of one 8 x 8 super-block (12 strips) and advance through
 // the samples in step.
 // LDS: per operand and stage, sample group g (8 samples, 16 bytes per feature)
-// holds 256 features with a 16-byte gap after every 8: the 16-byte writes of
-// 8 consecutive feature blocks and the operand reads of 8 consecutive
-// features both fall on distinct banks.
+// holds 256 features, feature f in 16-byte slot f ^ ((f >> 3) & 15): the
+// operand reads (16 consecutive features) and the loader's writes (features
+// 8 apart, f = 8 fb + c) both land on 16 distinct slots modulo 16, so neither
+// conflicts whether the hardware serves 8 lanes on 32 banks or 16 lanes on 64.
 constexpr int BG_TILE = 256;
 constexpr int BG_BK = 32;                               // samples per K-step
-constexpr int BG_GROUP_U16 = (BG_TILE + BG_TILE / 8) * 8;  // uint16 per sample group (4608 B)
-constexpr int BG_OP_U16 = (BG_BK / 8) * BG_GROUP_U16;      // one operand, one stage
-constexpr int BG_PF = 3;                                 // register stages of prefetch
+constexpr int BG_GROUP_U16 = BG_TILE * 8;               // uint16 per sample group (4 KB)
+constexpr int BG_OP_U16 = (BG_BK / 8) * BG_GROUP_U16;   // one operand, one stage
+constexpr int BG_PF = 3;                                // register stages of prefetch
 
-__device__ __forceinline__ int bg_slot(int f) { return (f + (f >> 3)) * 8; }  // uint16 offset of feature f
+__device__ __forceinline__ int bg_slot(int f) { return (f ^ ((f >> 3) & 15)) * 8; }  // uint16 offset of feature f
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void syrk_bf16_big(const uint16_t *__restrict__ X, int64_t n, int64_t d,
                                                      int64_t ldx, float *__restrict__ C, int64_t ldc, float alpha,
