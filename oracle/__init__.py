@@ -35,6 +35,8 @@ What it computes, each function citing the passage it follows:
   basis of RMT page, section 4.1).
 * :func:`project_weight`  the compressed weight W' = P^T W P of a d x d weight
   on a d x k basis (RMT page, section 4.1) and the low-rank factor W P.
+* :func:`tail_pair_screen` the S3 page's screen of swap candidates (section
+  3.1): |u_i^T v_j| over the tail singular vectors, same-head pairs below eps.
 
 All arithmetic is fp64.  bf16 inputs arrive as uint16 bit patterns and are
 widened exactly.
@@ -559,3 +561,23 @@ def project_weight(W, P):
     P = np.asarray(P, dtype=np.float64)
     X = W @ P
     return P.T @ X, X
+
+
+def tail_pair_screen(U, V, *, i0: int, t: int, head_dim: int, eps: float = 0.015):
+    """Screen of the swap candidates of the S3 page (section 3.1): for the left
+    singular vectors u_i and right singular vectors v_j of the tail, i and j in
+    [i0, i0 + t) (the page takes the last 10 %, i >= 0.9 N), the inner products
+    |u_i^T v_j|; a pair is kept when it lies in one head's index range (indices
+    split into consecutive blocks of head_dim: i // head_dim == j // head_dim)
+    and |u_i^T v_j| < eps (the page keeps |u_i^T v_j| below 0.015, from its
+    orthogonality constraint |u_i^T v_j| < eps, eps ~ 1e-2).
+
+    U, V: [N, >= i0 + t] with the singular vectors as columns (f32 widened
+    exactly, or f64).  Returns (absdot [t, t] fp64, keep [t, t] bool, count)."""
+    Ut = np.asarray(U)[:, i0:i0 + t].astype(np.float64)
+    Vt = np.asarray(V)[:, i0:i0 + t].astype(np.float64)
+    absdot = np.abs(Ut.T @ Vt)
+    idx = np.arange(i0, i0 + t)
+    same = (idx[:, None] // head_dim) == (idx[None, :] // head_dim)
+    keep = same & (absdot < eps)
+    return absdot, keep, int(np.sum(keep))

@@ -615,3 +615,50 @@ def test_ffn_golden_vs_lapack():
     ref = np.linalg.eigvalsh(C)[::-1]
     assert np.max(np.abs(z["eig"] - ref)) <= 1e-12 * ref[0]
     assert int(z["n_above_inertia"]) == int(np.sum(ref > oracle.mp_edges(1.0, 14336 / 65536)[1]))
+
+
+
+# ------------------------------------------------------------- S3 tail-pair screen
+
+def test_tail_pair_screen_pins():
+    # U = V = I: u_i^T v_j is the Kronecker delta, so every same-head pair but
+    # i = j is kept; the head blocks of the tail [3687, 4096) with head_dim 128
+    # have 25, 128, 128 and 128 indices
+    N = 4096
+    eye = np.eye(N, dtype=np.float32)
+    absdot, keep, count = oracle.tail_pair_screen(eye, eye, i0=3687, t=409, head_dim=128)
+    assert np.array_equal(absdot, np.eye(409))
+    assert count == sum(b * b - b for b in (25, 128, 128, 128))
+    assert not keep[0, 30]  # index 3687 (head 28) and 3717 (head 29)
+    # brute force on a tiny case
+    rng = np.random.default_rng(3)
+    U = rng.standard_normal((12, 10)).astype(np.float32)
+    V = rng.standard_normal((12, 10)).astype(np.float32)
+    absdot, keep, count = oracle.tail_pair_screen(U, V, i0=4, t=6, head_dim=3, eps=1.5)
+    for a in range(6):
+        for b in range(6):
+            i, j = 4 + a, 4 + b
+            dot = sum(float(U[k, i]) * float(V[k, j]) for k in range(12))
+            assert abs(absdot[a, b] - abs(dot)) <= 1e-12 * (1 + abs(dot))
+            assert keep[a, b] == ((i // 3 == j // 3) and abs(dot) < 1.5)
+    assert count == int(keep.sum())
+    # a planted pair: V = U R with R a rotation by theta in the plane of columns
+    # (p, q) gives u_p^T v_q = -sin(theta) and u_q^T v_q = cos(theta); strict
+    # threshold on both sides of eps
+    Q, _ = np.linalg.qr(rng.standard_normal((64, 64)))
+    for theta, kept in [(0.0149, True), (0.0151, False)]:
+        R = np.eye(64)
+        p, q = 60, 62
+        R[p, p] = R[q, q] = np.cos(theta)
+        R[p, q], R[q, p] = -np.sin(theta), np.sin(theta)
+        absdot, keep, _ = oracle.tail_pair_screen(Q, Q @ R, i0=58, t=6, head_dim=8)
+        assert abs(absdot[p - 58, q - 58] - np.sin(theta)) <= 1e-14
+        assert keep[p - 58, q - 58] == kept
+    # Haar-orthogonal U, V of the S3 workload: u_i^T v_j is about N(0, 1/N), so
+    # the kept fraction of same-head pairs is close to P(|Z| < 0.015 sqrt(N))
+    U, _ = np.linalg.qr(rng.standard_normal((1024, 1024)))
+    V, _ = np.linalg.qr(rng.standard_normal((1024, 1024)))
+    absdot, keep, count = oracle.tail_pair_screen(U, V, i0=922, t=102, head_dim=1024)
+    import scipy.stats
+    frac = count / 102 ** 2
+    assert abs(frac - (2 * scipy.stats.norm.cdf(0.015 * 32) - 1)) < 0.03
