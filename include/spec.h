@@ -302,6 +302,27 @@ int spec_descriptors(void *stream, const void *w, int wt, int64_t batch, int64_t
                      const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * S3 tail-pair screen ("S3 Spectral Null-Space Swap" page, section 3.1: swap
+ * candidates (u_i, v_j) come from the tail singular vectors, i, j >= 0.9 N, must
+ * satisfy |u_i^T v_j| < 0.015, and i and j must lie in the same head's index
+ * range).  Exact: the t x t inner products of the tail columns of U and V, in
+ * fp64 (f32 inputs widened exactly), on MFMA.
+ *
+ * U, V:   [n][ldu], [n][ldv] device, type dt = SPEC_F32 or SPEC_F64 (else
+ *         SPEC_EUNSUPPORTED), row-major with the singular vectors as columns
+ *         (U's column i is u_i); columns i0 .. i0 + t - 1 are read.
+ * absdot: f64 [t][ldo] device or NULL: |u_{i0+a}^T v_{i0+b}| at [a][b].
+ * keep:   uint8 [t][ldk] device: 1 where (i0 + a) / head_dim == (i0 + b) / head_dim
+ *         and the product is below eps (strict), else 0.
+ * count:  int64 [1] device or NULL: the number of kept pairs.
+ * Requires n >= 1, i0 >= 0, 1 <= t <= 65535, i0 + t <= ldu and ldv, head_dim >= 1,
+ * 0 < eps finite, ldk >= t, ldo >= t when absdot is given; else SPEC_EINVAL.
+ * ---------------------------------------------------------------------- */
+int spec_tail_pair_screen(void *stream, const void *U, const void *V, int dt, int64_t n, int64_t ldu, int64_t ldv,
+                          int64_t i0, int64_t t, int64_t head_dim, double eps, double *absdot, int64_t ldo,
+                          uint8_t *keep, int64_t ldk, int64_t *count);
+
+/* ------------------------------------------------------------------------
  * spec_descriptors_static: spec_descriptors for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same records, computed by the same kernels, with

@@ -233,3 +233,24 @@ def test_project_weight_validation(L):
     assert call(a11=31) == EINVAL                 # ldx < k with X given
     assert call(a1=FAKE + 8) == EINVAL            # W not 16-byte aligned
     assert call(a13=b.value - 1) == EWORKSPACE
+
+
+def test_tail_pair_screen_validation(L):
+    f = L.spec_tail_pair_screen
+    ok = [None, FAKE, FAKE, spec.F32, 4096, 4096, 4096, 3687, 409, 128, 0.015, FAKE, 409, FAKE, 409, FAKE]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a3=spec.BF16) == EUNSUPPORTED
+    assert call(a8=410) == EINVAL             # i0 + t > ldu
+    assert call(a8=0) == EINVAL               # t < 1
+    assert call(a9=0) == EINVAL               # head_dim < 1
+    assert call(a10=0.0) == EINVAL            # eps <= 0
+    assert call(a10=float("inf")) == EINVAL
+    assert call(a14=408) == EINVAL            # ldk < t
+    assert call(a12=10) == EINVAL             # ldo < t with absdot given
+    assert call(a13=None) == EINVAL           # keep NULL
+    assert call(a1=FAKE + 2) == EINVAL        # f32 U misaligned
+    assert call(a15=FAKE + 4) == EINVAL       # count misaligned

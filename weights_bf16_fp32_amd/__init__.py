@@ -97,7 +97,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
-           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static"]
+           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen"]
 
 _lib = None
 
@@ -130,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.spec_project_weight.argtypes = [vp, vp, i32, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp,
                                           ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
+        L.spec_tail_pair_screen.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, dbl, vp, i64, vp, i64,
+                                             vp]
         L.spec_descriptors_static.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp]
         L.spec_timing_enable.argtypes = [ctypes.c_uint]
         L.spec_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -408,3 +410,31 @@ def project_weight(W, P, k=None, Wp=None, X=None, want_factor: bool = True, ws=N
                                      Wp.stride(0), None if X is None else _dev(X), 0 if X is None else X.stride(0),
                                      _dev(ws), ws.numel()))
     return Wp, X
+
+
+def tail_pair_screen(U, V, *, i0: int | None = None, t: int | None = None, head_dim: int = 128,
+                     eps: float = 0.015, absdot=None, keep=None, count=None):
+    """S3 swap-candidate screen: |u_i^T v_j| for the tail columns [i0, i0 + t) of
+    U and V (singular vectors as columns; default tail: i >= 0.9 N), and the
+    same-head pairs below eps.  Returns (absdot [t, t] f64, keep [t, t] uint8,
+    count [1] int64), device tensors."""
+    import math
+    torch = _torch()
+    N = U.shape[1]
+    if i0 is None:
+        i0 = int(math.ceil(0.9 * N))
+    if t is None:
+        t = N - i0
+    if U.dtype != V.dtype or U.stride(1) != 1 or V.stride(1) != 1 or U.shape[0] != V.shape[0]:
+        raise SpecError(-1, "U and V must be row-major with the same dtype and row count")
+    dev = U.device
+    if absdot is None:
+        absdot = torch.empty((t, t), dtype=torch.float64, device=dev)
+    if keep is None:
+        keep = torch.empty((t, t), dtype=torch.uint8, device=dev)
+    if count is None:
+        count = torch.empty((1,), dtype=torch.int64, device=dev)
+    _check(lib().spec_tail_pair_screen(_stream(), _dev(U), _dev(V), _dt(U), U.shape[0], U.stride(0), V.stride(0),
+                                       int(i0), int(t), int(head_dim), float(eps), _dev(absdot), absdot.stride(0),
+                                       _dev(keep), keep.stride(0), _dev(count)))
+    return absdot, keep, count

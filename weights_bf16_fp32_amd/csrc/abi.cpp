@@ -229,4 +229,18 @@ int spec_project_weight(void *stream, const void *W, int wt, int64_t d, int64_t 
                                           ldo, (float *)X, ldx, ws));
 }
 
+int spec_tail_pair_screen(void *stream, const void *U, const void *V, int dt, int64_t n, int64_t ldu, int64_t ldv,
+                          int64_t i0, int64_t t, int64_t head_dim, double eps, double *absdot, int64_t ldo,
+                          uint8_t *keep, int64_t ldk, int64_t *count)
+{
+    if (dt != SPEC_F32 && dt != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if (U == nullptr || V == nullptr || keep == nullptr) return SPEC_EINVAL;
+    if (n < 1 || i0 < 0 || t < 1 || t > 65535 || head_dim < 1 || !(eps > 0.0 && isfinite(eps))) return SPEC_EINVAL;
+    if (i0 + t > ldu || i0 + t > ldv || ldk < t || (absdot != nullptr && ldo < t)) return SPEC_EINVAL;
+    if (!aligned(U, elt_size(dt)) || !aligned(V, elt_size(dt))) return SPEC_EINVAL;
+    if ((absdot != nullptr && !aligned(absdot, 8)) || (count != nullptr && !aligned(count, 8))) return SPEC_EINVAL;
+    return from_hip(launch_tail_pair_screen((hipStream_t)stream, U, V, dt, n, ldu, ldv, i0, t, head_dim, eps, absdot,
+                                            ldo, keep, ldk, count));
+}
+
 }  // extern "C"

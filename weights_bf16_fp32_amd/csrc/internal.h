@@ -45,6 +45,10 @@ hipError_t launch_spectrum_robust(hipStream_t stream, const void *w, int wt, int
 hipError_t launch_topk_ritz(hipStream_t stream, const float *A, int64_t n, int64_t lda, const float *Omega, int q,
                             float *w, float *P, int64_t ldp, void *ws, int32_t *info);
 
+hipError_t launch_tail_pair_screen(hipStream_t stream, const void *U, const void *V, int dt, int64_t n, int64_t ldu,
+                                   int64_t ldv, int64_t i0, int64_t t, int64_t head_dim, double eps, double *absdot,
+                                   int64_t ldo, uint8_t *keep, int64_t ldk, int64_t *count);
+
 size_t project_weight_workspace_bytes(int64_t d);
 
 hipError_t launch_project_weight(hipStream_t stream, const void *W, int wt, int64_t d, int64_t ldw, const float *P,

@@ -196,6 +196,15 @@ def s3_layer_f64(layer: int, d: int = 4096, sigma_min: float = 1e-3) -> np.ndarr
     return (U * s3_sigma(d, sigma_min)) @ V.T
 
 
+def s3_factors(layer: int, d: int = 4096, sigma_min: float = 1e-3):
+    """(U, sigma, V) of one layer, fp64: W = U diag(sigma) V^T (the singular
+    vectors the S3 tail-pair screen takes)."""
+    rng = rng_for("s3", 1 + layer)
+    U = haar_orthogonal(rng, d)
+    V = haar_orthogonal(rng, d)
+    return U, s3_sigma(d, sigma_min), V
+
+
 def s3_layer(layer: int, d: int = 4096, sigma_min: float = 1e-3) -> np.ndarray:
     """f32 [d, d] weight of one layer (fp64 product rounded to nearest f32)."""
     return s3_layer_f64(layer, d, sigma_min).astype(np.float32)
