@@ -199,10 +199,15 @@ def phase_rows(torch, spec, synth, dev, with_cpu):
                      ("desc_windows", lambda: spec.descriptors(ww, n_samples=N, p_dim=d, k=8, out=dw, ws=wsw,
                                                                 to_host=False))]:
         part[name] = timed(torch, fn, 10)
+    # the same spectra and records from the fused entry point (one kernel after the band)
+    fused = timed(torch, lambda: spec.eigvalsh_batched_band_desc(band, n=N, scale=1.0 / N, n_samples=N, p_dim=d,
+                                                                k=8, w=ww, info=iw, out=dw, ws=wsw,
+                                                                to_host=False), 10)
     tot = sum(part.values())
     rounds = float(iw.float().mean())
     rows["eigentrack_256x512x4096_N30"] = {
         "ms": tot, "phases_ms": part, "windows": S * W, "window_spectra_per_s": S * W / (tot / 1e3),
+        "eig_desc_fused_ms": fused, "ms_fused_path": part["gram_band"] + fused,
         "gram_band": {"bound": "hbm", "achieved_GBs": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / 1e9,
                       "frac": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / PEAK_HBM},
         "eig_windows": {"bound": "alu",
@@ -211,7 +216,7 @@ def phase_rows(torch, spec, synth, dev, with_cpu):
         "desc_windows": {"bound": "hbm", "achieved_GBs": S * W * (N * 4 + 144) / (part["desc_windows"] / 1e3) / 1e9}}
     rows["eigentrack_256x512x4096_N30"]["eig_windows"]["frac"] = \
         rows["eigentrack_256x512x4096_N30"]["eig_windows"]["achieved_TFLOPs"] * 1e12 / PEAK_F32_VALU
-    log(f"eigentrack: {tot:.3f} ms ({part})")
+    log(f"eigentrack: {tot:.3f} ms ({part}); fused eig+desc {fused:.3f} ms")
     if with_cpu:
         import oracle
         t0 = time.perf_counter()

@@ -323,6 +323,22 @@ int spec_tail_pair_screen(void *stream, const void *U, const void *V, int dt, in
                           uint8_t *keep, int64_t ldk, int64_t *count);
 
 /* ------------------------------------------------------------------------
+ * A3 + A5 fused: the eigenvalues of each small matrix and their descriptors in
+ * one pass ([RMT] section 3.2: per window, the spectrum and then its
+ * descriptors).  The same eigenvalues as spec_eigvalsh_batched and the same
+ * records as spec_descriptors on them (wt = SPEC_F32, r = n, ldw = n), computed
+ * while the spectrum is still in registers; each record's sums are taken in a
+ * different order, so fields may differ from the two-call path in the last
+ * bits.
+ * src, batch, info: as spec_eigvalsh_batched; w may be NULL (spectra not kept).
+ * p, out, ws, ws_bytes: as spec_descriptors with r = n (ws >= spec_descriptors_workspace(n)).
+ * Requires 2 <= n <= 32 (else SPEC_EINVAL, or SPEC_EUNSUPPORTED above 32) and
+ * the conditions of both calls.
+ * ---------------------------------------------------------------------- */
+int spec_eigvalsh_batched_desc(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info,
+                               const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * spec_descriptors_static: spec_descriptors for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same records, computed by the same kernels, with

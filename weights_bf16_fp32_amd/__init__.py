@@ -97,7 +97,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
-           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen"]
+           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen", "spec_eigvalsh_batched_desc"]
 
 _lib = None
 
@@ -130,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.spec_project_weight.argtypes = [vp, vp, i32, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp,
                                           ctypes.c_size_t]
         L.spec_spectrum_robust.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(RobustParams), vp]
+        L.spec_eigvalsh_batched_desc.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, vp,
+                                                  ctypes.POINTER(DescParams), vp, vp, ctypes.c_size_t]
         L.spec_tail_pair_screen.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, dbl, vp, i64, vp, i64,
                                              vp]
         L.spec_descriptors_static.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp]
@@ -438,3 +440,59 @@ def tail_pair_screen(U, V, *, i0: int | None = None, t: int | None = None, head_
                                        int(i0), int(t), int(head_dim), float(eps), _dev(absdot), absdot.stride(0),
                                        _dev(keep), keep.stride(0), _dev(count)))
     return absdot, keep, count
+
+
+def eigvalsh_batched_band_desc(band, n: int, scale: float, *, n_samples: int, p_dim: int, k: int = 1,
+                               stride: int = 1, mode: int = MODE_EIG, sigma2: float = 1.0,
+                               sigma2_mode: int = SIGMA2_GIVEN, top_frac: float = 0.2, small_rel: float = 1e-2,
+                               tail_frac: float = 0.7, w=None, keep_w: bool = True, info=None, out=None, ws=None,
+                               to_host: bool = True):
+    """Window spectra and their descriptors in one pass (spec_eigvalsh_batched_desc)
+    from the band [S, T, n] of gram_window.  Returns (w or None, info, records)."""
+    torch = _torch()
+    S, T, N = band.shape
+    if N != n or not band.is_contiguous():
+        raise SpecError(-1, "band must be a contiguous [streams, T, n] tensor")
+    batch = S * ((T - n) // stride + 1)
+    src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
+    dev = band.device
+    if w is None and keep_w:
+        w = torch.empty((batch, n), dtype=torch.float32, device=dev)
+    if info is None:
+        info = torch.empty((batch,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((batch, DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = torch.empty((descriptors_workspace(n),), dtype=torch.uint8, device=dev)
+    p = DescParams(mode, sigma2_mode, float(sigma2), int(n_samples), int(p_dim), int(k), float(top_frac),
+                   float(small_rel), float(tail_frac))
+    _check(lib().spec_eigvalsh_batched_desc(_stream(), ctypes.byref(src), batch, n,
+                                            _dev(w) if w is not None else None, _dev(info), ctypes.byref(p),
+                                            _dev(out), _dev(ws), ws.numel()))
+    rec = out.cpu().numpy().view(DESC_DTYPE).reshape(batch) if to_host else out
+    return w, info, rec
+
+
+def eigvalsh_batched_dense_desc(A, *, n_samples: int, p_dim: int, k: int = 1, w=None, info=None, out=None,
+                                ws=None, **kw):
+    """Dense batch [batch, n, n] (lower read): spectra and descriptors in one pass."""
+    torch = _torch()
+    if A.dim() == 2:
+        A = A.unsqueeze(0)
+    batch, n, _ = A.shape
+    src = BatchSrc(SRC_DENSE, _dev(A), A.stride(1), A.stride(0), 0, 0, 1, 1.0)
+    dev = A.device
+    if w is None:
+        w = torch.empty((batch, n), dtype=torch.float32, device=dev)
+    if info is None:
+        info = torch.empty((batch,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((batch, DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = torch.empty((descriptors_workspace(n),), dtype=torch.uint8, device=dev)
+    p = DescParams(kw.get("mode", MODE_EIG), kw.get("sigma2_mode", SIGMA2_GIVEN), float(kw.get("sigma2", 1.0)),
+                   int(n_samples), int(p_dim), int(k), float(kw.get("top_frac", 0.2)),
+                   float(kw.get("small_rel", 1e-2)), float(kw.get("tail_frac", 0.7)))
+    _check(lib().spec_eigvalsh_batched_desc(_stream(), ctypes.byref(src), batch, n, _dev(w), _dev(info),
+                                            ctypes.byref(p), _dev(out), _dev(ws), ws.numel()))
+    return w, info, out.cpu().numpy().view(DESC_DTYPE).reshape(batch)

@@ -15,6 +15,19 @@ inline int from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_EHIP
 
 inline size_t elt_size(int t) { return t == SPEC_BF16 ? 2 : (t == SPEC_F32 ? 4 : 8); }
 
+// the descriptor parameters for spectra of r values
+int check_desc_params(int64_t r, const spec_desc_params *p)
+{
+    if (p == nullptr || r < 2) return SPEC_EINVAL;
+    if (p->k < 1 || p->k >= r || p->n_samples < 1 || p->p_dim < 1) return SPEC_EINVAL;
+    if (!(p->top_frac >= 0.0 && p->top_frac <= 1.0) || !(p->tail_frac >= 0.0 && p->tail_frac <= 1.0) ||
+        !(p->small_rel >= 0.0))
+        return SPEC_EINVAL;
+    if (p->sigma2_mode < SPEC_SIGMA2_GIVEN || p->sigma2_mode > SPEC_SIGMA2_MEAN) return SPEC_EINVAL;
+    if (p->sigma2_mode == SPEC_SIGMA2_GIVEN && !(p->sigma2 > 0.0 && isfinite(p->sigma2))) return SPEC_EINVAL;
+    return SPEC_OK;
+}
+
 // the checks spec_descriptors and spec_descriptors_static share
 int check_descriptors(const void *w, int wt, int64_t batch, int64_t r, int64_t ldw, const spec_desc_params *p,
                       spec_desc *out)
@@ -102,6 +115,32 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
     }
     KTimer kt((hipStream_t)stream, SPEC_KT_SMALL_EIG);
     return from_hip(launch_eigvalsh_batched((hipStream_t)stream, src, batch, n, w, info));
+}
+
+int spec_eigvalsh_batched_desc(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info,
+                               const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes)
+{
+    if (src == nullptr || src->a == nullptr || out == nullptr) return SPEC_EINVAL;
+    if (n < 2 || n > 32) return n > 32 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+    if (batch < 0 || batch > ((int64_t)1 << 31) - 1) return SPEC_EINVAL;
+    const int st = check_desc_params(n, p);
+    if (st != SPEC_OK) return st;
+    if ((w != nullptr && !aligned(w, 4)) || !aligned(src->a, 4) || (info != nullptr && !aligned(info, 4)) ||
+        !aligned(out, 8))
+        return SPEC_EINVAL;
+    if (src->kind == SPEC_SRC_DENSE) {
+        if (src->lda < n || src->stride_a < (int64_t)n * src->lda) return SPEC_EINVAL;
+    } else if (src->kind == SPEC_SRC_BAND) {
+        if (src->streams < 1 || src->T < n || src->stride < 1 || !isfinite(src->scale)) return SPEC_EINVAL;
+        const int64_t W = (src->T - n) / src->stride + 1;
+        if (batch != src->streams * W) return SPEC_EINVAL;
+    } else {
+        return SPEC_EINVAL;
+    }
+    if (ws == nullptr || ws_bytes < descriptors_workspace_bytes(n)) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    KTimer kt((hipStream_t)stream, SPEC_KT_SMALL_EIG);
+    return from_hip(launch_eigvalsh_batched_desc((hipStream_t)stream, src, batch, n, w, info, p, out, ws));
 }
 
 int spec_eigvalsh_large_workspace(int64_t n, int t, size_t *bytes)

@@ -221,14 +221,19 @@ hipError_t scratch_on(hipStream_t stream, double **out)
 
 size_t descriptors_workspace_bytes(int64_t r) { return (size_t)((r + 31) / 32 * 32) * sizeof(double); }
 
+hipError_t launch_mp_table(hipStream_t stream, const spec_desc_params *p, int64_t r, void *ws)
+{
+    const double c = p->p_dim <= p->n_samples ? (double)p->p_dim / (double)p->n_samples
+                                               : (double)p->n_samples / (double)p->p_dim;
+    hipLaunchKernelGGL(mp_table, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, stream, c, r, (double *)ws);
+    return hipGetLastError();
+}
+
 hipError_t launch_descriptors(hipStream_t stream, const void *w, int wt, int64_t batch, int64_t r, int64_t ldw,
                               const spec_desc_params *p, spec_desc *out, void *ws)
 {
     double *q = (double *)ws;
-    const double c = p->p_dim <= p->n_samples ? (double)p->p_dim / (double)p->n_samples
-                                               : (double)p->n_samples / (double)p->p_dim;
-    hipLaunchKernelGGL(mp_table, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, stream, c, r, q);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_mp_table(stream, p, r, ws);
     if (e != hipSuccess) return e;
     if (batch == 0) return hipSuccess;
     const unsigned grid = (unsigned)std::min<int64_t>((batch + DW - 1) / DW, 8192);

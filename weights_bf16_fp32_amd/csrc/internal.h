@@ -27,6 +27,12 @@ hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64
 
 size_t descriptors_workspace_bytes(int64_t r);
 
+// the MP quantile table of r levels for the aspect ratio of p, into ws
+hipError_t launch_mp_table(hipStream_t stream, const spec_desc_params *p, int64_t r, void *ws);
+
+hipError_t launch_eigvalsh_batched_desc(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
+                                        int32_t *info, const spec_desc_params *p, spec_desc *out, void *ws);
+
 // spectra lengths the library-held MP table of spec_descriptors_static covers
 constexpr int64_t DESC_SCRATCH_MAX_R = 32768;
 

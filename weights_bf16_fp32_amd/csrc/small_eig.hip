@@ -208,19 +208,109 @@ __global__ __launch_bounds__(64) void small_eig_batched(spec_batch_src src, int6
     if (info != nullptr && lane == 0) info[b] = it;
 }
 
+// The descriptors of one spectrum held by a half-wave (lane i of the half has
+// the i-th largest value lam, i < r), as spec_descriptors computes them from
+// memory: the same formulas, fp64, half-wave sums; written by lane 0 of the
+// half.  lamsh is a per-half LDS row of the clamped values.
+__device__ __forceinline__ double hsum(double x) { return half_sum(x); }
+
+__device__ void desc_half(float lamf, int i, int r, const spec_desc_params &p, const double *__restrict__ qtab,
+                          double *__restrict__ lamsh, spec_desc *__restrict__ out, bool live)
+{
+    const bool in = i < r;
+    double v = (double)lamf;
+    v = v > 0.0 ? v : (v == v ? 0.0 : v);  // clamp round-off, keep NaN
+    v = in ? v : 0.0;
+    wave_sync();
+    lamsh[i] = v;
+    wave_sync();
+    auto lam = [&](int k) { return lamsh[k]; };
+    const int kt = (int)floor(p.top_frac * (double)r);
+    const bool fin = isfinite(v);
+    const double vf = fin ? v : 0.0, sg = sqrt(vf);
+    const double S = hsum(in && fin ? vf : 0.0);
+    const double Ssig = hsum(in && fin ? sg : 0.0);
+    const double Stop = hsum(in && fin && i < kt ? vf : 0.0);
+    const double Stop_sig = hsum(in && fin && i < kt ? sg : 0.0);
+    const double rpos = hsum(in && fin && vf > 0.0 ? 1.0 : 0.0);
+    const double bad = hsum(in && !fin ? 1.0 : 0.0);
+    const double l0 = lam(0), l1 = r > 1 ? lam(1) : 0.0;
+    double sigma2;
+    if (p.sigma2_mode == SPEC_SIGMA2_MEDIAN)
+        sigma2 = 0.5 * (lam((r - 1) / 2) + lam(r / 2));
+    else if (p.sigma2_mode == SPEC_SIGMA2_MEAN)
+        sigma2 = S / (double)p.p_dim;
+    else
+        sigma2 = p.sigma2;
+    const double c = (double)p.p_dim / (double)p.n_samples;
+    const double lplus = sigma2 * (1.0 + sqrt(c)) * (1.0 + sqrt(c));
+    const double sig1 = sqrt(l0);
+    const double small_thr = p.small_rel * sig1;
+    const bool companion = p.p_dim > p.n_samples;
+    const double mu_scale = companion ? (double)p.n_samples / (double)p.p_dim : 1.0;
+    double hs = 0.0;
+    if (in && fin && S > 0.0) {
+        const double pi = vf / S;
+        if (pi > 0.0) hs = -pi * log(pi);
+    }
+    const double Hs = hsum(hs);
+    const double w1 = hsum(in && fin ? fabs(mu_scale * vf - sigma2 * qtab[in ? r - 1 - i : 0]) : 0.0);
+    const double above = hsum(in && fin && vf > lplus ? 1.0 : 0.0);
+    const double small = hsum(in && fin && sg < small_thr ? 1.0 : 0.0);
+    if (i == 0 && live) {
+        spec_desc d;
+        const double nan = __builtin_nan("");
+        int64_t flags = 0;
+        if (bad > 0.0) flags |= SPEC_FLAG_NONFINITE;
+        if (!(S > 0.0)) flags |= SPEC_FLAG_S_ZERO;
+        d.S = S;
+        d.H = S > 0.0 ? Hs : nan;
+        d.erank = S > 0.0 ? exp(Hs) : nan;
+        d.m1 = S > 0.0 ? l0 / S : nan;
+        const int k = (int)p.k;
+        if (k < r && lam(k) > 0.0) {
+            d.gk = lam(k - 1) / lam(k);
+        } else {
+            d.gk = nan;
+            flags |= SPEC_FLAG_GK_UNDEF;
+        }
+        d.g1 = (r > 1 && l1 > 0.0) ? l0 / l1 : nan;
+        d.sigma2 = sigma2;
+        d.lambda_plus = lplus;
+        d.mp_w1 = sigma2 > 0.0 ? w1 / (double)r : nan;
+        d.top_energy = S > 0.0 ? Stop / S : nan;
+        d.top_sigma_share = Ssig > 0.0 ? Stop_sig / Ssig : nan;
+        int th = (int)floor(p.tail_frac * (double)r);
+        if (th > r - 1) th = r - 1;
+        d.tail_head = sqrt(lam(th));
+        d.tail_min = sqrt(lam(r - 1));
+        d.sigma1 = sig1;
+        d.n_above = (int64_t)above;
+        d.n_small = (int64_t)small;
+        d.r_pos = (int64_t)rpos;
+        d.flags = flags;
+        *out = d;
+    }
+}
+
 // Two matrices per wave for n <= 32: half h = lane / 32 takes matrix 2 g + h
 // and lane i = lane % 32 its row i.  Every sum is a half-wave butterfly, the
 // broadcasts go through per-half LDS rows, and each lane finds its own
 // eigenvalue, counting at both interior points of its interval in one pass
 // (two independent Sturm recurrences).  The arithmetic is that of
 // small_eig_batched, value for value.
+template <int NM, bool DESC>
 __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t batch, int n,
-                                                     float *__restrict__ w, int32_t *__restrict__ info)
+                                                     float *__restrict__ w, int32_t *__restrict__ info,
+                                                     spec_desc_params dp, const double *__restrict__ qtab,
+                                                     spec_desc *__restrict__ dout)
 {
-    constexpr int NM = 32;
-    __shared__ __attribute__((aligned(16))) float vs[2][NM];
-    __shared__ __attribute__((aligned(16))) float wsh[2][NM];
-    __shared__ __attribute__((aligned(16))) float dsh[2][NM + 1];
+    static_assert(NM <= 32, "a half-wave per matrix");
+    __shared__ __attribute__((aligned(16))) float vs[2][32];
+    __shared__ __attribute__((aligned(16))) float wsh[2][32];
+    __shared__ __attribute__((aligned(16))) float dsh[2][33];
+    __shared__ int cnt[2][64];
+    __shared__ double lamsh[2][32];
     const int lane = threadIdx.x, h = lane >> 5, i = lane & 31;
     const int64_t b = 2 * (int64_t)blockIdx.x + h;
     const bool live = b < batch;
@@ -303,11 +393,11 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
         for (int j = 0; j < NM; ++j) last = j == n - 2 ? a[j] : last;
         wave_sync();
         dsh[h][i] = diag;
-        if (n >= 2 && i == n - 1) dsh[h][NM] = last;
+        if (n >= 2 && i == n - 1) dsh[h][32] = last;
         wave_sync();
     }
     float d[NM], e2[NM];
-    const float elast = n >= 2 ? dsh[h][NM] : 0.f;
+    const float elast = n >= 2 ? dsh[h][32] : 0.f;
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
         d[k] = k < n ? dsh[h][k] : FLT_MAX;
@@ -337,18 +427,10 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
     const float pivmin = FLT_MIN * fmaxf(1.f, emax);
     const float atol = 0.0625f * FLT_EPSILON * span;
 
-    // ---- eigenvalue l = i (descending), ascending index n - 1 - l: trisection,
-    // the counts below both interior points in one pass
-    const int l = i;
-    const int target = n - 1 - min(l, n - 1);
-    float lo_l = lo, hi_l = hi;
-    int it = 0;
-    for (; it < 64; ++it) {
-        const float width = hi_l - lo_l;
-        const bool done = width <= fmaxf(atol, 2.f * FLT_EPSILON * fmaxf(fabsf(lo_l), fabsf(hi_l)));
-        if (__all(done || l >= n || !live)) break;
-        const float x1 = lo_l + width * (1.f / 3.f), x2 = lo_l + width * (2.f / 3.f);
-        int c1 = 0, c2 = 0;
+    // the Sturm counts below two points in one pass (two independent recurrences)
+    auto count2 = [&](float x1, float x2, int &c1, int &c2) __attribute__((always_inline)) {
+        c1 = 0;
+        c2 = 0;
         float q1 = 1.f, q2 = 1.f;
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
@@ -360,6 +442,47 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
             c1 += q1 < 0.f;
             c2 += q2 < 0.f;
         }
+    };
+    // ---- eigenvalue l = i (descending), ascending index n - 1 - l.  First a
+    // multisection shared by the half: its 32 lanes count below the 64 points
+    // lo + (q + 1) (hi - lo) / 65, and each lane takes the cell whose points
+    // bracket its eigenvalue (a binary search over the counts, which do not
+    // decrease); then trisection, the counts below both interior points in one
+    // pass.
+    const int l = i;
+    const int target = n - 1 - min(l, n - 1);
+    float lo_l = lo, hi_l = hi;
+    {
+        const float step = (hi - lo) * (1.f / 65.f);
+        int ca, cb;
+        count2(lo + (float)(2 * i + 1) * step, lo + (float)(2 * i + 2) * step, ca, cb);
+        wave_sync();
+        cnt[h][2 * i] = ca;
+        cnt[h][2 * i + 1] = cb;
+        wave_sync();
+        // the first point q with cnt[q] > target (64 if none): 65 answers, so
+        // seven halvings of [a0, a1), each only while the range is not empty
+        int a0 = 0, a1 = 64;
+#pragma unroll
+        for (int s = 0; s < 7; ++s) {
+            if (a0 < a1) {
+                const int mid = (a0 + a1) >> 1;  // < 64
+                const bool le = cnt[h][mid] <= target;
+                a0 = le ? mid + 1 : a0;
+                a1 = le ? a1 : mid;
+            }
+        }
+        lo_l = a0 == 0 ? lo : lo + (float)a0 * step;
+        hi_l = a0 == 64 ? hi : lo + (float)(a0 + 1) * step;
+    }
+    int it = 1;
+    for (; it < 64; ++it) {
+        const float width = hi_l - lo_l;
+        const bool done = width <= fmaxf(atol, 2.f * FLT_EPSILON * fmaxf(fabsf(lo_l), fabsf(hi_l)));
+        if (__all(done || l >= n || !live)) break;
+        const float x1 = lo_l + width * (1.f / 3.f), x2 = lo_l + width * (2.f / 3.f);
+        int c1, c2;
+        count2(x1, x2, c1, c2);
         if (!done) {
             if (c1 > target) {
                 hi_l = x1;
@@ -371,8 +494,10 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
             }
         }
     }
-    if (live && l < n) w[b * n + l] = bad ? __int_as_float(0x7fc00000) : 0.5f * (lo_l + hi_l);
+    const float lam_l = bad ? __int_as_float(0x7fc00000) : 0.5f * (lo_l + hi_l);
+    if (w != nullptr && live && l < n) w[b * n + l] = lam_l;
     if (live && info != nullptr && i == 0) info[b] = bad ? -1 : it;
+    if constexpr (DESC) desc_half(lam_l, i, n, dp, qtab, lamsh[h], dout + (live ? b : 0), live);
 }
 
 }  // namespace
@@ -381,10 +506,28 @@ hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src
                                    int32_t *info)
 {
     if (batch == 0) return hipSuccess;
-    if (n <= 32)
-        hipLaunchKernelGGL(small_eig_pair, dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src, batch, n, w,
-                           info);
+    const spec_desc_params none{};
+    if (n == 30)  // the EigenTrack window: no padding rows in the Sturm counts
+        hipLaunchKernelGGL((small_eig_pair<30, false>), dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src,
+                           batch, n, w, info, none, (const double *)nullptr, (spec_desc *)nullptr);
+    else if (n <= 32)
+        hipLaunchKernelGGL((small_eig_pair<32, false>), dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src,
+                           batch, n, w, info, none, (const double *)nullptr, (spec_desc *)nullptr);
     else
         hipLaunchKernelGGL(small_eig_batched<64>, dim3((unsigned)batch), dim3(64), 0, stream, *src, batch, n, w, info);
+    return hipGetLastError();
+}
+
+hipError_t launch_eigvalsh_batched_desc(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
+                                        int32_t *info, const spec_desc_params *p, spec_desc *out, void *ws)
+{
+    hipError_t e = launch_mp_table(stream, p, n, ws);
+    if (e != hipSuccess || batch == 0) return e;
+    if (n == 30)
+        hipLaunchKernelGGL((small_eig_pair<30, true>), dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src,
+                           batch, n, w, info, *p, (const double *)ws, out);
+    else
+        hipLaunchKernelGGL((small_eig_pair<32, true>), dim3((unsigned)((batch + 1) / 2)), dim3(64), 0, stream, *src,
+                           batch, n, w, info, *p, (const double *)ws, out);
     return hipGetLastError();
 }
