@@ -24,7 +24,8 @@
 //     for a tridiagonal within a few ulps of T entry by entry (Kahan's and
 //     Demmel's analysis of the bisection count), so the eigenvalues are within
 //     a small multiple of eps_f32 ||A||.  Intervals stop at 2 ulps of |lambda|
-//     or ||T|| / 2^24.
+//     or eps_f32 ||T|| (the default absolute tolerance of LAPACK's bisection),
+//     below the error the fp32 reduction already carries.
 #include <float.h>
 
 #include "common.h"
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64) void small_eig_batched(spec_batch_src src, int6
     lo -= 4.f * FLT_EPSILON * span;
     hi += 4.f * FLT_EPSILON * span;
     const float pivmin = FLT_MIN * fmaxf(1.f, emax);
-    const float atol = 0.0625f * FLT_EPSILON * span;
+    const float atol = FLT_EPSILON * span;
 
     auto below = [&](float x) {
         int cnt = 0;
@@ -296,9 +297,7 @@ __device__ void desc_half(float lamf, int i, int r, const spec_desc_params &p, c
 // Two matrices per wave for n <= 32: half h = lane / 32 takes matrix 2 g + h
 // and lane i = lane % 32 its row i.  Every sum is a half-wave butterfly, the
 // broadcasts go through per-half LDS rows, and each lane finds its own
-// eigenvalue, counting at both interior points of its interval in one pass
-// (two independent Sturm recurrences).  The arithmetic is that of
-// small_eig_batched, value for value.
+// eigenvalue.  The reduction is that of small_eig_batched, value for value.
 template <int NM, bool DESC>
 __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t batch, int n,
                                                      float *__restrict__ w, int32_t *__restrict__ info,
@@ -425,8 +424,20 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
     lo -= 4.f * FLT_EPSILON * span;
     hi += 4.f * FLT_EPSILON * span;
     const float pivmin = FLT_MIN * fmaxf(1.f, emax);
-    const float atol = 0.0625f * FLT_EPSILON * span;
+    const float atol = FLT_EPSILON * span;
 
+    // the Sturm count below x
+    auto count1 = [&](float x) __attribute__((always_inline)) {
+        int c = 0;
+        float q = 1.f;
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            q = (d[k] - x) - (k > 0 ? e2[k - 1] : 0.f) * __builtin_amdgcn_rcpf(q);
+            q = fabsf(q) < pivmin ? -pivmin : q;
+            c += q < 0.f;
+        }
+        return c;
+    };
     // the Sturm counts below two points in one pass (two independent recurrences)
     auto count2 = [&](float x1, float x2, int &c1, int &c2) __attribute__((always_inline)) {
         c1 = 0;
@@ -447,8 +458,9 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
     // multisection shared by the half: its 32 lanes count below the 64 points
     // lo + (q + 1) (hi - lo) / 65, and each lane takes the cell whose points
     // bracket its eigenvalue (a binary search over the counts, which do not
-    // decrease); then trisection, the counts below both interior points in one
-    // pass.
+    // decrease); then bisection, one count per lane and step: the kernel is
+    // bound by VALU issue, and a halving costs half a trisection's two counts
+    // for 1 bit against log2(3) bits.
     const int l = i;
     const int target = n - 1 - min(l, n - 1);
     float lo_l = lo, hi_l = hi;
@@ -480,18 +492,13 @@ __global__ __launch_bounds__(64) void small_eig_pair(spec_batch_src src, int64_t
         const float width = hi_l - lo_l;
         const bool done = width <= fmaxf(atol, 2.f * FLT_EPSILON * fmaxf(fabsf(lo_l), fabsf(hi_l)));
         if (__all(done || l >= n || !live)) break;
-        const float x1 = lo_l + width * (1.f / 3.f), x2 = lo_l + width * (2.f / 3.f);
-        int c1, c2;
-        count2(x1, x2, c1, c2);
+        const float x = lo_l + 0.5f * width;
+        const int c = count1(x);
         if (!done) {
-            if (c1 > target) {
-                hi_l = x1;
-            } else if (c2 > target) {
-                lo_l = x1;
-                hi_l = x2;
-            } else {
-                lo_l = x2;
-            }
+            if (c > target)
+                hi_l = x;
+            else
+                lo_l = x;
         }
     }
     const float lam_l = bad ? __int_as_float(0x7fc00000) : 0.5f * (lo_l + hi_l);
