@@ -339,6 +339,33 @@ int spec_eigvalsh_batched_desc(void *stream, const spec_batch_src *src, int64_t 
                                const spec_desc_params *p, spec_desc *out, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Sliding-window spectra by incremental updates ("Random matrix theory
+ * spectral methods" page, section 3.2: update the window decomposition as the
+ * window moves instead of recomputing it).  The windows of spec_eigvalsh_batched
+ * with a SPEC_SRC_BAND source, with the eigenvalues carried from window to
+ * window: each step drops the oldest row of the window Gram (secular equation
+ * of the principal submatrix) and appends the new one (arrowhead secular
+ * equation), with the eigenvectors kept in fp64 and recomputed from the roots
+ * (Gu-Eisenstat weights), so they stay orthogonal to working precision.
+ * A chain restarts from an empty window every `restart` windows of a stream,
+ * which bounds the accumulated round-off and sets the launch's parallelism
+ * (streams * ceil(W / restart) chains).
+ * src:     SPEC_SRC_BAND only (else SPEC_EINVAL); batch = streams * W.
+ * restart: windows per chain, >= 1.
+ * w:       f32 [batch][n], eigenvalues descending (fp64 arithmetic, rounded).
+ * info:    int32 [batch] (may be NULL): the largest secular iteration count of
+ *          the updates that led to the window, or -1 if the window holds a step
+ *          whose band row has a non-finite value within the window (its
+ *          eigenvalues are then NaN; the chain restarts after that step).
+ * Requires 1 <= n <= 64 and the band conditions of spec_eigvalsh_batched.
+ * Currently switched off: after validation every call returns
+ * SPEC_EUNSUPPORTED and enqueues nothing (the kernel faulted on its first GPU
+ * run and the cause is not yet found).
+ * ---------------------------------------------------------------------- */
+int spec_eigvalsh_sliding(void *stream, const spec_batch_src *src, int64_t batch, int n, int restart, float *w,
+                          int32_t *info);
+
+/* ------------------------------------------------------------------------
  * spec_descriptors_static: spec_descriptors for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same records, computed by the same kernels, with

@@ -16,6 +16,9 @@ What it computes, each function citing the passage it follows:
   covariance (1/N) H^T H, whose nonzero spectrum equals that of G_w).
 * :func:`band_gram`       <h_t, h_{t-j}> for 0 <= j < N, the only inner products
   the windows use.
+* :func:`band_window_gram` the window Gram rebuilt from a band, scale *
+  B[w*stride + max(i, j), |i - j|]: what the windows' eigensolvers (batched, or
+  by incremental updates as RMT page, section 3.2 suggests) see as input.
 * :func:`eigvalsh_small`  cyclic Jacobi (C, fp64), descending.
 * :func:`eigvalsh_large`  Householder tridiagonalisation + Sturm bisection.
 * :func:`mp_quantiles`    quantiles of the Marchenko-Pastur law (RMT page,
@@ -153,6 +156,21 @@ def window_gram(H: np.ndarray, dtype: str, N: int, windows=None, stride: int = 1
         hw = h[w * stride: w * stride + N]
         out.append(hw @ hw.T / N)
     return np.array(out, dtype=np.float64)
+
+
+def band_window_gram(B: np.ndarray, N: int, scale: float, stride: int = 1, windows=None) -> np.ndarray:
+    """K_w[i, j] = scale * B[w*stride + max(i, j), |i - j|] for one stream's band
+    B [T, N] (entry j of row t is <h_t, h_{t-j}>): the window Gram of window w
+    written out from the band, fp64 ("Random matrix theory spectral methods"
+    page, section 3.1; with scale = 1/N it is window_gram)."""
+    B = np.asarray(B, dtype=np.float64)
+    T = B.shape[0]
+    W = (T - N) // stride + 1
+    idx = range(W) if windows is None else windows
+    i = np.arange(N)
+    rows = np.maximum.outer(i, i)
+    lags = np.abs(np.subtract.outer(i, i))
+    return np.array([scale * B[w * stride + rows, lags] for w in idx], dtype=np.float64).reshape(-1, N, N)
 
 
 # ---------------------------------------------------------------- spectra

@@ -94,6 +94,21 @@ def test_batched_validation(L):
     assert f(None, None, 4, 30, FAKE, None) == EINVAL
 
 
+def test_sliding_validation(L):
+    f = L.spec_eigvalsh_sliding
+    band = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 100, 1, 1 / 30)
+    dense = spec.BatchSrc(spec.SRC_DENSE, FAKE, 30, 900, 0, 0, 1, 1.0)
+    assert f(None, ctypes.byref(dense), 4, 30, 64, FAKE, None) == EINVAL  # band sources only
+    assert f(None, ctypes.byref(band), 2 * 71, 30, 0, FAKE, None) == EINVAL  # restart < 1
+    assert f(None, ctypes.byref(band), 2 * 70, 30, 64, FAKE, None) == EINVAL  # batch != S * W
+    assert f(None, ctypes.byref(band), 2 * 71, 65, 64, FAKE, None) == EUNSUPPORTED
+    assert f(None, ctypes.byref(band), 2 * 71, 0, 64, FAKE, None) == EINVAL
+    assert f(None, ctypes.byref(band), 2 * 71, 30, 64, FAKE + 2, None) == EINVAL  # misaligned w
+    assert f(None, ctypes.byref(band), 2 * 71, 30, 64, None, None) == EINVAL
+    short = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 20, 1, 1 / 30)
+    assert f(None, ctypes.byref(short), 0, 30, 64, FAKE, None) == EINVAL  # T < n
+
+
 def test_alignment_codes(L):
     """Every device pointer must be aligned to its element size, workspaces to 256
     bytes, and the large eigensolver's A to 16 bytes; anything less is SPEC_EINVAL."""

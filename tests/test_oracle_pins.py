@@ -133,6 +133,34 @@ def test_window_gram_duality_and_band():
                 assert abs(G[w, i, j] - B[1, w + max(i, j), abs(i - j)] / N) <= 1e-12 * G[w, 0, 0]
 
 
+def test_band_window_gram_pins():
+    """The window Gram rebuilt from a band: equal to window_gram straight from H
+    (stride 1 and 3), entries by hand-indexed loops, and consecutive windows
+    sharing their (N-1) x (N-1) block, whose spectrum interlaces both windows'
+    (Cauchy), so a shifted or transposed band index fails."""
+    H = synth.eigentrack(streams=1, T=60, d=40)[0]
+    N = 9
+    B = oracle.band_gram(H, "bf16", N)[0]
+    for stride in (1, 3):
+        K = oracle.band_window_gram(B, N, 1.0 / N, stride=stride)
+        G = oracle.window_gram(H, "bf16", N, stride=stride)
+        assert K.shape == G.shape == ((60 - N) // stride + 1, N, N)
+        assert np.max(np.abs(K - G)) <= 1e-12 * np.max(np.abs(G))
+    K = oracle.band_window_gram(B, N, 2.0, stride=2, windows=[4])[0]
+    for i in range(N):
+        for j in range(N):
+            t, lag = 8 + max(i, j), abs(i - j)
+            assert K[i, j] == 2.0 * B[t, lag]
+    K = oracle.band_window_gram(B, N, 1.0)
+    for w in range(0, K.shape[0] - 1, 7):
+        assert np.array_equal(K[w, 1:, 1:], K[w + 1, :-1, :-1])
+        inner = np.linalg.eigvalsh(K[w, 1:, 1:])
+        for A in (K[w], K[w + 1]):
+            lam = np.linalg.eigvalsh(A)
+            tol = 1e-12 * lam[-1]
+            assert np.all(lam[:-1] <= inner + tol) and np.all(inner <= lam[1:] + tol)
+
+
 # ------------------------------------------------------------- P5 MP bulk
 
 def test_mp_bulk_pure_noise():

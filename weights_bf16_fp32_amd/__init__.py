@@ -97,7 +97,8 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_eigvalsh_batched", "spec_eigvalsh_large_workspace", "spec_eigvalsh_large",
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
-           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen", "spec_eigvalsh_batched_desc"]
+           "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen", "spec_eigvalsh_batched_desc",
+           "spec_eigvalsh_sliding"]
 
 _lib = None
 
@@ -231,6 +232,24 @@ def eigvalsh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, i
     batch = S * ((T - n) // stride + 1)
     src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
     return _batched(src, batch, n, w, info, band.device)
+
+
+def eigvalsh_sliding(band, n: int, scale: float, stride: int = 1, restart: int = 64, w=None, info=None):
+    """The spectra of eigvalsh_batched_band by rank-one down/up-dates along each
+    stream (fp64, a fresh start every `restart` windows).  info[b] = largest
+    secular iteration count of the window's updates, or -1 (non-finite step)."""
+    torch = _torch()
+    S, T, N = band.shape
+    if N != n or not band.is_contiguous():
+        raise SpecError(-1, "band must be a contiguous [streams, T, n] tensor")
+    batch = S * ((T - n) // stride + 1)
+    src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
+    if w is None:
+        w = torch.empty((batch, n), dtype=torch.float32, device=band.device)
+    if info is None:
+        info = torch.empty((batch,), dtype=torch.int32, device=band.device)
+    _check(lib().spec_eigvalsh_sliding(_stream(), ctypes.byref(src), batch, n, int(restart), _dev(w), _dev(info)))
+    return w, info
 
 
 def eigvalsh_large_workspace(n: int, dtype) -> int:

@@ -20,6 +20,9 @@ hipError_t launch_gram_dense(hipStream_t stream, const void *H, int ht, int64_t 
 hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
                                    int32_t *info);
 
+hipError_t launch_eigvalsh_sliding(hipStream_t stream, const spec_batch_src *src, int n, int restart, float *w,
+                                   int32_t *info);
+
 size_t eig_large_workspace_bytes(int64_t n, int t);
 
 hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64_t lda, void *w, void *ws,
