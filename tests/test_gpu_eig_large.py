@@ -118,3 +118,28 @@ def test_eig_large_f32_trace_preserved(spec, n):
     eps = float(np.finfo(np.float32).eps)
     print(f"[trace] n={n} |sum(lambda) - tr(A)| = {drift:.3g}, n eps lambda_max = {n * eps * w[0]:.3g}", flush=True)
     assert drift <= 0.25 * n * eps * float(w[0])
+
+
+@pytest.mark.parametrize("kind", ["zero", "identity", "graded"])
+def test_eig_large_panel_qr_paths(spec, kind):
+    """Panels tall enough for the CholeskyQR panel factorisation (n = 600): zero
+    and identity matrices give all-zero panels (the pivots fail and TSQR takes
+    over), graded spectra over eight decades give ill-conditioned panels (the
+    second pass, or TSQR), against the known eigenvalues."""
+    n = 600
+    rng = np.random.default_rng(31)
+    if kind == "zero":
+        lam = np.zeros(n)
+    elif kind == "identity":
+        lam = np.ones(n)
+    else:
+        lam = np.logspace(0, -8, n)
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    A = np.eye(n) * lam[0] if kind != "graded" else (Q * lam) @ Q.T
+    if kind == "zero":
+        A = np.zeros((n, n))
+    ref = np.sort(lam)[::-1]
+    for dt, tol in ((np.float32, 2e-5), (np.float64, 1e-11)):
+        w, info = _run(spec, A, dt)
+        assert info == 0
+        assert np.max(np.abs(w - ref)) <= tol * max(1.0, ref[0]), (kind, dt)

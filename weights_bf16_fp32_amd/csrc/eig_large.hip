@@ -284,8 +284,10 @@ __global__ __launch_bounds__(256) void k_panel_direct(T *__restrict__ Pg, int64_
 // ---- TSQR, step 1: local QR of row block b (rows [b*per, min(m, (b+1)*per)), per <= NT)
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_tsqr_local(const T *__restrict__ Pg, int64_t lda, int m, int per,
-                                                   T *__restrict__ Vloc, T *__restrict__ Tloc, T *__restrict__ Rstack)
+                                                   T *__restrict__ Vloc, T *__restrict__ Tloc, T *__restrict__ Rstack,
+                                                   const int *__restrict__ gate)
 {
+    if (gate != nullptr && *gate != 1) return;  // runs only for a panel whose CholeskyQR broke down (state 1)
     __shared__ RegQr<T, NT> S;
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
@@ -315,8 +317,10 @@ __global__ __launch_bounds__(NT) void k_tsqr_local(const T *__restrict__ Pg, int
 template <typename T, int NW>
 __global__ __launch_bounds__(64 * NW) void k_tsqr_wave(const T *__restrict__ Pg, int64_t lda, int m, int per,
                                                        T *__restrict__ Vloc, T *__restrict__ Tloc,
-                                                       T *__restrict__ Rstack, T *__restrict__ Kt)
+                                                       T *__restrict__ Rstack, T *__restrict__ Kt,
+                                                       const int *__restrict__ gate)
 {
+    if (gate != nullptr && *gate != 1) return;  // runs only for a panel whose CholeskyQR broke down (state 1)
     static_assert(std::is_same<T, float>::value, "rows of 32 fp32 columns in registers");
     constexpr int RPL = 4;
     __shared__ __attribute__((aligned(16))) T red[NW][NB];  // per-wave column sums
@@ -474,8 +478,10 @@ __global__ __launch_bounds__(64 * NW) void k_tsqr_wave(const T *__restrict__ Pg,
 // (Q_top [I; 0] = [I; 0] - V_top K)
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_tsqr_top(const T *__restrict__ Rstack, int nblk, T *__restrict__ Rf,
-                                                 T *__restrict__ Vtop, T *__restrict__ Kt)
+                                                 T *__restrict__ Vtop, T *__restrict__ Kt,
+                                                 const int *__restrict__ gate)
 {
+    if (gate != nullptr && *gate != 1) return;  // runs only for a panel whose CholeskyQR broke down (state 1)
     __shared__ RegQr<T, NT> S;
     __shared__ T Vt[NB * LDP];
     const int tid = threadIdx.x;
@@ -510,8 +516,9 @@ __global__ __launch_bounds__(NT) void k_tsqr_top(const T *__restrict__ Rstack, i
 template <typename T>
 __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, const T *__restrict__ Tloc,
                                                  const T *__restrict__ Vtop, const T *__restrict__ Ktop, int m,
-                                                 int per, T *__restrict__ Q1)
+                                                 int per, T *__restrict__ Q1, const int *__restrict__ gate)
 {
+    if (gate != nullptr && *gate != 1) return;  // runs only for a panel whose CholeskyQR broke down (state 1)
     constexpr int L = NB + 1;  // padded rows: a lane per row reads without bank conflicts
     __shared__ T Vt[NB * L], Tb[NB * L], Qb[NB * L], Y[NB * L], K[NB * L];
     const int tid = threadIdx.x;
@@ -600,6 +607,218 @@ __global__ __launch_bounds__(256) void k_tsqr_q1(const T *__restrict__ Vloc, con
 #pragma unroll
         for (int jj = 0; jj < NB; ++jj) s -= vrow[jj] * K[jj * L + c];
         Q1[(int64_t)(r0 + i) * NB + c] = s;
+    }
+}
+
+// ---- Panel QR by CholeskyQR2 in fp64: G = P^T P (partial Grams of CQ_ROWS-row
+// blocks, summed by one workgroup), R = chol(G), Q = P R^{-1}, and the same
+// once more on Q; the product of the two R factors is the panel's R and the
+// second Q its orthonormal factor Q1 (Yamamoto, Nakatsukasa, Yanagisawa and
+// Fukaya's CholeskyQR2).  All of it is parallel over the panel's rows, where
+// Householder QR of the same panel runs NB dependent column steps.  With the
+// Gram in fp64 the first pass leaves Q orthogonal to ~cond(P)^2 eps64 and the
+// second to working precision, for cond(P) up to ~1e6: a pivot below CQ_TOL
+// times its column's squared norm (or a zero or non-finite one) sets the
+// panel's flag, and the TSQR kernels, which run only when it is set, factor the
+// panel instead.
+constexpr int CQ_ROWS = 256;     // rows per Gram workgroup (two LDS chunks of 128)
+constexpr int CQ_AROWS = 32;     // rows per workgroup of Q = P R^{-1}
+constexpr double CQ_TOL = 1e-12;
+
+// States of a panel's CholeskyQR (one int in the workspace).
+enum : int {
+    CQ_DONE1 = 0,   // one pass was enough: Q1 and Rf written by the first pass
+    CQ_BROKE = 1,   // a pivot failed: TSQR factors the panel
+    CQ_NEED2 = 2,   // the first pass's Q (fp64) goes through a second pass
+    CQ_DONE2 = 3,   // the second pass succeeded
+};
+// One pass leaves Q orthogonal to ~cond(P)^2 eps64: below fp32 rounding while
+// cond_F(R) = |R|_F |R^{-1}|_F stays under this (fp32 panels only).
+constexpr double CQ_ONE_PASS_COND = 2000.0;
+
+// The partial Grams of P's CQ_ROWS-row blocks (the second pass only in state CQ_NEED2).
+template <typename Tin>
+__global__ __launch_bounds__(256) void k_cqr_gram(const Tin *__restrict__ P, int64_t ldp, int m,
+                                                  double *__restrict__ Gpart, const int *__restrict__ flag)
+{
+    if (flag != nullptr && *flag != CQ_NEED2) return;
+    constexpr int LS = NB + 2;  // 16-byte aligned rows
+    constexpr int CH = 128;     // rows per LDS chunk
+    constexpr int PER = CH * NB / 256;
+    __shared__ __attribute__((aligned(16))) double S[CH * LS];
+    const int tid = threadIdx.x;
+    // four row groups of 32 rows per chunk; in each, thread t owns the 4 x 4
+    // tile (t / 8, t % 8) of the 32 x 32 Gram
+    const int g = tid >> 6, t = tid & 63, i0 = 4 * (t >> 3), j0 = 4 * (t & 7);
+    double acc[4][4] = {};
+#pragma unroll 1
+    for (int ch = 0; ch < CQ_ROWS / CH; ++ch) {
+        const int64_t r0 = (int64_t)blockIdx.x * CQ_ROWS + ch * CH;
+        // every load of the chunk in flight before the first LDS store
+        Tin v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int p = tid + 256 * q, r = p / NB, c = p % NB;
+            v[q] = r0 + r < m ? P[(r0 + r) * ldp + c] : (Tin)0;
+        }
+        if (ch > 0) __syncthreads();  // the previous chunk is consumed
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int p = tid + 256 * q;
+            S[(p / NB) * LS + p % NB] = (double)v[q];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int r = g * 32; r < g * 32 + 32; ++r) {
+            const double2 a01 = *(const double2 *)&S[r * LS + i0], a23 = *(const double2 *)&S[r * LS + i0 + 2];
+            const double2 b01 = *(const double2 *)&S[r * LS + j0], b23 = *(const double2 *)&S[r * LS + j0 + 2];
+            const double a[4] = {a01.x, a01.y, a23.x, a23.y}, bb[4] = {b01.x, b01.y, b23.x, b23.y};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w] = fma(a[u], bb[w], acc[u][w]);
+        }
+    }
+    __syncthreads();
+    double *red = S;  // 4 x NB x NB partial sums (4096 doubles <= CH * LS)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) red[g * NB * NB + (i0 + u) * NB + j0 + w] = acc[u][w];
+    __syncthreads();
+    for (int p = tid; p < NB * NB; p += 256)
+        Gpart[(int64_t)blockIdx.x * NB * NB + p] = (red[p] + red[NB * NB + p]) + (red[2 * NB * NB + p] + red[3 * NB * NB + p]);
+}
+
+// G = the sum of nblk partial Grams; R (upper, G = R^T R) and R^{-1} together
+// by Gauss-Jordan elimination on [G | I] without pivoting (G is symmetric
+// positive definite): after it the left half is U = D L^T and the right half
+// L^{-1} (G = L D L^T, L unit lower), so R = D^{-1/2} U and R^{-1} =
+// L^{-T} D^{-1/2}.  One thread per entry of the 32 x 64 system, one barrier
+// per column.
+// First pass (second == false): R into R1 and R^{-1} into Rinv; the state
+// becomes CQ_BROKE on a failed pivot, else CQ_DONE1 (with Rf = R) when T is
+// fp32 and cond_F(R) is below CQ_ONE_PASS_COND, else CQ_NEED2.  Second pass
+// (only in state CQ_NEED2): Rf = R R1 and R^{-1} into Rinv, state CQ_DONE2, or
+// CQ_BROKE on a failed pivot.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_cqr_chol(const double *__restrict__ Gpart, int nblk, bool second,
+                                                   double *__restrict__ R1, double *__restrict__ Rinv,
+                                                   T *__restrict__ Rf, int *__restrict__ flag)
+{
+    if (second && *flag != CQ_NEED2) return;
+    constexpr int L2 = 2 * NB + 1;
+    __shared__ double A[NB * L2], diag0[NB], rs[NB], nr[32], ni[32];
+    __shared__ int bad;
+    const int tid = threadIdx.x;
+    {
+        // the sum over the partial Grams: eight independent chains of loads
+        const int p = tid;
+        double s8[8] = {};
+        int b = 0;
+        for (; b + 8 <= nblk; b += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s8[u] += Gpart[(int64_t)(b + u) * NB * NB + p];
+        }
+        for (int u = 0; b + u < nblk; ++u) s8[u] += Gpart[(int64_t)(b + u) * NB * NB + p];
+        const double sum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+        const int i = p / NB, j = p % NB;
+        A[i * L2 + j] = sum;
+        A[i * L2 + NB + j] = i == j ? 1.0 : 0.0;
+        if (i == j) diag0[i] = sum;
+    }
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    for (int k = 0; k < NB; ++k) {
+        const double piv = A[k * L2 + k];
+        if (!(piv > CQ_TOL * diag0[k] && piv <= DBL_MAX)) {  // the same in every thread
+            if (tid == 0) bad = 1;
+            break;
+        }
+        const double inv = 1.0 / piv;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int p = tid + 1024 * h, i = p >> 6, j = p & 63;
+            if (i > k && j > k) A[i * L2 + j] -= (A[i * L2 + k] * inv) * A[k * L2 + j];
+        }
+        __syncthreads();
+    }
+    __syncthreads();
+    if (bad) {
+        if (tid == 0) *flag = CQ_BROKE;
+        return;
+    }
+    if (tid < NB) rs[tid] = 1.0 / sqrt(A[tid * L2 + tid]);
+    __syncthreads();
+    const int i = tid / NB, j = tid % NB;
+    const double r = j >= i ? A[i * L2 + j] * rs[i] : 0.0;       // R = D^{-1/2} U
+    const double ri = j >= i ? A[j * L2 + NB + i] * rs[j] : 0.0;  // R^{-1} = L^{-T} D^{-1/2}
+    Rinv[tid] = ri;
+    if (second) {
+        double x = 0.0;  // Rf = R R1
+        for (int l = i; l <= j; ++l) x += A[i * L2 + l] * rs[i] * R1[l * NB + j];
+        Rf[tid] = (T)x;
+        if (tid == 0) *flag = CQ_DONE2;
+        return;
+    }
+    R1[tid] = r;
+    // cond_F(R): wave sums, then the 16 waves' partials
+    double sr = r * r, si = ri * ri;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sr += __shfl_xor(sr, o);
+        si += __shfl_xor(si, o);
+    }
+    if ((tid & 63) == 0) {
+        nr[tid >> 6] = sr;
+        ni[tid >> 6] = si;
+    }
+    __syncthreads();
+    double tr = 0.0, ti = 0.0;
+    for (int w = 0; w < 16; ++w) {
+        tr += nr[w];
+        ti += ni[w];
+    }
+    const bool one = sizeof(T) == 4 && sqrt(tr * ti) < CQ_ONE_PASS_COND;
+    if (one) Rf[tid] = (T)r;
+    if (tid == 0) *flag = one ? CQ_DONE1 : CQ_NEED2;
+}
+
+// First pass of Q = P R^{-1} (CQ_AROWS rows per workgroup; thread (r, c) forms
+// entry c of row r from the row in LDS and column c of R^{-1}): into Q1 (T) in
+// state CQ_DONE1, into Qd (fp64) in state CQ_NEED2, nothing otherwise.  Second
+// pass (Qd -> Q1): only in state CQ_DONE2.
+template <typename Tin, typename T>
+__global__ __launch_bounds__(256) void k_cqr_apply(const Tin *__restrict__ P, int64_t ldp, int m,
+                                                   const double *__restrict__ Rinv, bool second,
+                                                   T *__restrict__ Q1, double *__restrict__ Qd,
+                                                   const int *__restrict__ flag)
+{
+    const int st = *flag;
+    if (second ? st != CQ_DONE2 : (st != CQ_DONE1 && st != CQ_NEED2)) return;
+    constexpr int L = NB + 1;
+    __shared__ double Ri[NB * L], Ps[CQ_AROWS * L];
+    const int tid = threadIdx.x, c = tid & 31, rr = tid >> 5;
+    const int64_t r0 = (int64_t)blockIdx.x * CQ_AROWS;
+    for (int p = tid; p < NB * NB; p += 256) Ri[(p / NB) * L + p % NB] = Rinv[p];
+    for (int p = tid; p < CQ_AROWS * NB; p += 256) {
+        const int64_t r = r0 + p / NB;
+        Ps[(p / NB) * L + p % NB] = r < m ? (double)P[r * ldp + p % NB] : 0.0;
+    }
+    __syncthreads();
+    const bool to_q1 = second || st == CQ_DONE1;
+#pragma unroll
+    for (int q = 0; q < CQ_AROWS / 8; ++q) {
+        const int lr = rr + 8 * q;
+        const int64_t r = r0 + lr;
+        double x = 0.0;
+        for (int i = 0; i <= c; ++i) x = fma(Ps[lr * L + i], Ri[i * L + c], x);
+        if (r < m) {
+            if (to_q1)
+                Q1[r * NB + c] = (T)x;
+            else
+                Qd[r * NB + c] = x;
+        }
     }
 }
 
@@ -1899,8 +2118,8 @@ struct Ws {
 template <typename T>
 struct Bufs {
     T *band, *V, *V2, *W, *X, *Xpart, *Q1, *Vloc, *Tloc, *Rstack, *Rf, *Vtop, *Ttop, *Ktop, *U, *Tm, *Ppart;
-    int32_t *prog;
-    double *dd, *ee2, *bounds;
+    int32_t *prog, *cqf;
+    double *dd, *ee2, *bounds, *Qd, *Gp, *R1, *Rinv;
     float2 *de32;
 };
 
@@ -1933,6 +2152,11 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.ee2 = ws.take<double>((size_t)n);
     b.bounds = ws.take<double>(4);
     b.de32 = ws.take<float2>((size_t)n);
+    b.Qd = ws.take<double>((size_t)n * NB);
+    b.Gp = ws.take<double>((size_t)cdiv_h(n, CQ_ROWS) * NB * NB);
+    b.R1 = ws.take<double>((size_t)NB * NB);
+    b.Rinv = ws.take<double>((size_t)NB * NB);
+    b.cqf = ws.take<int32_t>(1);
     return ws.off;
 }
 
@@ -2021,6 +2245,26 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                 hipLaunchKernelGGL(k_panel_direct<T>, dim3(1), dim3(256), 0, s, P, lda, (int)m, Vout, b.Tm);
                 LAUNCH_OK();
             } else {
+                // CholeskyQR2 into Q1 and Rf; the TSQR below runs only if it breaks down
+                const int ng = (int)cdiv_h(m, CQ_ROWS), na = (int)cdiv_h(m, CQ_AROWS);
+                hipLaunchKernelGGL(k_cqr_gram<T>, dim3(ng), dim3(256), 0, s, (const T *)P, lda, (int)m, b.Gp,
+                                   (const int *)nullptr);
+                LAUNCH_OK();
+                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(1024), 0, s, b.Gp, ng, false, b.R1, b.Rinv, b.Rf,
+                                   b.cqf);
+                LAUNCH_OK();
+                hipLaunchKernelGGL((k_cqr_apply<T, T>), dim3(na), dim3(256), 0, s, (const T *)P, lda, (int)m,
+                                   b.Rinv, false, b.Q1, b.Qd, b.cqf);
+                LAUNCH_OK();
+                hipLaunchKernelGGL(k_cqr_gram<double>, dim3(ng), dim3(256), 0, s, (const double *)b.Qd, (int64_t)NB,
+                                   (int)m, b.Gp, b.cqf);
+                LAUNCH_OK();
+                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(1024), 0, s, b.Gp, ng, true, b.R1, b.Rinv, b.Rf,
+                                   b.cqf);
+                LAUNCH_OK();
+                hipLaunchKernelGGL((k_cqr_apply<double, T>), dim3(na), dim3(256), 0, s, (const double *)b.Qd,
+                                   (int64_t)NB, (int)m, b.Rinv, true, b.Q1, b.Qd, b.cqf);
+                LAUNCH_OK();
                 // row blocks of about 256 rows, at most TOP_BLOCKS of them (the stacked R
                 // factors of all blocks are factored by one workgroup)
                 const int nblk = (int)std::min<int64_t>(TOP_BLOCKS, cdiv_h(m, 256));
@@ -2031,48 +2275,48 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                 if constexpr (std::is_same<T, float>::value) {
                     if (per <= 256)
                         hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(nblk), dim3(64), 0, s, P, lda, (int)m, per, b.Vloc,
-                                           b.Tloc, b.Rstack, (T *)nullptr);
+                                           b.Tloc, b.Rstack, (T *)nullptr, (const int *)b.cqf);
                     else if (per <= 512)
                         hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(nblk), dim3(128), 0, s, P, lda, (int)m, per,
-                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr, (const int *)b.cqf);
                     else
                         hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(nblk), dim3(256), 0, s, P, lda, (int)m, per,
-                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr);
+                                           b.Vloc, b.Tloc, b.Rstack, (T *)nullptr, (const int *)b.cqf);
                     LAUNCH_OK();
                     if (rows_top <= 256)
                         hipLaunchKernelGGL((k_tsqr_wave<T, 1>), dim3(1), dim3(64), 0, s, b.Rstack, (int64_t)NB, rows_top,
-                                           rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                                           rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)b.cqf);
                     else if (rows_top <= 512)
                         hipLaunchKernelGGL((k_tsqr_wave<T, 2>), dim3(1), dim3(128), 0, s, b.Rstack, (int64_t)NB,
-                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)b.cqf);
                     else
                         hipLaunchKernelGGL((k_tsqr_wave<T, 4>), dim3(1), dim3(256), 0, s, b.Rstack, (int64_t)NB,
-                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                                           rows_top, rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)b.cqf);
                     LAUNCH_OK();
                 } else {
                     if (per <= 256)
                         hipLaunchKernelGGL((k_tsqr_local<T, 256>), dim3(nblk), dim3(256), 0, s, P, lda, (int)m, per,
-                                           b.Vloc, b.Tloc, b.Rstack);
+                                           b.Vloc, b.Tloc, b.Rstack, (const int *)b.cqf);
                     else if (per <= 512)
                         hipLaunchKernelGGL((k_tsqr_local<T, 512>), dim3(nblk), dim3(512), 0, s, P, lda, (int)m, per,
-                                           b.Vloc, b.Tloc, b.Rstack);
+                                           b.Vloc, b.Tloc, b.Rstack, (const int *)b.cqf);
                     else
                         hipLaunchKernelGGL((k_tsqr_local<T, 1024>), dim3(nblk), dim3(1024), 0, s, P, lda, (int)m, per,
-                                           b.Vloc, b.Tloc, b.Rstack);
+                                           b.Vloc, b.Tloc, b.Rstack, (const int *)b.cqf);
                     LAUNCH_OK();
                     if (rows_top <= 256)
                         hipLaunchKernelGGL((k_tsqr_top<T, 256>), dim3(1), dim3(256), 0, s, b.Rstack, nblk, b.Rf, b.Vtop,
-                                           b.Ktop);
+                                           b.Ktop, (const int *)b.cqf);
                     else if (rows_top <= 512)
                         hipLaunchKernelGGL((k_tsqr_top<T, 512>), dim3(1), dim3(512), 0, s, b.Rstack, nblk, b.Rf, b.Vtop,
-                                           b.Ktop);
+                                           b.Ktop, (const int *)b.cqf);
                     else
                         hipLaunchKernelGGL((k_tsqr_top<T, 1024>), dim3(1), dim3(1024), 0, s, b.Rstack, nblk, b.Rf,
-                                           b.Vtop, b.Ktop);
+                                           b.Vtop, b.Ktop, (const int *)b.cqf);
                     LAUNCH_OK();
                 }
                 hipLaunchKernelGGL(k_tsqr_q1<T>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, s, b.Vloc, b.Tloc,
-                                   b.Vtop, b.Ktop, (int)m, per, b.Q1);
+                                   b.Vtop, b.Ktop, (int)m, per, b.Q1, (const int *)b.cqf);
                 LAUNCH_OK();
                 hipLaunchKernelGGL(k_tsqr_recon<T>, dim3(1), dim3(64), 0, s, b.Q1, b.Rf, P, lda, Vout, b.U, b.Tm);
                 LAUNCH_OK();
@@ -2396,26 +2640,26 @@ hipError_t run_topk(hipStream_t st, const float *A, int64_t n, int64_t lda, cons
         const int rows_top = nblk * NB;
         if (per <= 256)
             hipLaunchKernelGGL((k_tsqr_wave<float, 1>), dim3(nblk), dim3(64), 0, st, b.X, (int64_t)NB, m, per,
-                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr, (const int *)nullptr);
         else if (per <= 512)
             hipLaunchKernelGGL((k_tsqr_wave<float, 2>), dim3(nblk), dim3(128), 0, st, b.X, (int64_t)NB, m, per,
-                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr, (const int *)nullptr);
         else
             hipLaunchKernelGGL((k_tsqr_wave<float, 4>), dim3(nblk), dim3(256), 0, st, b.X, (int64_t)NB, m, per,
-                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr);
+                               b.Vloc, b.Tloc, b.Rstack, (float *)nullptr, (const int *)nullptr);
         LAUNCH_OK();
         if (rows_top <= 256)
             hipLaunchKernelGGL((k_tsqr_wave<float, 1>), dim3(1), dim3(64), 0, st, b.Rstack, (int64_t)NB, rows_top,
-                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)nullptr);
         else if (rows_top <= 512)
             hipLaunchKernelGGL((k_tsqr_wave<float, 2>), dim3(1), dim3(128), 0, st, b.Rstack, (int64_t)NB, rows_top,
-                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)nullptr);
         else
             hipLaunchKernelGGL((k_tsqr_wave<float, 4>), dim3(1), dim3(256), 0, st, b.Rstack, (int64_t)NB, rows_top,
-                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop);
+                               rows_top, b.Vtop, b.Ttop, b.Rf, b.Ktop, (const int *)nullptr);
         LAUNCH_OK();
         hipLaunchKernelGGL(k_tsqr_q1<float>, dim3((unsigned)cdiv_h(per, 8), nblk), dim3(256), 0, st, b.Vloc, b.Tloc,
-                           b.Vtop, b.Ktop, m, per, b.Q1);
+                           b.Vtop, b.Ktop, m, per, b.Q1, (const int *)nullptr);
         return hipGetLastError();
     };
     hipError_t e;
