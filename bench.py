@@ -165,139 +165,140 @@ def timed(torch, fn, reps):
     return a.elapsed_time(b) / reps
 
 
-def phase_rows(torch, spec, synth, dev, with_cpu):
+def phase_rows(torch, spec, synth, dev, with_cpu, which=("tiny", "eigentrack", "swiftsvd", "s3")):
     rows = {}
-    # ---- tiny: 64 x 32 f32 -> C (alpha = 1/64) -> 32 eigenvalues -> descriptors
-    X1 = torch.from_numpy(synth.tiny()).to(dev)
-    C1 = torch.empty((32, 32), dtype=torch.float32, device=dev)
-    w1 = torch.empty((1, 32), dtype=torch.float32, device=dev)
-    i1 = torch.empty((1,), dtype=torch.int32, device=dev)
-    d1 = torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    ws1 = torch.empty((spec.descriptors_workspace(32),), dtype=torch.uint8, device=dev)
+    if "tiny" in which:
+        # ---- tiny: 64 x 32 f32 -> C (alpha = 1/64) -> 32 eigenvalues -> descriptors
+        X1 = torch.from_numpy(synth.tiny()).to(dev)
+        C1 = torch.empty((32, 32), dtype=torch.float32, device=dev)
+        w1 = torch.empty((1, 32), dtype=torch.float32, device=dev)
+        i1 = torch.empty((1,), dtype=torch.int32, device=dev)
+        d1 = torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        ws1 = torch.empty((spec.descriptors_workspace(32),), dtype=torch.uint8, device=dev)
 
-    def tiny():
-        spec.cov_accumulate(X1, C1, alpha=1.0 / 64, beta=0.0)
-        spec.eigvalsh_batched_dense(C1, w=w1, info=i1)
-        spec.descriptors(w1, n_samples=64, p_dim=32, k=1, out=d1, ws=ws1, to_host=False)
-    ms = timed(torch, tiny, 200)
-    rows["tiny_64x32"] = {"ms": ms, "eigensolves_per_s": 1e3 / ms, "bound": "launch latency (4 kernels)"}
-    log(f"tiny: {ms * 1e3:.1f} us per pass")
+        def tiny():
+            spec.cov_accumulate(X1, C1, alpha=1.0 / 64, beta=0.0)
+            spec.eigvalsh_batched_dense(C1, w=w1, info=i1)
+            spec.descriptors(w1, n_samples=64, p_dim=32, k=1, out=d1, ws=ws1, to_host=False)
+        ms = timed(torch, tiny, 200)
+        rows["tiny_64x32"] = {"ms": ms, "eigensolves_per_s": 1e3 / ms, "bound": "launch latency (4 kernels)"}
+        log(f"tiny: {ms * 1e3:.1f} us per pass")
+    if "eigentrack" in which:
+        # ---- EigenTrack windows: band Gram -> 123,648 window spectra -> descriptors
+        S, T, d, N = 256, 512, 4096, 30
+        W = T - N + 1
+        H = synth.eigentrack(streams=S, T=T, d=d)
+        Hd = torch.from_numpy(H.view(np.int16)).to(dev).view(torch.bfloat16)
+        band = torch.empty((S, T, N), dtype=torch.float32, device=dev)
+        ww = torch.empty((S * W, N), dtype=torch.float32, device=dev)
+        iw = torch.empty((S * W,), dtype=torch.int32, device=dev)
+        dw = torch.empty((S * W, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        wsw = torch.empty((spec.descriptors_workspace(N),), dtype=torch.uint8, device=dev)
+        part = {}
+        for name, fn in [("gram_band", lambda: spec.gram_window(Hd, N=N, out=band)),
+                         ("eig_windows", lambda: spec.eigvalsh_batched_band(band, n=N, scale=1.0 / N, w=ww, info=iw)),
+                         ("desc_windows", lambda: spec.descriptors(ww, n_samples=N, p_dim=d, k=8, out=dw, ws=wsw,
+                                                                    to_host=False))]:
+            part[name] = timed(torch, fn, 10)
+        # the same spectra and records from the fused entry point (one kernel after the band)
+        fused = timed(torch, lambda: spec.eigvalsh_batched_band_desc(band, n=N, scale=1.0 / N, n_samples=N, p_dim=d,
+                                                                    k=8, w=ww, info=iw, out=dw, ws=wsw,
+                                                                    to_host=False), 10)
+        tot = sum(part.values())
+        rounds = float(iw.float().mean())
+        rows["eigentrack_256x512x4096_N30"] = {
+            "ms": tot, "phases_ms": part, "windows": S * W, "window_spectra_per_s": S * W / (tot / 1e3),
+            "eig_desc_fused_ms": fused, "ms_fused_path": part["gram_band"] + fused,
+            "gram_band": {"bound": "hbm", "achieved_GBs": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / 1e9,
+                          "frac": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / PEAK_HBM},
+            "eig_windows": {"bound": "alu",
+                            "achieved_TFLOPs": S * W * (4.0 / 3.0 * N ** 3 + 2 * rounds * N * 4) / (part["eig_windows"] / 1e3) / 1e12,
+                            "mean_bisection_rounds": rounds},
+            "desc_windows": {"bound": "hbm", "achieved_GBs": S * W * (N * 4 + 144) / (part["desc_windows"] / 1e3) / 1e9}}
+        rows["eigentrack_256x512x4096_N30"]["eig_windows"]["frac"] = \
+            rows["eigentrack_256x512x4096_N30"]["eig_windows"]["achieved_TFLOPs"] * 1e12 / PEAK_F32_VALU
+        log(f"eigentrack: {tot:.3f} ms ({part}); fused eig+desc {fused:.3f} ms")
+        if with_cpu:
+            import oracle
+            t0 = time.perf_counter()
+            for s in range(2):
+                G = oracle.window_gram(H[s], "bf16", N)
+                w, _ = oracle.eigvalsh_small(G)
+                for b in range(w.shape[0]):
+                    oracle.descriptors(w[b], n_samples=N, p_dim=d, k=8)
+            t = (time.perf_counter() - t0) * S / 2
+            rows["eigentrack_256x512x4096_N30"]["cpu_baseline"] = {
+                "value": S * W / t, "unit": "window spectra/s", "cores": os.cpu_count(), "kind": "oracle",
+                "sample": "2 of 256 streams (966 windows: fp64 Gram, Jacobi, descriptors) x 128"}
+        del Hd, band, ww, iw, dw, H
+    if "swiftsvd" in which:
+        # ---- Swift-SVD: 32 chunks -> C 4096^2 -> eigvalsh 4096 f32 -> descriptors
+        Xs = synth.swiftsvd(chunks=32, n=2048, d=4096)
+        Xsd = torch.from_numpy(Xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        Cs = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+        wsb = torch.empty((4096,), dtype=torch.float32, device=dev)
+        wss = torch.empty((spec.eigvalsh_large_workspace(4096, torch.float32),), dtype=torch.uint8, device=dev)
+        infos = torch.zeros((1,), dtype=torch.int32, device=dev)
+        ds = torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        dss = torch.empty((spec.descriptors_workspace(4096),), dtype=torch.uint8, device=dev)
 
-    # ---- EigenTrack windows: band Gram -> 123,648 window spectra -> descriptors
-    S, T, d, N = 256, 512, 4096, 30
-    W = T - N + 1
-    H = synth.eigentrack(streams=S, T=T, d=d)
-    Hd = torch.from_numpy(H.view(np.int16)).to(dev).view(torch.bfloat16)
-    band = torch.empty((S, T, N), dtype=torch.float32, device=dev)
-    ww = torch.empty((S * W, N), dtype=torch.float32, device=dev)
-    iw = torch.empty((S * W,), dtype=torch.int32, device=dev)
-    dw = torch.empty((S * W, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    wsw = torch.empty((spec.descriptors_workspace(N),), dtype=torch.uint8, device=dev)
-    part = {}
-    for name, fn in [("gram_band", lambda: spec.gram_window(Hd, N=N, out=band)),
-                     ("eig_windows", lambda: spec.eigvalsh_batched_band(band, n=N, scale=1.0 / N, w=ww, info=iw)),
-                     ("desc_windows", lambda: spec.descriptors(ww, n_samples=N, p_dim=d, k=8, out=dw, ws=wsw,
-                                                                to_host=False))]:
-        part[name] = timed(torch, fn, 10)
-    # the same spectra and records from the fused entry point (one kernel after the band)
-    fused = timed(torch, lambda: spec.eigvalsh_batched_band_desc(band, n=N, scale=1.0 / N, n_samples=N, p_dim=d,
-                                                                k=8, w=ww, info=iw, out=dw, ws=wsw,
-                                                                to_host=False), 10)
-    tot = sum(part.values())
-    rounds = float(iw.float().mean())
-    rows["eigentrack_256x512x4096_N30"] = {
-        "ms": tot, "phases_ms": part, "windows": S * W, "window_spectra_per_s": S * W / (tot / 1e3),
-        "eig_desc_fused_ms": fused, "ms_fused_path": part["gram_band"] + fused,
-        "gram_band": {"bound": "hbm", "achieved_GBs": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / 1e9,
-                      "frac": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / PEAK_HBM},
-        "eig_windows": {"bound": "alu",
-                        "achieved_TFLOPs": S * W * (4.0 / 3.0 * N ** 3 + 2 * rounds * N * 4) / (part["eig_windows"] / 1e3) / 1e12,
-                        "mean_bisection_rounds": rounds},
-        "desc_windows": {"bound": "hbm", "achieved_GBs": S * W * (N * 4 + 144) / (part["desc_windows"] / 1e3) / 1e9}}
-    rows["eigentrack_256x512x4096_N30"]["eig_windows"]["frac"] = \
-        rows["eigentrack_256x512x4096_N30"]["eig_windows"]["achieved_TFLOPs"] * 1e12 / PEAK_F32_VALU
-    log(f"eigentrack: {tot:.3f} ms ({part}); fused eig+desc {fused:.3f} ms")
-    if with_cpu:
-        import oracle
-        t0 = time.perf_counter()
-        for s in range(2):
-            G = oracle.window_gram(H[s], "bf16", N)
-            w, _ = oracle.eigvalsh_small(G)
-            for b in range(w.shape[0]):
-                oracle.descriptors(w[b], n_samples=N, p_dim=d, k=8)
-        t = (time.perf_counter() - t0) * S / 2
-        rows["eigentrack_256x512x4096_N30"]["cpu_baseline"] = {
-            "value": S * W / t, "unit": "window spectra/s", "cores": os.cpu_count(), "kind": "oracle",
-            "sample": "2 of 256 streams (966 windows: fp64 Gram, Jacobi, descriptors) x 128"}
-    del Hd, band, ww, iw, dw, H
-
-    # ---- Swift-SVD: 32 chunks -> C 4096^2 -> eigvalsh 4096 f32 -> descriptors
-    Xs = synth.swiftsvd(chunks=32, n=2048, d=4096)
-    Xsd = torch.from_numpy(Xs.view(np.int16)).to(dev).view(torch.bfloat16)
-    Cs = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
-    wsb = torch.empty((4096,), dtype=torch.float32, device=dev)
-    wss = torch.empty((spec.eigvalsh_large_workspace(4096, torch.float32),), dtype=torch.uint8, device=dev)
-    infos = torch.zeros((1,), dtype=torch.int32, device=dev)
-    ds = torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    dss = torch.empty((spec.descriptors_workspace(4096),), dtype=torch.uint8, device=dev)
-
-    def sw_syrk():
-        for k in range(32):
-            spec.cov_accumulate(Xsd[k], Cs, alpha=1.0, beta=0.0 if k == 0 else 1.0)
-    part = {"syrk": timed(torch, sw_syrk, 5)}
-    part["eig_large"] = timed(torch, lambda: (sw_syrk(), spec.eigvalsh_large(Cs, w=wsb, ws=wss, info=infos)), 3) \
-        - part["syrk"]
-    part["desc"] = timed(torch, lambda: spec.descriptors(wsb, n_samples=65536, p_dim=4096, k=1,
-                                                         sigma2_mode=spec.SIGMA2_MEAN, out=ds, ws=dss,
-                                                         to_host=False), 10)
-    tot = sum(part.values())
-    f = 65536.0 * 4096 * 4097
-    rows["swiftsvd_32x2048x4096"] = {
-        "ms": tot, "phases_ms": part, "eigensolves_per_s": 1e3 / tot,
-        "syrk": {"bound": "mfma", "achieved_TFLOPs": f / (part["syrk"] / 1e3) / 1e12,
-                 "frac": f / (part["syrk"] / 1e3) / PEAK_BF16_MFMA},
-        "eig_4096_f32_per_s": 1e3 / part["eig_large"]}
-    assert int(infos.cpu()[0]) == 0
-    log(f"swiftsvd: {tot:.3f} ms ({part})")
-    del Xsd, Xs, Cs, wss
-
-    # ---- S3: 32 layers W (4096^2 f32) -> fp64 Gram -> fp64 eigvalsh -> singular descriptors
-    t0 = time.time()
-    Wl = synth.s3_layers_device(32, 4096, device=dev)
-    torch.cuda.synchronize()
-    log(f"s3 layers generated on the GPU in {time.time() - t0:.1f} s")
-    C5 = torch.empty((4096, 4096), dtype=torch.float64, device=dev)
-    w5 = torch.empty((32, 4096), dtype=torch.float64, device=dev)
-    ws5 = torch.empty((spec.eigvalsh_large_workspace(4096, torch.float64),), dtype=torch.uint8, device=dev)
-    i5 = torch.zeros((1,), dtype=torch.int32, device=dev)
-    d5 = torch.empty((32, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    dss5 = torch.empty((spec.descriptors_workspace(4096),), dtype=torch.uint8, device=dev)
-    acc = {"syrk_f64": 0.0, "eig_large_f64": 0.0}
-    spec.cov_accumulate(Wl[0], C5, alpha=1.0, beta=0.0)  # warm-up
-    spec.eigvalsh_large(C5, w=w5[0], ws=ws5, info=i5)
-    torch.cuda.synchronize()
-    for l in range(32):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        spec.cov_accumulate(Wl[l], C5, alpha=1.0, beta=0.0)
-        e[1].record()
-        spec.eigvalsh_large(C5, w=w5[l], ws=ws5, info=i5)
-        e[2].record()
+        def sw_syrk():
+            for k in range(32):
+                spec.cov_accumulate(Xsd[k], Cs, alpha=1.0, beta=0.0 if k == 0 else 1.0)
+        part = {"syrk": timed(torch, sw_syrk, 5)}
+        part["eig_large"] = timed(torch, lambda: (sw_syrk(), spec.eigvalsh_large(Cs, w=wsb, ws=wss, info=infos)), 3) \
+            - part["syrk"]
+        part["desc"] = timed(torch, lambda: spec.descriptors(wsb, n_samples=65536, p_dim=4096, k=1,
+                                                             sigma2_mode=spec.SIGMA2_MEAN, out=ds, ws=dss,
+                                                             to_host=False), 10)
+        tot = sum(part.values())
+        f = 65536.0 * 4096 * 4097
+        rows["swiftsvd_32x2048x4096"] = {
+            "ms": tot, "phases_ms": part, "eigensolves_per_s": 1e3 / tot,
+            "syrk": {"bound": "mfma", "achieved_TFLOPs": f / (part["syrk"] / 1e3) / 1e12,
+                     "frac": f / (part["syrk"] / 1e3) / PEAK_BF16_MFMA},
+            "eig_4096_f32_per_s": 1e3 / part["eig_large"]}
+        assert int(infos.cpu()[0]) == 0
+        log(f"swiftsvd: {tot:.3f} ms ({part})")
+        del Xsd, Xs, Cs, wss
+    if "s3" in which:
+        # ---- S3: 32 layers W (4096^2 f32) -> fp64 Gram -> fp64 eigvalsh -> singular descriptors
+        t0 = time.time()
+        Wl = synth.s3_layers_device(32, 4096, device=dev)
         torch.cuda.synchronize()
-        acc["syrk_f64"] += e[0].elapsed_time(e[1])
-        acc["eig_large_f64"] += e[1].elapsed_time(e[2])
-    acc["desc"] = timed(torch, lambda: spec.descriptors(w5, mode=spec.MODE_SINGULAR, n_samples=4096, p_dim=4096,
-                                                        k=1, out=d5, ws=dss5, to_host=False), 5)
-    tot = sum(acc.values())
-    f = 32 * 4096.0 * 4096 * 4097
-    rows["s3_32x4096x4096"] = {
-        "ms": tot, "phases_ms": acc, "layers": 32, "layer_spectra_per_s": 32e3 / tot,
-        "syrk_f64": {"bound": "mfma", "achieved_TFLOPs": f / (acc["syrk_f64"] / 1e3) / 1e12,
-                     "frac": f / (acc["syrk_f64"] / 1e3) / PEAK_F64_MFMA},
-        "eig_4096_f64_per_s": 32e3 / acc["eig_large_f64"]}
-    assert int(i5.cpu()[0]) == 0
-    log(f"s3: {tot:.1f} ms ({acc})")
-    del Wl, C5, w5, ws5
+        log(f"s3 layers generated on the GPU in {time.time() - t0:.1f} s")
+        C5 = torch.empty((4096, 4096), dtype=torch.float64, device=dev)
+        w5 = torch.empty((32, 4096), dtype=torch.float64, device=dev)
+        ws5 = torch.empty((spec.eigvalsh_large_workspace(4096, torch.float64),), dtype=torch.uint8, device=dev)
+        i5 = torch.zeros((1,), dtype=torch.int32, device=dev)
+        d5 = torch.empty((32, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+        dss5 = torch.empty((spec.descriptors_workspace(4096),), dtype=torch.uint8, device=dev)
+        acc = {"syrk_f64": 0.0, "eig_large_f64": 0.0}
+        spec.cov_accumulate(Wl[0], C5, alpha=1.0, beta=0.0)  # warm-up
+        spec.eigvalsh_large(C5, w=w5[0], ws=ws5, info=i5)
+        torch.cuda.synchronize()
+        for l in range(32):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            spec.cov_accumulate(Wl[l], C5, alpha=1.0, beta=0.0)
+            e[1].record()
+            spec.eigvalsh_large(C5, w=w5[l], ws=ws5, info=i5)
+            e[2].record()
+            torch.cuda.synchronize()
+            acc["syrk_f64"] += e[0].elapsed_time(e[1])
+            acc["eig_large_f64"] += e[1].elapsed_time(e[2])
+        acc["desc"] = timed(torch, lambda: spec.descriptors(w5, mode=spec.MODE_SINGULAR, n_samples=4096, p_dim=4096,
+                                                            k=1, out=d5, ws=dss5, to_host=False), 5)
+        tot = sum(acc.values())
+        f = 32 * 4096.0 * 4096 * 4097
+        rows["s3_32x4096x4096"] = {
+            "ms": tot, "phases_ms": acc, "layers": 32, "layer_spectra_per_s": 32e3 / tot,
+            "syrk_f64": {"bound": "mfma", "achieved_TFLOPs": f / (acc["syrk_f64"] / 1e3) / 1e12,
+                         "frac": f / (acc["syrk_f64"] / 1e3) / PEAK_F64_MFMA},
+            "eig_4096_f64_per_s": 32e3 / acc["eig_large_f64"]}
+        assert int(i5.cpu()[0]) == 0
+        log(f"s3: {tot:.1f} ms ({acc})")
+        del Wl, C5, w5, ws5
     return rows
 
 
@@ -346,6 +347,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the other workloads' phase rows")
     ap.add_argument("--no-postproc", action="store_true", help="skip the rows beyond the hot path")
+    ap.add_argument("--phases", default="tiny,eigentrack,swiftsvd,s3",
+                    help="comma-separated phase rows to run (tiny, eigentrack, swiftsvd, s3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -436,7 +439,7 @@ def main():
 
     phase = None
     if not args.no_phases:
-        phase = phase_rows(torch, spec, synth, dev, not args.no_cpu_baseline)
+        phase = phase_rows(torch, spec, synth, dev, not args.no_cpu_baseline, tuple(args.phases.split(",")))
     post = None
     if not args.no_postproc:
         post = postproc_rows(torch, spec, dev)
