@@ -211,8 +211,10 @@ def phase_rows(torch, spec, synth, dev, with_cpu, which=("tiny", "eigentrack", "
             "eig_desc_fused_ms": fused, "ms_fused_path": part["gram_band"] + fused,
             "gram_band": {"bound": "hbm", "achieved_GBs": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / 1e9,
                           "frac": (H.nbytes + S * T * N * 4) / (part["gram_band"] / 1e3) / PEAK_HBM},
+            # per window: Householder (4/3) N^3, then Sturm counts of 4 flop per step
+            # of N: 64 multisection points and N bisections of `rounds` counts each
             "eig_windows": {"bound": "alu",
-                            "achieved_TFLOPs": S * W * (4.0 / 3.0 * N ** 3 + 2 * rounds * N * 4) / (part["eig_windows"] / 1e3) / 1e12,
+                            "achieved_TFLOPs": S * W * (4.0 / 3.0 * N ** 3 + 4.0 * N * (64 + rounds * N)) / (part["eig_windows"] / 1e3) / 1e12,
                             "mean_bisection_rounds": rounds},
             "desc_windows": {"bound": "hbm", "achieved_GBs": S * W * (N * 4 + 144) / (part["desc_windows"] / 1e3) / 1e9}}
         rows["eigentrack_256x512x4096_N30"]["eig_windows"]["frac"] = \
@@ -357,7 +359,7 @@ def main():
 
     import torch
     import weights_bf16_fp32_amd as spec
-    from weights_bf16_fp32_amd import synth
+    from gen import synth
 
     dev = torch.device("cuda:0")
     n, d = FFN["n"], FFN["d"]

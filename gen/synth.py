@@ -1,9 +1,10 @@
 """Seeded synthetic inputs for the spectral hot path.
 
-This module is the only code shared by the GPU path, the fp64 oracle and the
-benchmark.  It draws random matrices with the shapes and value distributions of
-the workloads the pages describe and holds none of the method's arithmetic
-(no covariance, no eigen-solve, no descriptor).
+This module is the only code the tests of the GPU path, the fp64 oracle's
+stored expected values and the benchmark share.  It draws random matrices with
+the shapes and value distributions of the workloads the pages describe and
+holds none of the method's arithmetic (no covariance, no eigen-solve, no
+descriptor); the library itself never imports it.
 
 Workloads (all seeded from ``numpy.random.SeedSequence(0).spawn(5)[i]`` with
 PCG64, in a fixed draw order):

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from weights_bf16_fp32_amd import synth  # noqa: E402
+from gen import synth  # noqa: E402
 
 DESC_KW = {
     "swiftsvd": dict(n_samples=32 * 2048, p_dim=4096, k=1),

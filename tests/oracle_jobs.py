@@ -12,7 +12,7 @@ def oracle_windows(worker, nworkers):
     Window Grams come from the oracle's band of inner products, which the CPU
     pins tie to the windows' definition."""
     import oracle as orc
-    from weights_bf16_fp32_amd import synth as syn
+    from gen import synth as syn
     S, T, d, N = 256, 512, 4096, 30
     W = T - N + 1
     H = syn.eigentrack(streams=S, T=T, d=d)

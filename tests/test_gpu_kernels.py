@@ -14,7 +14,7 @@ import pytest
 import oracle
 from gpu_util import (DESC_FLOAT_FIELDS, DESC_INT_FIELDS, EPS32, EPS64, dev, dev_bf16, print_case,
                       syrk_bound)
-from weights_bf16_fp32_amd import synth
+from gen import synth
 
 pytestmark = pytest.mark.gpu
 

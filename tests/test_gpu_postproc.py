@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from gpu_util import DESC_FLOAT_FIELDS, dev, dev_bf16, print_case
-from weights_bf16_fp32_amd import synth
+from gen import synth
 
 pytestmark = pytest.mark.gpu
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 from gpu_util import EPS64, dev, print_case
-from weights_bf16_fp32_amd import synth
+from gen import synth
 
 pytestmark = pytest.mark.gpu
 

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from gpu_util import dev, dev_bf16, print_case
-from weights_bf16_fp32_amd import synth
+from gen import synth
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skip(
     reason="spec_eigvalsh_sliding is switched off: its kernel faulted (illegal address) on its first GPU run; "

@@ -15,7 +15,7 @@ import scipy.integrate
 import scipy.linalg
 
 import oracle
-from weights_bf16_fp32_amd import synth
+from gen import synth
 
 
 def _sym(rng, n, scale=1.0):
