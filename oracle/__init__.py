@@ -472,8 +472,9 @@ def robust_stats(w, *, n_samples: int, p_dim: int, sigma2: float = 1.0, sigma2_m
       counted in the end bins) from the MP bin masses q_b -- section 2.3 (KL form
       of the MP deviation); sigma^2 by sigma2_mode (GIVEN, MEDIAN, MEAN = S/p,
       WINSOR = sigma2_winsor) and the companion form for p > n as in mp_w1.
-    Undefined values are NaN (flags: 1 non-finite input, which makes every
-    order statistic, sum and sigma^2 estimate NaN; 4 no finite positive value)."""
+    Undefined values are NaN (flags: 1 non-finite input -- a NaN makes every
+    order statistic, sum and sigma^2 estimate NaN, an infinity enters them as a
+    value; 4 no finite positive value)."""
     raw = np.asarray(w, dtype=np.float64)
     flags = 0 if np.all(np.isfinite(raw)) else 1
     lam = np.sort(np.maximum(raw, 0.0))[::-1]

@@ -422,6 +422,14 @@ def test_robust_stats_by_hand():
     # all zero: no positive value, no MP reference
     r = oracle.robust_stats(np.zeros(6), n_samples=10, p_dim=6, sigma2_mode=oracle.SIGMA2_MEDIAN)
     assert r["flags"] == 4 and math.isnan(r["log_mean"]) and math.isnan(r["kl_mp"])
+    # a NaN value: flag 1, every order statistic and sigma^2 estimate NaN, while
+    # the log statistics keep to the finite positive values (the reading for a case
+    # the pages leave open), here ln 8, ln 2 and ln 1
+    r = oracle.robust_stats([np.nan, 8.0, 2.0, 1.0, 0.0], n_samples=10, p_dim=5)
+    assert r["flags"] & 1 and math.isnan(r["median"]) and math.isnan(r["sigma2_winsor"])
+    assert abs(r["log_mean"] - math.log(16.0) / 3) <= 1e-15
+    lg = np.log([8.0, 2.0, 1.0])
+    assert abs(r["log_std"] - math.sqrt(np.mean((lg - lg.mean()) ** 2))) <= 1e-15
 
 
 def test_mad_normal_consistency():
