@@ -327,7 +327,17 @@ def postproc_rows(torch, spec, dev):
     spec.descriptors(wwin, n_samples=N, p_dim=4096, k=8, out=dwin, ws=wsd, to_host=False)
     sm_out = torch.empty_like(dwin)
     rb_win = torch.empty((S * W, spec.ROBUST_DTYPE.itemsize), dtype=torch.uint8, device=dev)
+    # eigenvalues and the eigenvectors of the 0.8 d largest (the keep set of a
+    # 0.8 keep ratio) on the same covariance; the solver destroys its input, so
+    # each call starts from a copy (a 64 MB device copy, ~20 us)
+    k_e = int(0.8 * d)
+    Ce = torch.empty_like(C)
+    w_e = torch.empty((d,), dtype=torch.float32, device=dev)
+    Z_e = torch.empty((d, k_e), dtype=torch.float32, device=dev)
+    ws_e = torch.empty((spec.eigh_large_workspace(d, torch.float32, k_e),), dtype=torch.uint8, device=dev)
     post = {
+        "eigvalsh_large_4096_f32": lambda: (Ce.copy_(C), spec.eigvalsh_large(Ce, w=w_e, ws=ws)),
+        "eigh_4096_f32_k3276": lambda: (Ce.copy_(C), spec.eigh_large(Ce, k_e, w=w_e, Z=Z_e, ws=ws_e)),
         "desc_smooth_123648": lambda: spec.desc_smooth(dwin, streams=S, W=W, alpha=0.2, out=sm_out, to_host=False),
         "robust_windows_123648": lambda: spec.spectrum_robust(wwin, n_samples=N, p_dim=4096,
                                                               sigma2_mode=spec.SIGMA2_MEDIAN, bins=8, out=rb_win,

@@ -165,6 +165,37 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
                         size_t ws_bytes, int32_t *info);
 
 /* ------------------------------------------------------------------------
+ * Eigenvalues and the eigenvectors of the k largest ("Random matrix theory
+ * spectral methods" page, section 4.1: the projection basis P = [u_1 .. u_k]
+ * of the eigenvectors beyond the MP edge; section 4.2's code keeps
+ * k = int(keep_ratio d) of them).  The solve of spec_eigvalsh_large, keeping
+ * the reduction: each stage-1 panel's Householder vectors (in A's strictly
+ * lower part below the band) and block factor T, and every bulge reflector;
+ * then, in fp64 on the tridiagonal T: its unreduced blocks (a block ends where
+ * |e_i| <= eps ||T||, eps of type t), each block's eigenvalues by multisection,
+ * their ranks among all blocks' values, and inverse iteration on the block (one
+ * eigenvalue per thread; eigenvalues of one block closer than 1e-9 ||T|| are
+ * done in order by one thread and orthogonalised against each other, at
+ * O(c^2 m) for a cluster of c in a block of m rows); then the
+ * back-transformation through the reflectors and the panels.
+ *
+ * A, t, n, lda, w, info: as spec_eigvalsh_large (A destroyed; w all n
+ *       eigenvalues, descending).
+ * Z:    n x k of type t, row-major with row stride ldz >= k: column j is the
+ *       unit eigenvector of w[j] (sign arbitrary).
+ * ws:   device workspace of spec_eigh_large_workspace(n, t, k) bytes (256-byte
+ *       aligned): spec_eigvalsh_large's, then the reflectors (about n^2/64 x 33
+ *       values), the panels' T, and 4 n k doubles of scratch.
+ * Requires 1 <= k <= n <= 8192 (else SPEC_EINVAL, or SPEC_EUNSUPPORTED above
+ * 8192: the back-transformation keeps columns of Z in LDS) and the conditions
+ * of spec_eigvalsh_large.
+ * ---------------------------------------------------------------------- */
+int spec_eigh_large_workspace(int64_t n, int t, int64_t k, size_t *bytes);
+
+int spec_eigh_large(void *stream, void *A, int t, int64_t n, int64_t lda, void *w, void *Z, int64_t ldz, int64_t k,
+                    void *ws, size_t ws_bytes, int32_t *info);
+
+/* ------------------------------------------------------------------------
  * Leading eigenvalues by random projection ("Random matrix theory spectral
  * methods" page, section 3.2: top-k eigenvalues from a random projection in
  * O(k d^2) rather than O(d^3)): the randomised range finder with q steps of

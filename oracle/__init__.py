@@ -21,6 +21,9 @@ What it computes, each function citing the passage it follows:
   by incremental updates as RMT page, section 3.2 suggests) see as input.
 * :func:`eigvalsh_small`  cyclic Jacobi (C, fp64), descending.
 * :func:`eigvalsh_large`  Householder tridiagonalisation + Sturm bisection.
+* :func:`eigh_vectors`    the k largest eigenpairs by LAPACK's symmetric solver
+  (the eigenvectors' plain definition A u = lambda u, |u| = 1, up to sign), the
+  projection basis of RMT page, section 4.1.
 * :func:`mp_quantiles`    quantiles of the Marchenko-Pastur law (RMT page,
   section 2.1) by Gauss-Legendre quadrature of the density.
 * :func:`descriptors`     spectral entropy, effective rank, leading mass,
@@ -225,6 +228,17 @@ def eigvalsh_large(A: np.ndarray) -> np.ndarray:
     w = np.empty(n, dtype=np.float64)
     _load().oracle_eigvalsh_dense(n, _dp(M), _dp(w))
     return w
+
+
+def eigh_vectors(A: np.ndarray, k: int):
+    """(w, U): the k largest eigenvalues of the symmetric A, descending, and
+    their unit eigenvectors as U's columns (fp64, LAPACK's dsyevd as the library
+    step; signs as LAPACK returns them) -- "Random matrix theory spectral
+    methods" page, section 4.1 (P = [u_1 .. u_k], the eigenvectors of the
+    largest eigenvalues)."""
+    A = np.asarray(A, dtype=np.float64)
+    w, U = np.linalg.eigh((A + A.T) / 2)
+    return w[::-1][:k].copy(), U[:, ::-1][:, :k].copy()
 
 
 def count_below_dense(A: np.ndarray, x: float) -> int:

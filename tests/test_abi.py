@@ -31,6 +31,8 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert set(spec.EXPORTS) == declared
+    for name in spec.EXPORTS:  # every entry point is called with declared C types, never ctypes' int default
+        assert getattr(L, name).argtypes is not None, name
 
 
 def test_strerror_and_version(L):
@@ -107,6 +109,24 @@ def test_sliding_validation(L):
     assert f(None, ctypes.byref(band), 2 * 71, 30, 64, None, None) == EINVAL
     short = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 20, 1, 1 / 30)
     assert f(None, ctypes.byref(short), 0, 30, 64, FAKE, None) == EINVAL  # T < n
+
+
+def test_eigh_large_validation(L):
+    b = ctypes.c_size_t(0)
+    f = L.spec_eigh_large_workspace
+    assert f(1000, spec.F32, 0, ctypes.byref(b)) == EINVAL  # k < 1
+    assert f(1000, spec.F32, 1001, ctypes.byref(b)) == EINVAL  # k > n
+    assert f(9000, spec.F32, 10, ctypes.byref(b)) == EUNSUPPORTED  # n past the vector path's limit
+    assert f(1000, spec.BF16, 10, ctypes.byref(b)) == EUNSUPPORTED
+    assert f(1000, spec.F32, 10, ctypes.byref(b)) == 0 and b.value > 0
+    small = ctypes.c_size_t(0)
+    assert L.spec_eigvalsh_large_workspace(1000, spec.F32, ctypes.byref(small)) == 0 and small.value < b.value
+    g = L.spec_eigh_large
+    need = b.value
+    assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE, 5, 10, FAKE, need, None) == EINVAL  # ldz < k
+    assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, None, 10, 10, FAKE, need, None) == EINVAL  # Z NULL
+    assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE, 10, 10, FAKE, need - 1, None) == EWORKSPACE
+    assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE + 2, 10, 10, FAKE, need, None) == EINVAL  # misaligned Z
 
 
 def test_alignment_codes(L):

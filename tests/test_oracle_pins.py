@@ -359,6 +359,26 @@ def test_s3_weyl_bound_reduced():
 
 # ------------------------------------------------------------- P10 inertia counts
 
+def test_eigh_vectors_pins():
+    """The oracle's eigenpairs: A u = lambda u and U^T U = I to rounding, its
+    eigenvalues equal to the Householder + bisection ones, and the 2 x 2
+    rotation in closed form (tan 2 theta = 2b / (a - c))."""
+    rng = np.random.default_rng(17)
+    A = _sym(rng, 120)
+    w, U = oracle.eigh_vectors(A, 120)
+    assert np.max(np.abs(A @ U - U * w)) <= 1e-12 * np.max(np.abs(w))
+    assert np.max(np.abs(U.T @ U - np.eye(120))) <= 1e-13
+    assert np.max(np.abs(w - oracle.eigvalsh_large(A))) <= 1e-12 * np.max(np.abs(w))
+    w5, U5 = oracle.eigh_vectors(A, 5)
+    assert np.array_equal(w5, w[:5]) and np.allclose(np.abs(U5), np.abs(U[:, :5]))
+    a, b, c = 3.0, 1.5, -1.0
+    th = 0.5 * math.atan2(2 * b, a - c)
+    w2, U2 = oracle.eigh_vectors(np.array([[a, b], [b, c]]), 2)
+    u = np.array([math.cos(th), math.sin(th)])
+    assert abs(abs(U2[:, 0] @ u) - 1.0) <= 1e-14
+    assert abs(w2[0] - ((a + c) / 2 + math.hypot((a - c) / 2, b))) <= 1e-14
+
+
 def test_inertia_counts_match_spectrum():
     X = synth.tiny()
     C = oracle.covariance(X, "f32", 1.0 / 64)

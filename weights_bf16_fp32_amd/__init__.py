@@ -98,7 +98,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
            "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen", "spec_eigvalsh_batched_desc",
-           "spec_eigvalsh_sliding"]
+           "spec_eigvalsh_sliding", "spec_eigh_large_workspace", "spec_eigh_large"]
 
 _lib = None
 
@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.spec_eigvalsh_batched.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, vp]
         L.spec_eigvalsh_large_workspace.argtypes = [i64, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.spec_eigvalsh_large.argtypes = [vp, vp, i32, i64, i64, vp, vp, ctypes.c_size_t, vp]
+        L.spec_eigh_large_workspace.argtypes = [i64, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.spec_eigh_large.argtypes = [vp, vp, i32, i64, i64, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
         L.spec_descriptors_workspace.argtypes = [i64, ctypes.POINTER(ctypes.c_size_t)]
         L.spec_descriptors.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp, vp,
                                        ctypes.c_size_t]
@@ -136,6 +138,7 @@ def lib() -> ctypes.CDLL:
         L.spec_tail_pair_screen.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, dbl, vp, i64, vp, i64,
                                              vp]
         L.spec_descriptors_static.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp]
+        L.spec_eigvalsh_sliding.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, i32, vp, vp]
         L.spec_timing_enable.argtypes = [ctypes.c_uint]
         L.spec_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in EXPORTS[2:]:
@@ -250,6 +253,34 @@ def eigvalsh_sliding(band, n: int, scale: float, stride: int = 1, restart: int =
         info = torch.empty((batch,), dtype=torch.int32, device=band.device)
     _check(lib().spec_eigvalsh_sliding(_stream(), ctypes.byref(src), batch, n, int(restart), _dev(w), _dev(info)))
     return w, info
+
+
+def eigh_large_workspace(n: int, dtype, k: int) -> int:
+    torch = _torch()
+    t = F32 if dtype == torch.float32 else F64
+    b = ctypes.c_size_t(0)
+    _check(lib().spec_eigh_large_workspace(n, t, k, ctypes.byref(b)))
+    return b.value
+
+
+def eigh_large(A, k: int, w=None, Z=None, ws=None, info=None):
+    """All eigenvalues (descending) of the symmetric A [n, n] (lower triangle
+    read, A destroyed) and the eigenvectors of the k largest, Z [n, k] (column j
+    for w[j])."""
+    torch = _torch()
+    n = A.shape[0]
+    if A.stride(1) != 1:
+        raise SpecError(-1, "A must be row-major")
+    if w is None:
+        w = torch.empty((n,), dtype=A.dtype, device=A.device)
+    if Z is None:
+        Z = torch.empty((n, k), dtype=A.dtype, device=A.device)
+    if ws is None:
+        ws = torch.empty((eigh_large_workspace(n, A.dtype, k),), dtype=torch.uint8, device=A.device)
+    ip = _dev(info) if info is not None else None
+    _check(lib().spec_eigh_large(_stream(), _dev(A), _dt(A), n, A.stride(0), _dev(w), _dev(Z), Z.stride(0), k,
+                                 _dev(ws), ws.numel(), ip))
+    return w, Z
 
 
 def eigvalsh_large_workspace(n: int, dtype) -> int:

@@ -182,6 +182,31 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
     return from_hip(launch_eig_large((hipStream_t)stream, A, t, n, lda, w, ws, info));
 }
 
+int spec_eigh_large_workspace(int64_t n, int t, int64_t k, size_t *bytes)
+{
+    if (bytes == nullptr || n < 1 || k < 1 || k > n) return SPEC_EINVAL;
+    if (t != SPEC_F32 && t != SPEC_F64) return SPEC_EUNSUPPORTED;
+    if (n > EIGVEC_MAX_N) return SPEC_EUNSUPPORTED;
+    *bytes = eigh_large_workspace_bytes(n, t, k);
+    return SPEC_OK;
+}
+
+int spec_eigh_large(void *stream, void *A, int t, int64_t n, int64_t lda, void *w, void *Z, int64_t ldz, int64_t k,
+                    void *ws, size_t ws_bytes, int32_t *info)
+{
+    size_t need = 0;
+    int st = spec_eigh_large_workspace(n, t, k, &need);
+    if (st != SPEC_OK) return st;
+    if (A == nullptr || w == nullptr || Z == nullptr || lda < n || lda >= ((int64_t)1 << 22) || ldz < k)
+        return SPEC_EINVAL;
+    if (!aligned(A, 16) || !aligned(w, elt_size(t)) || !aligned(Z, elt_size(t)) ||
+        (info != nullptr && !aligned(info, 4)))
+        return SPEC_EINVAL;
+    if (ws == nullptr || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (!aligned(ws, 256)) return SPEC_EINVAL;
+    return from_hip(launch_eigh_large((hipStream_t)stream, A, t, n, lda, w, Z, ldz, k, ws, info));
+}
+
 int spec_descriptors_workspace(int64_t r, size_t *bytes)
 {
     if (bytes == nullptr || r < 1) return SPEC_EINVAL;

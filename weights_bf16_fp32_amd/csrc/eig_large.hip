@@ -1562,6 +1562,21 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
 
 constexpr int BW = 2 * NB;  // band storage: band[c * BW + (r - c)] = A[r][c], 0 <= r - c < BW
 
+// Reflector (s, k) of the bulge chase (sweep s, task k) is kept, when the
+// eigenvectors are wanted, at index refl_index(n, s) + k: sweeps in order, each
+// with its (n - 2 - s) / NB + 1 tasks, RFL entries each (v, then tau).
+constexpr int RFL = NB + 1;
+__host__ __device__ inline int64_t refl_g(int64_t x)  // sum of u / NB over 0 <= u <= x
+{
+    const int64_t q = x / NB, r = x % NB;
+    return NB * q * (q - 1) / 2 + q * (r + 1);
+}
+__host__ __device__ inline int64_t refl_index(int64_t n, int64_t s)
+{
+    const int64_t N = n - 2;
+    return s + refl_g(N) - refl_g(N - s);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_band_copy(const T *__restrict__ A, int64_t lda, int64_t n,
                                                    T *__restrict__ band, int32_t *__restrict__ prog)
@@ -1638,7 +1653,7 @@ __device__ __forceinline__ void band_store(__amdgpu_buffer_rsrc_t rs, T x, int v
 
 template <typename T, int G, int CAPR>
 __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
-                                                        uint64_t spin_ticks)
+                                                        uint64_t spin_ticks, T *__restrict__ refl)
 {
     constexpr int LA = 2;  // the ring holds the lead's chunks up to the next step's (LA - 1 ahead)
     static_assert(CAPR % NB == 0 && (LA + 2 * G - 1) * NB <= CAPR, "ring too small");
@@ -1839,6 +1854,11 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 }
                 wave_sync();
                 if (h == 0) v[ci] = vi;
+                if (refl != nullptr && h == 0) {  // kept for the eigenvectors (rows past the band end: v = 0)
+                    T *rp = refl + (refl_index(n, s) + k) * RFL;
+                    rp[ci] = vi;
+                    if (ci == 0) rp[NB] = tau_k;
+                }
                 if (tau_k != 0) {
                     // column sums, reduced over the 32 rows of each half (lane ci ends
                     // with column h*16 + ci/2): w = O^T v and the part of D v that
@@ -2099,6 +2119,375 @@ __global__ void k_info(const int32_t *__restrict__ err, int32_t *__restrict__ in
     if (threadIdx.x == 0) info[0] = err[0] != 0 ? 1 : 0;
 }
 
+// ---------------------------------------------------------------- eigenvectors
+// The eigenvectors of the k largest eigenvalues, in three steps after stage 3:
+//  * inverse iteration on the tridiagonal T (fp64, one thread per eigenvalue):
+//    three solves of (T - lambda I) z = x by Gaussian elimination with row
+//    interchanges, factored and forward-eliminated in one pass (U's three
+//    diagonals and the eliminated right-hand side are kept per row), then back
+//    substitution; lambda from fp64 bisection.  Eigenvalues closer than
+//    1e-9 ||T|| form a cluster whose vectors one thread computes in order,
+//    each orthogonalised against the cluster's earlier ones after every solve
+//    (inverse iteration alone leaves them parallel).
+//  * the bulge chase's reflectors in reverse order: T = H_M ... H_1 B H_1 ... H_M,
+//    so an eigenvector of the band B is H_1 ... H_M y.  A workgroup keeps two
+//    columns of Z in LDS and applies every reflector to both (half-wave dot
+//    products).
+//  * the stage-1 panels in reverse order: A = Q_1 ... Q_P B Q_P^T ... Q_1^T,
+//    Q_p = I - V_p T_p V_p^T, so x = Q_1 (... (Q_P y)): per panel W = V^T Z,
+//    W <- T W, Z -= V W on 32-column blocks of Z.
+// V_p is kept in the strictly lower part of A's panel (below the band, free
+// once the panel is factored), T_p in the workspace.
+
+// keep panel p: V (m x NB, unit lower, contiguous) into the strictly lower part
+// of the panel block P of A, T into Tk
+template <typename T>
+__global__ __launch_bounds__(256) void k_keep_panel(const T *__restrict__ V, const T *__restrict__ Tm, int m,
+                                                    T *__restrict__ P, int64_t lda, T *__restrict__ Tk)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blockIdx.x == 0)
+        for (int q = threadIdx.x; q < NB * NB; q += 256) Tk[q] = Tm[q];
+    const int64_t i = idx / NB;
+    const int j = (int)(idx % NB);
+    if (i < m && i > j) P[i * lda + j] = V[i * NB + j];
+}
+
+// a value in [-1, 1) from (i, c): the start vector of inverse iteration
+__device__ __forceinline__ double start_entry(int64_t i, int64_t c)
+{
+    uint64_t x = (uint64_t)i * 0x9E3779B97F4A7C15ull ^ ((uint64_t)c + 0x632BE59BD9B4E019ull) * 0xBF58476D1CE4E5B9ull;
+    x ^= x >> 31;
+    x *= 0x94D049BB133111EBull;
+    x ^= x >> 29;
+    return (double)(x >> 11) * (2.0 / 9007199254740992.0) - 1.0;
+}
+
+// Unreduced blocks of the tridiagonal: row i lies in rows blo[i] .. bhi[i] - 1,
+// a block ending after row i when |e_i| <= thr ||T|| (zeroing such an e_i moves
+// no eigenvalue by more than thr ||T||, the size of the rounding the reduction
+// leaves in T).  Vectors of different blocks are orthogonal by their supports.
+// One workgroup, n <= VS_ROWS; prefix max / suffix min scans in LDS.
+constexpr int VS_ROWS = 8192;
+static_assert(VS_ROWS >= EIGVEC_MAX_N, "one workgroup splits every row");
+template <typename T>
+__global__ __launch_bounds__(1024) void k_vsplit(const T *__restrict__ band, int64_t n,
+                                                 const double *__restrict__ bounds, double thr,
+                                                 int32_t *__restrict__ blo, int32_t *__restrict__ bhi)
+{
+    constexpr int R = VS_ROWS / 1024;
+    __shared__ int32_t sa[VS_ROWS], sb[VS_ROWS];
+    const int tid = threadIdx.x;
+    const double cut = thr * fmax(fabs(bounds[0]), fabs(bounds[1]));
+    auto brk = [&](int64_t i) {  // a block starts at row i
+        return i == 0 || fabs((double)band[i * BW + 1]) <= cut;  // e_{i-1} = A[i][i-1]
+    };
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid * R + r;
+        sa[i] = i < n && brk(i) ? i : 0;
+        sb[i] = i + 1 < n ? (brk(i + 1) ? i + 1 : (int32_t)n) : (int32_t)n;
+    }
+    __syncthreads();
+    for (int o = 1; o < VS_ROWS; o <<= 1) {
+        int32_t ta[R], tb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid * R + r;
+            ta[r] = i >= o ? max(sa[i], sa[i - o]) : sa[i];
+            tb[r] = i + o < VS_ROWS ? min(sb[i], sb[i + o]) : sb[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            sa[tid * R + r] = ta[r];
+            sb[tid * R + r] = tb[r];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid * R + r;
+        if (i < n) {
+            blo[i] = sa[i];
+            bhi[i] = sb[i];
+        }
+    }
+}
+
+// mu[i] = the (i - blo[i])-th largest eigenvalue of row i's block, by the same
+// 16-point multisection as the whole-matrix bisection, to 2 eps ||T||
+__global__ __launch_bounds__(64) void k_vbisect(const double *__restrict__ dd, const double *__restrict__ ee2,
+                                                int64_t n, const double *__restrict__ bounds,
+                                                const int32_t *__restrict__ blo, const int32_t *__restrict__ bhi,
+                                                double *__restrict__ mu)
+{
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, j = lane & 15;
+    const int64_t i = blockIdx.x * 4 + g;
+    const bool live = i < n;
+    const int64_t lo = live ? blo[i] : 0, hi = live ? bhi[i] : 1;
+    const int64_t target = hi - 1 - (live ? i : 0);  // ascending index within the block
+    double a = bounds[0], b = bounds[1];
+    const double pivmin = bounds[2];
+    const double tol = 2.0 * DBL_EPSILON * fmax(fabs(a), fabs(b)) + 4.0 * pivmin;
+    for (int it = 0; it < 40; ++it) {
+        const double width = b - a;
+        const bool done = width <= tol;
+        const double x = a + width * (double)(j + 1) / 17.0;
+        const int cnt = (live && !done) ? sturm_below(dd + lo, ee2 + lo, hi - lo, x, pivmin) : 0;
+        const bool le = cnt <= target;
+        double na = le ? x : -INFINITY;
+        double nb = le ? INFINITY : x;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+            na = fmax(na, __shfl_xor(na, o, 16));
+            nb = fmin(nb, __shfl_xor(nb, o, 16));
+        }
+        if (!done) {
+            if (na > a) a = na;
+            if (nb < b) b = nb;
+        }
+        if (__all(done || !live)) break;
+    }
+    if (live && j == 0) mu[i] = 0.5 * (a + b);
+}
+
+// rank[i] = position of mu[i] in the descending order of all blocks' values
+// (ties by row), so that column rank[i] of Z belongs to w[rank[i]]
+__global__ __launch_bounds__(256) void k_vrank(const double *__restrict__ mu, int64_t n, int32_t *__restrict__ rank)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const double x = mu[i];
+    int64_t r = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        const double y = mu[j];
+        r += (y > x) || (y == x && j < i);
+    }
+    rank[i] = (int32_t)r;
+}
+
+// Z <- 0 on [n][k] (the rows outside a vector's block stay zero)
+template <typename T>
+__global__ __launch_bounds__(256) void k_zfill(T *__restrict__ Z, int64_t n, int64_t k, int64_t ldz)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx < n * k) Z[(idx / k) * ldz + idx % k] = (T)0;
+}
+
+// Inverse iteration, one thread per row i of the tridiagonal whose eigenvalue
+// mu[i] ranks below k: three steps of (T_b - mu I) y <- y on row i's block T_b,
+// each a partial-pivoting LU solve (a factor and the right-hand side's
+// elimination in one pass, then back substitution), the iterate scaled by its
+// largest entry and normalised.  Eigenvalues of one block closer than
+// 1e-9 ||T|| form a cluster, whose first row computes all its vectors in turn,
+// each orthogonalised against the earlier ones (modified Gram-Schmidt) after
+// every step.  The iteration runs on T / ||T||; pivots are floored at eps.
+// Scratch: 4 arrays of [n][k] doubles, entry q of the thread's slot (its rank)
+// at q * k + slot.
+template <typename T>
+__global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_t n,
+                                              const double *__restrict__ bounds, const int32_t *__restrict__ blo,
+                                              const int32_t *__restrict__ bhi, const double *__restrict__ mu,
+                                              const int32_t *__restrict__ rank, int64_t k, double *__restrict__ scr,
+                                              T *__restrict__ Z, int64_t ldz)
+{
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t slot = rank[i];
+    if (slot >= k) return;
+    const int64_t lo = blo[i], hi = bhi[i], m = hi - lo;
+    const double norm = fmax(fabs(bounds[0]), fabs(bounds[1]));
+    const double ortol = 1e-9 * norm;
+    if (i > lo && mu[i - 1] - mu[i] < ortol) return;  // inside a cluster: its first row does it
+    const double si = norm > 0.0 ? 1.0 / norm : 1.0;
+    const double tiny = DBL_EPSILON;
+    const int64_t nk = n * k;
+    double *u0 = scr + slot, *u1 = scr + nk + slot, *u2 = scr + 2 * nk + slot, *y = scr + 3 * nk + slot;
+    auto D = [&](int64_t q) { return (double)band[(lo + q) * BW] * si; };
+    auto E = [&](int64_t q) { return q + 1 < m ? (double)band[(lo + q + 1) * BW + 1] * si : 0.0; };
+    auto floor_piv = [&](double x) { return fabs(x) < tiny ? (x < 0.0 ? -tiny : tiny) : x; };
+    for (int64_t c = i;; ++c) {
+        const int64_t rc = rank[c];
+        const double sh = mu[c] * si;
+        for (int64_t q = 0; q < m; ++q) y[q * k] = start_entry(q, rc);
+        for (int it = 0; it < 3; ++it) {
+            // rows (cd, cu, 0 | cr) and (dl, nd, ndu | nr): the larger of cd, dl pivots
+            double cd = D(0) - sh, cu = E(0), cr = y[0];
+#pragma unroll 4
+            for (int64_t q = 0; q + 1 < m; ++q) {
+                const double dl = E(q), nd = D(q + 1) - sh, ndu = E(q + 1), nr = y[(q + 1) * k];
+                const bool sw = !(fabs(cd) >= fabs(dl));
+                const double p0 = sw ? dl : floor_piv(cd);
+                const double p1 = sw ? nd : cu, p2 = sw ? ndu : 0.0, pr = sw ? nr : cr;
+                const double f = (sw ? cd : dl) / p0;
+                u0[q * k] = p0;
+                u1[q * k] = p1;
+                u2[q * k] = p2;
+                y[q * k] = pr;
+                cd = (sw ? cu : nd) - f * p1;
+                cu = (sw ? 0.0 : ndu) - f * p2;
+                cr = (sw ? cr : nr) - f * pr;
+            }
+            u0[(m - 1) * k] = floor_piv(cd);
+            y[(m - 1) * k] = cr;
+            double z1 = 0.0, z2 = 0.0, amax = 0.0;
+            bool fin = true;
+#pragma unroll 4
+            for (int64_t q = m - 1; q >= 0; --q) {
+                const double zq = (y[q * k] - u1[q * k] * z1 - u2[q * k] * z2) / u0[q * k];
+                y[q * k] = zq;
+                z2 = z1;
+                z1 = zq;
+                fin = fin && fabs(zq) <= DBL_MAX;
+                amax = fmax(amax, fabs(zq));
+            }
+            if (!fin || !(amax > 0.0)) {  // overflow or a zero solve: start again from another vector
+                for (int64_t q = 0; q < m; ++q) y[q * k] = start_entry(q, rc + 7919 * (it + 1));
+                amax = 1.0;
+            }
+            const double ia = 1.0 / amax;
+            for (int64_t q = 0; q < m; ++q) y[q * k] *= ia;
+            for (int64_t p = i; p < c; ++p) {  // the cluster's earlier vectors, already in Z
+                const T *zp = Z + lo * ldz + rank[p];
+                double dp = 0.0;
+                for (int64_t q = 0; q < m; ++q) dp += y[q * k] * (double)zp[q * ldz];
+                for (int64_t q = 0; q < m; ++q) y[q * k] -= dp * (double)zp[q * ldz];
+            }
+            double ss = 0.0;
+            for (int64_t q = 0; q < m; ++q) ss += y[q * k] * y[q * k];
+            const double sc = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+            for (int64_t q = 0; q < m; ++q) y[q * k] *= sc;
+        }
+        for (int64_t q = 0; q < m; ++q) Z[(lo + q) * ldz + rc] = (T)y[q * k];
+        if (!(c + 1 < hi && mu[c] - mu[c + 1] < ortol && rank[c + 1] < k)) break;
+    }
+}
+
+// Z <- H_1 ... H_M Z for the kept bulge reflectors, last first; cpb (1 or 2)
+// columns per workgroup (64 lanes: row q = lane % 32 of a reflector's rows,
+// column lane / 32), the columns in LDS (cpb n entries).  Reflectors arrive in
+// chunks of BT_CH, each lane loading its own entry of each into registers.
+constexpr int BT_CH = 32;
+template <typename T>
+__global__ __launch_bounds__(64) void k_bt_bulge(const T *__restrict__ refl, int64_t n, int64_t k, int cpb,
+                                                 T *__restrict__ Z, int64_t ldz)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char zsh_raw[];
+    const int lane = threadIdx.x, q = lane & 31, col = lane >> 5;
+    const bool act = col < cpb;
+    T *zs = (T *)zsh_raw + (act ? col : 0) * n;  // lanes of an unused half shadow column 0 and store nothing
+    const int64_t c = (int64_t)blockIdx.x * cpb + col;
+    const bool live = act && c < k;
+    for (int64_t i = q; i < n; i += 32)
+        if (act) zs[i] = live ? Z[i * ldz + c] : (T)0;
+    wave_sync();
+    const int64_t nsw = n - 2;
+    const int64_t total = refl_index(n, nsw);
+    int64_t s = nsw - 1, kk = 0;  // the last reflector: the last sweep has one task
+    for (int64_t top = total; top > 0; top -= BT_CH) {
+        T vr[BT_CH], tr[BT_CH];
+#pragma unroll
+        for (int u = 0; u < BT_CH; ++u) {
+            const int64_t idx = top - 1 - u;
+            const bool ok = idx >= 0;
+            vr[u] = ok ? refl[idx * RFL + q] : (T)0;
+            tr[u] = ok ? refl[idx * RFL + NB] : (T)0;
+        }
+#pragma unroll
+        for (int u = 0; u < BT_CH; ++u) {
+            // uniform: every lane holds the same tau (0 past the first reflector)
+            if (tr[u] != (T)0) {
+                const int64_t r = s + 1 + kk * NB + q;
+                const T zq = r < n ? zs[r] : (T)0;
+                const T dot = half_sum(vr[u] * zq);
+                if (act && r < n) zs[r] = zq - tr[u] * dot * vr[u];
+                wave_sync();
+            }
+            if (--kk < 0) {  // the previous sweep's last task
+                --s;
+                kk = (nsw - s) / NB;
+            }
+        }
+    }
+    for (int64_t i = q; i < n; i += 32)
+        if (live) Z[i * ldz + c] = zs[i];
+}
+
+// Z[r0:, :] <- (I - V T V^T) Z[r0:, :] for the kept panel (V in A's panel
+// block P, m rows, unit lower with the strict part stored; T in Tk, as the
+// reduction applied it), on one 32-column block of Z per workgroup:
+// W = V^T Z, Y = T W, Z -= V Y, V and Z through LDS in row chunks
+template <typename T>
+__global__ __launch_bounds__(256) void k_bt_panel(const T *__restrict__ P, int64_t lda, int m,
+                                                  const T *__restrict__ Tk, int64_t k, T *__restrict__ Zr,
+                                                  int64_t ldz)
+{
+    constexpr int CR = 64;  // rows per LDS chunk
+    constexpr int L = NB + 1;
+    __shared__ T Vs[CR * L], Zs[CR * L], Ws[NB * L], Ts[NB * L];
+    const int tid = threadIdx.x;
+    const int64_t cb = (int64_t)blockIdx.x * NB;
+    auto vload = [&](int64_t i, int a) -> T {  // V[i][a]
+        return i == a ? (T)1 : (i > a ? P[i * lda + a] : (T)0);
+    };
+    for (int p = tid; p < NB * NB; p += 256) Ts[(p / NB) * L + p % NB] = Tk[p];
+    // W = V^T Z: thread (a, b4) accumulates W[a][4 b4 .. 4 b4 + 3]
+    const int a = tid / 8, b4 = (tid % 8) * 4;
+    T acc[4] = {};
+    for (int64_t r0 = 0; r0 < m; r0 += CR) {
+        __syncthreads();
+        for (int p = tid; p < CR * NB; p += 256) {
+            const int rr = p / NB, cc = p % NB;
+            const int64_t i = r0 + rr;
+            Vs[rr * L + cc] = i < m ? vload(i, cc) : (T)0;
+            Zs[rr * L + cc] = i < m && cb + cc < k ? Zr[i * ldz + cb + cc] : (T)0;
+        }
+        __syncthreads();
+        for (int rr = 0; rr < CR; ++rr) {
+            const T va = Vs[rr * L + a];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] += va * Zs[rr * L + b4 + u];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Ws[a * L + b4 + u] = acc[u];
+    __syncthreads();
+    // Y = T W
+    T yv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        T x = 0;
+        for (int l = 0; l < NB; ++l) x += Ts[a * L + l] * Ws[l * L + b4 + u];
+        yv[u] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Ws[a * L + b4 + u] = yv[u];
+    // Z -= V Y, thread (row rr, column cc) of each chunk
+    for (int64_t r0 = 0; r0 < m; r0 += CR) {
+        __syncthreads();
+        for (int p = tid; p < CR * NB; p += 256) {
+            const int rr = p / NB, cc = p % NB;
+            const int64_t i = r0 + rr;
+            Vs[rr * L + cc] = i < m ? vload(i, cc) : (T)0;
+        }
+        __syncthreads();
+        for (int p = tid; p < CR * NB; p += 256) {
+            const int rr = p / NB, cc = p % NB;
+            const int64_t i = r0 + rr;
+            if (i < m && cb + cc < k) {
+                T x = Zr[i * ldz + cb + cc];
+#pragma unroll 8
+                for (int aa = 0; aa < NB; ++aa) x -= Vs[rr * L + aa] * Ws[aa * L + cc];
+                Zr[i * ldz + cb + cc] = x;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 inline int64_t cdiv_h(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -2213,8 +2602,21 @@ hipError_t aux_for(hipStream_t st, Aux **out)
         if (e_ != hipSuccess) return e_;                \
     } while (0)
 
+// What the eigenvector path adds to a solve: the k columns of Z (n x k,
+// row-major, column j for the j-th largest eigenvalue) and the workspace it
+// keeps the reduction in.
 template <typename T>
-hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int32_t *info)
+struct VecReq {
+    T *Z;
+    int64_t ldz, k;
+    T *refl, *keepT;          // bulge reflectors (refl_index layout), panel T factors
+    int32_t *blo, *bhi, *rk;  // each row's block of the tridiagonal, the rank of its eigenvalue
+    double *mu, *scr;         // per-block eigenvalues (fp64), inverse-iteration scratch
+};
+
+template <typename T>
+hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int32_t *info,
+               const VecReq<T> *vec = nullptr)
 {
     Bufs<T> b;
     layout<T>(n, (char *)ws, b);
@@ -2325,6 +2727,11 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
             hipLaunchKernelGGL(k_vw<T>, dim3((unsigned)cdiv_h(m, VW_R)), dim3(VW_T), 0, s, b.Q1, b.U, b.Tm, (int)m,
                                m <= DIRECT_ROWS ? (int)m : NB, Vout, b.W);
             LAUNCH_OK();
+            if (vec != nullptr) {  // the panel's V below the band and its T, for the eigenvectors
+                hipLaunchKernelGGL(k_keep_panel<T>, dim3((unsigned)cdiv_h(m * NB, 256)), dim3(256), 0, s, Vout, b.Tm,
+                                   (int)m, P, lda, vec->keepT + (c0 / NB) * NB * NB);
+                LAUNCH_OK();
+            }
         return hipSuccess;
     };
     if (n - NB >= 2) {
@@ -2408,7 +2815,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         {
             KTimer kt(st, SPEC_KT_BULGE);
             hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * (G + 2)), 0, st, b.band, n,
-                               b.prog, spin_ticks);
+                               b.prog, spin_ticks, vec != nullptr ? vec->refl : (T *)nullptr);
         }
         LAUNCH_OK();
     }
@@ -2426,6 +2833,38 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
     }
     }
     LAUNCH_OK();
+    if (vec != nullptr) {
+        // ---- eigenvectors: the tridiagonal's blocks and their fp64 eigenvalues,
+        // inverse iteration, then back through the bulge reflectors and the panels
+        const double thr = sizeof(T) == 4 ? (double)FLT_EPSILON : DBL_EPSILON;
+        hipLaunchKernelGGL(k_vsplit<T>, dim3(1), dim3(1024), 0, st, b.band, n, b.bounds, thr, vec->blo, vec->bhi);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_vbisect, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds,
+                           vec->blo, vec->bhi, vec->mu);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_vrank, dim3((unsigned)cdiv_h(n, 256)), dim3(256), 0, st, vec->mu, n, vec->rk);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_zfill<T>, dim3((unsigned)cdiv_h(n * vec->k, 256)), dim3(256), 0, st, vec->Z, n, vec->k,
+                           vec->ldz);
+        LAUNCH_OK();
+        hipLaunchKernelGGL(k_invit<T>, dim3((unsigned)cdiv_h(n, 64)), dim3(64), 0, st, b.band, n, b.bounds, vec->blo,
+                           vec->bhi, vec->mu, vec->rk, vec->k, vec->scr, vec->Z, vec->ldz);
+        LAUNCH_OK();
+        if (n >= 3) {
+            const int cpb = 2 * n * (int64_t)sizeof(T) <= 65536 ? 2 : 1;
+            hipLaunchKernelGGL(k_bt_bulge<T>, dim3((unsigned)cdiv_h(vec->k, cpb)), dim3(64),
+                               (unsigned)(cpb * n * sizeof(T)), st, vec->refl, n, vec->k, cpb, vec->Z, vec->ldz);
+            LAUNCH_OK();
+        }
+        for (int64_t c0 = std::max<int64_t>(0, n - NB - 2) / NB * NB; c0 >= 0; c0 -= NB) {
+            const int64_t r0 = c0 + NB, m = n - r0;
+            if (m < 2) continue;
+            hipLaunchKernelGGL(k_bt_panel<T>, dim3((unsigned)cdiv_h(vec->k, NB)), dim3(256), 0, st,
+                               A + r0 * lda + c0, lda, (int)m, vec->keepT + (c0 / NB) * NB * NB, vec->k,
+                               vec->Z + r0 * vec->ldz, vec->ldz);
+            LAUNCH_OK();
+        }
+    }
     if (info != nullptr) {
         hipLaunchKernelGGL(k_info, dim3(1), dim3(64), 0, st, b.prog + n, info);
         LAUNCH_OK();
@@ -2700,6 +3139,61 @@ size_t eig_large_workspace_bytes(int64_t n, int t)
     }
     Bufs<double> b;
     return layout<double>(n, nullptr, b);
+}
+
+namespace {
+
+// the eigenvector path's workspace after the solver's own: reflectors, panel
+// T factors, the tridiagonal's blocks, eigenvalues and ranks, inverse-iteration
+// scratch (4 n k doubles)
+template <typename T>
+size_t vec_layout(int64_t n, int64_t k, char *base, VecReq<T> &v)
+{
+    Ws ws;
+    ws.base = base;
+    const int64_t nrefl = n >= 3 ? refl_index(n, n - 2) : 0;
+    v.refl = ws.take<T>((size_t)std::max<int64_t>(1, nrefl) * RFL);
+    v.keepT = ws.take<T>((size_t)(n / NB + 1) * NB * NB);
+    v.blo = ws.take<int32_t>((size_t)n);
+    v.bhi = ws.take<int32_t>((size_t)n);
+    v.rk = ws.take<int32_t>((size_t)n);
+    v.mu = ws.take<double>((size_t)n);
+    v.scr = ws.take<double>((size_t)4 * n * k);
+    return ws.off;
+}
+
+}  // namespace
+
+size_t eigh_large_workspace_bytes(int64_t n, int t, int64_t k)
+{
+    const size_t base = (eig_large_workspace_bytes(n, t) + 255) / 256 * 256;
+    if (t == SPEC_F32) {
+        VecReq<float> v;
+        return base + vec_layout<float>(n, k, nullptr, v);
+    }
+    VecReq<double> v;
+    return base + vec_layout<double>(n, k, nullptr, v);
+}
+
+hipError_t launch_eigh_large(hipStream_t stream, void *A, int t, int64_t n, int64_t lda, void *w, void *Z,
+                             int64_t ldz, int64_t k, void *ws, int32_t *info)
+{
+    const size_t base = (eig_large_workspace_bytes(n, t) + 255) / 256 * 256;
+    char *extra = (char *)ws + base;
+    if (t == SPEC_F32) {
+        VecReq<float> v;
+        vec_layout<float>(n, k, extra, v);
+        v.Z = (float *)Z;
+        v.ldz = ldz;
+        v.k = k;
+        return run<float>(stream, (float *)A, n, lda, (float *)w, ws, info, &v);
+    }
+    VecReq<double> v;
+    vec_layout<double>(n, k, extra, v);
+    v.Z = (double *)Z;
+    v.ldz = ldz;
+    v.k = k;
+    return run<double>(stream, (double *)A, n, lda, (double *)w, ws, info, &v);
 }
 
 hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64_t lda, void *w, void *ws,

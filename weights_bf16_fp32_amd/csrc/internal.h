@@ -25,6 +25,15 @@ hipError_t launch_eigvalsh_sliding(hipStream_t stream, const spec_batch_src *src
 
 size_t eig_large_workspace_bytes(int64_t n, int t);
 
+// the eigenvector path: eig_large's workspace followed by its own
+size_t eigh_large_workspace_bytes(int64_t n, int t, int64_t k);
+
+hipError_t launch_eigh_large(hipStream_t stream, void *A, int t, int64_t n, int64_t lda, void *w, void *Z,
+                             int64_t ldz, int64_t k, void *ws, int32_t *info);
+
+// largest n of the eigenvector path (its back-transformation keeps columns in LDS)
+constexpr int64_t EIGVEC_MAX_N = 8192;
+
 hipError_t launch_eig_large(hipStream_t stream, void *A, int t, int64_t n, int64_t lda, void *w, void *ws,
                             int32_t *info);
 
