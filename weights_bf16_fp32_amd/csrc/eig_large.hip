@@ -2365,54 +2365,142 @@ __global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_
     }
 }
 
-// Z <- H_1 ... H_M Z for the kept bulge reflectors, last first; cpb (1 or 2)
-// columns per workgroup (64 lanes: row q = lane % 32 of a reflector's rows,
-// column lane / 32), the columns in LDS (cpb n entries).  Reflectors arrive in
-// chunks of BT_CH, each lane loading its own entry of each into registers.
-constexpr int BT_CH = 32;
+// Z <- H_1 ... H_M Z for the kept bulge reflectors.  Reflector (s, k) acts on
+// rows s + 1 + 32 k .. s + 32 + 32 k; two reflectors that share a row must be
+// applied last-created first, and (s, k) shares rows only with (s - d, k + j)
+// for 32 (j - 1) < d < 32 (j + 1), j >= 0.  So the order "k ascending, s
+// descending within k" is valid: pass k slides a 32-row window up one row per
+// reflector.  Lane = column of Z (64 per workgroup), the window in registers
+// (row r in slot r mod 32, bodies of 32 steps aligned so the slots are
+// compile-time), no cross-lane work.  The WV waves of a workgroup run passes
+// k = w, w + WV, ... as a pipeline: pass k takes each row after pass k - 1 has
+// released it (a row leaves a window at its bottom); rows move through Z
+// itself (coherent loads and stores, as in the bulge chase), progress through
+// one LDS counter per wave (pass k at PS k + (BASE - lowest step done)).  A
+// pass runs virtual steps above its first reflector and below s = 0 (no
+// reflector) so that its rows enter and leave at the same pace.  Waits are
+// bounded: on time-out the error flag is set and the workgroup leaves.
+constexpr int BTB_PS = 16384;  // progress stride per pass (> steps per pass)
 template <typename T>
-__global__ __launch_bounds__(64) void k_bt_bulge(const T *__restrict__ refl, int64_t n, int64_t k, int cpb,
-                                                 T *__restrict__ Z, int64_t ldz)
+struct BtBulgeCfg {
+    static constexpr int WV = sizeof(T) == 4 ? 8 : 4;  // passes in flight per workgroup
+};
+template <typename T>
+__global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__restrict__ refl, int64_t n,
+                                                                     int64_t k, T *__restrict__ Z, int64_t ldz,
+                                                                     uint64_t spin_ticks, int32_t *__restrict__ err)
 {
-    extern __shared__ __attribute__((aligned(16))) unsigned char zsh_raw[];
-    const int lane = threadIdx.x, q = lane & 31, col = lane >> 5;
-    const bool act = col < cpb;
-    T *zs = (T *)zsh_raw + (act ? col : 0) * n;  // lanes of an unused half shadow column 0 and store nothing
-    const int64_t c = (int64_t)blockIdx.x * cpb + col;
-    const bool live = act && c < k;
-    for (int64_t i = q; i < n; i += 32)
-        if (act) zs[i] = live ? Z[i * ldz + c] : (T)0;
-    wave_sync();
-    const int64_t nsw = n - 2;
-    const int64_t total = refl_index(n, nsw);
-    int64_t s = nsw - 1, kk = 0;  // the last reflector: the last sweep has one task
-    for (int64_t top = total; top > 0; top -= BT_CH) {
-        T vr[BT_CH], tr[BT_CH];
+    constexpr int WV = BtBulgeCfg<T>::WV;
+    constexpr int PER = (NB * RFL + 63) / 64;  // reflector entries per lane per body
+    __shared__ int32_t prog[WV];
+    __shared__ int32_t quit;
+    __shared__ T rs[WV][NB * RFL];  // the body's 32 reflectors, per wave
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+    const bool live = col < k;
+    T *zc = Z + (live ? col : 0);
+    const int nsw = (int)n - 2;
+    const int KK = nsw / NB;           // passes 0 .. KK
+    const int BASE = (int)n + 2 * NB;  // BASE - s > 0 for every step s >= -32
+    if (threadIdx.x < WV) prog[threadIdx.x] = (int32_t)threadIdx.x * BTB_PS;
+    if (threadIdx.x == 0) quit = 0;
+    __syncthreads();
+    T *rw = rs[wv];
+    // the 32 reflectors of body sb (steps s = sb - u) of pass kk, entry e of the
+    // body at rw[e]: lane-strided loads (tau = 0 for steps without a reflector)
+    auto fetch = [&](int kk, int sb, int shi, T (&pre)[PER]) {
 #pragma unroll
-        for (int u = 0; u < BT_CH; ++u) {
-            const int64_t idx = top - 1 - u;
-            const bool ok = idx >= 0;
-            vr[u] = ok ? refl[idx * RFL + q] : (T)0;
-            tr[u] = ok ? refl[idx * RFL + NB] : (T)0;
+        for (int j = 0; j < PER; ++j) {
+            const int e = lane + 64 * j;
+            const int u = e / RFL, q = e % RFL;
+            const int sr = sb - u;
+            T x = (T)0;
+            if (e < NB * RFL && sr >= 0 && sr <= shi) x = refl[(refl_index(n, sr) + kk) * RFL + q];
+            pre[j] = x;
         }
+    };
+    auto park = [&](const T (&pre)[PER]) {
 #pragma unroll
-        for (int u = 0; u < BT_CH; ++u) {
-            // uniform: every lane holds the same tau (0 past the first reflector)
-            if (tr[u] != (T)0) {
-                const int64_t r = s + 1 + kk * NB + q;
-                const T zq = r < n ? zs[r] : (T)0;
-                const T dot = half_sum(vr[u] * zq);
-                if (act && r < n) zs[r] = zq - tr[u] * dot * vr[u];
-                wave_sync();
+        for (int j = 0; j < PER; ++j) {
+            const int e = lane + 64 * j;
+            if (e < NB * RFL) rw[e] = pre[j];
+        }
+    };
+    for (int kk = wv; kk <= KK; kk += WV) {
+        const int shi = kk == 0 ? nsw - 1 : nsw - NB * kk;  // the pass's first reflector
+        const int rlo = 1 + NB * kk;                        // rows the pass touches: rlo .. n - 1
+        // bodies start at sb with sb + 1 = 0 mod 32, the first at or above shi + 31
+        const int sb0 = ((shi + 31 + 1 + NB - 1) / NB) * NB - 1;
+        const int pneed_base = (kk - 1) * BTB_PS + BASE;  // + (-(s_done)) of pass kk - 1
+        T z[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) z[q] = (T)0;
+        T pre[PER];
+        fetch(kk, sb0, shi, pre);
+        for (int sb = sb0; sb >= -NB; sb -= NB) {
+            // rows entering at steps u = 0..31: r = sb + 1 - u + 32 kk.  Pass kk - 1
+            // stores the bottom row s + 32 kk of its step s at its next step, so
+            // once it has published steps down to s_d, rows >= s_d + 1 + 32 kk
+            // are in Z.
+            const int top = sb + 1 + NB * kk;  // row entering at u = 0
+            const int rmin = max(top - (NB - 1), rlo), rmax = min(top, (int)n - 1);
+            if (kk > 0 && rmin <= rmax) {
+                const int s_need = rmin - 1 - NB * kk;
+                const int32_t need = pneed_base - s_need;
+                const int pw = (wv + WV - 1) % WV;
+                if (__hip_atomic_load(&prog[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+                    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                    while (__hip_atomic_load(&prog[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+                        if (__hip_atomic_load(&quit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0 ||
+                            __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
+                            __hip_atomic_store(&quit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                            if (lane == 0) cstore(err, 1);
+                            return;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
             }
-            if (--kk < 0) {  // the previous sweep's last task
-                --s;
-                kk = (nsw - s) / NB;
+            T ent[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int r = top - u;
+                ent[u] = (live && r >= rlo && r <= (int)n - 1) ? cload(zc + (int64_t)r * ldz) : (T)0;
             }
+            wave_sync();
+            park(pre);
+            wave_sync();
+            if (sb - NB >= -NB) fetch(kk, sb - NB, shi, pre);  // the next body's reflectors, in flight
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                // release the bottom row of the previous step (slot of the entering row)
+                const int slot = (NB - u) & (NB - 1);
+                const int rb = top - u + NB;  // row leaving: bottom of step u - 1's window
+                if (live && rb >= rlo && rb <= (int)n - 1) cstore(zc + (int64_t)rb * ldz, z[slot]);
+                z[slot] = ent[u];
+                const T tau = rw[u * RFL + NB];
+                if (tau != (T)0) {  // uniform: one reflector per step
+                    T d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+#pragma unroll
+                    for (int q = 0; q < NB; q += 4) {
+                        d0 += rw[u * RFL + q] * z[(q - u) & (NB - 1)];
+                        d1 += rw[u * RFL + q + 1] * z[(q + 1 - u) & (NB - 1)];
+                        d2 += rw[u * RFL + q + 2] * z[(q + 2 - u) & (NB - 1)];
+                        d3 += rw[u * RFL + q + 3] * z[(q + 3 - u) & (NB - 1)];
+                    }
+                    const T td = tau * ((d0 + d1) + (d2 + d3));
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) z[(q - u) & (NB - 1)] -= td * rw[u * RFL + q];
+                }
+            }
+            // publish: this body's rows are stored, steps down to sb - 31 done
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lane == 0)
+                __hip_atomic_store(&prog[wv], kk * BTB_PS + BASE - (sb - (NB - 1)), __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
-    for (int64_t i = q; i < n; i += 32)
-        if (live) Z[i * ldz + c] = zs[i];
 }
 
 // Z[r0:, :] <- (I - V T V^T) Z[r0:, :] for the kept panel (V in A's panel
@@ -2851,9 +2939,9 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                            vec->bhi, vec->mu, vec->rk, vec->k, vec->scr, vec->Z, vec->ldz);
         LAUNCH_OK();
         if (n >= 3) {
-            const int cpb = 2 * n * (int64_t)sizeof(T) <= 65536 ? 2 : 1;
-            hipLaunchKernelGGL(k_bt_bulge<T>, dim3((unsigned)cdiv_h(vec->k, cpb)), dim3(64),
-                               (unsigned)(cpb * n * sizeof(T)), st, vec->refl, n, vec->k, cpb, vec->Z, vec->ldz);
+            const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
+            hipLaunchKernelGGL(k_bt_bulge<T>, dim3((unsigned)cdiv_h(vec->k, 64)), dim3(64 * BtBulgeCfg<T>::WV), 0,
+                               st, vec->refl, n, vec->k, vec->Z, vec->ldz, spin_ticks, b.prog + n);
             LAUNCH_OK();
         }
         for (int64_t c0 = std::max<int64_t>(0, n - NB - 2) / NB * NB; c0 >= 0; c0 -= NB) {
