@@ -1988,6 +1988,17 @@ __global__ __launch_bounds__(256) void k_tridiag_prep(const T *__restrict__ band
     }
 }
 
+// Sturm count (number of negative pivots of T - x I) in fp64.  1 / q by the
+// hardware reciprocal and two Newton steps (relative error a few ulps: the
+// count is exact for a matrix whose e_{i-1}^2 differ by a few ulps, within
+// the bisection's own tolerance); rows in chunks of 8, the chunk's loads
+// issued before its recurrence.
+__device__ __forceinline__ double recip64(double q)
+{
+    double r = __builtin_amdgcn_rcp(q);
+    r = fma(r, fma(-q, r, 1.0), r);
+    return fma(r, fma(-q, r, 1.0), r);
+}
 __device__ __forceinline__ int sturm_below(const double *__restrict__ dd, const double *__restrict__ ee2, int64_t n,
                                            double x, double pivmin)
 {
@@ -1995,8 +2006,23 @@ __device__ __forceinline__ int sturm_below(const double *__restrict__ dd, const 
     double q = dd[0] - x;
     if (fabs(q) < pivmin) q = -pivmin;
     cnt += q < 0.0;
-    for (int64_t i = 1; i < n; ++i) {
-        q = (dd[i] - x) - ee2[i - 1] / q;
+    int64_t i = 1;
+    for (; i + 8 <= n; i += 8) {
+        double d8[8], e8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            d8[u] = dd[i + u];
+            e8[u] = ee2[i + u - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            q = (d8[u] - x) - e8[u] * recip64(q);
+            if (fabs(q) < pivmin) q = -pivmin;
+            cnt += q < 0.0;
+        }
+    }
+    for (; i < n; ++i) {
+        q = (dd[i] - x) - ee2[i - 1] * recip64(q);
         if (fabs(q) < pivmin) q = -pivmin;
         cnt += q < 0.0;
     }
@@ -2279,13 +2305,17 @@ __global__ __launch_bounds__(256) void k_zfill(T *__restrict__ Z, int64_t n, int
 // Inverse iteration, one thread per row i of the tridiagonal whose eigenvalue
 // mu[i] ranks below k: three steps of (T_b - mu I) y <- y on row i's block T_b,
 // each a partial-pivoting LU solve (a factor and the right-hand side's
-// elimination in one pass, then back substitution), the iterate scaled by its
-// largest entry and normalised.  Eigenvalues of one block closer than
-// 1e-9 ||T|| form a cluster, whose first row computes all its vectors in turn,
-// each orthogonalised against the earlier ones (modified Gram-Schmidt) after
-// every step.  The iteration runs on T / ||T||; pivots are floored at eps.
-// Scratch: 4 arrays of [n][k] doubles, entry q of the thread's slot (its rank)
-// at q * k + slot.
+// elimination in one forward pass, then back substitution), the iterate
+// normalised.  Eigenvalues of one block closer than 1e-9 ||T|| form a cluster,
+// whose first row computes all its vectors in turn, each orthogonalised
+// against the earlier ones (modified Gram-Schmidt) after every step.  The
+// iteration runs on T / ||T||; pivots are floored at eps.  Passes over the
+// block: the start vector is generated inside the first forward pass, the
+// back substitution accumulates max |y| and |y|^2, and the normalisation is
+// applied inside the next pass (or the final store); rows move in chunks of
+// IV_CH, loads of a chunk issued before its arithmetic.  Scratch: 4 arrays of
+// [n][k] doubles, entry q of the thread's slot (its rank) at q * k + slot.
+constexpr int IV_CH = 8;
 template <typename T>
 __global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_t n,
                                               const double *__restrict__ bounds, const int32_t *__restrict__ blo,
@@ -2305,62 +2335,118 @@ __global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_
     const double tiny = DBL_EPSILON;
     const int64_t nk = n * k;
     double *u0 = scr + slot, *u1 = scr + nk + slot, *u2 = scr + 2 * nk + slot, *y = scr + 3 * nk + slot;
-    auto D = [&](int64_t q) { return (double)band[(lo + q) * BW] * si; };
-    auto E = [&](int64_t q) { return q + 1 < m ? (double)band[(lo + q + 1) * BW + 1] * si : 0.0; };
+    const T *dg = band + lo * BW;  // d_q = dg[q BW], e_q = dg[(q + 1) BW + 1]
+    auto D = [&](int64_t q) { return (double)dg[q * BW] * si; };
+    auto E = [&](int64_t q) { return q + 1 < m ? (double)dg[(q + 1) * BW + 1] * si : 0.0; };
     auto floor_piv = [&](double x) { return fabs(x) < tiny ? (x < 0.0 ? -tiny : tiny) : x; };
     for (int64_t c = i;; ++c) {
         const int64_t rc = rank[c];
         const double sh = mu[c] * si;
-        for (int64_t q = 0; q < m; ++q) y[q * k] = start_entry(q, rc);
+        double scale = 1.0;  // y holds the iterate times 1 / scale
+        bool fresh = true;   // the right-hand side is the start vector (not in y)
+        int64_t seed = rc;
         for (int it = 0; it < 3; ++it) {
-            // rows (cd, cu, 0 | cr) and (dl, nd, ndu | nr): the larger of cd, dl pivots
-            double cd = D(0) - sh, cu = E(0), cr = y[0];
-#pragma unroll 4
-            for (int64_t q = 0; q + 1 < m; ++q) {
-                const double dl = E(q), nd = D(q + 1) - sh, ndu = E(q + 1), nr = y[(q + 1) * k];
-                const bool sw = !(fabs(cd) >= fabs(dl));
-                const double p0 = sw ? dl : floor_piv(cd);
-                const double p1 = sw ? nd : cu, p2 = sw ? ndu : 0.0, pr = sw ? nr : cr;
-                const double f = (sw ? cd : dl) / p0;
-                u0[q * k] = p0;
-                u1[q * k] = p1;
-                u2[q * k] = p2;
-                y[q * k] = pr;
-                cd = (sw ? cu : nd) - f * p1;
-                cu = (sw ? 0.0 : ndu) - f * p2;
-                cr = (sw ? cr : nr) - f * pr;
+            // ---- forward: rows (cd, cu, 0 | cr) and (dl, nd, ndu | nr), the larger
+            // of cd, dl pivots
+            double cd = D(0) - sh, cu = E(0), cr = fresh ? start_entry(0, seed) : y[0] * scale;
+            for (int64_t q0 = 0; q0 + 1 < m; q0 += IV_CH) {
+                const int cnt = (int)min<int64_t>(IV_CH, m - 1 - q0);
+                double ee[IV_CH + 1], dd[IV_CH], rr[IV_CH];
+#pragma unroll
+                for (int j = 0; j <= IV_CH; ++j) ee[j] = j <= cnt ? E(q0 + j) : 0.0;
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j) {
+                    const int64_t q = q0 + j + 1;
+                    dd[j] = j < cnt ? D(q) - sh : 0.0;
+                    rr[j] = j < cnt ? (fresh ? start_entry(q, seed) : y[q * k] * scale) : 0.0;
+                }
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j) {
+                    if (j < cnt) {
+                        const int64_t q = q0 + j;
+                        const double dl = ee[j], nd = dd[j], ndu = ee[j + 1], nr = rr[j];
+                        const bool sw = !(fabs(cd) >= fabs(dl));
+                        const double p0 = sw ? dl : floor_piv(cd);
+                        const double p1 = sw ? nd : cu, p2 = sw ? ndu : 0.0, pr = sw ? nr : cr;
+                        const double f = (sw ? cd : dl) / p0;
+                        u0[q * k] = p0;
+                        u1[q * k] = p1;
+                        u2[q * k] = p2;
+                        y[q * k] = pr;
+                        cd = (sw ? cu : nd) - f * p1;
+                        cu = (sw ? 0.0 : ndu) - f * p2;
+                        cr = (sw ? cr : nr) - f * pr;
+                    }
+                }
             }
             u0[(m - 1) * k] = floor_piv(cd);
             y[(m - 1) * k] = cr;
-            double z1 = 0.0, z2 = 0.0, amax = 0.0;
-            bool fin = true;
-#pragma unroll 4
-            for (int64_t q = m - 1; q >= 0; --q) {
-                const double zq = (y[q * k] - u1[q * k] * z1 - u2[q * k] * z2) / u0[q * k];
-                y[q * k] = zq;
-                z2 = z1;
-                z1 = zq;
-                fin = fin && fabs(zq) <= DBL_MAX;
-                amax = fmax(amax, fabs(zq));
+            // ---- back substitution, in place, with max |y| and |y|^2
+            double z1 = 0.0, z2 = 0.0, amax = 0.0, ss = 0.0;
+            for (int64_t qe = m; qe > 0; qe -= IV_CH) {
+                const int cnt = (int)min<int64_t>(IV_CH, qe);
+                double a0[IV_CH], a1[IV_CH], a2[IV_CH], yy[IV_CH];
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j) {
+                    const int64_t q = qe - 1 - j;
+                    const bool ok = j < cnt;
+                    a0[j] = ok ? u0[q * k] : 1.0;
+                    a1[j] = ok ? u1[q * k] : 0.0;
+                    a2[j] = ok ? u2[q * k] : 0.0;
+                    yy[j] = ok ? y[q * k] : 0.0;
+                }
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j) {
+                    if (j < cnt) {
+                        const double zq = (yy[j] - a1[j] * z1 - a2[j] * z2) / a0[j];
+                        yy[j] = zq;
+                        z2 = z1;
+                        z1 = zq;
+                        amax = fmax(amax, fabs(zq));
+                        ss += zq * zq;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j)
+                    if (j < cnt) y[(qe - 1 - j) * k] = yy[j];
             }
-            if (!fin || !(amax > 0.0)) {  // overflow or a zero solve: start again from another vector
-                for (int64_t q = 0; q < m; ++q) y[q * k] = start_entry(q, rc + 7919 * (it + 1));
-                amax = 1.0;
+            fresh = false;
+            if (!(amax <= DBL_MAX) || !(amax > 0.0) || ss != ss) {
+                // overflow, a NaN or a zero solve: start again from another vector
+                seed = rc + 7919 * (it + 1);
+                ss = 0.0;
+                for (int64_t q = 0; q < m; ++q) {
+                    const double x = start_entry(q, seed);
+                    y[q * k] = x;
+                    ss += x * x;
+                }
+            } else if (!(ss <= DBL_MAX) || !(ss > 0.0)) {
+                // |y|^2 out of range: scale by the largest entry first
+                const double ia = 1.0 / amax;
+                ss = 0.0;
+                for (int64_t q = 0; q < m; ++q) {
+                    const double x = y[q * k] * ia;
+                    y[q * k] = x;
+                    ss += x * x;
+                }
             }
-            const double ia = 1.0 / amax;
-            for (int64_t q = 0; q < m; ++q) y[q * k] *= ia;
-            for (int64_t p = i; p < c; ++p) {  // the cluster's earlier vectors, already in Z
-                const T *zp = Z + lo * ldz + rank[p];
-                double dp = 0.0;
-                for (int64_t q = 0; q < m; ++q) dp += y[q * k] * (double)zp[q * ldz];
-                for (int64_t q = 0; q < m; ++q) y[q * k] -= dp * (double)zp[q * ldz];
+            scale = 1.0 / sqrt(ss);
+            if (c > i) {
+                // a later member of a cluster: normalise, then against the cluster's
+                // earlier vectors (already in Z), then normalise again
+                for (int64_t q = 0; q < m; ++q) y[q * k] *= scale;
+                for (int64_t p = i; p < c; ++p) {
+                    const T *zp = Z + lo * ldz + rank[p];
+                    double dp = 0.0;
+                    for (int64_t q = 0; q < m; ++q) dp += y[q * k] * (double)zp[q * ldz];
+                    for (int64_t q = 0; q < m; ++q) y[q * k] -= dp * (double)zp[q * ldz];
+                }
+                double s2 = 0.0;
+                for (int64_t q = 0; q < m; ++q) s2 += y[q * k] * y[q * k];
+                scale = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
             }
-            double ss = 0.0;
-            for (int64_t q = 0; q < m; ++q) ss += y[q * k] * y[q * k];
-            const double sc = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
-            for (int64_t q = 0; q < m; ++q) y[q * k] *= sc;
         }
-        for (int64_t q = 0; q < m; ++q) Z[(lo + q) * ldz + rc] = (T)y[q * k];
+        for (int64_t q = 0; q < m; ++q) Z[(lo + q) * ldz + rc] = (T)(y[q * k] * scale);
         if (!(c + 1 < hi && mu[c] - mu[c + 1] < ortol && rank[c + 1] < k)) break;
     }
 }
@@ -2503,76 +2589,126 @@ __global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__
     }
 }
 
-// Z[r0:, :] <- (I - V T V^T) Z[r0:, :] for the kept panel (V in A's panel
-// block P, m rows, unit lower with the strict part stored; T in Tk, as the
-// reduction applied it), on one 32-column block of Z per workgroup:
-// W = V^T Z, Y = T W, Z -= V Y, V and Z through LDS in row chunks
+// Z[r0:, :] <- (I - V T V^T) Z[r0:, :] for a kept panel (V in A's panel
+// block P: m rows, unit lower with the strict part stored; T in Tk, as the
+// reduction applied it), in three kernels over the whole grid:
+//   Wp[c] = V[rows of chunk c]^T Z[rows of chunk c]   (BTP_RC-row chunks)
+//   Y = T sum_c Wp[c]
+//   Z -= V Y                                           (64 x 64 tiles)
+constexpr int BTP_RC = 128;  // rows per partial
 template <typename T>
-__global__ __launch_bounds__(256) void k_bt_panel(const T *__restrict__ P, int64_t lda, int m,
-                                                  const T *__restrict__ Tk, int64_t k, T *__restrict__ Zr,
-                                                  int64_t ldz)
+__device__ __forceinline__ T panel_v(const T *__restrict__ P, int64_t lda, int64_t i, int a)
 {
-    constexpr int CR = 64;  // rows per LDS chunk
-    constexpr int L = NB + 1;
-    __shared__ T Vs[CR * L], Zs[CR * L], Ws[NB * L], Ts[NB * L];
+    return i == a ? (T)1 : (i > a ? P[i * lda + a] : (T)0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_btp_w(const T *__restrict__ P, int64_t lda, int m,
+                                               const T *__restrict__ Zr, int64_t ldz, int64_t k,
+                                               T *__restrict__ Wp)
+{
+    constexpr int LV = NB + 1, LZ = 64 + 4;
+    __shared__ T Vs[BTP_RC * LV], Zs[BTP_RC * LZ];
     const int tid = threadIdx.x;
-    const int64_t cb = (int64_t)blockIdx.x * NB;
-    auto vload = [&](int64_t i, int a) -> T {  // V[i][a]
-        return i == a ? (T)1 : (i > a ? P[i * lda + a] : (T)0);
-    };
-    for (int p = tid; p < NB * NB; p += 256) Ts[(p / NB) * L + p % NB] = Tk[p];
-    // W = V^T Z: thread (a, b4) accumulates W[a][4 b4 .. 4 b4 + 3]
-    const int a = tid / 8, b4 = (tid % 8) * 4;
-    T acc[4] = {};
-    for (int64_t r0 = 0; r0 < m; r0 += CR) {
-        __syncthreads();
-        for (int p = tid; p < CR * NB; p += 256) {
-            const int rr = p / NB, cc = p % NB;
-            const int64_t i = r0 + rr;
-            Vs[rr * L + cc] = i < m ? vload(i, cc) : (T)0;
-            Zs[rr * L + cc] = i < m && cb + cc < k ? Zr[i * ldz + cb + cc] : (T)0;
-        }
-        __syncthreads();
-        for (int rr = 0; rr < CR; ++rr) {
-            const T va = Vs[rr * L + a];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] += va * Zs[rr * L + b4 + u];
-        }
+    const int64_t cb = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.y * BTP_RC;
+    for (int p = tid; p < BTP_RC * NB; p += 256) {
+        const int rr = p / NB, a = p % NB;
+        const int64_t i = r0 + rr;
+        Vs[rr * LV + a] = i < m ? panel_v(P, lda, i, a) : (T)0;
+    }
+    for (int p = tid; p < BTP_RC * 64; p += 256) {
+        const int rr = p / 64, c = p % 64;
+        const int64_t i = r0 + rr;
+        Zs[rr * LZ + c] = i < m && cb + c < k ? Zr[i * ldz + cb + c] : (T)0;
     }
     __syncthreads();
+    const int a = tid / 8, c8 = (tid % 8) * 8;
+    T acc[8] = {};
+    for (int rr = 0; rr < BTP_RC; ++rr) {
+        const T va = Vs[rr * LV + a];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Ws[a * L + b4 + u] = acc[u];
+        for (int j = 0; j < 8; ++j) acc[j] += va * Zs[rr * LZ + c8 + j];
+    }
+    T *out = Wp + ((int64_t)blockIdx.y * NB + a) * k + cb + c8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (cb + c8 + j < k) out[j] = acc[j];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_btp_y(const T *__restrict__ Wp, int nch, const T *__restrict__ Tk,
+                                               int64_t k, T *__restrict__ Y)
+{
+    constexpr int L = 64 + 4;
+    __shared__ T Ts[NB * (NB + 1)], Ws[NB * L];
+    const int tid = threadIdx.x;
+    for (int p = tid; p < NB * NB; p += 256) Ts[(p / NB) * (NB + 1) + p % NB] = Tk[p];
+    const int64_t cb = (int64_t)blockIdx.x * 64;
+    const int a = tid / 8, c8 = (tid % 8) * 8;
+    // W[a][c8 .. c8 + 7] = sum over the row chunks
+    T w[8] = {};
+#pragma unroll 2
+    for (int ch = 0; ch < nch; ++ch) {
+        const T *src = Wp + ((int64_t)ch * NB + a) * k + cb + c8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] += cb + c8 + j < k ? src[j] : (T)0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Ws[a * L + c8 + j] = w[j];
     __syncthreads();
-    // Y = T W
-    T yv[4];
+    T y[8] = {};
+#pragma unroll 4
+    for (int l = 0; l < NB; ++l) {
+        const T t = Ts[a * (NB + 1) + l];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        T x = 0;
-        for (int l = 0; l < NB; ++l) x += Ts[a * L + l] * Ws[l * L + b4 + u];
-        yv[u] = x;
+        for (int j = 0; j < 8; ++j) y[j] += t * Ws[l * L + c8 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (cb + c8 + j < k) Y[(int64_t)a * k + cb + c8 + j] = y[j];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_btp_u(const T *__restrict__ P, int64_t lda, int m,
+                                               const T *__restrict__ Y, int64_t k, T *__restrict__ Zr,
+                                               int64_t ldz)
+{
+    constexpr int LV = NB + 1, LY = 64 + 4;
+    __shared__ T Vs[64 * LV], Ys[NB * LY];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * 64, cb = (int64_t)blockIdx.y * 64;
+    for (int p = tid; p < 64 * NB; p += 256) {
+        const int rr = p / NB, a = p % NB;
+        const int64_t i = r0 + rr;
+        Vs[rr * LV + a] = i < m ? panel_v(P, lda, i, a) : (T)0;
+    }
+    for (int p = tid; p < NB * 64; p += 256) {
+        const int a = p / 64, c = p % 64;
+        Ys[a * LY + c] = cb + c < k ? Y[(int64_t)a * k + cb + c] : (T)0;
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) Ws[a * L + b4 + u] = yv[u];
-    // Z -= V Y, thread (row rr, column cc) of each chunk
-    for (int64_t r0 = 0; r0 < m; r0 += CR) {
-        __syncthreads();
-        for (int p = tid; p < CR * NB; p += 256) {
-            const int rr = p / NB, cc = p % NB;
-            const int64_t i = r0 + rr;
-            Vs[rr * L + cc] = i < m ? vload(i, cc) : (T)0;
-        }
-        __syncthreads();
-        for (int p = tid; p < CR * NB; p += 256) {
-            const int rr = p / NB, cc = p % NB;
-            const int64_t i = r0 + rr;
-            if (i < m && cb + cc < k) {
-                T x = Zr[i * ldz + cb + cc];
+    const int tr = (tid / 16) * 4, tc = (tid % 16) * 4;
+    T acc[4][4] = {};
 #pragma unroll 8
-                for (int aa = 0; aa < NB; ++aa) x -= Vs[rr * L + aa] * Ws[aa * L + cc];
-                Zr[i * ldz + cb + cc] = x;
-            }
-        }
+    for (int a = 0; a < NB; ++a) {
+        T v[4], y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = Vs[(tr + i) * LV + a];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = Ys[a * LY + tc + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] += v[i] * y[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + tr + i;
+        if (r >= m) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (cb + tc + j < k) Zr[r * ldz + cb + tc + j] -= acc[i][j];
     }
 }
 
@@ -2700,6 +2836,7 @@ struct VecReq {
     T *refl, *keepT;          // bulge reflectors (refl_index layout), panel T factors
     int32_t *blo, *bhi, *rk;  // each row's block of the tridiagonal, the rank of its eigenvalue
     double *mu, *scr;         // per-block eigenvalues (fp64), inverse-iteration scratch
+    T *wp, *yb;               // panel back-transformation: partial V^T Z per row chunk, Y = T V^T Z
 };
 
 template <typename T>
@@ -2947,9 +3084,19 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         for (int64_t c0 = std::max<int64_t>(0, n - NB - 2) / NB * NB; c0 >= 0; c0 -= NB) {
             const int64_t r0 = c0 + NB, m = n - r0;
             if (m < 2) continue;
-            hipLaunchKernelGGL(k_bt_panel<T>, dim3((unsigned)cdiv_h(vec->k, NB)), dim3(256), 0, st,
-                               A + r0 * lda + c0, lda, (int)m, vec->keepT + (c0 / NB) * NB * NB, vec->k,
-                               vec->Z + r0 * vec->ldz, vec->ldz);
+            const T *Pp = A + r0 * lda + c0;
+            T *Zr = vec->Z + r0 * vec->ldz;
+            const int nch = (int)cdiv_h(m, BTP_RC);
+            const unsigned ncb = (unsigned)cdiv_h(vec->k, 64);
+            hipLaunchKernelGGL(k_btp_w<T>, dim3(ncb, (unsigned)nch), dim3(256), 0, st, Pp, lda, (int)m,
+                               (const T *)Zr, vec->ldz, vec->k, vec->wp);
+            LAUNCH_OK();
+            hipLaunchKernelGGL(k_btp_y<T>, dim3(ncb), dim3(256), 0, st,
+                               (const T *)vec->wp, nch, (const T *)(vec->keepT + (c0 / NB) * NB * NB), vec->k,
+                               vec->yb);
+            LAUNCH_OK();
+            hipLaunchKernelGGL(k_btp_u<T>, dim3((unsigned)cdiv_h(m, 64), ncb), dim3(256), 0, st, Pp, lda, (int)m,
+                               (const T *)vec->yb, vec->k, Zr, vec->ldz);
             LAUNCH_OK();
         }
     }
@@ -3233,7 +3380,7 @@ namespace {
 
 // the eigenvector path's workspace after the solver's own: reflectors, panel
 // T factors, the tridiagonal's blocks, eigenvalues and ranks, inverse-iteration
-// scratch (4 n k doubles)
+// scratch (4 n k doubles), the panel back-transformation's partials
 template <typename T>
 size_t vec_layout(int64_t n, int64_t k, char *base, VecReq<T> &v)
 {
@@ -3247,6 +3394,8 @@ size_t vec_layout(int64_t n, int64_t k, char *base, VecReq<T> &v)
     v.rk = ws.take<int32_t>((size_t)n);
     v.mu = ws.take<double>((size_t)n);
     v.scr = ws.take<double>((size_t)4 * n * k);
+    v.wp = ws.take<T>((size_t)(n / BTP_RC + 1) * NB * k);
+    v.yb = ws.take<T>((size_t)NB * k);
     return ws.off;
 }
 
