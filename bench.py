@@ -330,12 +330,21 @@ def postproc_rows(torch, spec, dev):
     # eigenvalues and the eigenvectors of the 0.8 d largest (the keep set of a
     # 0.8 keep ratio) on the same covariance; the solver destroys its input, so
     # each call starts from a copy (a 64 MB device copy, ~20 us)
+    # the window eigenpairs at the EigenTrack shape: 256 streams x 512 steps,
+    # N = 30, from a band of the same shape (positive window Grams)
+    Hw = torch.from_numpy(rng.standard_normal((S, 512, 64)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    bandw = spec.gram_window(Hw, N=N)
+    ww_e = torch.empty((S * W, N), dtype=torch.float32, device=dev)
+    Vw_e = torch.empty((S * W, N, N), dtype=torch.float32, device=dev)
+    iw_e = torch.empty((S * W,), dtype=torch.int32, device=dev)
     k_e = int(0.8 * d)
     Ce = torch.empty_like(C)
     w_e = torch.empty((d,), dtype=torch.float32, device=dev)
     Z_e = torch.empty((d, k_e), dtype=torch.float32, device=dev)
     ws_e = torch.empty((spec.eigh_large_workspace(d, torch.float32, k_e),), dtype=torch.uint8, device=dev)
     post = {
+        "eigh_windows_123648_N30": lambda: spec.eigh_batched_band(bandw, n=N, scale=1.0 / N, w=ww_e, V=Vw_e,
+                                                                   info=iw_e),
         "eigvalsh_large_4096_f32": lambda: (Ce.copy_(C), spec.eigvalsh_large(Ce, w=w_e, ws=ws)),
         "eigh_4096_f32_k3276": lambda: (Ce.copy_(C), spec.eigh_large(Ce, k_e, w=w_e, Z=Z_e, ws=ws_e)),
         "desc_smooth_123648": lambda: spec.desc_smooth(dwin, streams=S, W=W, alpha=0.2, out=sm_out, to_host=False),

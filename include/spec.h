@@ -139,6 +139,30 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
                           int32_t *info);
 
 /* ------------------------------------------------------------------------
+ * Eigenvalues and eigenvectors of the same batches (n <= 32): the window
+ * decomposition of "Random matrix theory spectral methods", section 3.1,
+ * which yields the eigenvalues {lambda_i} and the eigenvectors of each
+ * window covariance (of the N x N window Gram here; an eigenvector u of the
+ * d x d covariance H^T H / N is H^T v / sqrt(N lambda) for the Gram's v).
+ * Parallel cyclic Jacobi with the rotations accumulated into V, one wave per
+ * matrix padded to 32 x 32, in fp32: a pair rotates while
+ * |a_pq| > max(2e-6 sqrt(|a_pp a_qq|), 1e-7 max|a_ij|), at most 30 sweeps.
+ *
+ * src, batch: as spec_eigvalsh_batched.
+ * w:    f32 [batch][n], eigenvalues descending.
+ * V:    f32 [batch][n][n], V[b][i][j] = component i of the unit eigenvector of
+ *       w[b][j] (sign arbitrary).
+ * info: int32 [batch] (may be NULL): the number of sweeps (>= 1), -2 if the
+ *       30 sweeps ended with a pair still above the threshold (outputs are
+ *       written, less accurate), or -1 if the matrix has a non-finite entry
+ *       (every output of that matrix is NaN).
+ * Requires 1 <= n <= 32 (else SPEC_EINVAL, or SPEC_EUNSUPPORTED above 32),
+ * V 4-byte aligned and the conditions of spec_eigvalsh_batched.
+ * ---------------------------------------------------------------------- */
+int spec_eigh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, float *V,
+                      int32_t *info);
+
+/* ------------------------------------------------------------------------
  * A4  Large symmetric eigenvalues (the single eigendecomposition of the
  *     aggregated covariance in [SWIFT] sections 2 and 7; the O(d^3) step [RMT]
  *     section 6.1 names as the cost for large d).

@@ -111,6 +111,19 @@ def test_sliding_validation(L):
     assert f(None, ctypes.byref(short), 0, 30, 64, FAKE, None) == EINVAL  # T < n
 
 
+def test_eigh_batched_validation(L):
+    f = L.spec_eigh_batched
+    dense = spec.BatchSrc(spec.SRC_DENSE, FAKE, 30, 900, 0, 0, 1, 1.0)
+    assert f(None, ctypes.byref(dense), 4, 30, FAKE, None, None) == EINVAL  # V NULL
+    assert f(None, ctypes.byref(dense), 4, 33, FAKE, FAKE, None) == EUNSUPPORTED  # n > 32
+    assert f(None, ctypes.byref(dense), 4, 0, FAKE, FAKE, None) == EINVAL
+    assert f(None, ctypes.byref(dense), 4, 30, FAKE, FAKE + 2, None) == EINVAL  # misaligned V
+    short = spec.BatchSrc(spec.SRC_DENSE, FAKE, 29, 900, 0, 0, 1, 1.0)
+    assert f(None, ctypes.byref(short), 4, 30, FAKE, FAKE, None) == EINVAL  # lda < n
+    band = spec.BatchSrc(spec.SRC_BAND, FAKE, 0, 0, 2, 100, 1, 1.0 / 30)
+    assert f(None, ctypes.byref(band), 2 * 71 + 1, 30, FAKE, FAKE, None) == EINVAL  # batch != streams * W
+
+
 def test_eigh_large_validation(L):
     b = ctypes.c_size_t(0)
     f = L.spec_eigh_large_workspace

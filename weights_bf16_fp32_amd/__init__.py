@@ -98,7 +98,7 @@ EXPORTS = ["spec_strerror", "spec_version", "spec_cov_accumulate", "spec_gram_wi
            "spec_descriptors_workspace", "spec_descriptors", "spec_desc_smooth", "spec_spectrum_robust",
            "spec_eigvalsh_topk", "spec_eigvecs_topk", "spec_project_weight_workspace",
            "spec_project_weight", "spec_timing_enable", "spec_timing_read", "spec_descriptors_static", "spec_tail_pair_screen", "spec_eigvalsh_batched_desc",
-           "spec_eigvalsh_sliding", "spec_eigh_large_workspace", "spec_eigh_large"]
+           "spec_eigvalsh_sliding", "spec_eigh_large_workspace", "spec_eigh_large", "spec_eigh_batched"]
 
 _lib = None
 
@@ -139,6 +139,7 @@ def lib() -> ctypes.CDLL:
                                              vp]
         L.spec_descriptors_static.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(DescParams), vp]
         L.spec_eigvalsh_sliding.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, i32, vp, vp]
+        L.spec_eigh_batched.argtypes = [vp, ctypes.POINTER(BatchSrc), i64, i32, vp, vp, vp]
         L.spec_timing_enable.argtypes = [ctypes.c_uint]
         L.spec_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in EXPORTS[2:]:
@@ -235,6 +236,39 @@ def eigvalsh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, i
     batch = S * ((T - n) // stride + 1)
     src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
     return _batched(src, batch, n, w, info, band.device)
+
+
+def _eigh_batched(src, batch, n, w, V, info, device):
+    torch = _torch()
+    if w is None:
+        w = torch.empty((batch, n), dtype=torch.float32, device=device)
+    if V is None:
+        V = torch.empty((batch, n, n), dtype=torch.float32, device=device)
+    if info is None:
+        info = torch.empty((batch,), dtype=torch.int32, device=device)
+    _check(lib().spec_eigh_batched(_stream(), ctypes.byref(src), batch, n, _dev(w), _dev(V), _dev(info)))
+    return w, V, info
+
+
+def eigh_batched_dense(A, w=None, V=None, info=None):
+    """Eigenvalues (descending) and eigenvectors of A [batch, n, n] f32 (lower
+    triangle read, n <= 32): V[b][:, j] belongs to w[b][j].  info[b] = Jacobi
+    sweeps, -2 (sweep limit) or -1 (non-finite entry)."""
+    if A.dim() == 2:
+        A = A.unsqueeze(0)
+    batch, n, _ = A.shape
+    src = BatchSrc(SRC_DENSE, _dev(A), A.stride(1), A.stride(0), 0, 0, 1, 1.0)
+    return _eigh_batched(src, batch, n, w, V, info, A.device)
+
+
+def eigh_batched_band(band, n: int, scale: float, stride: int = 1, w=None, V=None, info=None):
+    """Eigenpairs of every window's Gram scale * G_w from the band [S, T, n] of gram_window."""
+    S, T, N = band.shape
+    if N != n or not band.is_contiguous():
+        raise SpecError(-1, "band must be a contiguous [streams, T, n] tensor")
+    batch = S * ((T - n) // stride + 1)
+    src = BatchSrc(SRC_BAND, _dev(band), 0, 0, S, T, stride, float(scale))
+    return _eigh_batched(src, batch, n, w, V, info, band.device)
 
 
 def eigvalsh_sliding(band, n: int, scale: float, stride: int = 1, restart: int = 64, w=None, info=None):

@@ -98,12 +98,12 @@ int spec_gram_window(void *stream, const void *H, int ht, int64_t streams, int64
     return SPEC_EINVAL;
 }
 
-int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info)
+// the batch source of the small solvers: its kind, strides and batch count
+static int check_batch_src(const spec_batch_src *src, int64_t batch, int n)
 {
-    if (src == nullptr || w == nullptr || src->a == nullptr) return SPEC_EINVAL;
-    if (n < 1 || n > 64) return n > 64 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+    if (src == nullptr || src->a == nullptr) return SPEC_EINVAL;
     if (batch < 0 || batch > ((int64_t)1 << 31) - 1) return SPEC_EINVAL;
-    if (!aligned(w, 4) || !aligned(src->a, 4) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
+    if (!aligned(src->a, 4)) return SPEC_EINVAL;
     if (src->kind == SPEC_SRC_DENSE) {
         if (src->lda < n || src->stride_a < (int64_t)n * src->lda) return SPEC_EINVAL;
     } else if (src->kind == SPEC_SRC_BAND) {
@@ -113,8 +113,29 @@ int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch
     } else {
         return SPEC_EINVAL;
     }
+    return SPEC_OK;
+}
+
+int spec_eigvalsh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info)
+{
+    if (src == nullptr || w == nullptr || src->a == nullptr) return SPEC_EINVAL;
+    if (n < 1 || n > 64) return n > 64 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+    if (!aligned(w, 4) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
+    const int st = check_batch_src(src, batch, n);
+    if (st != SPEC_OK) return st;
     KTimer kt((hipStream_t)stream, SPEC_KT_SMALL_EIG);
     return from_hip(launch_eigvalsh_batched((hipStream_t)stream, src, batch, n, w, info));
+}
+
+int spec_eigh_batched(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, float *V,
+                      int32_t *info)
+{
+    if (src == nullptr || w == nullptr || V == nullptr || src->a == nullptr) return SPEC_EINVAL;
+    if (n < 1 || n > 32) return n > 32 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+    if (!aligned(w, 4) || !aligned(V, 4) || (info != nullptr && !aligned(info, 4))) return SPEC_EINVAL;
+    const int st = check_batch_src(src, batch, n);
+    if (st != SPEC_OK) return st;
+    return from_hip(launch_eigh_batched((hipStream_t)stream, src, batch, n, w, V, info));
 }
 
 int spec_eigvalsh_sliding(void *stream, const spec_batch_src *src, int64_t batch, int n, int restart, float *w,

@@ -2280,16 +2280,20 @@ __global__ __launch_bounds__(64) void k_vbisect(const double *__restrict__ dd, c
 }
 
 // rank[i] = position of mu[i] in the descending order of all blocks' values
-// (ties by row), so that column rank[i] of Z belongs to w[rank[i]]
+// (ties by row, a NaN after every number), so that column rank[i] of Z belongs
+// to w[rank[i]] and the ranks are a permutation whatever the values
 __global__ __launch_bounds__(256) void k_vrank(const double *__restrict__ mu, int64_t n, int32_t *__restrict__ rank)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const double x = mu[i];
+    const bool xn = isnan(x);
     int64_t r = 0;
     for (int64_t j = 0; j < n; ++j) {
         const double y = mu[j];
-        r += (y > x) || (y == x && j < i);
+        const bool yn = isnan(y);
+        const bool before = xn ? (!yn || j < i) : (!yn && (y > x || (y == x && j < i)));
+        r += before;
     }
     rank[i] = (int32_t)r;
 }

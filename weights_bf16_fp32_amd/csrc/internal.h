@@ -19,6 +19,8 @@ hipError_t launch_gram_dense(hipStream_t stream, const void *H, int ht, int64_t 
 
 hipError_t launch_eigvalsh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w,
                                    int32_t *info);
+hipError_t launch_eigh_batched(hipStream_t stream, const spec_batch_src *src, int64_t batch, int n, float *w, float *V,
+                               int32_t *info);
 
 hipError_t launch_eigvalsh_sliding(hipStream_t stream, const spec_batch_src *src, int n, int restart, float *w,
                                    int32_t *info);
