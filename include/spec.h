@@ -413,9 +413,6 @@ int spec_eigvalsh_batched_desc(void *stream, const spec_batch_src *src, int64_t 
  *          whose band row has a non-finite value within the window (its
  *          eigenvalues are then NaN; the chain restarts after that step).
  * Requires 1 <= n <= 64 and the band conditions of spec_eigvalsh_batched.
- * Currently switched off: after validation every call returns
- * SPEC_EUNSUPPORTED and enqueues nothing (the kernel faulted on its first GPU
- * run and the cause is not yet found).
  * ---------------------------------------------------------------------- */
 int spec_eigvalsh_sliding(void *stream, const spec_batch_src *src, int64_t batch, int n, int restart, float *w,
                           int32_t *info);

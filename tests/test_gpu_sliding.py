@@ -11,9 +11,7 @@ import oracle
 from gpu_util import dev, dev_bf16, print_case
 from gen import synth
 
-pytestmark = [pytest.mark.gpu, pytest.mark.skip(
-    reason="spec_eigvalsh_sliding is switched off: its kernel faulted (illegal address) on its first GPU run; "
-           "no cause is found yet by reading the code or by the host emulation of the same source")]
+pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module")

@@ -148,11 +148,7 @@ int spec_eigvalsh_sliding(void *stream, const spec_batch_src *src, int64_t batch
     if (src->streams < 1 || src->T < n || src->stride < 1 || !isfinite(src->scale)) return SPEC_EINVAL;
     const int64_t W = (src->T - n) / src->stride + 1;
     if (batch != src->streams * W) return SPEC_EINVAL;
-    // Switched off: the kernel's first GPU run ended in an illegal-address
-    // fault whose cause is not found yet (its host emulation is in bounds), so
-    // nothing is enqueued until it is.
-    (void)stream;
-    return SPEC_EUNSUPPORTED;
+    return from_hip(launch_eigvalsh_sliding((hipStream_t)stream, src, n, restart, w, info));
 }
 
 int spec_eigvalsh_batched_desc(void *stream, const spec_batch_src *src, int64_t batch, int n, float *w, int32_t *info,
