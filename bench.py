@@ -343,6 +343,8 @@ def postproc_rows(torch, spec, dev):
     Z_e = torch.empty((d, k_e), dtype=torch.float32, device=dev)
     ws_e = torch.empty((spec.eigh_large_workspace(d, torch.float32, k_e),), dtype=torch.uint8, device=dev)
     post = {
+        "sliding_windows_123648_N30_r64": lambda: spec.eigvalsh_sliding(bandw, n=N, scale=1.0 / N, restart=64,
+                                                                       w=ww_e, info=iw_e),
         "eigh_windows_123648_N30": lambda: spec.eigh_batched_band(bandw, n=N, scale=1.0 / N, w=ww_e, V=Vw_e,
                                                                    info=iw_e),
         "eigvalsh_large_4096_f32": lambda: (Ce.copy_(C), spec.eigvalsh_large(Ce, w=w_e, ws=ws)),
