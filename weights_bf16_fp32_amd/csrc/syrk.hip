@@ -296,25 +296,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const int st = (int)(k & 1);
                 const uint16_t *la = &lds[st][0][0] + gsel;
                 const uint16_t *lb = &lds[st][diag ? 0 : 1][0] + gsel;
-                if (active) {
+                // every wave computes (on a diagonal tile the block above the
+                // diagonal is computed and dropped at the store), so the step is
+                // one basic block: the loads, the first K-half's operands, its 16
+                // MFMAs each with two permutes of the next stage, the second
+                // K-half's operands, its 16 MFMAs with the LDS writes
 #pragma unroll
-                    for (int kk = 0; kk < BG_BK / 16; ++kk) {
-                        bf16x8_t fa[4], fbv[4];
+                for (int kk = 0; kk < BG_BK / 16; ++kk) {
+                    bf16x8_t fa[4], fbv[4];
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            fa[m] = *reinterpret_cast<const bf16x8_t *>(
-                                la + 2 * kk * BG_GROUP_U16 + bg_slot(wm * 128 + m * 32 + (lane & 31)));
-                            fbv[m] = *reinterpret_cast<const bf16x8_t *>(
-                                lb + 2 * kk * BG_GROUP_U16 + bg_slot(wn * 128 + m * 32 + (lane & 31)));
-                        }
-#pragma unroll
-                        for (int a = 0; a < 4; ++a)
-#pragma unroll
-                            for (int b = 0; b < 4; ++b)
-                                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fbv[b], acc[a][b], 0, 0, 0);
+                    for (int m = 0; m < 4; ++m) {
+                        fa[m] = *reinterpret_cast<const bf16x8_t *>(
+                            la + 2 * kk * BG_GROUP_U16 + bg_slot(wm * 128 + m * 32 + (lane & 31)));
+                        fbv[m] = *reinterpret_cast<const bf16x8_t *>(
+                            lb + 2 * kk * BG_GROUP_U16 + bg_slot(wn * 128 + m * 32 + (lane & 31)));
                     }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fbv[b], acc[a][b], 0, 0, 0);
                 }
                 lstore(vb[(u + 1) % BG_PF], st ^ 1);
+                __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                static_for<0, 16>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                });
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                static_for<0, 8>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                });
+                static_for<0, 8>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); });
                 __syncthreads();
             });
         }
