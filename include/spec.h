@@ -211,8 +211,8 @@ int spec_eigvalsh_large(void *stream, void *A, int t, int64_t n, int64_t lda, vo
  *       aligned): spec_eigvalsh_large's, then the reflectors (about n^2/64 x 33
  *       values), the panels' T, and 4 n k doubles of scratch.
  * Requires 1 <= k <= n <= 8192 (else SPEC_EINVAL, or SPEC_EUNSUPPORTED above
- * 8192: the back-transformation keeps columns of Z in LDS) and the conditions
- * of spec_eigvalsh_large.
+ * 8192), (n + 128) * ldz * sizeof(t) < 2^31 (Z is addressed with 32-bit byte
+ * offsets; else SPEC_EUNSUPPORTED) and the conditions of spec_eigvalsh_large.
  * ---------------------------------------------------------------------- */
 int spec_eigh_large_workspace(int64_t n, int t, int64_t k, size_t *bytes);
 

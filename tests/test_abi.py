@@ -140,6 +140,7 @@ def test_eigh_large_validation(L):
     assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, None, 10, 10, FAKE, need, None) == EINVAL  # Z NULL
     assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE, 10, 10, FAKE, need - 1, None) == EWORKSPACE
     assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE + 2, 10, 10, FAKE, need, None) == EINVAL  # misaligned Z
+    assert g(None, FAKE, spec.F32, 1000, 1000, FAKE, FAKE, 1 << 19, 10, FAKE, need, None) == EUNSUPPORTED  # Z past 2^31 bytes
 
 
 def test_alignment_codes(L):

@@ -219,6 +219,8 @@ int spec_eigh_large(void *stream, void *A, int t, int64_t n, int64_t lda, void *
     if (!aligned(A, 16) || !aligned(w, elt_size(t)) || !aligned(Z, elt_size(t)) ||
         (info != nullptr && !aligned(info, 4)))
         return SPEC_EINVAL;
+    // Z is addressed with 32-bit byte offsets (rows up to n + 128 reached)
+    if ((n + 128) * ldz * (int64_t)elt_size(t) >= ((int64_t)1 << 31)) return SPEC_EUNSUPPORTED;
     if (ws == nullptr || ws_bytes < need) return SPEC_EWORKSPACE;
     if (!aligned(ws, 256)) return SPEC_EINVAL;
     return from_hip(launch_eigh_large((hipStream_t)stream, A, t, n, lda, w, Z, ldz, k, ws, info));

@@ -2482,32 +2482,42 @@ __global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__
 {
     constexpr int WV = BtBulgeCfg<T>::WV;
     constexpr int PER = (NB * RFL + 63) / 64;  // reflector entries per lane per body
+    constexpr uint32_t OOB = 0x7FFFFFFFu;      // a row offset past every record
     __shared__ int32_t prog[WV];
     __shared__ int32_t quit;
     __shared__ T rs[WV][NB * RFL];  // the body's 32 reflectors, per wave
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t col = (int64_t)blockIdx.x * 64 + lane;
-    const bool live = col < k;
-    T *zc = Z + (live ? col : 0);
-    const int nsw = (int)n - 2;
-    const int KK = nsw / NB;           // passes 0 .. KK
-    const int BASE = (int)n + 2 * NB;  // BASE - s > 0 for every step s >= -32
+    const int nn = (int)n;
+    const int nsw = nn - 2;
+    const int KK = nsw / NB;        // passes 0 .. KK
+    const int BASE = nn + 2 * NB;   // BASE - s > 0 for every step s >= -32
+    // Z and the reflectors through buffer resources with 32-bit offsets (the
+    // caller guarantees (n + 64) ldz sizeof(T) < 2^31): a row past n, or a
+    // column past k (offset 2^31), is out of range, so its load reads 0 and its
+    // store is dropped; Z moves with the coherent policy of the bulge chase
+    const uint32_t ldzb = (uint32_t)ldz * (uint32_t)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(Z, 0, (int)(ldzb * (uint32_t)nn), 0x00020000);
+    const int nrefl = refl_index(n, nsw);
+    const __amdgpu_buffer_rsrc_t rr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)refl, 0, (int)((uint32_t)nrefl * RFL * sizeof(T)), 0x00020000);
+    const uint32_t vcol = col < k ? (uint32_t)col * (uint32_t)sizeof(T) : 0x80000000u;
     if (threadIdx.x < WV) prog[threadIdx.x] = (int32_t)threadIdx.x * BTB_PS;
     if (threadIdx.x == 0) quit = 0;
     __syncthreads();
     T *rw = rs[wv];
-    // the 32 reflectors of body sb (steps s = sb - u) of pass kk, entry e of the
-    // body at rw[e]: lane-strided loads (tau = 0 for steps without a reflector)
+    // the 32 reflectors of body sb (steps s = sb - u) of pass kk: lane-strided
+    // loads of their (v, tau) records (0 for steps without a reflector)
     auto fetch = [&](int kk, int sb, int shi, T (&pre)[PER]) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int e = lane + 64 * j;
             const int u = e / RFL, q = e % RFL;
             const int sr = sb - u;
-            T x = (T)0;
-            if (e < NB * RFL && sr >= 0 && sr <= shi) x = refl[(refl_index(n, sr) + kk) * RFL + q];
-            pre[j] = x;
+            const bool ok = e < NB * RFL && sr >= 0 && sr <= shi;
+            const uint32_t off = ok ? ((uint32_t)(refl_index(n, sr) + kk) * RFL + q) * (uint32_t)sizeof(T) : OOB;
+            pre[j] = band_load<T>(rr, (int)off, 0);
         }
     };
     auto park = [&](const T (&pre)[PER]) {
@@ -2534,7 +2544,7 @@ __global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__
             // once it has published steps down to s_d, rows >= s_d + 1 + 32 kk
             // are in Z.
             const int top = sb + 1 + NB * kk;  // row entering at u = 0
-            const int rmin = max(top - (NB - 1), rlo), rmax = min(top, (int)n - 1);
+            const int rmin = max(top - (NB - 1), rlo), rmax = min(top, nn - 1);
             if (kk > 0 && rmin <= rmax) {
                 const int s_need = rmin - 1 - NB * kk;
                 const int32_t need = pneed_base - s_need;
@@ -2552,12 +2562,12 @@ __global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__
                     }
                 }
             }
+            // row offsets: rows below the pass's range map past every record
+            // (rows past n are past it anyway)
+            auto roff = [&](int r) { return r >= rlo ? (uint32_t)r * ldzb : OOB; };
             T ent[NB];
 #pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const int r = top - u;
-                ent[u] = (live && r >= rlo && r <= (int)n - 1) ? cload(zc + (int64_t)r * ldz) : (T)0;
-            }
+            for (int u = 0; u < NB; ++u) ent[u] = band_load<T>(rz, (int)(vcol + roff(top - u)), 0);
             wave_sync();
             park(pre);
             wave_sync();
@@ -2566,8 +2576,7 @@ __global__ __launch_bounds__(64 * BtBulgeCfg<T>::WV) void k_bt_bulge(const T *__
             for (int u = 0; u < NB; ++u) {
                 // release the bottom row of the previous step (slot of the entering row)
                 const int slot = (NB - u) & (NB - 1);
-                const int rb = top - u + NB;  // row leaving: bottom of step u - 1's window
-                if (live && rb >= rlo && rb <= (int)n - 1) cstore(zc + (int64_t)rb * ldz, z[slot]);
+                band_store<T>(rz, z[slot], (int)(vcol + roff(top - u + NB)), 0);
                 z[slot] = ent[u];
                 const T tau = rw[u * RFL + NB];
                 if (tau != (T)0) {  // uniform: one reflector per step
