@@ -2313,8 +2313,9 @@ __global__ __launch_bounds__(256) void k_zfill(T *__restrict__ Z, int64_t n, int
 // normalised.  Eigenvalues of one block closer than 1e-9 ||T|| form a cluster,
 // whose first row computes all its vectors in turn, each orthogonalised
 // against the earlier ones (modified Gram-Schmidt) after every step.  The
-// iteration runs on T / ||T||; pivots are floored at eps.  Passes over the
-// block: the start vector is generated inside the first forward pass, the
+// iteration runs on T / ||T||; pivots are floored at eps, and divide by way
+// of their reciprocal (hardware estimate and two Newton steps, a few ulps).
+// Passes over the block: the start vector is generated inside the first forward pass, the
 // back substitution accumulates max |y| and |y|^2, and the normalisation is
 // applied inside the next pass (or the final store); rows move in chunks of
 // IV_CH, loads of a chunk issued before its arithmetic.  Scratch: 4 arrays of
@@ -2372,7 +2373,7 @@ __global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_
                         const bool sw = !(fabs(cd) >= fabs(dl));
                         const double p0 = sw ? dl : floor_piv(cd);
                         const double p1 = sw ? nd : cu, p2 = sw ? ndu : 0.0, pr = sw ? nr : cr;
-                        const double f = (sw ? cd : dl) / p0;
+                        const double f = (sw ? cd : dl) * recip64(p0);
                         u0[q * k] = p0;
                         u1[q * k] = p1;
                         u2[q * k] = p2;
@@ -2399,10 +2400,13 @@ __global__ __launch_bounds__(64) void k_invit(const T *__restrict__ band, int64_
                     a2[j] = ok ? u2[q * k] : 0.0;
                     yy[j] = ok ? y[q * k] : 0.0;
                 }
+                double ra[IV_CH];  // the pivots' reciprocals, off the recurrence
+#pragma unroll
+                for (int j = 0; j < IV_CH; ++j) ra[j] = recip64(a0[j]);
 #pragma unroll
                 for (int j = 0; j < IV_CH; ++j) {
                     if (j < cnt) {
-                        const double zq = (yy[j] - a1[j] * z1 - a2[j] * z2) / a0[j];
+                        const double zq = (yy[j] - a1[j] * z1 - a2[j] * z2) * ra[j];
                         yy[j] = zq;
                         z2 = z1;
                         z1 = zq;
