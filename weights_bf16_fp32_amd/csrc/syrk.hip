@@ -224,7 +224,7 @@ __device__ __forceinline__ int bg_slot(int f) { return (f ^ ((f >> 3) & 15)) * 8
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void syrk_bf16_big(const uint16_t *__restrict__ X, int64_t n, int64_t d,
                                                      int64_t ldx, float *__restrict__ C, int64_t ldc, float alpha,
-                                                     float beta, int64_t ntiles, int round)
+                                                     float beta, int64_t ntiles, int round, int64_t tile0, int splits)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BG_OP_U16];
     const int nt = (int)((d + BG_TILE - 1) / BG_TILE);
@@ -233,13 +233,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // loader: operand op, 8-feature block fb (0..31), 8-sample group kb (0..3)
     const int fb = tid & 31, kb = (tid >> 5) & 3, op = tid >> 7;
     const uint32_t ldb = (uint32_t)(ldx * 2);
-    const int64_t nsteps = (n + BG_BK - 1) / BG_BK;
+    // splits == 1: tiles 0 .. ntiles-1 in rounds (below); splits > 1: workgroup
+    // b takes tile tile0 + b / splits over its share of the K-steps and adds
+    // alpha times its partial product to C atomically (C was scaled by beta)
+    const int64_t nsteps_all = (n + BG_BK - 1) / BG_BK;
+    const int sp = splits > 1 ? (int)(blockIdx.x % splits) : 0;
+    const int64_t per = (nsteps_all + splits - 1) / splits;
+    const int64_t n_begin = min<int64_t>(n, sp * per * BG_BK);
+    const int64_t n_end = min<int64_t>(n, (sp + 1) * per * BG_BK);
+    const int64_t nsteps = (n_end - n_begin + BG_BK - 1) / BG_BK;
     // rounds of `round` consecutive workgroups run together (one per CU); in a
     // full round, the hardware deals workgroup b to XCD b % 8, and that XCD's
     // round/8 workgroups take consecutive tiles of the blocked order
     const int64_t b = blockIdx.x;
     const int64_t r0 = b / round * round;
-    const int64_t t = r0 + round <= ntiles ? r0 + (b % 8) * (round / 8) + (b - r0) / 8 : b;
+    const int64_t t = splits > 1 ? tile0 + b / splits
+                                 : (r0 + round <= ntiles ? r0 + (b % 8) * (round / 8) + (b - r0) / 8 : b);
     {
         int ti, tj;
         tri_tile_blocked(t, nt, ti, tj);
@@ -252,8 +261,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int e = 0; e < 8; ++e)
             voff[e] = fbase < d && loader ? (uint32_t)(kb * 8 + e) * ldb + (uint32_t)fbase * 2u : 0xFFFFFFF0u;
         u32x4_t vb[BG_PF][8];
-        auto gload = [&](u32x4_t (&v)[8], int64_t k0) {
-            const int64_t rem = (n - k0) * ldx * 2;
+        auto gload = [&](u32x4_t (&v)[8], int64_t kr) {
+            const int64_t k0 = n_begin + kr;  // first sample of the K-step
+            const int64_t rem = (n_end - k0) * ldx * 2;
             const int num = (int)(rem <= 0 ? 0 : (rem < 0x7FFFFFF0 ? rem : 0x7FFFFFF0));
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(X + (rem > 0 ? k0 : 0) * ldx), 0, num, 0x00020000);
@@ -364,6 +374,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         off[e] = ok ? lane_off + (uint32_t)(dr * ldc4 + b * 128) : 0x80000000u;
                     }
                     float v[16];
+                    if (splits > 1) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(alpha * acc[a][b][e], rc, (int)off[e], 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        continue;
+                    }
                     if (beta != 0.f) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
@@ -574,6 +591,25 @@ inline int64_t tri_count(int64_t t) { return t * (t + 1) / 2; }
 
 }  // namespace
 
+// C <- beta C on the lower triangle of 256 x 256 tiles tile0 .. tile0 + count - 1
+// (blocked order), before their split-K partial products are added
+__global__ __launch_bounds__(256) void syrk_scale_tiles(float *__restrict__ C, int64_t ldc, int64_t d, float beta,
+                                                        int64_t tile0)
+{
+    const int nt = (int)((d + BG_TILE - 1) / BG_TILE);
+    int ti, tj;
+    tri_tile_blocked(tile0 + blockIdx.x, nt, ti, tj);
+    const int64_t i0 = (int64_t)ti * BG_TILE, j0 = (int64_t)tj * BG_TILE;
+    const int64_t c = j0 + threadIdx.x;
+    for (int r = 0; r < BG_TILE; ++r) {
+        const int64_t i = i0 + r;
+        if (i < d && c < d && c <= i) {
+            float *p = C + i * ldc + c;
+            *p = beta == 0.f ? 0.f : beta * *p;
+        }
+    }
+}
+
 hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int64_t d, int64_t ldx, void *C, int ct,
                        int64_t ldc, double alpha, double beta)
 {
@@ -589,8 +625,22 @@ hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int
             if (hipStreamGetDevice(stream, &dev) == hipSuccess)
                 (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             const int round = cus >= 8 ? cus / 8 * 8 : 8;
-            hipLaunchKernelGGL(syrk_bf16_big, dim3((unsigned)big_tiles), dim3(256), 0, stream, (const uint16_t *)X, n,
-                               d, ldx, (float *)C, ldc, (float)alpha, (float)beta, big_tiles, round);
+            // full rounds as they are; a last round under half full is split along
+            // the samples (up to 4 ways, the partial products added atomically)
+            // so that its workgroups fill the chip
+            const int64_t full = big_tiles / round * round, tail = big_tiles - full;
+            const int splits = tail > 0 && tail <= round / 2 ? (int)std::min<int64_t>(4, round / tail) : 1;
+            const int64_t main = splits > 1 ? full : big_tiles;
+            if (main > 0)
+                hipLaunchKernelGGL(syrk_bf16_big, dim3((unsigned)main), dim3(256), 0, stream, (const uint16_t *)X, n,
+                                   d, ldx, (float *)C, ldc, (float)alpha, (float)beta, main, round, (int64_t)0, 1);
+            if (splits > 1) {
+                hipLaunchKernelGGL(syrk_scale_tiles, dim3((unsigned)tail), dim3(256), 0, stream, (float *)C, ldc, d,
+                                   (float)beta, full);
+                hipLaunchKernelGGL(syrk_bf16_big, dim3((unsigned)(tail * splits)), dim3(256), 0, stream,
+                                   (const uint16_t *)X, n, d, ldx, (float *)C, ldc, (float)alpha, (float)beta, tail,
+                                   round, full, splits);
+            }
         } else if (vec) {
             int64_t tiles = tri_count((d + SB_TILE - 1) / SB_TILE);
             hipLaunchKernelGGL(syrk_bf16_mfma, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint16_t *)X, n, d,
