@@ -388,61 +388,77 @@ def main():
     X = synth.ffn(n=n, d=d)
     log(f"ffn input generated in {time.time() - t0:.1f} s")
     Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
-    C = torch.empty((d, d), dtype=torch.float32, device=dev)
-    w = torch.empty((d,), dtype=torch.float32, device=dev)
-    ws = torch.empty((spec.eigvalsh_large_workspace(d, torch.float32),), dtype=torch.uint8, device=dev)
-    info = torch.zeros((1,), dtype=torch.int32, device=dev)
-    desc = torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev)
-    dws = torch.empty((spec.descriptors_workspace(d),), dtype=torch.uint8, device=dev)
+    # two batches in flight: step i runs on stream i % 2 with buffer set i % 2,
+    # so one step's SYRK and band reduction run beside the previous step's bulge
+    # chase (a latency chain on a quarter of the CUs); every step is the whole
+    # path over its batch
+    def buffers():
+        return {"C": torch.empty((d, d), dtype=torch.float32, device=dev),
+                "w": torch.empty((d,), dtype=torch.float32, device=dev),
+                "ws": torch.empty((spec.eigvalsh_large_workspace(d, torch.float32),), dtype=torch.uint8, device=dev),
+                "info": torch.zeros((1,), dtype=torch.int32, device=dev),
+                "desc": torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev),
+                "dws": torch.empty((spec.descriptors_workspace(d),), dtype=torch.uint8, device=dev)}
+    sets = [buffers(), buffers()]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
 
     phases = ["syrk", "eig_large", "desc"]
     ev = {p: ev_pair(torch) for p in phases}
 
-    def step(timed_step):
+    def step(b, events=False):
         def mark(p, i):
-            if timed_step:
+            if events:
                 ev[p][i].record()
         mark("syrk", 0)
-        spec.cov_accumulate(Xd, C, alpha=1.0 / n, beta=0.0)
+        spec.cov_accumulate(Xd, b["C"], alpha=1.0 / n, beta=0.0)
         mark("syrk", 1)
         mark("eig_large", 0)
-        spec.eigvalsh_large(C, w=w, ws=ws, info=info)
+        spec.eigvalsh_large(b["C"], w=b["w"], ws=b["ws"], info=b["info"])
         mark("eig_large", 1)
         mark("desc", 0)
-        spec.descriptors(w, n_samples=n, p_dim=d, k=1, out=desc, ws=dws, to_host=False)
+        spec.descriptors(b["w"], n_samples=n, p_dim=d, k=1, out=b["desc"], ws=b["dws"], to_host=False)
         mark("desc", 1)
 
+    def pipelined(i):
+        with torch.cuda.stream(streams[i % 2]):
+            step(sets[i % 2])
+
     for i in range(args.warmup):
-        step(False)
-        torch.cuda.synchronize()
-        log(f"warmup step {i + 1}/{args.warmup} done")
+        pipelined(i)
+        log(f"warmup step {i + 1}/{args.warmup} enqueued")
+    torch.cuda.synchronize()
+    log("warmup done")
     # inside the timed steps only the kernels launched once per step carry HIP
     # events (an event pair costs a few microseconds of device time, and the
     # reduction launches ~900 panel kernels per step); the per-launch kernels of
-    # the reduction are timed in one census step after them
+    # the reduction are timed in one census step after them, and the phases of
+    # one batch alone in a step of their own before it
     single = ["syrk", "bulge", "tridiag", "desc"]
     multi = ["symm", "syr2k", "panel"]
     spec.timing_enable(single)
-    acc = {p: 0.0 for p in phases}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        for p in phases:
-            acc[p] += ev[p][0].elapsed_time(ev[p][1])
+        pipelined(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kt = {k: spec.timing_read(k) for k in single}
+    spec.timing_enable([])
+    step(sets[0], events=True)  # one batch alone, phase events only
+    torch.cuda.synchronize()
+    acc = {p: ev[p][0].elapsed_time(ev[p][1]) for p in phases}
     spec.timing_enable(multi)
-    step(False)
+    step(sets[0])
     torch.cuda.synchronize()
     kt.update({k: tuple(x * args.steps for x in spec.timing_read(k)) for k in multi})  # as if over K steps
     spec.timing_enable([])
+    # the SYRK alone (in the timed steps it shares the GPU with a bulge chase)
+    syrk_alone_ms = timed(torch, lambda: spec.cov_accumulate(Xd, sets[0]["C"], alpha=1.0 / n, beta=0.0), 3)
     log(f"{args.steps} timed steps in {wall:.3f} s")
-    ms = {p: acc[p] / args.steps for p in phases}
+    info, desc = sets[0]["info"], sets[0]["desc"]
+    assert all(int(b["info"].cpu()[0]) == 0 for b in sets), "large eigensolver reported a failure"
+    ms = dict(acc)  # one batch alone (the census step)
     ms_step = wall * 1e3 / args.steps
-    assert int(info.cpu()[0]) == 0, "large eigensolver reported a failure"
     rec = np.frombuffer(desc.cpu().numpy().tobytes(), dtype=spec.DESC_DTYPE)[0]
 
     per_step = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps,
@@ -480,10 +496,14 @@ def main():
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16->f32", "data": "synthetic (seeded generator shaped like the FFN-width workload)",
         "config": {"workload": "ffn 65536x14336 bf16 -> SYRK C = X^T X / 65536 (f32) -> eigvalsh 14336 f32 "
-                               "-> descriptors", "covariance_rows": n, "covariance_dim": d},
+                               "-> descriptors", "covariance_rows": n, "covariance_dim": d,
+                   "batches_in_flight": 2},
+        "ms_per_step_one_batch_in_flight": sum(ms.values()),
         "syrk_tflops": syrk_tflops,
+        "syrk_alone": {"ms": syrk_alone_ms, "TFLOPs": n * d * (d + 1) / (syrk_alone_ms / 1e3) / 1e12,
+                       "frac_bf16_mfma": n * d * (d + 1) / (syrk_alone_ms / 1e3) / PEAK_BF16_MFMA},
         "eigensolves_per_s": 1e3 / ms_step,
-        "phases_ms": ms,
+        "phases_ms_one_batch": ms,
         "kernels_per_step": per_step,
         "n_above": int(rec["n_above"]),
         "roofline": roof,
