@@ -193,3 +193,27 @@ def test_eigh_swift_svd_shape(spec):
     C = (X.T.astype(np.float64) @ X.astype(np.float64)) / 6144
     cols = np.unique(np.linspace(0, 3275, 192).astype(int))
     _check(spec, C, np.float32, 3276, "f32 d=4096 k=3276", cols=cols)
+
+
+def test_eigh_max_size(spec):
+    """n = 8192, the vector path's limit (f32, k = 512): all eigenvalues against
+    LAPACK's fp64 eigvalsh of the same matrix; residual and orthogonality on
+    128 sampled columns (the full oracle decomposition would take minutes)."""
+    import torch
+    print_case("eigh_8192")
+    rng = np.random.default_rng(111)
+    d, k = 8192, 512
+    X = rng.standard_normal((2048, d)).astype(np.float32) * (1.0 / np.sqrt(1.0 + np.arange(d) / 128)).astype(np.float32)
+    A = ((X.T.astype(np.float64) @ X.astype(np.float64)) / 2048).astype(np.float32)
+    w, Z, info = _run(spec, A.astype(np.float64), np.float32, k)
+    A64 = A.astype(np.float64)
+    wr = np.linalg.eigvalsh(A64)[::-1]
+    normA = np.max(np.abs(wr))
+    cols = np.unique(np.linspace(0, k - 1, 128).astype(int))
+    Zs = Z[:, cols]
+    res = np.max(np.linalg.norm(A64 @ Zs - Zs * w[cols], axis=0)) / normA
+    orth = np.max(np.abs(Zs.T @ Zs - np.eye(len(cols))))
+    werr = np.max(np.abs(w - wr)) / normA
+    print(f"[eigh] f32 n=8192 k=512: residual {res:.2e} orth {orth:.2e} max |dw|/|A| {werr:.2e}", flush=True)
+    assert info == 0 and np.all(np.isfinite(Z))
+    assert werr <= 1e-4 and res <= 5e-5 and orth <= 5e-5
