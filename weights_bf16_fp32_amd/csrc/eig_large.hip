@@ -1651,30 +1651,58 @@ __device__ __forceinline__ void band_store(__amdgpu_buffer_rsrc_t rs, T x, int v
     }
 }
 
+// Bulge-task reductions on the 8 x 8 lane grid (lane = 8 I + J):
+// sum8 adds over the 8 lanes of a row group (J = 0..7: lane xor 1, xor 2, then
+// the half-row mirror, which pairs the two quads of the group); sum_cols adds
+// over the 8 lanes of a column group (I = 0..7: lane xor 8 by a row rotation of
+// 8, then xor 16 and xor 32 by the row swaps).  Every lane ends with the sum.
+template <typename T>
+__device__ __forceinline__ T sum8(T x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x;
+}
+template <typename T>
+__device__ __forceinline__ T sum_cols(T x)
+{
+    x += dpp<0x128>(x);
+    T a = x, b = x;
+    rowswap16(a, b);
+    x = a + b;
+    a = x;
+    b = x;
+    halfswap32(a, b);
+    return a + b;
+}
+
 template <typename T, int G, int CAPR>
 __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, int64_t n, int32_t *__restrict__ wm,
                                                         uint64_t spin_ticks, T *__restrict__ refl)
 {
     constexpr int LA = 2;  // the ring holds the lead's chunks up to the next step's (LA - 1 ahead)
     static_assert(CAPR % NB == 0 && (LA + 2 * G - 1) * NB <= CAPR, "ring too small");
-    constexpr int LDW = BW + 1;
+    constexpr int LDW = BW + 7;  // 71 = 8 (mod 32) - 1: row-group lanes land on distinct banks
     constexpr int RB = BW * sizeof(T);  // bytes per band row
     constexpr int QI = 4096 / RB;       // rows reachable from one base through the instruction offset
     __shared__ T WRbuf[NB + CAPR * LDW + 64];
     T *const WR = WRbuf + NB;  // NB guard entries before the first ring row
     constexpr int SINK = CAPR * LDW;  // 64 entries after the ring: target of masked-off stores
     __shared__ T vsw[G][NB];
-    __shared__ T red[G][NB];
     __shared__ T w2s[G][NB];
     __shared__ int abort_flag[2];  // set at step t in entry t & 1, read by every wave after that step
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int ci = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: sweep, task and row counts stay scalar
+    const int I = lane >> 3, J = lane & 7;  // compute waves: row group and column group of the lane
     const int nn = (int)n;
     const int nsw = nn - 2;
     int32_t *err = wm + n;
-    const int g = blockIdx.x;
-    const int s0 = g * G;
-    const int Ge = min(G, nsw - s0);
+    const int ngroups = (nsw + G - 1) / G;
+    // a persistent grid: workgroup b runs groups b, b + gridDim.x, ... in turn
+    // (each group's lifetime is far shorter than gridDim.x group start offsets,
+    // so the next group of a workgroup is due only after its previous one ends)
+    int g = blockIdx.x, s0 = 0, Ge = 0, ntl = 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(band, 0, nn * RB, 0x00020000);
     // ring slot of row r, counted from the group's first row so that the lead's
     // NB-row chunks never wrap
@@ -1683,7 +1711,6 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     // a task (s, k) reads and writes only rows s + 1 + k NB .. s + (k + 1) NB
     auto minrow = [&](int s, int k) { return k <= 0 ? s + 1 : s + 1 + k * NB; };
     auto lastrow = [&](int s, int k) { return min(s + (k + 1) * NB, nn - 1); };
-    const int ntl = ntasks(s0);  // tasks of the lead sweep
     // rows loaded into the ring once the lead's task k has been fetched
     auto loaded_to = [&](int k) { return k < 0 ? s0 + 1 : lastrow(s0, min(k, ntl - 1)) + 1; };
 
@@ -1746,6 +1773,10 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
         }
     };
 
+    for (; g < ngroups; g += gridDim.x) {
+    s0 = g * G;
+    Ge = min(G, nsw - s0);
+    ntl = ntasks(s0);  // tasks of the lead sweep
     if (tid < 2) abort_flag[tid] = 0;
     __syncthreads();
     // ---- prologue: the lead's first chunk
@@ -1763,6 +1794,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
 
     int wst = s0 + 1;  // rows below wst have been handed to the storer
     int wmk = s0 + 1;  // rows below wmk are released
+    int wpoll = 0;       // loader: the previous group's watermark as last requested
     T taup = 0;          // compute wave: tau of the previous reflector of its sweep
     int ab = 0;          // abort flag of the previous step
     // the group's last sweep ends last: its last task is the group's last step
@@ -1770,13 +1802,19 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     for (int t = 2 * s0; t < t_end; ++t) {
         const int k0 = t - 2 * s0;
         if (wv == G) {
-            // the lead's chunk for the next step
+            // the lead's chunk for the next step.  The previous group's watermark
+            // was requested behind the last step's row loads, so it has usually
+            // arrived: if it already covers the chunk the rows are loaded at
+            // once (watermarks only grow, so an older value is a safe bound),
+            // else the loader waits as at the start.
             const int kn = k0 + LA - 1;
             if (kn < ntl) {
                 const int lo = loaded_to(kn - 1), hi = loaded_to(kn);
-                if (wait_rows(hi - 1, t & 1)) {
+                const int seen = g > 0 ? __builtin_amdgcn_readfirstlane(wpoll) : nn;
+                if (seen > hi - 1 || wait_rows(hi - 1, t & 1)) {
                     T ld[NB];
                     load_chunk(lo, ld);
+                    if (g > 0) wpoll = cload(wm + g - 1);  // for the next step, in flight behind the rows
                     write_chunk(lo, ld);
                 }
             }
@@ -1792,52 +1830,81 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
             const int s = s0 + wv;
             const int k = t - 2 * s;
             if (wv < Ge && k >= 0 && k < ntasks(s)) {
-                // Lane (ci, h) holds row r0 + ci of the task's block in registers: the
-                // columns h*16 .. h*16+15 of O = A[r0.., c0 .. c0+NB) (k > 0) and of the
-                // lower triangle of the diagonal block D = A[r0.., r0..].  All of it lies
-                // in the lane's own ring row at fixed offsets, so the loads issue back to
-                // back; entries outside the task are masked after loading (the guard
-                // before the ring keeps every offset inside the array).
+                // Lane (I, J) = (lane / 8, lane % 8) holds rows I + 8a and columns
+                // J + 8b (a, b = 0..3) of the task's two blocks: O = A[r0.., c0 ..
+                // c0 + NB) (k > 0) and the whole symmetric diagonal block D =
+                // A[r0.., r0..] (entries above its diagonal read from their lower
+                // mirror).  Sums along a row reduce over the 8 lanes of a row group
+                // (three DPP adds), sums down a column over the 8 lanes of a column
+                // group (a DPP row rotation and the two row swaps).  With the ring
+                // stride LDW = 8 (mod 32) - 1 every one of these block accesses
+                // hits distinct banks (or the same word, for the two copies of a
+                // diagonal-block entry).
                 const int r0 = s + 1 + k * NB;
                 const int L = lastrow(s, k) - r0 + 1;
-                const bool rowok = ci < L;
-                const int rb = slot(r0 + ci) * LDW;  // ring slot of row r0 + ci
-                const int e = rowok ? ci - h * 16 : -1;          // D column c of this lane is in the lower triangle iff c <= e
-                T *v = vsw[wv];
-                T o[16], dd[16], vp[16];
+                const int sl0 = slot(r0);
+                int rbI[4], rbJ[4];  // ring offsets of rows r0 + I + 8a and r0 + J + 8a
+                bool rv[4], cv[4];   // row I + 8a, column J + 8a inside the task
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    dd[c] = WR[rb + ci - h * 16 - c];
-                    o[c] = WR[rb + NB + ci - h * 16 - c];
-                    vp[c] = v[h * 16 + c];  // the previous task's reflector
+                for (int a = 0; a < 4; ++a) {
+                    int x = sl0 + I + 8 * a;
+                    x -= x >= CAPR ? CAPR : 0;
+                    rbI[a] = x * LDW;
+                    int y = sl0 + J + 8 * a;
+                    y -= y >= CAPR ? CAPR : 0;
+                    rbJ[a] = y * LDW;
+                    rv[a] = I + 8 * a < L;
+                    cv[a] = J + 8 * a < L;
                 }
-                const T xs = WR[rb + ci + 1];  // column s
-                const T dg = rowok ? WR[rb] : (T)0;
+                T *v = vsw[wv];
+                T o[4][4], dd[4][4], vp[4];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) dd[c] = c <= e ? dd[c] : (T)0;
+                for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        o[a][b] = WR[rbI[a] + NB + I - J + 8 * (a - b)];
+                        if (a > b)
+                            dd[a][b] = WR[rbI[a] + I - J + 8 * (a - b)];
+                        else if (a < b)
+                            dd[a][b] = WR[rbJ[b] + J - I + 8 * (b - a)];
+                        else
+                            dd[a][b] = WR[I >= J ? rbI[a] + I - J : rbJ[a] + J - I];
+                    }
+                    vp[a] = v[J + 8 * a];  // the previous task's reflector at column J + 8a
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) dd[a][b] = rv[a] && cv[b] ? dd[a][b] : (T)0;
                 if (L < NB) {
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) o[c] = rowok ? o[c] : (T)0;
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) o[a][b] = rv[a] ? o[a][b] : (T)0;
                 }
-                T x;
+                T x[4];  // the column the reflector annihilates (rows I + 8a; lanes J == 0 for k > 0)
                 if (k == 0) {
-                    x = rowok ? xs : (T)0;
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) x[a] = rv[a] ? WR[rbI[a] + I + 8 * a + 1] : (T)0;  // column s
                 } else {
                     // right: O <- O (I - taup vp vp^T)
                     if (taup != 0) {
-                        T u = 0;
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) u += o[c] * vp[c];
-                        u = taup * pair32_sum(u);
+                        for (int a = 0; a < 4; ++a) {
+                            const T u = taup * sum8((o[a][0] * vp[0] + o[a][1] * vp[1]) + (o[a][2] * vp[2] + o[a][3] * vp[3]));
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) o[c] -= u * vp[c];
+                            for (int b = 0; b < 4; ++b) o[a][b] -= u * vp[b];
+                        }
                     }
-                    x = from_lower_half(o[0]);  // column c0, held by the lanes of half 0
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) x[a] = o[a][0];  // column c0
                 }
                 // reflector (I - tau v v^T) x = mu e_0, v_0 = 1
-                const T sigma = half_sum(ci >= 1 ? x * x : (T)0);
-                const T x0 = readlane0(x);
-                T tau_k = 0, mu = 0, vi = 0;
+                T sp = (I > 0 ? x[0] * x[0] : (T)0) + x[1] * x[1] + (x[2] * x[2] + x[3] * x[3]);
+                const T sigma = readlane0(sum_cols(sp));  // lane 0 sums column group J = 0
+                const T x0 = readlane0(x[0]);
+                T tau_k = 0, mu = 0;
+                T vr[4] = {0, 0, 0, 0};  // v at rows I + 8a (lanes J == 0 until exchanged)
                 if (sigma > 0) {
                     mu = sqrt(x0 * x0 + sigma);
                     // v_0 and 1/v_0 need not be exact: tau below is computed from the
@@ -1845,7 +1912,9 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     // annihilates is set to mu e_0 explicitly
                     const T v0 = x0 <= 0 ? x0 - mu : -sigma * recip(x0 + mu);
                     const T iv0 = recip(v0);
-                    vi = ci == 0 ? (T)1 : x * iv0;
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) vr[a] = x[a] * iv0;
+                    if (I == 0) vr[0] = 1;
                     // tau = 2 / v^T v with v^T v = 1 + sigma iv0^2, the same iv0 that
                     // scales v: I - tau v v^T is orthogonal up to the rounding of the
                     // entries (a tau from v0 alone, whose reciprocal is rounded
@@ -1853,66 +1922,81 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     tau_k = (T)2 / ((T)1 + sigma * iv0 * iv0);
                 }
                 wave_sync();
-                if (h == 0) v[ci] = vi;
-                if (refl != nullptr && h == 0) {  // kept for the eigenvectors (rows past the band end: v = 0)
-                    T *rp = refl + (refl_index(n, s) + k) * RFL;
-                    rp[ci] = vi;
-                    if (ci == 0) rp[NB] = tau_k;
-                }
-                if (tau_k != 0) {
-                    // column sums, reduced over the 32 rows of each half (lane ci ends
-                    // with column h*16 + ci/2): w = O^T v and the part of D v that
-                    // comes from the upper triangle, sum_{j >= i} D[j][i] v_j
-                    T q[16];
-                    if (k > 0) {
+                if (J == 0) {
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) q[c] = vi * o[c];
-                        const T wj = reduce_scatter16(q, ci);
-                        if ((ci & 1) == 0) red[wv][h * 16 + (ci >> 1)] = wj;
+                    for (int a = 0; a < 4; ++a) v[I + 8 * a] = vr[a];
+                    if (refl != nullptr) {  // kept for the eigenvectors (rows past the band end: v = 0)
+                        T *rp = refl + (refl_index(n, s) + k) * RFL;
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) rp[I + 8 * a] = vr[a];
+                        if (I == 0) rp[NB] = tau_k;
                     }
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) q[c] = vi * dd[c];
-                    const T pj = reduce_scatter16(q, ci);
-                    if ((ci & 1) == 0) w2s[wv][h * 16 + (ci >> 1)] = pj;
                 }
                 wave_sync();
-                T vr[16];
+                T vc[4];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) vr[c] = v[h * 16 + c];
+                for (int a = 0; a < 4; ++a) {
+                    vr[a] = v[I + 8 * a];
+                    vc[a] = v[J + 8 * a];
+                }
                 if (tau_k != 0) {
-                    const T pcol = w2s[wv][ci];
                     if (k > 0) {
-                        const T tv = tau_k * vi;
+                        // left: O <- (I - tau v v^T) O, then the annihilated column is mu e_0
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) o[c] -= tv * red[wv][h * 16 + c];
-                        if (h == 0) o[0] = ci == 0 ? mu : (T)0;
+                        for (int b = 0; b < 4; ++b) {
+                            const T wb = tau_k * sum_cols((vr[0] * o[0][b] + vr[1] * o[1][b]) + (vr[2] * o[2][b] + vr[3] * o[3][b]));
+#pragma unroll
+                            for (int a = 0; a < 4; ++a) o[a][b] -= vr[a] * wb;
+                        }
+                        if (J == 0) {
+#pragma unroll
+                            for (int a = 0; a < 4; ++a) o[a][0] = 0;
+                            if (I == 0) o[0][0] = mu;
+                        }
                     }
                     // two-sided on D: p = tau D v, w = p - (tau/2)(p^T v) v, D -= v w^T + w v^T
-                    T pp = 0;
+                    T p[4];
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) pp += dd[c] * vr[c];
-                    pp = tau_k * (pair32_sum(pp) + pcol - dg * vi);
-                    const T pv = half_sum(pp * vi);
-                    const T w2 = pp - (T)0.5 * tau_k * pv * vi;
-                    wave_sync();
-                    if (h == 0) w2s[wv][ci] = w2;
-                    wave_sync();
+                    for (int a = 0; a < 4; ++a)
+                        p[a] = tau_k * sum8((dd[a][0] * vc[0] + dd[a][1] * vc[1]) + (dd[a][2] * vc[2] + dd[a][3] * vc[3]));
+                    const T pv = sum_cols((p[0] * vr[0] + p[1] * vr[1]) + (p[2] * vr[2] + p[3] * vr[3]));
+                    T w2[4];
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) dd[c] -= vi * w2s[wv][h * 16 + c] + w2 * vr[c];
-                }
-                if (rowok) {
-                    if (k == 0) {
-                        if (tau_k != 0) WR[rb + ci + 1] = ci == 0 ? mu : (T)0;
-                    } else {
+                    for (int a = 0; a < 4; ++a) w2[a] = p[a] - (T)0.5 * tau_k * pv * vr[a];
+                    if (J == 0) {
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) WR[rb + NB + ci - h * 16 - c] = o[c];
+                        for (int a = 0; a < 4; ++a) w2s[wv][I + 8 * a] = w2[a];
                     }
+                    wave_sync();
+                    T wc[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) wc[b] = w2s[wv][J + 8 * b];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) dd[a][b] -= vr[a] * wc[b] + w2[a] * vc[b];
+                }
+                // stores: masked-off entries go to the sink, so they need no branches
+                if (k == 0) {
+                    if (tau_k != 0 && J == 0) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+                            WR[rv[a] ? rbI[a] + I + 8 * a + 1 : SINK + lane] = (I == 0 && a == 0) ? mu : (T)0;
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) WR[rv[a] ? rbI[a] + NB + I - J + 8 * (a - b) : SINK + lane] = o[a][b];
                 }
                 if (tau_k != 0) {
-                    // entries above the block's diagonal go to the sink, so the 16
-                    // stores need no branches
+                    // the lower triangle: entries with a > b, and a == b where I >= J
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) WR[c <= e ? rb + ci - h * 16 - c : SINK + lane] = dd[c];
+                    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                        for (int b = 0; b < a; ++b) WR[rv[a] ? rbI[a] + I - J + 8 * (a - b) : SINK + lane] = dd[a][b];
+                        WR[rv[a] && I >= J ? rbI[a] + I - J : SINK + lane] = dd[a][a];
+                    }
                 }
                 taup = tau_k;
             }
@@ -1941,6 +2025,8 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
         store_rows(wst, nn);
         __builtin_amdgcn_s_waitcnt(0);
         if (lane == 0) cstore(wm + g, (int32_t)nn);
+    }
+    __syncthreads();  // the ring and the flags are reused by the workgroup's next group
     }
 }
 
@@ -3053,10 +3139,14 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         constexpr int CAPR = sizeof(T) == 4 ? 288 : 256;
         const int64_t nsw = n - 2;
         const int64_t ngroups = cdiv_h(nsw, G);
+        // about n / (2 G NB) groups are active at once (a group lives for the
+        // ~n / NB steps of its lead sweep, groups start 2 G steps apart): a
+        // persistent grid of that many plus a margin keeps the other CUs free
+        const int64_t nwg = std::min<int64_t>(ngroups, n / (2 * G * NB) * 5 / 4 + 16);
         const uint64_t spin_ticks = 100000000ull * 10;  // 10 s at the 100 MHz real-time counter
         {
             KTimer kt(st, SPEC_KT_BULGE);
-            hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)ngroups), dim3(64 * (G + 2)), 0, st, b.band, n,
+            hipLaunchKernelGGL((k_bulge<T, G, CAPR>), dim3((unsigned)nwg), dim3(64 * (G + 2)), 0, st, b.band, n,
                                b.prog, spin_ticks, vec != nullptr ? vec->refl : (T *)nullptr);
         }
         LAUNCH_OK();
