@@ -297,15 +297,43 @@ def phase_rows(torch, spec, synth, dev, with_cpu, which=("tiny", "eigentrack", "
             acc["eig_large_f64"] += e[1].elapsed_time(e[2])
         acc["desc"] = timed(torch, lambda: spec.descriptors(w5, mode=spec.MODE_SINGULAR, n_samples=4096, p_dim=4096,
                                                             k=1, out=d5, ws=dss5, to_host=False), 5)
-        tot = sum(acc.values())
+        tot_seq = sum(acc.values())
+        # the 32 layers as one batch with two solves in flight: layer l runs on
+        # stream l % 2 with its own C and workspace (each solve is a latency
+        # chain, two of them share the GPU), descriptors of all 32 spectra after
+        C5b, ws5b, i5b = [C5, torch.empty_like(C5)], [ws5, torch.empty_like(ws5)], [i5, torch.zeros_like(i5)]
+        st5 = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+
+        def s3_batch():
+            cur = torch.cuda.current_stream()
+            for s_ in st5:
+                s_.wait_stream(cur)
+            for l in range(32):
+                j = l % 2
+                with torch.cuda.stream(st5[j]):
+                    spec.cov_accumulate(Wl[l], C5b[j], alpha=1.0, beta=0.0)
+                    spec.eigvalsh_large(C5b[j], w=w5[l], ws=ws5b[j], info=i5b[j])
+            for s_ in st5:
+                cur.wait_stream(s_)
+            spec.descriptors(w5, mode=spec.MODE_SINGULAR, n_samples=4096, p_dim=4096, k=1, out=d5, ws=dss5,
+                             to_host=False)
+
+        s3_batch()  # warm-up (creates the second stream's state)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s3_batch()
+        torch.cuda.synchronize()
+        tot = (time.perf_counter() - t0) * 1e3
+        assert all(int(x.cpu()[0]) == 0 for x in i5b)
         f = 32 * 4096.0 * 4096 * 4097
         rows["s3_32x4096x4096"] = {
-            "ms": tot, "phases_ms": acc, "layers": 32, "layer_spectra_per_s": 32e3 / tot,
+            "ms": tot, "two_in_flight": True, "ms_one_at_a_time": tot_seq, "phases_ms_one_at_a_time": acc,
+            "layers": 32, "layer_spectra_per_s": 32e3 / tot,
             "syrk_f64": {"bound": "mfma", "achieved_TFLOPs": f / (acc["syrk_f64"] / 1e3) / 1e12,
                          "frac": f / (acc["syrk_f64"] / 1e3) / PEAK_F64_MFMA},
             "eig_4096_f64_per_s": 32e3 / acc["eig_large_f64"]}
         assert int(i5.cpu()[0]) == 0
-        log(f"s3: {tot:.1f} ms ({acc})")
+        log(f"s3: {tot:.1f} ms two in flight, {tot_seq:.1f} ms one at a time ({acc})")
         del Wl, C5, w5, ws5
     return rows
 
@@ -373,6 +401,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--in-flight", type=int, default=2, help="batches in flight on their own streams in the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the other workloads' phase rows")
     ap.add_argument("--no-postproc", action="store_true", help="skip the rows beyond the hot path")
@@ -394,10 +423,10 @@ def main():
     X = synth.ffn(n=n, d=d)
     log(f"ffn input generated in {time.time() - t0:.1f} s")
     Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
-    # two batches in flight: step i runs on stream i % 2 with buffer set i % 2,
-    # so one step's SYRK and band reduction run beside the previous step's bulge
-    # chase (a latency chain on a quarter of the CUs); every step is the whole
-    # path over its batch
+    # F batches in flight: step i runs on stream i % F with buffer set i % F,
+    # so one step's SYRK and band reduction run beside the previous steps' bulge
+    # chases (latency chains on a quarter of the CUs) and panel factorisations;
+    # every step is the whole path over its batch
     def buffers():
         return {"C": torch.empty((d, d), dtype=torch.float32, device=dev),
                 "w": torch.empty((d,), dtype=torch.float32, device=dev),
@@ -405,8 +434,9 @@ def main():
                 "info": torch.zeros((1,), dtype=torch.int32, device=dev),
                 "desc": torch.empty((1, spec.DESC_DTYPE.itemsize), dtype=torch.uint8, device=dev),
                 "dws": torch.empty((spec.descriptors_workspace(d),), dtype=torch.uint8, device=dev)}
-    sets = [buffers(), buffers()]
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    F = args.in_flight
+    sets = [buffers() for _ in range(F)]
+    streams = [torch.cuda.Stream() for _ in range(F)]  # default priority
 
     phases = ["syrk", "eig_large", "desc"]
     ev = {p: ev_pair(torch) for p in phases}
@@ -426,12 +456,15 @@ def main():
         mark("desc", 1)
 
     def pipelined(i):
-        with torch.cuda.stream(streams[i % 2]):
-            step(sets[i % 2])
+        with torch.cuda.stream(streams[i % F]):
+            step(sets[i % F])
 
-    for i in range(args.warmup):
+    # every stream of the pipeline runs at least once before the timed steps
+    # (its first solve creates the stream's helper for the panel factorisations)
+    W = max(args.warmup, F)
+    for i in range(W):
         pipelined(i)
-        log(f"warmup step {i + 1}/{args.warmup} enqueued")
+        log(f"warmup step {i + 1}/{W} enqueued")
     torch.cuda.synchronize()
     log("warmup done")
     # inside the timed steps only the kernels launched once per step carry HIP
@@ -445,7 +478,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        pipelined(args.warmup + i)
+        pipelined(W + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kt = {k: spec.timing_read(k) for k in single}
@@ -498,12 +531,12 @@ def main():
         "metric": METRIC,
         "value": 1e3 / ms_step,
         "unit": "eigensolves/s (65536x14336 bf16 -> 14336^2 f32 covariance -> all eigenvalues + descriptors)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": W,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16->f32", "data": "synthetic (seeded generator shaped like the FFN-width workload)",
         "config": {"workload": "ffn 65536x14336 bf16 -> SYRK C = X^T X / 65536 (f32) -> eigvalsh 14336 f32 "
                                "-> descriptors", "covariance_rows": n, "covariance_dim": d,
-                   "batches_in_flight": 2},
+                   "batches_in_flight": F},
         "ms_per_step_one_batch_in_flight": sum(ms.values()),
         "syrk_tflops": syrk_tflops,
         "syrk_alone": {"ms": syrk_alone_ms, "TFLOPs": n * d * (d + 1) / (syrk_alone_ms / 1e3) / 1e12,

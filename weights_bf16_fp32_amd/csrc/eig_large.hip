@@ -2882,15 +2882,19 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
 // the look-ahead on every panel).
 constexpr int64_t LOOKAHEAD_MIN = 6144;
 
-// The helper stream of stage 1 (one per device, default priority, created on
-// first use) and the two events that order it with the caller's stream.
+// The helper stream of stage 1 (one per caller stream and device, default
+// priority, created on first use) and the two events that order it with the
+// caller's stream.  Solves on different caller streams get different helpers,
+// so their panel factorisations overlap instead of queueing on one stream.
 struct Aux {
-    hipStream_t s = nullptr;
+    hipStream_t key = nullptr;  // the caller's stream
+    int dev = -1;
+    hipStream_t s = nullptr;    // nullptr: free slot
     hipEvent_t fork = nullptr, join = nullptr;
     std::mutex mu;
 };
-constexpr int AUX_DEVICES = 64;
-Aux aux_dev[AUX_DEVICES];
+constexpr int AUX_SLOTS = 64;
+Aux aux_tab[AUX_SLOTS];
 std::mutex aux_init_mu;
 
 hipError_t aux_for(hipStream_t st, Aux **out)
@@ -2898,28 +2902,47 @@ hipError_t aux_for(hipStream_t st, Aux **out)
     hipDevice_t dev = 0;
     hipError_t e = hipStreamGetDevice(st, &dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= AUX_DEVICES) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> g(aux_init_mu);
-    Aux &a = aux_dev[dev];
-    if (a.s == nullptr) {
-        int cur = 0;
-        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
-        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-        hipStream_t s = nullptr;
-        hipEvent_t f = nullptr, j = nullptr;
-        e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
-        if (cur != dev) {
-            hipError_t e2 = hipSetDevice(cur);
-            if (e == hipSuccess) e = e2;
+    Aux *fallback = nullptr;
+    for (Aux &a : aux_tab) {
+        if (a.s != nullptr && a.dev == dev) {
+            if (a.key == st) {
+                *out = &a;
+                return hipSuccess;
+            }
+            if (fallback == nullptr) fallback = &a;
         }
-        if (e != hipSuccess) return e;
-        a.fork = f;
-        a.join = j;
-        a.s = s;
     }
-    *out = &a;
+    Aux *slot = nullptr;
+    for (Aux &a : aux_tab)
+        if (a.s == nullptr) {
+            slot = &a;
+            break;
+        }
+    if (slot == nullptr) {  // table full: share a helper of this device (its calls then queue on it)
+        if (fallback == nullptr) return hipErrorOutOfMemory;
+        *out = fallback;
+        return hipSuccess;
+    }
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (cur != dev) {
+        hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    slot->key = st;
+    slot->dev = dev;
+    slot->fork = f;
+    slot->join = j;
+    slot->s = s;
+    *out = slot;
     return hipSuccess;
 }
 
