@@ -1410,11 +1410,12 @@ __global__ __launch_bounds__(256) void k_syr2k_cols(T *__restrict__ A, int64_t l
 }
 
 // ---- A22 -= V Z^T + Z V^T on lower 128 x 128 tiles
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int S2_T = 128;
 constexpr int S2_K = 2 * NB;
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, int m, const T *__restrict__ V,
+__global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void k_syr2k(T *__restrict__ A, int64_t lda, int m, const T *__restrict__ V,
                                                const T *__restrict__ Z)
 {
     __shared__ T Ls[S2_T * (S2_K + 1)];
@@ -1437,67 +1438,131 @@ __global__ __launch_bounds__(256) void k_syr2k(T *__restrict__ A, int64_t lda, i
         const int64_t extent = ((int64_t)(S2_T - 1) * lda + S2_T) * 4;               // the whole tile, < 2^31
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(A + corner, 0, (int)(span < extent ? span : extent), 0x00020000);
-        const int rl = wm * 64 + (lane >> 5) * 4, cl = wn * 64 + (lane & 31);  // lane's first row and column
+        // Off the diagonal the product is formed transposed (the MFMA takes R
+        // as its first operand), so a lane holds one tile row and 4 x 4
+        // consecutive columns: its old values come and go as 16-byte accesses
+        // (row wm*64 + qa*32 + lane%32, columns wn*64 + qb*32 + 8 jb + 4 (lane/32)
+        // .. + 3).  A diagonal tile keeps the untransposed layout (a lane holds
+        // one column, 16 rows) and masks the part above the diagonal element
+        // by element.
+        const int rT = wm * 64 + (lane & 31), cT = wn * 64 + 4 * (lane >> 5);
+        auto voff = [&](int qa, int qb, int jb) {
+            return (uint32_t)((rT + qa * 32) * (int)lda + cT + qb * 32 + 8 * jb) * 4u;
+        };
+        const int rl = wm * 64 + (lane >> 5) * 4, cl = wn * 64 + (lane & 31);  // diagonal: lane's first row and column
         const uint32_t vbase = (uint32_t)(rl * (int)lda + cl) * 4u;
         // element (qa, qb, e): row rl + qa*32 + (e>>2)*8 + (e&3), column cl + qb*32
         auto eoff = [&](int qa, int qb, int e) {
             const int dr = qa * 32 + (e >> 2) * 8 + (e & 3);
-            const bool ok = !diag || rl + dr >= cl + qb * 32;
+            const bool ok = rl + dr >= cl + qb * 32;
             return ok ? vbase + (uint32_t)(dr * (int)lda + qb * 32) * 4u : 0x80000000u;
         };
-        // L = [V | Z] rows i0.., R = [Z | V] rows j0..
+        // L = [V | Z] rows i0.., R = [Z | V] rows j0.. (16-byte loads, rows
+        // clamped to m - 1 and masked after, so all stay in flight together)
+        constexpr int SQ = S2_T * NB / (4 * 256);
+        {
+            float4 v_i[SQ], z_i[SQ], v_j[SQ], z_j[SQ];
 #pragma unroll
-        for (int q = 0; q < S2_T * NB / 256; ++q) {
-            const int idx = tid + 256 * q, r = idx / NB, c = idx % NB;
-            const int i = i0 + r, j = j0 + r;
-            // rows clamped to m - 1 and masked: unconditional loads stay in flight
-            // together (a load under a branch would wait for all before it)
-            const int64_t ic = min(i, m - 1), jc = min(j, m - 1);
-            const T v_i = V[ic * NB + c], z_i = Z[ic * NB + c], v_j = V[jc * NB + c], z_j = Z[jc * NB + c];
-            const T vi = i < m ? v_i : (T)0, zi = i < m ? z_i : (T)0;
-            const T vj = j < m ? v_j : (T)0, zj = j < m ? z_j : (T)0;
-            Ls[r * (S2_K + 1) + c] = vi;
-            Ls[r * (S2_K + 1) + NB + c] = zi;
-            Rs[r * (S2_K + 1) + c] = zj;
-            Rs[r * (S2_K + 1) + NB + c] = vj;
+            for (int q = 0; q < SQ; ++q) {
+                const int idx = tid + 256 * q, r = idx >> 3, c4 = (idx & 7) * 4;
+                const int64_t ic = min(i0 + r, m - 1), jc = min(j0 + r, m - 1);
+                v_i[q] = *reinterpret_cast<const float4 *>(V + ic * NB + c4);
+                z_i[q] = *reinterpret_cast<const float4 *>(Z + ic * NB + c4);
+                v_j[q] = *reinterpret_cast<const float4 *>(V + jc * NB + c4);
+                z_j[q] = *reinterpret_cast<const float4 *>(Z + jc * NB + c4);
+            }
+#pragma unroll
+            for (int q = 0; q < SQ; ++q) {
+                const int idx = tid + 256 * q, r = idx >> 3, c4 = (idx & 7) * 4;
+                const bool iok = i0 + r < m, jok = j0 + r < m;
+                const float vi[4] = {v_i[q].x, v_i[q].y, v_i[q].z, v_i[q].w};
+                const float zi[4] = {z_i[q].x, z_i[q].y, z_i[q].z, z_i[q].w};
+                const float vj[4] = {v_j[q].x, v_j[q].y, v_j[q].z, v_j[q].w};
+                const float zj[4] = {z_j[q].x, z_j[q].y, z_j[q].z, z_j[q].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    Ls[r * (S2_K + 1) + c4 + u] = iok ? vi[u] : 0.f;
+                    Ls[r * (S2_K + 1) + NB + c4 + u] = iok ? zi[u] : 0.f;
+                    Rs[r * (S2_K + 1) + c4 + u] = jok ? zj[u] : 0.f;
+                    Rs[r * (S2_K + 1) + NB + c4 + u] = jok ? vj[u] : 0.f;
+                }
+            }
         }
         __syncthreads();
         if (!live) return;
-        // the old values are requested after the staging (memory counters
-        // retire in issue order, so earlier they would hold up the LDS stores)
-        // and are in flight while the MFMAs run
-        float old[2][2][16];
-#pragma unroll
-        for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    old[qa][qb][e] =
-                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)eoff(qa, qb, e), 0, 0));
+        // the old values are requested after the staging and are in flight
+        // while the MFMAs run
         f32x16_t acc[2][2] = {};
-#pragma unroll 4
-        for (int kk = 0; kk < S2_K; kk += 2) {
-            float a[2], b[2];
+        if (!diag) {
+            float4 oldv[2][2][4];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                a[q] = Ls[(wm * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
-                b[q] = Rs[(wn * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
+            for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+                        oldv[qa][qb][jb] = __builtin_bit_cast(
+                            float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff(qa, qb, jb), 0, 0));
+#pragma unroll 4
+            for (int kk = 0; kk < S2_K; kk += 2) {
+                float a[2], b[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    a[q] = Ls[(wm * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
+                    b[q] = Rs[(wn * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
+                }
+#pragma unroll
+                for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        acc[qa][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[qb], a[qa], acc[qa][qb], 0, 0, 0);
             }
 #pragma unroll
             for (int qa = 0; qa < 2; ++qa)
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
-                    acc[qa][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) {
+                        const float4 o = oldv[qa][qb][jb];
+                        const float4 nv = make_float4(o.x - acc[qa][qb][4 * jb], o.y - acc[qa][qb][4 * jb + 1],
+                                                      o.z - acc[qa][qb][4 * jb + 2], o.w - acc[qa][qb][4 * jb + 3]);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, nv), rs,
+                                                               (int)voff(qa, qb, jb), 0, 0);
+                    }
+        } else {
+            float old[2][2][16];  // masked-off elements (the dead quadrant included) read as zero
+#pragma unroll
+            for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        old[qa][qb][e] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)eoff(qa, qb, e), 0, 0));
+#pragma unroll 4
+            for (int kk = 0; kk < S2_K; kk += 2) {
+                float a[2], b[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    a[q] = Ls[(wm * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
+                    b[q] = Rs[(wn * 64 + q * 32 + (lane & 31)) * (S2_K + 1) + kk + (lane >> 5)];
+                }
+#pragma unroll
+                for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        acc[qa][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[qa], b[qb], acc[qa][qb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __builtin_bit_cast(uint32_t, old[qa][qb][e] - acc[qa][qb][e]), rs, (int)eoff(qa, qb, e),
+                            0, 0);
         }
-#pragma unroll
-        for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(uint32_t, old[qa][qb][e] - acc[qa][qb][e]), rs, (int)eoff(qa, qb, e), 0, 0);
     } else {
         // L = [V | Z] rows i0.., R = [Z | V] rows j0..
 #pragma unroll
