@@ -22,12 +22,14 @@
 //   builds a reflector from its first column, applies it from the left and to
 //   the diagonal block from both sides.  Task (s, k) may run once task
 //   (s-1, k+1) is done, so the tasks (s, t - 2s) of one time step t are
-//   independent.  A workgroup runs G consecutive sweeps, one wave each, a time
-//   step at a time, with their rows in an LDS ring and each task's block in
-//   the wave's registers; a loader wave and a storer wave move band rows
-//   between the ring and global memory; consecutive groups are ordered by a
-//   row watermark (rows below it are final and stored back), with a bounded
-//   wait.  Each reflector's tau is 2 / v^T v of the v it is applied with, so
+//   independent.  A group of G consecutive sweeps runs in one workgroup, one
+//   wave per sweep, a time step at a time, with their rows in an LDS ring and
+//   each task's block in the wave's registers; a loader wave and a storer wave
+//   move band rows between the ring and global memory; consecutive groups are
+//   ordered by a row watermark (rows below it are final and stored back), with
+//   a bounded wait.  The grid is persistent and about as large as the number
+//   of groups that can be active at once: each workgroup runs every
+//   gridDim.x-th group, so the waiting groups hold no CUs.  Each reflector's tau is 2 / v^T v of the v it is applied with, so
 //   every reflection is orthogonal to rounding.
 // Stage 3, eigenvalues of the tridiagonal: 16-section on the Sturm count
 //   (number of negative pivots of LDL^T(T - xI)), 16 lanes per eigenvalue, from
@@ -1679,8 +1681,8 @@ __device__ __forceinline__ void cstore(T *p, T v)
 }
 
 
-// One workgroup per group of G consecutive sweeps s0 .. s0+G-1: G compute
-// waves, a loader wave and a storer wave.  At time step t compute wave i runs
+// One group of G consecutive sweeps s0 .. s0+G-1 at a time per workgroup: G
+// compute waves, a loader wave and a storer wave.  At time step t compute wave i runs
 // task (s0 + i, t - 2 (s0 + i)); the tasks of one time step touch disjoint rows
 // and depend only on tasks of earlier steps ("(s, k) after (s - 1, k + 1)"), so
 // the G waves run them side by side.  The rows of the group stay in an LDS ring
