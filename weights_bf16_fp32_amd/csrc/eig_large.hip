@@ -2252,21 +2252,68 @@ __device__ __forceinline__ int sturm_below_f32(const float2 *__restrict__ de, in
 // fp32 multisection: 4 eigenvalues per wave, 16 lanes (15 interior points + 1)
 // each, down to 2 ulps of |lambda| or 1/16 ulp of ||T||, below the accuracy of
 // the count itself
+// The starting interval of every fp32 eigenvalue: the fp64 Gershgorin bounds,
+// rounded outwards with a few ulps of slack, and the absolute tolerance.
+struct BisectStartF32 {
+    float a, b, pivmin, atol;
+};
+__device__ __forceinline__ BisectStartF32 bisect_start_f32(const double *__restrict__ bounds)
+{
+    float a = (float)bounds[0], b = (float)bounds[1];
+    const float span = fmaxf(fabsf(a), fabsf(b));
+    a -= 4.f * 1.1920929e-7f * span;
+    b += 4.f * 1.1920929e-7f * span;
+    return {a, b, (float)bounds[3], 0.0625f * 1.1920929e-7f * span};
+}
+
+// A multisection grid shared by all eigenvalues of an fp32 tridiagonal: the
+// Sturm counts at SG_P points evenly inside the starting interval (one lane
+// per point), so that each eigenvalue's search starts from the grid cell that
+// holds it, about three rounds of 17-section later than from the whole
+// interval, for the cost of SG_P counts instead of 16 n.
+constexpr int SG_P = 4096;      // grid points (16^3: a three-level 16-way search)
+constexpr int SG_MIN_N = 2048;  // below this the grid costs more than it saves
+
+__global__ __launch_bounds__(64) void k_sturm_grid_f32(const float2 *__restrict__ de, int n,
+                                                       const double *__restrict__ bounds, float *__restrict__ gx,
+                                                       int *__restrict__ gc)
+{
+    const BisectStartF32 st = bisect_start_f32(bounds);
+    const int p = blockIdx.x * 64 + threadIdx.x;
+    const float x = st.a + (st.b - st.a) * ((float)(p + 1) * (1.f / (float)(SG_P + 1)));
+    gx[p] = x;
+    gc[p] = sturm_below_f32(de, n, x, st.pivmin);
+}
+
 __global__ __launch_bounds__(64) void k_bisect_f32(const float2 *__restrict__ de, int n,
-                                                   const double *__restrict__ bounds, float *__restrict__ w)
+                                                   const double *__restrict__ bounds, const float *__restrict__ gx,
+                                                   const int *__restrict__ gc, float *__restrict__ w)
 {
     const int lane = threadIdx.x;
     const int g = lane >> 4, j = lane & 15;
     const int kidx = blockIdx.x * 4 + g;  // descending index
     const bool live = kidx < n;
     const int target = n - 1 - (live ? kidx : 0);  // ascending index
-    // the fp64 Gershgorin bounds, rounded outwards, with a few ulps of slack
-    float a = (float)bounds[0], b = (float)bounds[1];
-    const float span = fmaxf(fabsf(a), fabsf(b));
-    a -= 4.f * 1.1920929e-7f * span;
-    b += 4.f * 1.1920929e-7f * span;
-    const float pivmin = (float)bounds[3];
-    const float atol = 0.0625f * 1.1920929e-7f * span;
+    const BisectStartF32 st = bisect_start_f32(bounds);
+    float a = st.a, b = st.b;
+    const float pivmin = st.pivmin, atol = st.atol;
+    if (gc != nullptr) {
+        // the number of grid points whose count is <= target (the counts grow
+        // with x): a 16-way search in three levels, the 16 lanes of a group
+        // probing one level's 16 points and counting the hits in their ballot
+        const unsigned long long gmask = 0xFFFFull << (16 * g);
+        int base = 0;
+#pragma unroll
+        for (int sp = SG_P / 16; sp >= 1; sp /= 16) {
+            const int pj = base + (j + 1) * sp - 1;
+            const bool le = pj < SG_P && gc[min(pj, SG_P - 1)] <= target;
+            base += (int)__popcll(__ballot(le) & gmask) * sp;
+        }
+        // the cell's ends bound the search only where their own counts confirm
+        // it: count(a) <= target < count(b)
+        if (base > 0 && gc[base - 1] <= target) a = fmaxf(a, gx[base - 1]);
+        if (base < SG_P && gc[base] > target) b = fminf(b, gx[base]);
+    }
     for (int it = 0; it < 40; ++it) {
         const float width = b - a;
         const bool done = width <= fmaxf(atol, 2.f * 1.1920929e-7f * fmaxf(fabsf(a), fabsf(b)));
@@ -2904,6 +2951,8 @@ struct Bufs {
     int32_t *prog, *cqf;
     double *dd, *ee2, *bounds, *Qd, *Gp, *R1, *Rinv;
     float2 *de32;
+    float *sgx;    // multisection grid of the fp32 eigenvalue search: points
+    int32_t *sgc;  // and their Sturm counts
 };
 
 constexpr int KS_MAX = 8;
@@ -2935,6 +2984,8 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.ee2 = ws.take<double>((size_t)n);
     b.bounds = ws.take<double>(4);
     b.de32 = ws.take<float2>((size_t)n);
+    b.sgx = ws.take<float>((size_t)SG_P);
+    b.sgc = ws.take<int32_t>((size_t)SG_P);
     b.Qd = ws.take<double>((size_t)n * NB);
     b.Gp = ws.take<double>((size_t)cdiv_h(n, CQ_ROWS) * NB * NB);
     b.R1 = ws.take<double>((size_t)NB * NB);
@@ -3248,7 +3299,14 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                        sizeof(T) == 4 ? b.de32 : nullptr);
     LAUNCH_OK();
     if constexpr (sizeof(T) == 4) {
-        hipLaunchKernelGGL(k_bisect_f32, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.de32, (int)n, b.bounds, w);
+        const bool grid = n >= SG_MIN_N;
+        if (grid) {
+            hipLaunchKernelGGL(k_sturm_grid_f32, dim3(SG_P / 64), dim3(64), 0, st, b.de32, (int)n, b.bounds, b.sgx,
+                               b.sgc);
+            LAUNCH_OK();
+        }
+        hipLaunchKernelGGL(k_bisect_f32, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.de32, (int)n, b.bounds,
+                           grid ? b.sgx : nullptr, grid ? b.sgc : nullptr, w);
     } else {
         hipLaunchKernelGGL(k_bisect<T>, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds,
                            4e-16, w);
