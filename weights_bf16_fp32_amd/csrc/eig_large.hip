@@ -2183,9 +2183,30 @@ __device__ __forceinline__ int sturm_below(const double *__restrict__ dd, const 
 }
 
 // 4 eigenvalues per 64-lane workgroup, 16 lanes (15 interior points + 1) each
+// A multisection grid shared by all eigenvalues of a tridiagonal: the Sturm
+// counts at SG_P points evenly inside the starting interval (one lane per
+// point), so that each eigenvalue's search starts from the grid cell that
+// holds it, about three rounds of 17-section later than from the whole
+// interval, for the cost of SG_P counts instead of 16 n.
+constexpr int SG_P = 4096;      // grid points (16^3: a three-level 16-way search)
+constexpr int SG_MIN_N = 2048;  // below this the grid costs more than it saves
+
+// The grid of the fp64 search (k_sturm_grid_f32 below is the fp32 one).
+__global__ __launch_bounds__(64) void k_sturm_grid(const double *__restrict__ dd, const double *__restrict__ ee2,
+                                                   int64_t n, const double *__restrict__ bounds,
+                                                   double *__restrict__ gx, int *__restrict__ gc)
+{
+    const double a = bounds[0], b = bounds[1], pivmin = bounds[2];
+    const int p = blockIdx.x * 64 + threadIdx.x;
+    const double x = a + (b - a) * (double)(p + 1) / (double)(SG_P + 1);
+    gx[p] = x;
+    gc[p] = sturm_below(dd, ee2, n, x, pivmin);
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void k_bisect(const double *__restrict__ dd, const double *__restrict__ ee2,
                                                int64_t n, const double *__restrict__ bounds, double rel_tol,
+                                               const double *__restrict__ gx, const int *__restrict__ gc,
                                                T *__restrict__ w)
 {
     const int lane = threadIdx.x;
@@ -2195,6 +2216,18 @@ __global__ __launch_bounds__(64) void k_bisect(const double *__restrict__ dd, co
     const int64_t target = n - 1 - (live ? kidx : 0);  // ascending index
     double a = bounds[0], b = bounds[1];
     const double pivmin = bounds[2];
+    if (gc != nullptr) {  // the starting cell from the shared grid, as in the fp32 search
+        const unsigned long long gmask = 0xFFFFull << (16 * g);
+        int base = 0;
+#pragma unroll
+        for (int sp = SG_P / 16; sp >= 1; sp /= 16) {
+            const int pj = base + (j + 1) * sp - 1;
+            const bool le = pj < SG_P && gc[min(pj, SG_P - 1)] <= target;
+            base += (int)__popcll(__ballot(le) & gmask) * sp;
+        }
+        if (base > 0 && gc[base - 1] <= target) a = fmax(a, gx[base - 1]);
+        if (base < SG_P && gc[base] > target) b = fmin(b, gx[base]);
+    }
     for (int it = 0; it < 40; ++it) {
         const double width = b - a;
         const bool done = width <= rel_tol * fmax(fabs(a), fabs(b)) + 4.0 * pivmin;
@@ -2266,14 +2299,8 @@ __device__ __forceinline__ BisectStartF32 bisect_start_f32(const double *__restr
     return {a, b, (float)bounds[3], 0.0625f * 1.1920929e-7f * span};
 }
 
-// A multisection grid shared by all eigenvalues of an fp32 tridiagonal: the
-// Sturm counts at SG_P points evenly inside the starting interval (one lane
-// per point), so that each eigenvalue's search starts from the grid cell that
-// holds it, about three rounds of 17-section later than from the whole
-// interval, for the cost of SG_P counts instead of 16 n.
-constexpr int SG_P = 4096;      // grid points (16^3: a three-level 16-way search)
-constexpr int SG_MIN_N = 2048;  // below this the grid costs more than it saves
-
+// The grid of the fp32 search (the multisection grid above, in fp32 from the
+// same starting interval as k_bisect_f32).
 __global__ __launch_bounds__(64) void k_sturm_grid_f32(const float2 *__restrict__ de, int n,
                                                        const double *__restrict__ bounds, float *__restrict__ gx,
                                                        int *__restrict__ gc)
@@ -2951,8 +2978,9 @@ struct Bufs {
     int32_t *prog, *cqf;
     double *dd, *ee2, *bounds, *Qd, *Gp, *R1, *Rinv;
     float2 *de32;
-    float *sgx;    // multisection grid of the fp32 eigenvalue search: points
-    int32_t *sgc;  // and their Sturm counts
+    float *sgx;    // multisection grid of the eigenvalue search: points (fp32
+    double *sgxd;  // or fp64) and their Sturm counts
+    int32_t *sgc;
 };
 
 constexpr int KS_MAX = 8;
@@ -2985,6 +3013,7 @@ size_t layout(int64_t n, char *base, Bufs<T> &b)
     b.bounds = ws.take<double>(4);
     b.de32 = ws.take<float2>((size_t)n);
     b.sgx = ws.take<float>((size_t)SG_P);
+    b.sgxd = ws.take<double>((size_t)SG_P);
     b.sgc = ws.take<int32_t>((size_t)SG_P);
     b.Qd = ws.take<double>((size_t)n * NB);
     b.Gp = ws.take<double>((size_t)cdiv_h(n, CQ_ROWS) * NB * NB);
@@ -3308,8 +3337,14 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         hipLaunchKernelGGL(k_bisect_f32, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.de32, (int)n, b.bounds,
                            grid ? b.sgx : nullptr, grid ? b.sgc : nullptr, w);
     } else {
+        const bool grid = n >= SG_MIN_N;
+        if (grid) {
+            hipLaunchKernelGGL(k_sturm_grid, dim3(SG_P / 64), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds, b.sgxd,
+                               b.sgc);
+            LAUNCH_OK();
+        }
         hipLaunchKernelGGL(k_bisect<T>, dim3((unsigned)cdiv_h(n, 4)), dim3(64), 0, st, b.dd, b.ee2, n, b.bounds,
-                           4e-16, w);
+                           4e-16, grid ? b.sgxd : nullptr, grid ? b.sgc : nullptr, w);
     }
     }
     LAUNCH_OK();
