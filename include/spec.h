@@ -20,9 +20,12 @@
  *     A violation returns SPEC_EINVAL.  Where a pointer is 16-byte aligned and
  *     its leading dimension a multiple of 16 bytes, a faster kernel is chosen
  *     (spec_cov_accumulate); otherwise a general one computes the same result.
- *   - The library holds no state between calls and is thread-safe; calls that
+ *   - The library keeps no data between calls and is thread-safe; calls that
  *     share output or workspace buffers on different streams race, as any
- *     stream-ordered work does.
+ *     stream-ordered work does.  The large eigensolvers create, on first use,
+ *     one helper stream and two events per caller stream and device (kept
+ *     until the process ends, at most 64 such sets) to factor panels beside
+ *     the trailing update.
  *
  * Page citations name the page title and its section:
  *   [RMT]   "Random matrix theory spectral methods: EigenTrack and RMT-KD"
@@ -171,7 +174,8 @@ int spec_eigh_batched(void *stream, const spec_batch_src *src, int64_t batch, in
  * band form (bandwidth 32; tall panels by TSQR with Householder reconstruction;
  * trailing updates on MFMA), bulge chasing from band to tridiagonal in one
  * persistent kernel, then all eigenvalues of the tridiagonal by multisection
- * on Sturm counts (fp64).  t is SPEC_F32 or SPEC_F64; the reductions run in t.
+ * on Sturm counts in t's precision (from a shared 4096-point grid of counts for
+ * n >= 2048).  t is SPEC_F32 or SPEC_F64; the reductions run in t.
  *
  * A: n x n, lower triangle read, DESTROYED (used as the working matrix).
  * w: n values of type t, descending.
