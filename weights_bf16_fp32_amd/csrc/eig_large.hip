@@ -1863,7 +1863,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
     int wmk = s0 + 1;  // rows below wmk are released
     int wpoll = 0;       // loader: the previous group's watermark as last requested
     T taup = 0;          // compute wave: tau of the previous reflector of its sweep
-    int ab = 0;          // abort flag of the previous step
+    T vpk[4] = {0, 0, 0, 0};  // compute wave: that reflector at columns J + 8b
     // the group's last sweep ends last: its last task is the group's last step
     const int t_end = 2 * (s0 + Ge - 1) + ntasks(s0 + Ge - 1);
     for (int t = 2 * s0; t < t_end; ++t) {
@@ -1937,7 +1937,7 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                         else
                             dd[a][b] = WR[I >= J ? rbI[a] + I - J : rbJ[a] + J - I];
                     }
-                    vp[a] = v[J + 8 * a];  // the previous task's reflector at column J + 8a
+                    vp[a] = vpk[a];  // the previous task's reflector at column J + 8a
                 }
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
@@ -2066,11 +2066,16 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     }
                 }
                 taup = tau_k;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) vpk[b] = vc[b];
             }
         }
-        if (ab) return;  // every wave leaves at the same step
+        // a wait that timed out at the previous step set its entry before that
+        // step's barrier; every wave reads it here (it is not written again
+        // before the next barrier) and all leave at the same step, the read
+        // completing with the task's own LDS stores
+        if (abort_flag[(t - 1) & 1]) return;
         __syncthreads();
-        ab = abort_flag[t & 1];  // not written again before the next barrier
         // ---- uniform bookkeeping: the storer has taken [wst, wmk); rows below the
         // first row of every remaining task, and already in the ring, are released.
         // At step t + 1 sweep s0 + i is at task x - 2 i (x = t + 1 - 2 s0): the
