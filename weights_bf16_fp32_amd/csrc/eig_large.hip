@@ -1939,15 +1939,15 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                     }
                     vp[a] = vpk[a];  // the previous task's reflector at column J + 8a
                 }
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) dd[a][b] = rv[a] && cv[b] ? dd[a][b] : (T)0;
-                if (L < NB) {
+                const bool full = L == NB;  // every row of the task inside the band (all but a sweep's last task)
+                if (!full) {
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) o[a][b] = rv[a] ? o[a][b] : (T)0;
+                        for (int b = 0; b < 4; ++b) {
+                            dd[a][b] = rv[a] && cv[b] ? dd[a][b] : (T)0;
+                            o[a][b] = rv[a] ? o[a][b] : (T)0;
+                        }
                 }
                 T x[4];  // the column the reflector annihilates (rows I + 8a; lanes J == 0 for k > 0)
                 if (k == 0) {
@@ -2050,6 +2050,11 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                         for (int a = 0; a < 4; ++a)
                             WR[rv[a] ? rbI[a] + I + 8 * a + 1 : SINK + lane] = (I == 0 && a == 0) ? mu : (T)0;
                     }
+                } else if (full) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) WR[rbI[a] + NB + I - J + 8 * (a - b)] = o[a][b];
                 } else {
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
@@ -2058,11 +2063,20 @@ __global__ __launch_bounds__(64 * (G + 2)) void k_bulge(T *__restrict__ band, in
                 }
                 if (tau_k != 0) {
                     // the lower triangle: entries with a > b, and a == b where I >= J
+                    if (full) {
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
+                        for (int a = 0; a < 4; ++a) {
 #pragma unroll
-                        for (int b = 0; b < a; ++b) WR[rv[a] ? rbI[a] + I - J + 8 * (a - b) : SINK + lane] = dd[a][b];
-                        WR[rv[a] && I >= J ? rbI[a] + I - J : SINK + lane] = dd[a][a];
+                            for (int b = 0; b < a; ++b) WR[rbI[a] + I - J + 8 * (a - b)] = dd[a][b];
+                            WR[I >= J ? rbI[a] + I - J : SINK + lane] = dd[a][a];
+                        }
+                    } else {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                            for (int b = 0; b < a; ++b) WR[rv[a] ? rbI[a] + I - J + 8 * (a - b) : SINK + lane] = dd[a][b];
+                            WR[rv[a] && I >= J ? rbI[a] + I - J : SINK + lane] = dd[a][a];
+                        }
                     }
                 }
                 taup = tau_k;
