@@ -696,26 +696,33 @@ __global__ __launch_bounds__(256) void k_cqr_gram(const Tin *__restrict__ P, int
 // by Gauss-Jordan elimination on [G | I] without pivoting (G is symmetric
 // positive definite): after it the left half is U = D L^T and the right half
 // L^{-1} (G = L D L^T, L unit lower), so R = D^{-1/2} U and R^{-1} =
-// L^{-T} D^{-1/2}.  One thread per entry of the 32 x 64 system, one barrier
-// per column.
+// L^{-T} D^{-1/2}.  Four waves sum the partial Grams (four entries a thread);
+// the 32 elimination steps run in one wave without a barrier: lane l holds
+// column l of the 32 x 64 system in registers, and step k takes its pivot and
+// multipliers from lane k's column by readlane.  A 256-thread workgroup also
+// starts on a CU that other kernels' workgroups partly hold, where the
+// former 1024-thread one (one barrier per column) waited for a free CU.
 // First pass (second == false): R into R1 and R^{-1} into Rinv; the state
 // becomes CQ_BROKE on a failed pivot, else CQ_DONE1 (with Rf = R) when T is
 // fp32 and cond_F(R) is below CQ_ONE_PASS_COND, else CQ_NEED2.  Second pass
 // (only in state CQ_NEED2): Rf = R R1 and R^{-1} into Rinv, state CQ_DONE2, or
 // CQ_BROKE on a failed pivot.
+constexpr int CH_T = 256;  // threads of k_cqr_chol
 template <typename T>
-__global__ __launch_bounds__(1024) void k_cqr_chol(const double *__restrict__ Gpart, int nblk, bool second,
+__global__ __launch_bounds__(CH_T) void k_cqr_chol(const double *__restrict__ Gpart, int nblk, bool second,
                                                    double *__restrict__ R1, double *__restrict__ Rinv,
                                                    T *__restrict__ Rf, int *__restrict__ flag)
 {
     if (second && *flag != CQ_NEED2) return;
     constexpr int L2 = 2 * NB + 1;
-    __shared__ double A[NB * L2], diag0[NB], rs[NB], nr[32], ni[32];
+    constexpr int EPT = NB * NB / CH_T;  // entries per thread
+    __shared__ double A[NB * L2], diag0[NB], rs[NB], nr[CH_T / 64], ni[CH_T / 64];
     __shared__ int bad;
     const int tid = threadIdx.x;
-    {
-        // the sum over the partial Grams: eight independent chains of loads
-        const int p = tid;
+    // the sum over the partial Grams: eight independent chains of loads per entry
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int p = tid + CH_T * q;
         double s8[8] = {};
         int b = 0;
         for (; b + 8 <= nblk; b += 8) {
@@ -729,21 +736,31 @@ __global__ __launch_bounds__(1024) void k_cqr_chol(const double *__restrict__ Gp
         A[i * L2 + NB + j] = i == j ? 1.0 : 0.0;
         if (i == j) diag0[i] = sum;
     }
-    if (tid == 0) bad = 0;
     __syncthreads();
-    for (int k = 0; k < NB; ++k) {
-        const double piv = A[k * L2 + k];
-        if (!(piv > CQ_TOL * diag0[k] && piv <= DBL_MAX)) {  // the same in every thread
-            if (tid == 0) bad = 1;
-            break;
-        }
-        const double inv = 1.0 / piv;
+    if (tid < 64) {
+        const int l = tid;  // column l of [G | I]
+        double a[NB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int p = tid + 1024 * h, i = p >> 6, j = p & 63;
-            if (i > k && j > k) A[i * L2 + j] -= (A[i * L2 + k] * inv) * A[k * L2 + j];
+        for (int i = 0; i < NB; ++i) a[i] = A[i * L2 + l];
+        int failed = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const double piv = readlane_t(a[k], k);  // uniform: every lane takes the same branch
+            if (!(piv > CQ_TOL * diag0[k] && piv <= DBL_MAX)) {
+                failed = 1;
+                break;
+            }
+            const double inv = 1.0 / piv;
+#pragma unroll
+            for (int i = k + 1; i < NB; ++i) {
+                const double mi = readlane_t(a[i], k) * inv;
+                const double upd = a[i] - mi * a[k];
+                a[i] = l > k ? upd : a[i];
+            }
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NB; ++i) A[i * L2 + l] = a[i];
+        if (l == 0) bad = failed;
     }
     __syncthreads();
     if (bad) {
@@ -752,20 +769,31 @@ __global__ __launch_bounds__(1024) void k_cqr_chol(const double *__restrict__ Gp
     }
     if (tid < NB) rs[tid] = 1.0 / sqrt(A[tid * L2 + tid]);
     __syncthreads();
-    const int i = tid / NB, j = tid % NB;
-    const double r = j >= i ? A[i * L2 + j] * rs[i] : 0.0;       // R = D^{-1/2} U
-    const double ri = j >= i ? A[j * L2 + NB + i] * rs[j] : 0.0;  // R^{-1} = L^{-T} D^{-1/2}
-    Rinv[tid] = ri;
+    double r[EPT];
+    double sr = 0.0, si = 0.0;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int p = tid + CH_T * q, i = p / NB, j = p % NB;
+        r[q] = j >= i ? A[i * L2 + j] * rs[i] : 0.0;                 // R = D^{-1/2} U
+        const double ri = j >= i ? A[j * L2 + NB + i] * rs[j] : 0.0;  // R^{-1} = L^{-T} D^{-1/2}
+        Rinv[p] = ri;
+        sr += r[q] * r[q];
+        si += ri * ri;
+    }
     if (second) {
-        double x = 0.0;  // Rf = R R1
-        for (int l = i; l <= j; ++l) x += A[i * L2 + l] * rs[i] * R1[l * NB + j];
-        Rf[tid] = (T)x;
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int p = tid + CH_T * q, i = p / NB, j = p % NB;
+            double x = 0.0;  // Rf = R R1
+            for (int l = i; l <= j; ++l) x += A[i * L2 + l] * rs[i] * R1[l * NB + j];
+            Rf[p] = (T)x;
+        }
         if (tid == 0) *flag = CQ_DONE2;
         return;
     }
-    R1[tid] = r;
-    // cond_F(R): wave sums, then the 16 waves' partials
-    double sr = r * r, si = ri * ri;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) R1[tid + CH_T * q] = r[q];
+    // cond_F(R): wave sums, then the waves' partials
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         sr += __shfl_xor(sr, o);
@@ -777,12 +805,15 @@ __global__ __launch_bounds__(1024) void k_cqr_chol(const double *__restrict__ Gp
     }
     __syncthreads();
     double tr = 0.0, ti = 0.0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < CH_T / 64; ++w) {
         tr += nr[w];
         ti += ni[w];
     }
     const bool one = sizeof(T) == 4 && sqrt(tr * ti) < CQ_ONE_PASS_COND;
-    if (one) Rf[tid] = (T)r;
+    if (one) {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) Rf[tid + CH_T * q] = (T)r[q];
+    }
     if (tid == 0) *flag = one ? CQ_DONE1 : CQ_NEED2;
 }
 
@@ -3169,7 +3200,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                 hipLaunchKernelGGL(k_cqr_gram<T>, dim3(ng), dim3(256), 0, s, (const T *)P, lda, (int)m, b.Gp,
                                    (const int *)nullptr);
                 LAUNCH_OK();
-                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(1024), 0, s, b.Gp, ng, false, b.R1, b.Rinv, b.Rf,
+                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(CH_T), 0, s, b.Gp, ng, false, b.R1, b.Rinv, b.Rf,
                                    b.cqf);
                 LAUNCH_OK();
                 hipLaunchKernelGGL((k_cqr_apply<T, T>), dim3(na), dim3(256), 0, s, (const T *)P, lda, (int)m,
@@ -3178,7 +3209,7 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
                 hipLaunchKernelGGL(k_cqr_gram<double>, dim3(ng), dim3(256), 0, s, (const double *)b.Qd, (int64_t)NB,
                                    (int)m, b.Gp, b.cqf);
                 LAUNCH_OK();
-                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(1024), 0, s, b.Gp, ng, true, b.R1, b.Rinv, b.Rf,
+                hipLaunchKernelGGL(k_cqr_chol<T>, dim3(1), dim3(CH_T), 0, s, b.Gp, ng, true, b.R1, b.Rinv, b.Rf,
                                    b.cqf);
                 LAUNCH_OK();
                 hipLaunchKernelGGL((k_cqr_apply<double, T>), dim3(na), dim3(256), 0, s, (const double *)b.Qd,
