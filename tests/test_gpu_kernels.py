@@ -79,13 +79,17 @@ def test_syrk_bf16_huge_row_stride(spec, ldx):
     del flat, X
 
 
-@pytest.mark.parametrize("n,d,beta", [(300, 5888, 0.0), (97, 6000, 0.0), (64, 6000, 1.0)])
+@pytest.mark.parametrize("n,d,beta", [(300, 5888, 0.0), (97, 6000, 0.0), (64, 6000, 1.0),
+                                      (300, 4096, 0.0), (97, 4000, 0.0), (64, 5632, 1.0), (12288, 4096, 1.0)])
 def test_syrk_bf16_large_d(spec, n, d, beta):
-    """d large enough for the 256 x 256 tile kernel (>= 256 tiles): a ragged d
-    (6000 = 23 full tiles + 112), a sample count that is not a multiple of the
-    32-sample step, and beta = 1 on a random old C; every lower-triangle entry
-    against the oracle within the (n + 2) u bound, the strict upper triangle
-    untouched."""
+    """d large enough for the 256 x 256 tile kernel (at least 128 tiles): a
+    ragged d (6000 = 23 full tiles + 112, 4000 = 15 + 160), fewer tiles than
+    CUs (d = 4096: 136 tiles; 5632: 253), 12288 samples at d = 4096 so that
+    every tile is split three ways along the samples (C scaled by beta first,
+    the partial products added atomically), a sample count that is not a
+    multiple of the 32-sample step, and beta = 1 on a random old C; every
+    lower-triangle entry against the oracle within the (n + 2) u bound, the
+    strict upper triangle untouched."""
     torch = _torch()
     print_case("syrk_bf16_large_d", n=n, d=d, beta=beta)
     rng = np.random.default_rng(n + d)

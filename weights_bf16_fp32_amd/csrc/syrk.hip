@@ -618,18 +618,38 @@ hipError_t launch_syrk(hipStream_t stream, const void *X, int xt, int64_t n, int
         // offsets: 64 * ldx * 2 bytes must stay below the resource limit
         const bool vec = d % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X % 16) == 0 && ldx <= ((int64_t)1 << 24) - 8;
         const int64_t big_tiles = tri_count((d + BG_TILE - 1) / BG_TILE);
-        if (vec && big_tiles >= 256 && ldc < ((int64_t)1 << 21)) {
+        hipDevice_t dev = 0;
+        int cus = 256;
+        if (hipStreamGetDevice(stream, &dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const int round = cus >= 8 ? cus / 8 * 8 : 8;
+        if (vec && big_tiles >= round / 2 && ldc < ((int64_t)1 << 21)) {
             // large d: 256 x 256 tiles in rounds of one workgroup per CU
-            hipDevice_t dev = 0;
-            int cus = 256;
-            if (hipStreamGetDevice(stream, &dev) == hipSuccess)
-                (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            const int round = cus >= 8 ? cus / 8 * 8 : 8;
-            // full rounds as they are; a last round under half full is split along
-            // the samples (up to 4 ways, the partial products added atomically)
-            // so that its workgroups fill the chip
-            const int64_t full = big_tiles / round * round, tail = big_tiles - full;
-            const int splits = tail > 0 && tail <= round / 2 ? (int)std::min<int64_t>(4, round / tail) : 1;
+            int64_t full, tail;
+            int splits = 1;
+            if (big_tiles >= round) {
+                // full rounds as they are; a last round under half full is split along
+                // the samples (up to 4 ways, the partial products added atomically)
+                // so that its workgroups fill the chip
+                full = big_tiles / round * round;
+                tail = big_tiles - full;
+                splits = tail > 0 && tail <= round / 2 ? (int)std::min<int64_t>(4, round / tail) : 1;
+            } else {
+                // fewer tiles than CUs (d from 3848 to 5632 on 256 CUs): every tile split
+                // the same number of ways (up to 8, at least 4096 samples each),
+                // the count whose rounds are fullest
+                full = 0;
+                tail = big_tiles;
+                double best = 0.0;
+                for (int s = 1; s <= 8 && (s == 1 || n / s >= 4096); ++s) {
+                    const int64_t wgs = big_tiles * s, rounds = (wgs + round - 1) / round;
+                    const double fill = (double)wgs / (double)(rounds * round);
+                    if (fill > best + 0.02) {
+                        best = fill;
+                        splits = s;
+                    }
+                }
+            }
             const int64_t main = splits > 1 ? full : big_tiles;
             if (main > 0)
                 hipLaunchKernelGGL(syrk_bf16_big, dim3((unsigned)main), dim3(256), 0, stream, (const uint16_t *)X, n,
