@@ -3033,7 +3033,7 @@ struct Bufs {
     int32_t *sgc;
 };
 
-constexpr int KS_MAX = 8;
+constexpr int KS_MAX = 16;
 
 template <typename T>
 size_t layout(int64_t n, char *base, Bufs<T> &b)
@@ -3293,7 +3293,11 @@ hipError_t run(hipStream_t st, T *A, int64_t n, int64_t lda, T *w, void *ws, int
         T *A22 = A + r0 * lda + r0;
         T *Vc = Vbuf[(c0 / NB) & 1];
         const int nrb = (int)cdiv_h(m, SY_RB);
-        int ks = (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, cdiv_h(512, nrb)));
+        // column chunks per row block: fp32, about three workgroups per CU (the
+        // kernel's occupancy) without a partial round; fp64, about 512 workgroups
+        // and at most 8 chunks
+        int ks = std::is_same<T, float>::value ? (int)std::min<int64_t>(KS_MAX, std::max<int64_t>(1, 768 / nrb))
+                                               : (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv_h(512, nrb)));
         int chunk = (int)(cdiv_h(cdiv_h(m, ks), SY_JB) * SY_JB);
         ks = (int)cdiv_h(m, chunk);
         {
